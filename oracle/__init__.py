@@ -1,0 +1,168 @@
+"""Plain CPU oracle for decode attention over a shared-head KV cache.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package. The product path
+(``transformer_decode_attention_amd``) never imports, loads or calls it, and
+the two share no code: the C source here includes nothing from the HIP
+library, and this module imports nothing from the product package.
+
+The arithmetic lives in ``oracle.c`` (double precision, plain loops). This
+module is ctypes marshalling over numpy arrays only. Element type codes:
+``F32 = 0`` (binary32) and ``BF16 = 1`` (bfloat16 stored as uint16 bits).
+
+Sources, cited by page title and section:
+  [GQA notes] ybb.press "分组查询注意力（GQA）与多查询注意力（MQA）深度实战",
+              §一/§七 (KV bytes), §四/§五 (grouped math), §八 (cache write).
+  [MQA blog]  nanhubrain.csdn.net MQA article §2.2 (append on the sequence axis).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+F32 = 0
+BF16 = 1
+OK = 0
+BAD_LEN = 1
+BAD_SHAPE = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_SRC = os.path.join(_HERE, "oracle.c")
+
+
+def build() -> str:
+    """Compile oracle.c with the host C compiler (gcc) into liboracle.so."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror", "-fPIC",
+           "-shared", "-pthread", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, dp = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_double)
+        L.oracle_append_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32]
+        L.oracle_append_kv.restype = i32
+        L.oracle_decode_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                         i32, ctypes.c_float, vp, vp, i32]
+        L.oracle_decode_attn.restype = i32
+        L.oracle_mha_per_head.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_double, vp]
+        L.oracle_mha_per_head.restype = None
+        L.oracle_partial.argtypes = [vp, vp, vp, i32, ctypes.c_double, i32, i32, dp, dp, vp]
+        L.oracle_partial.restype = None
+        L.oracle_lse_combine.argtypes = [i32, vp, vp, vp, i32, vp]
+        L.oracle_lse_combine.restype = None
+        L.oracle_kv_bytes.argtypes = [i32, i32, ctypes.c_int64, i32, i32]
+        L.oracle_kv_bytes.restype = ctypes.c_uint64
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype in (np.uint16, np.int16):
+        return BF16
+    raise TypeError(f"oracle takes float32 or bfloat16 bits (uint16), got {a.dtype}")
+
+
+def _c(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a)
+
+
+def append_kv(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray,
+              v_new: np.ndarray, seq_lens: np.ndarray) -> int:
+    """In place: row seq_lens[i]-1 of every head of sequence i gets k_new/v_new.
+
+    k_cache, v_cache: [b, g, S, d] (float32 or bf16 bits); k_new, v_new: [b, g, d].
+    Returns the oracle status bits (BAD_LEN if some length is outside [1, S]).
+    """
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    b, g, S, d = k_cache.shape
+    sl = _c(seq_lens.astype(np.int32))
+    return lib().oracle_append_kv(_ptr(k_cache), _ptr(v_cache), _ptr(_c(k_new)),
+                                  _ptr(_c(v_new)), _ptr(sl), b, g, S, d,
+                                  _dtype_code(k_cache))
+
+
+def decode_attn(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                seq_lens: np.ndarray, scale: float, want_alpha: bool = False,
+                nthreads: int = 1):
+    """Plain-definition decode attention in double.
+
+    q: [b, h, d]; k_cache, v_cache: [b, g, S, d]; seq_lens: [b] (attended
+    lengths). Returns (out [b, h, d] float64, alpha [b, h, S] or None, status).
+    """
+    b, h, d = q.shape
+    _, g, S, _ = k_cache.shape
+    dt = _dtype_code(k_cache)
+    assert _dtype_code(q) == dt and _dtype_code(v_cache) == dt
+    out = np.empty((b, h, d), np.float64)
+    alpha = np.empty((b, h, S), np.float64) if want_alpha else None
+    sl = _c(seq_lens.astype(np.int32))
+    rc = lib().oracle_decode_attn(_ptr(_c(q)), _ptr(_c(k_cache)), _ptr(_c(v_cache)),
+                                  _ptr(sl), b, h, g, S, d, dt, ctypes.c_float(scale),
+                                  _ptr(out), _ptr(alpha), int(nthreads))
+    return out, alpha, rc
+
+
+def mha_per_head(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """Textbook MHA for one sequence: q [h, d], K and V [h, L, d] (float64)."""
+    q = _c(q.astype(np.float64))
+    K = _c(K.astype(np.float64))
+    V = _c(V.astype(np.float64))
+    h, L, d = K.shape
+    out = np.empty((h, d), np.float64)
+    lib().oracle_mha_per_head(_ptr(q), _ptr(K), _ptr(V), h, L, d, float(scale), _ptr(out))
+    return out
+
+
+def partial(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, t0: int, t1: int):
+    """Shard [t0, t1) of one query row: returns (m, l, o_unnormalised[d])."""
+    q = _c(q.astype(np.float64))
+    K = _c(K.astype(np.float64))
+    V = _c(V.astype(np.float64))
+    d = q.shape[0]
+    m, l = ctypes.c_double(), ctypes.c_double()
+    o = np.empty(d, np.float64)
+    lib().oracle_partial(_ptr(q), _ptr(K), _ptr(V), d, float(scale), t0, t1,
+                         ctypes.byref(m), ctypes.byref(l), _ptr(o))
+    return m.value, l.value, o
+
+
+def lse_combine(m: np.ndarray, l: np.ndarray, o: np.ndarray) -> np.ndarray:
+    """Combine n shards (m [n], l [n], o [n, d]) into the normalised output [d]."""
+    m = _c(np.asarray(m, np.float64))
+    l = _c(np.asarray(l, np.float64))
+    o = _c(np.asarray(o, np.float64))
+    n, d = o.shape
+    out = np.empty(d, np.float64)
+    lib().oracle_lse_combine(n, _ptr(m), _ptr(l), _ptr(o), d, _ptr(out))
+    return out
+
+
+def kv_bytes(layers: int, g: int, S: int, d: int, dtype_bytes: int) -> int:
+    """2 * layers * g * S * d * dtype_bytes ([GQA notes] §一, §七)."""
+    return int(lib().oracle_kv_bytes(layers, g, S, d, dtype_bytes))
+
+
+def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns (uint16) to float64."""
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -1,0 +1,227 @@
+/*
+ * Plain CPU oracle for decode attention over a shared-head KV cache.
+ * TEST INFRASTRUCTURE ONLY (tests, smoke check, bench CPU baseline); never
+ * linked into or called by the product path. See oracle.h for the sources.
+ *
+ * Every floating-point sum here is a plain left-to-right loop in double.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Read element idx of a buffer of the given type, widened exactly to double. */
+static double elem(const void *base, size_t idx, int dtype) {
+    if (dtype == ORACLE_F32) {
+        float f;
+        memcpy(&f, (const char *)base + 4 * idx, 4);
+        return (double)f;
+    }
+    uint16_t hbits;
+    memcpy(&hbits, (const char *)base + 2 * idx, 2);
+    uint32_t u = (uint32_t)hbits << 16; /* bfloat16 = top half of binary32 */
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static size_t elem_bytes(int dtype) { return dtype == ORACLE_F32 ? 4u : 2u; }
+
+int oracle_append_kv(void *k_cache, void *v_cache, const void *k_new,
+                     const void *v_new, const int32_t *seq_lens, int b, int g,
+                     int S, int d, int dtype) {
+    if (b < 1 || g < 1 || S < 1 || d < 1) return ORACLE_BAD_SHAPE;
+    int rc = ORACLE_OK;
+    size_t eb = elem_bytes(dtype);
+    size_t row = (size_t)d * eb;
+    for (int i = 0; i < b; i++) {
+        int L = seq_lens[i];
+        if (L < 1 || L > S) { /* never truncate or wrap silently */
+            rc |= ORACLE_BAD_LEN;
+            continue;
+        }
+        for (int j = 0; j < g; j++) {
+            size_t dst = (((size_t)i * g + j) * S + (size_t)(L - 1)) * row;
+            size_t src = ((size_t)i * g + j) * row;
+            memcpy((char *)k_cache + dst, (const char *)k_new + src, row);
+            memcpy((char *)v_cache + dst, (const char *)v_new + src, row);
+        }
+    }
+    return rc;
+}
+
+/* ---- decode attention: one (sequence, query head) row ---------------- */
+
+typedef struct {
+    const void *q, *k, *v;
+    const int32_t *seq_lens;
+    int b, h, g, S, d, dtype;
+    double scale;
+    double *out, *alpha;
+    int row_begin, row_end; /* rows are i*h + hq */
+    int flags;
+} decode_job;
+
+static void decode_row(decode_job *J, int row) {
+    int i = row / J->h, hq = row % J->h;
+    int d = J->d, S = J->S;
+    int G = J->h / J->g;      /* query heads per K/V head */
+    int j = hq / G;           /* [GQA notes] §五: j = i // (h/g) */
+    int L = J->seq_lens[i];
+    double *o = J->out + (size_t)row * d;
+    if (L < 1 || L > S) {
+        for (int x = 0; x < d; x++) o[x] = NAN;
+        J->flags |= ORACLE_BAD_LEN;
+        return;
+    }
+    size_t qoff = (size_t)row * d;
+    size_t kvoff = ((size_t)i * J->g + j) * (size_t)S * d;
+
+    double *s = (double *)malloc(sizeof(double) * (size_t)L);
+    /* score_t = (Q_i . K_j,t) * scale */
+    for (int t = 0; t < L; t++) {
+        double dot = 0.0;
+        for (int x = 0; x < d; x++)
+            dot += elem(J->q, qoff + x, J->dtype) *
+                   elem(J->k, kvoff + (size_t)t * d + x, J->dtype);
+        s[t] = J->scale * dot;
+    }
+    /* alpha_t = softmax_t(score); subtracting the max leaves it unchanged */
+    double m = s[0];
+    for (int t = 1; t < L; t++)
+        if (s[t] > m) m = s[t];
+    double Z = 0.0;
+    for (int t = 0; t < L; t++) {
+        s[t] = exp(s[t] - m);
+        Z += s[t];
+    }
+    for (int t = 0; t < L; t++) s[t] /= Z;
+    /* O_i = sum_t alpha_t V_j,t */
+    for (int x = 0; x < d; x++) {
+        double acc = 0.0;
+        for (int t = 0; t < L; t++)
+            acc += s[t] * elem(J->v, kvoff + (size_t)t * d + x, J->dtype);
+        o[x] = acc;
+    }
+    if (J->alpha) {
+        double *a = J->alpha + (size_t)row * S;
+        for (int t = 0; t < S; t++) a[t] = t < L ? s[t] : 0.0;
+    }
+    free(s);
+}
+
+static void *decode_worker(void *arg) {
+    decode_job *J = (decode_job *)arg;
+    for (int r = J->row_begin; r < J->row_end; r++) decode_row(J, r);
+    return NULL;
+}
+
+int oracle_decode_attn(const void *q, const void *k, const void *v,
+                       const int32_t *seq_lens, int b, int h, int g, int S,
+                       int d, int dtype, float scale, double *out,
+                       double *alpha, int nthreads) {
+    if (b < 1 || h < 1 || g < 1 || S < 1 || d < 1 || h % g != 0)
+        return ORACLE_BAD_SHAPE;
+    int rows = b * h;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > rows) nthreads = rows;
+    decode_job *jobs = (decode_job *)calloc((size_t)nthreads, sizeof(decode_job));
+    pthread_t *tid = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    for (int w = 0; w < nthreads; w++) {
+        decode_job J = {q, k, v, seq_lens, b, h, g, S, d, dtype, (double)scale,
+                        out, alpha, (int)((long)rows * w / nthreads),
+                        (int)((long)rows * (w + 1) / nthreads), 0};
+        jobs[w] = J;
+    }
+    for (int w = 1; w < nthreads; w++)
+        pthread_create(&tid[w], NULL, decode_worker, &jobs[w]);
+    decode_worker(&jobs[0]);
+    int rc = ORACLE_OK;
+    for (int w = 0; w < nthreads; w++) {
+        if (w) pthread_join(tid[w], NULL);
+        rc |= jobs[w].flags;
+    }
+    free(jobs);
+    free(tid);
+    return rc;
+}
+
+/* ---- textbook MHA, one K/V per query head ----------------------------- */
+
+void oracle_mha_per_head(const double *q, const double *K, const double *V,
+                         int h, int L, int d, double scale, double *out) {
+    double *logits = (double *)malloc(sizeof(double) * (size_t)L);
+    for (int hd = 0; hd < h; hd++) {
+        const double *qh = q + (size_t)hd * d;
+        const double *Kh = K + (size_t)hd * L * d;
+        const double *Vh = V + (size_t)hd * L * d;
+        double mx = -INFINITY;
+        for (int t = 0; t < L; t++) {
+            double acc = 0.0;
+            for (int x = 0; x < d; x++) acc += qh[x] * Kh[(size_t)t * d + x];
+            logits[t] = acc * scale;
+            mx = fmax(mx, logits[t]);
+        }
+        double den = 0.0;
+        for (int t = 0; t < L; t++) den += exp(logits[t] - mx);
+        for (int x = 0; x < d; x++) {
+            double num = 0.0;
+            for (int t = 0; t < L; t++)
+                num += exp(logits[t] - mx) * Vh[(size_t)t * d + x];
+            out[(size_t)hd * d + x] = num / den;
+        }
+    }
+    free(logits);
+}
+
+/* ---- shards and their log-sum-exp combination ------------------------ */
+
+void oracle_partial(const double *q, const double *K, const double *V, int d,
+                    double scale, int t0, int t1, double *m, double *l,
+                    double *o) {
+    for (int x = 0; x < d; x++) o[x] = 0.0;
+    if (t1 <= t0) {
+        *m = -INFINITY;
+        *l = 0.0;
+        return;
+    }
+    double mx = -INFINITY;
+    for (int t = t0; t < t1; t++) {
+        double s = 0.0;
+        for (int x = 0; x < d; x++) s += q[x] * K[(size_t)t * d + x];
+        mx = fmax(mx, s * scale);
+    }
+    double sum = 0.0;
+    for (int t = t0; t < t1; t++) {
+        double s = 0.0;
+        for (int x = 0; x < d; x++) s += q[x] * K[(size_t)t * d + x];
+        double w = exp(s * scale - mx);
+        sum += w;
+        for (int x = 0; x < d; x++) o[x] += w * V[(size_t)t * d + x];
+    }
+    *m = mx;
+    *l = sum;
+}
+
+void oracle_lse_combine(int n, const double *m, const double *l,
+                        const double *o, int d, double *out) {
+    double M = -INFINITY;
+    for (int s = 0; s < n; s++)
+        if (l[s] > 0.0 && m[s] > M) M = m[s];
+    double den = 0.0;
+    for (int x = 0; x < d; x++) out[x] = 0.0;
+    for (int s = 0; s < n; s++) {
+        if (!(l[s] > 0.0)) continue;
+        double w = exp(m[s] - M);
+        den += w * l[s];
+        for (int x = 0; x < d; x++) out[x] += w * o[(size_t)s * d + x];
+    }
+    for (int x = 0; x < d; x++) out[x] /= den;
+}
+
+uint64_t oracle_kv_bytes(int layers, int g, int64_t S, int d, int dtype_bytes) {
+    return 2ull * (uint64_t)layers * (uint64_t)g * (uint64_t)S * (uint64_t)d *
+           (uint64_t)dtype_bytes;
+}

@@ -1,0 +1,86 @@
+/*
+ * Plain CPU oracle for decode attention over a shared-head KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link,
+ * load or call this code: only the tests, the smoke check and the bench's
+ * CPU-baseline leg use it. It shares no header, table or helper with the HIP
+ * library, and it is written for obviousness, not speed: double precision,
+ * plain loops, no blocking, fusion or reordering beyond what the definitions
+ * state.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [GQA notes]  ybb.press, "分组查询注意力（GQA）与多查询注意力（MQA）深度实战"
+ *               §一 (KV bytes), §四 (GQA grouping), §五 (math form), §七 (h/g),
+ *               §八 (reference implementation: cache write, repeat_interleave).
+ *  [MQA blog]   nanhubrain.csdn.net MQA article, §2.2 (concat of the new K/V on
+ *               the sequence axis).
+ *  [MQA concept] compassingai.com "多查詢注意力", 技術原理 / "KV Cache 結構與
+ *               視訊記憶體佔用對比" (per-layer byte counts).
+ *
+ * Element types: ORACLE_F32 is IEEE binary32; ORACLE_BF16 is bfloat16, i.e.
+ * the upper 16 bits of a binary32 (decoded exactly by a 16-bit shift).
+ *
+ * Layouts (row-major, last index fastest):
+ *   q        [b][h][d]
+ *   k, v     [b][g][S][d]     (S = capacity; rows >= seq_lens[i] are unused)
+ *   k/v_new  [b][g][d]
+ *   out      [b][h][d]        (double)
+ *   alpha    [b][h][S]        (double, optional attention weights)
+ */
+#ifndef ORACLE_DECODE_ATTN_H
+#define ORACLE_DECODE_ATTN_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+/* Return bits. ORACLE_BAD_LEN: some seq_lens[i] outside [1, S]; those rows
+ * are left alone by append and set to NaN by decode. ORACLE_BAD_SHAPE: h not a
+ * multiple of g, or a size < 1; nothing is written. */
+enum { ORACLE_OK = 0, ORACLE_BAD_LEN = 1, ORACLE_BAD_SHAPE = 2 };
+
+/* Cache append: row seq_lens[i]-1 of every K/V head j of sequence i receives
+ * k_new[i][j][:] / v_new[i][j][:], byte for byte. [MQA blog] §2.2;
+ * [GQA notes] §八 (cache_k[:, start:start+T] = k). */
+int oracle_append_kv(void *k_cache, void *v_cache, const void *k_new,
+                     const void *v_new, const int32_t *seq_lens, int b, int g,
+                     int S, int d, int dtype);
+
+/* Decode attention, the plain definition ([GQA notes] §四, §五):
+ *   j = hq / (h/g);  score_t = scale * q[i,hq,:].k[i,j,t,:]   for t < L_i
+ *   alpha_t = softmax_t(score);  out[i,hq,:] = sum_t alpha_t v[i,j,t,:]
+ * nthreads >= 1 splits the (i, hq) rows across POSIX threads; each row is
+ * computed by the same loop either way. */
+int oracle_decode_attn(const void *q, const void *k, const void *v,
+                       const int32_t *seq_lens, int b, int h, int g, int S,
+                       int d, int dtype, float scale, double *out,
+                       double *alpha, int nthreads);
+
+/* Textbook multi-head attention for one sequence, one K/V head per query
+ * head (no sharing): q [h][d], K and V [h][L][d], all double.
+ * [GQA notes] §二: O_i = softmax(Q_i K_i^T / sqrt(d_h)) V_i. */
+void oracle_mha_per_head(const double *q, const double *K, const double *V,
+                         int h, int L, int d, double scale, double *out);
+
+/* One shard [t0, t1) of one query row: m = max score, l = sum exp(s - m),
+ * o[:] = sum exp(s - m) v[t,:] (unnormalised). q [d], K and V [L][d] double. */
+void oracle_partial(const double *q, const double *K, const double *V, int d,
+                    double scale, int t0, int t1, double *m, double *l,
+                    double *o);
+
+/* Log-sum-exp combine of n shards (m[s], l[s], o[s][d]) into out[d]:
+ * M = max m_s, out = sum_s e^(m_s-M) o_s / sum_s e^(m_s-M) l_s.
+ * Shards with l == 0 (empty) are skipped. */
+void oracle_lse_combine(int n, const double *m, const double *l,
+                        const double *o, int d, double *out);
+
+/* KV-cache bytes, [GQA notes] §一 and §七: 2 * layers * g * S * d * bytes. */
+uint64_t oracle_kv_bytes(int layers, int g, int64_t S, int d, int dtype_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,120 @@
+"""Seeded synthetic workloads for decode attention over a shared-head KV cache.
+
+Input generation only: shapes, seeds and value distributions. No step of the
+method is computed here; both the HIP path (through the tests and the bench)
+and the oracle consume what these generators produce.
+
+The configurations mirror the workload shapes on the pages (cited by title and
+section):
+  tiny-mqa   b=1, h=8, g=1, d=64, 128 cached + 1 appended, fp32
+             (freeguideonline "多查询注意力 MQA", §5: d_model=512, h=8, d_k=64)
+  mqa-1k     b=8, h=32, g=1, d=128, L=1024, bf16
+             (nanhubrain.csdn.net MQA article §2.1/§4.3: 32 heads, 1024 positions, batch 8)
+  gqa-70b    b=64, h=64, g=8, d=128, ragged L ~ U[1024, 4096], capacity 4096, bf16
+             (ybb.press GQA/MQA notes §一 and §七: LLaMA-2-70B-like h=64, g=8,
+             4K context, 64 concurrent sequences)
+  gqa-70b-full  the same with every L = 4096
+  mqa-32k    b=4, h=32, g=1, d=128, L=32768, bf16 (same notes §一: context of 32K)
+  sweep-g{1,8,32}  32 layers of b=16, h=32, d=128, L=8192, bf16, g in {1, 8, 32}
+             (compassingai "多查詢注意力", 技術原理: d_model=4096, h=32, seq 8192, 32 layers)
+
+Values: q, K, V, k_new, v_new are i.i.d. N(0, 1), drawn in fp32 with torch's
+seeded generator and rounded (round-to-nearest-even) to the cache dtype. The
+whole cache capacity is filled; the step's append then overwrites row L_i-1.
+seq_lens holds the post-append lengths. Seeds: base = 1000 * k for the k-th
+configuration; streams q +1, k_cache +2, v_cache +3, k_new +4, v_new +5,
+seq_lens +6 (a CPU generator), layer l adds 100 * l.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    b: int
+    h: int
+    g: int
+    d: int
+    S: int                 # cache capacity (rows per K/V head)
+    dtype: torch.dtype
+    seed: int
+    L: int | None = None   # fixed attended length; None -> ragged U[L_lo, L_hi]
+    L_lo: int = 0
+    L_hi: int = 0
+    layers: int = 1
+
+    @property
+    def G(self) -> int:
+        return self.h // self.g
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == torch.bfloat16 else 4
+
+
+WORKLOADS = {
+    "tiny-mqa": Workload("tiny-mqa", b=1, h=8, g=1, d=64, S=129, dtype=torch.float32,
+                         seed=1000, L=129),
+    "mqa-1k": Workload("mqa-1k", b=8, h=32, g=1, d=128, S=1024, dtype=torch.bfloat16,
+                       seed=2000, L=1024),
+    "gqa-70b": Workload("gqa-70b", b=64, h=64, g=8, d=128, S=4096, dtype=torch.bfloat16,
+                        seed=3000, L=None, L_lo=1024, L_hi=4096),
+    "gqa-70b-full": Workload("gqa-70b-full", b=64, h=64, g=8, d=128, S=4096,
+                             dtype=torch.bfloat16, seed=3000, L=4096),
+    "mqa-32k": Workload("mqa-32k", b=4, h=32, g=1, d=128, S=32768, dtype=torch.bfloat16,
+                        seed=4000, L=32768),
+    "sweep-g1": Workload("sweep-g1", b=16, h=32, g=1, d=128, S=8192, dtype=torch.bfloat16,
+                         seed=5000, L=8192, layers=32),
+    "sweep-g8": Workload("sweep-g8", b=16, h=32, g=8, d=128, S=8192, dtype=torch.bfloat16,
+                         seed=5000, L=8192, layers=32),
+    "sweep-g32": Workload("sweep-g32", b=16, h=32, g=32, d=128, S=8192,
+                          dtype=torch.bfloat16, seed=5000, L=8192, layers=32),
+}
+
+
+def shrink(w: Workload, **kw) -> Workload:
+    """A copy of a workload with some fields replaced (smaller parity cases)."""
+    return replace(w, **kw)
+
+
+def seq_lens(w: Workload) -> torch.Tensor:
+    """Post-append lengths [b] (int32, CPU)."""
+    if w.L is not None:
+        return torch.full((w.b,), w.L, dtype=torch.int32)
+    gen = torch.Generator().manual_seed(w.seed + 6)
+    return torch.randint(w.L_lo, w.L_hi + 1, (w.b,), generator=gen, dtype=torch.int32)
+
+
+def _normal(shape, seed: int, dtype: torch.dtype, device) -> torch.Tensor:
+    gen = torch.Generator(device=device).manual_seed(seed)
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    return x.to(dtype)
+
+
+def make_step(w: Workload, device="cpu", layer: int = 0) -> dict:
+    """One layer's inputs for one decode step.
+
+    Returns q [b,h,d], k_cache/v_cache [b,g,S,d] (every row filled), k_new and
+    v_new [b,g,d], seq_lens int32 [b] (post-append), all on `device`.
+    """
+    base = w.seed + 100 * layer
+    return {
+        "q": _normal((w.b, w.h, w.d), base + 1, w.dtype, device),
+        "k_cache": _normal((w.b, w.g, w.S, w.d), base + 2, w.dtype, device),
+        "v_cache": _normal((w.b, w.g, w.S, w.d), base + 3, w.dtype, device),
+        "k_new": _normal((w.b, w.g, w.d), base + 4, w.dtype, device),
+        "v_new": _normal((w.b, w.g, w.d), base + 5, w.dtype, device),
+        "seq_lens": seq_lens(w).to(device),
+    }
+
+
+def to_oracle(t: torch.Tensor):
+    """Host numpy view the oracle takes: float32 as is, bfloat16 as uint16 bits."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view("uint16")
+    return t.numpy()
