@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Decode-attention bench on one MI355X.
+
+One step = the whole hot path for one batch: mqa_append_kv then
+mqa_decode_attn for every layer of the workload, inputs resident in HBM.
+Default workload: gqa-70b (b=64, h=64, g=8, d=128, bf16 cache of capacity
+4096, ragged lengths U[1024, 4096], seeded N(0,1) values).
+
+Prints one JSON line:
+  value        achieved HBM GB/s of the step (algorithmic bytes / step time)
+  ms_per_step  step time (µs/step = 1000 * ms_per_step, also in "us_per_step")
+  roofline     for the dominant kernel launch (mqa_decode_attn), timed with
+               HIP events on the stream the kernels run on
+  cpu_baseline the CPU oracle, timed on the host's cores on a bounded sample
+
+Algorithmic bytes per decode launch and layer: the K and V rows attended
+(sum_i 2*g*L_i*d*B) + q (b*h*d*B) + out (b*h*d*4). The append adds
+2*b*g*d*B read and the same written. Bytes the method avoids (the h/g times
+larger MHA cache) are not counted.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+SRC = os.path.join(ROOT, "transformer_decode_attention_amd", "csrc", "mqa_decode.hip")
+
+
+def source_sha() -> str:
+    return hashlib.sha256(open(SRC, "rb").read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gqa-70b")
+    ap.add_argument("--split-chunk", type=int, default=0)
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="distinct cache copies rotated across steps (0: enough for >= 2 GiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="wall-clock budget of the CPU-oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build runs on a single MI355X and has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import transformer_decode_attention_amd as mqa
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.WORKLOADS[args.workload]
+    layers = w.layers
+    cache_bytes = 2 * w.b * w.g * w.S * w.d * w.elem_bytes  # K + V capacity, one layer
+    if layers > 1:
+        reps = layers  # every layer has its own cache
+    else:
+        reps = args.replicas or max(2, math.ceil((2 << 30) / cache_bytes))
+    print(f"[bench] workload {w.name}: b={w.b} h={w.h} g={w.g} d={w.d} S={w.S} layers={layers} "
+          f"copies={reps} ({reps * cache_bytes / 2**30:.2f} GiB of cache)", file=sys.stderr, flush=True)
+
+    steps_in = [W.make_step(w, dev, layer=r) for r in range(reps)]
+    lens = steps_in[0]["seq_lens"].cpu().numpy().astype(np.int64)
+    chunk = mqa.decode_resolve_chunk(w.b, w.h, w.g, w.S, w.d, w.dtype, args.split_chunk)
+    ws = torch.empty(mqa.decode_workspace_bytes(w.b, w.h, w.g, w.S, w.d, w.dtype, args.split_chunk),
+                     dtype=torch.uint8, device=dev)
+    outs = [torch.empty((w.b, w.h, w.d), dtype=torch.float32, device=dev) for _ in range(reps)]
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    B = w.elem_bytes
+    kv_read = int(sum(2 * w.g * int(L) * w.d * B for L in lens))
+    dec_bytes = kv_read + w.b * w.h * w.d * B + w.b * w.h * w.d * 4
+    app_bytes = 2 * (2 * w.b * w.g * w.d * B)
+    per_layer = dec_bytes + app_bytes
+    step_bytes = per_layer * layers
+    flops_per_step = 4 * w.h * int(lens.sum()) * w.d * layers
+
+    def layer_call(r, ev=None):
+        t = steps_in[r]
+        mqa.append_kv(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], t["seq_lens"], err_flags=err)
+        if ev is not None:
+            ev[0].record()
+        mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], out=outs[r],
+                        workspace=ws, split_chunk=args.split_chunk, err_flags=err)
+        if ev is not None:
+            ev[1].record()
+
+    def step(k, evs=None):
+        if layers > 1:
+            for l in range(layers):
+                layer_call(l, None if evs is None else evs[l])
+        else:
+            layer_call(k % reps, None if evs is None else evs[0])
+
+    # warmup
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, "device reported an error during warmup"
+
+    # timed region: the step alone
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for k in range(args.steps):
+        step(k)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+
+    # timed region again, with HIP events around every decode launch (same stream)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(layers)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        step(k, ev[k])
+    torch.cuda.synchronize()
+    dec_ms = [a.elapsed_time(b) for evk in ev for (a, b) in evk]
+    dec_ms_avg = float(np.mean(dec_ms))
+    assert int(err.item()) == 0, "device reported an error"
+
+    if args.copy_probe:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = dec_bytes / (dec_ms_avg * 1e-3) / 1e9
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", f"decode_{w.name}_traffic.json")
+    if os.path.exists(tf):
+        rec = json.load(open(tf))
+        if rec.get("source_sha") == source_sha() and rec.get("split_chunk", 0) == args.split_chunk:
+            traffic = rec.get("bytes_per_launch")
+
+    result = {
+        "metric": "decode-attn µs/step + achieved HBM GB/s (% peak), bf16 b=64 h=64 g=8 ctx 4096",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_step": round(ms_per_step * 1e3, 3),
+        "pct_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic: seeded N(0,1) q/K/V in HBM, no trained weights",
+        "config": {"workload": w.name, "b": w.b, "h": w.h, "g": w.g, "d_h": w.d, "capacity": w.S,
+                   "seq_lens": "fixed %d" % w.L if w.L else f"U[{w.L_lo},{w.L_hi}] (sum {int(lens.sum())})",
+                   "layers": layers, "split_chunk": chunk, "cache_copies_rotated": reps,
+                   "accumulate": "fp32", "out": "fp32"},
+        "algorithmic_bytes_per_step": step_bytes,
+        "flops_per_step": flops_per_step,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "mqa_decode_attn (partition + combine kernels)",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": dec_bytes,
+            "us_per_launch": round(dec_ms_avg * 1e3, 3),
+        },
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, steps_in[0], lens, per_layer, layers, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s):
+    """The oracle (plain double loops) on the host cores, one layer's step."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    nthreads = max(1, min(16, os.cpu_count() or 1))
+    args = [W.to_oracle(t["q"]), W.to_oracle(t["k_cache"]), W.to_oracle(t["v_cache"])]
+    scale = float(np.float32(1.0 / math.sqrt(w.d)))
+    lens32 = lens.astype(np.int32)
+    # bounded sample: the first sequences of the batch, sized to the budget
+    # from a one-sequence probe
+    t0 = time.perf_counter()
+    oracle.decode_attn(args[0][:1].copy(), args[1][:1].copy(), args[2][:1].copy(), lens32[:1],
+                       scale, nthreads=nthreads)
+    one = max(time.perf_counter() - t0, 1e-4) / max(int(lens32[0]), 1)  # s per position
+    nb = 1
+    while nb < w.b and one * int(lens32[:nb + 1].sum()) * 1.0 <= budget_s:
+        nb += 1
+    sub = [a[:nb].copy() for a in args]
+    t0 = time.perf_counter()
+    oracle.decode_attn(sub[0], sub[1], sub[2], lens32[:nb], scale, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    B = w.elem_bytes
+    sample_bytes = int(sum(2 * w.g * int(L) * w.d * B for L in lens32[:nb])) + nb * w.h * w.d * (B + 4)
+    gbs = sample_bytes / dt / 1e9
+    return {
+        "value": round(gbs, 4),
+        "unit": "GB/s",
+        "cores": nthreads,
+        "kind": "oracle",
+        "sample": f"decode attention of the first {nb} of {w.b} sequences of one layer "
+                  f"({int(lens32[:nb].sum())} positions), {dt:.2f} s wall",
+        "est_ms_per_step": round(1e3 * (per_layer_bytes * layers) / (gbs * 1e9), 3),
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

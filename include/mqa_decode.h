@@ -1,0 +1,137 @@
+/*
+ * mqa_decode.h - C ABI of the MI355X (gfx950) decode-attention library
+ * libmqa_decode.so: one autoregressive decode step over a KV cache in which
+ * h query heads share g K/V heads (g = 1: multi-query, 1 < g < h: grouped-
+ * query, g = h: multi-head attention).
+ *
+ * Sources, cited by page title and section:
+ *  [GQA notes]   ybb.press, "分组查询注意力（GQA）与多查询注意力（MQA）深度实战":
+ *                §一 and §七 (KV-cache bytes and the h/g ratio), §四 (g groups,
+ *                g divides h), §五 (head-to-group map j = i // (h/g), score,
+ *                softmax, weighted sum), §八 (preallocated cache of capacity
+ *                max_seq written at the current position), §十 (pitfalls:
+ *                divisibility, ragged batches).
+ *  [MQA blog]    nanhubrain.csdn.net MQA article: §2.2 (the new K/V is
+ *                concatenated onto the cache along the sequence axis), §4.3
+ *                (capacity overflow must not truncate silently).
+ *  [MQA concept] compassingai.com "多查詢注意力", 技術原理 (per-layer bytes).
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are contiguous, row-major, last index fastest, in device memory
+ *    owned by the caller. The library allocates nothing, keeps no global
+ *    state and never synchronises: work is enqueued on `stream` (a
+ *    hipStream_t; NULL is the default stream) and completes in stream order.
+ *  - Element type `dt` applies to q, k_cache, v_cache, k_new and v_new.
+ *    MQA_BF16 is bfloat16 (upper 16 bits of a binary32). Outputs are fp32.
+ *  - d (head dimension) is 64 or 128. Every tensor pointer must be 16-byte
+ *    aligned (the kernels use 128-bit loads).
+ *  - seq_lens[b] (device, int32) holds, for each sequence, the number of
+ *    positions attended INCLUDING the token appended this step; the append
+ *    writes cache row seq_lens[i]-1.
+ *  - Host-detectable argument errors return a status before anything is
+ *    enqueued. A HIP launch failure returns MQA_ERR_HIP.
+ *  - Device-detectable errors never truncate silently: a sequence whose
+ *    seq_lens[i] is outside [1, S] is skipped by the append, gets NaN in every
+ *    element of out[i,:,:] from the decode, and both OR MQA_DEVERR_SEQLEN into
+ *    *err_flags when err_flags is non-NULL (a device int32 the caller clears).
+ */
+#ifndef MQA_DECODE_H
+#define MQA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MQA_OK = 0,
+    MQA_ERR_NULL = 1,        /* a required pointer is NULL */
+    MQA_ERR_SHAPE = 2,       /* a size < 1, or h not a multiple of g */
+    MQA_ERR_UNSUPPORTED = 3, /* d not 64/128, unknown dtype, bad split_chunk */
+    MQA_ERR_ALIGN = 4,       /* a tensor pointer not 16-byte aligned */
+    MQA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+    MQA_ERR_HIP = 6          /* the HIP runtime reported a launch error */
+} mqa_status;
+
+typedef enum { MQA_F32 = 0, MQA_BF16 = 1 } mqa_dtype;
+
+/* Bit ORed into *err_flags by the kernels: some seq_lens[i] outside [1, S]. */
+#define MQA_DEVERR_SEQLEN 1
+
+/*
+ * Append this step's K/V rows to the cache, bit-exactly.
+ * [MQA blog] §2.2 (concat on the sequence axis); [GQA notes] §八 (cache
+ * written at the current position of a preallocated max_seq buffer).
+ *
+ *   k_cache, v_cache : [b][g][S][d] of dt, updated in place
+ *   k_new, v_new     : [b][g][d]    of dt
+ *   seq_lens         : [b] int32 device, post-append lengths
+ * For every i < b with 1 <= seq_lens[i] <= S and every j < g:
+ *   k_cache[i][j][seq_lens[i]-1][:] = k_new[i][j][:]   (same for v)
+ * No other byte of the caches is written.
+ */
+mqa_status mqa_append_kv(void *k_cache, void *v_cache, const void *k_new,
+                         const void *v_new, const int32_t *seq_lens, int b,
+                         int g, int S, int d, mqa_dtype dt, int32_t *err_flags,
+                         hipStream_t stream);
+
+/*
+ * Bytes of device workspace mqa_decode_attn needs for these sizes and this
+ * split_chunk (0 = automatic). Returns 0 if the arguments are invalid.
+ */
+size_t mqa_decode_workspace_bytes(int b, int h, int g, int S, int d,
+                                  mqa_dtype dt, int split_chunk);
+
+/*
+ * The sequence-split length (positions per partition) mqa_decode_attn uses
+ * for these sizes: split_chunk itself when non-zero, else the automatic
+ * choice. Returns -1 if the arguments are invalid.
+ */
+int mqa_decode_resolve_chunk(int b, int h, int g, int S, int d, mqa_dtype dt,
+                             int split_chunk);
+
+/*
+ * Decode attention for one step. [GQA notes] §四/§五: for query head hq of
+ * sequence i, with G = h/g and j = hq / G,
+ *   score_t = scale * q[i][hq][:] . k_cache[i][j][t][:],   0 <= t < seq_lens[i]
+ *   out[i][hq][:] = sum_t softmax_t(score)_t * v_cache[i][j][t][:]
+ * Cache rows t >= seq_lens[i] are never read into the result (they may hold
+ * anything, NaN included).
+ *
+ *   q                : [b][h][d] of dt
+ *   k_cache, v_cache : [b][g][S][d] of dt (read only)
+ *   seq_lens         : [b] int32 device
+ *   scale            : score scale, normally 1/sqrt(d)
+ *   out              : [b][h][d] fp32, fully overwritten
+ *   workspace        : >= mqa_decode_workspace_bytes(...) bytes of device
+ *                      memory, 16-byte aligned; holds per-partition partial
+ *                      results; contents on entry are ignored
+ *   split_chunk      : positions per partition, a multiple of 64, or 0 for
+ *                      the automatic choice
+ * The sequence is cut into partitions of split_chunk positions; each keeps
+ * a running max and sum (online softmax) and a log-sum-exp combine merges
+ * them. Concurrent calls must not share a workspace.
+ */
+mqa_status mqa_decode_attn(const void *q, const void *k_cache,
+                           const void *v_cache, const int32_t *seq_lens, int b,
+                           int h, int g, int S, int d, mqa_dtype dt,
+                           float scale, float *out, void *workspace,
+                           size_t workspace_bytes, int split_chunk,
+                           int32_t *err_flags, hipStream_t stream);
+
+/* Static text for a status code (never NULL). */
+const char *mqa_status_string(mqa_status s);
+
+/*
+ * KV-cache bytes of `layers` layers, [GQA notes] §一/§七 and [MQA concept]
+ * 技術原理: 2 * layers * g * S * d * dtype_bytes (the factor 2 is K and V).
+ */
+uint64_t mqa_kv_bytes(int layers, int g, int64_t S, int d, int dtype_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MQA_DECODE_H */

@@ -1,0 +1,134 @@
+"""The C ABI of libmqa_decode.so, checked without a GPU.
+
+Loads the library, checks that it exports every function include/mqa_decode.h
+declares, and exercises the host-side argument checks, which return before
+anything is enqueued (no HIP call is made on these paths). No kernel runs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_decode_attention_amd as mqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mqa_decode.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mqa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(mqa.EXPORTS)
+    lib = mqa.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    for s in range(7):
+        assert mqa.status_string(s)
+    assert mqa.status_string(0) == "ok"
+    assert "unknown" in mqa.status_string(99)
+
+
+def test_kv_bytes_formula():
+    # 2 * layers * g * S * d * bytes; the h/g shrink at h=32 (compassingai 技術原理)
+    assert mqa.kv_bytes(1, 32, 8192, 128, 2) == 134217728
+    assert mqa.kv_bytes(32, 1, 8192, 128, 2) == 134217728
+    assert mqa.kv_bytes(80, 64, 4096, 128, 2) == 10737418240
+    assert mqa.kv_bytes(1, 32, 8192, 128, 2) // mqa.kv_bytes(1, 1, 8192, 128, 2) == 32
+
+
+def test_chunk_resolution_and_workspace():
+    # explicit chunk is kept; automatic chunk is a multiple of 64 within [256, S rounded up]
+    assert mqa.decode_resolve_chunk(64, 64, 8, 4096, 128, mqa.BF16, 512) == 512
+    for (b, h, g, S) in [(64, 64, 8, 4096), (4, 32, 1, 32768), (1, 8, 1, 129), (16, 32, 32, 8192)]:
+        c = mqa.decode_resolve_chunk(b, h, g, S, 128, mqa.BF16, 0)
+        assert c % 64 == 0 and 64 <= c <= (S + 63) // 64 * 64
+        nsplit = -(-S // c)
+        ws = mqa.decode_workspace_bytes(b, h, g, S, 128, mqa.BF16, 0)
+        assert ws >= b * h * nsplit * (128 + 2) * 4
+    # invalid arguments: -1 / 0
+    assert mqa.decode_resolve_chunk(1, 6, 4, 10, 64, mqa.F32, 0) == -1     # h % g
+    assert mqa.decode_resolve_chunk(1, 8, 1, 10, 96, mqa.F32, 0) == -1     # d
+    assert mqa.decode_resolve_chunk(1, 8, 1, 10, 64, mqa.F32, 100) == -1   # chunk not /64
+    assert mqa.decode_workspace_bytes(0, 8, 1, 10, 64, mqa.F32, 0) == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)      # 16-byte aligned, never dereferenced: rejected first
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def decode(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, b=2, h=8, g=2, S=64, d=128, dt=mqa.BF16,
+             scale=0.088, out=FAKE, ws=FAKE, ws_bytes=0, chunk=0)
+    a.update(kw)
+    return mqa.lib().mqa_decode_attn(a["q"], a["k"], a["v"], a["lens"], a["b"], a["h"], a["g"],
+                                     a["S"], a["d"], a["dt"], ctypes.c_float(a["scale"]), a["out"],
+                                     a["ws"], a["ws_bytes"], a["chunk"], None, None)
+
+
+def append(**kw):
+    a = dict(k=FAKE, v=FAKE, kn=FAKE, vn=FAKE, lens=FAKE, b=2, g=2, S=64, d=128, dt=mqa.BF16)
+    a.update(kw)
+    return mqa.lib().mqa_append_kv(a["k"], a["v"], a["kn"], a["vn"], a["lens"], a["b"], a["g"],
+                                   a["S"], a["d"], a["dt"], None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), mqa.ERR_NULL),
+    (dict(lens=None), mqa.ERR_NULL),
+    (dict(out=None), mqa.ERR_NULL),
+    (dict(h=6, g=4), mqa.ERR_SHAPE),           # h not a multiple of g
+    (dict(b=0), mqa.ERR_SHAPE),
+    (dict(S=0), mqa.ERR_SHAPE),
+    (dict(d=96), mqa.ERR_UNSUPPORTED),
+    (dict(dt=7), mqa.ERR_UNSUPPORTED),
+    (dict(chunk=100), mqa.ERR_UNSUPPORTED),
+    (dict(chunk=-64), mqa.ERR_UNSUPPORTED),
+    (dict(k=MISALIGNED), mqa.ERR_ALIGN),
+    (dict(out=MISALIGNED), mqa.ERR_ALIGN),
+    (dict(ws=None, ws_bytes=1 << 30), mqa.ERR_WORKSPACE),
+    (dict(ws_bytes=16), mqa.ERR_WORKSPACE),
+])
+def test_decode_rejects_bad_arguments_before_launch(kw, status):
+    assert decode(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), mqa.ERR_NULL),
+    (dict(lens=None), mqa.ERR_NULL),
+    (dict(g=0), mqa.ERR_SHAPE),
+    (dict(d=32), mqa.ERR_UNSUPPORTED),
+    (dict(vn=MISALIGNED), mqa.ERR_ALIGN),
+])
+def test_append_rejects_bad_arguments_before_launch(kw, status):
+    assert append(**kw) == status
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 8, 64)
+    k = torch.zeros(1, 1, 16, 64)
+    with pytest.raises(ValueError):
+        mqa.decode_attn(q, k, k, torch.ones(1, dtype=torch.int32))
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The package imports nothing from oracle/ and names no oracle symbol."""
+    pkg = os.path.join(ROOT, "transformer_decode_attention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "oracle_" not in text and "liboracle" not in text, f

@@ -1,0 +1,246 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Every case: seeded synthetic inputs on the GPU, one step through
+mqa_append_kv + mqa_decode_attn, the exact bytes read back, the oracle run on
+them, and an element-by-element comparison.
+
+Tolerance (attention; fp32 accumulate, bf16 or fp32 inputs): for every output
+element, |gpu - ref| <= 2e-3 and |gpu - ref| / max(|ref|, rms(ref row)) <= 2e-3,
+where the row is out[i, hq, :]. The append must be bit-exact.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_decode_attention_amd as mqa
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+RTOL_ROW = 2e-3
+NTHREADS = min(16, os.cpu_count() or 1)
+DEV = "cuda:0"
+
+
+def compare(out_gpu: torch.Tensor, ref: np.ndarray, what: str = "") -> dict:
+    got = out_gpu.detach().cpu().double().numpy()
+    assert got.shape == ref.shape
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    rms = np.sqrt((ref ** 2).mean(axis=-1, keepdims=True))
+    rel = err / np.maximum(np.abs(ref), rms)
+    stats = {"max_abs": float(err.max()), "max_rel_row": float(rel.max())}
+    assert stats["max_abs"] <= ATOL and stats["max_rel_row"] <= RTOL_ROW, f"{what}: {stats}"
+    return stats
+
+
+def run_step(t: dict, split_chunk: int = 0, scale: float | None = None):
+    """append + decode on the device; returns (out, err_flags)."""
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    mqa.append_kv(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], t["seq_lens"], err_flags=err)
+    out = mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], scale=scale,
+                          split_chunk=split_chunk, err_flags=err)
+    torch.cuda.synchronize()
+    return out, err
+
+
+def oracle_ref(t: dict, scale: float | None = None):
+    d = t["q"].shape[-1]
+    s = np.float32(1.0 / math.sqrt(d)) if scale is None else np.float32(scale)
+    ref, _, rc = oracle.decode_attn(W.to_oracle(t["q"]), W.to_oracle(t["k_cache"]),
+                                    W.to_oracle(t["v_cache"]), t["seq_lens"].cpu().numpy(),
+                                    float(s), nthreads=NTHREADS)
+    return ref, rc
+
+
+def check_case(w: W.Workload, split_chunk: int = 0, layer: int = 0, q_scale: float = 1.0):
+    print(f"[case] {w.name} b={w.b} h={w.h} g={w.g} d={w.d} S={w.S} chunk={split_chunk}", flush=True)
+    t = W.make_step(w, DEV, layer)
+    if q_scale != 1.0:
+        t["q"] = (t["q"].float() * q_scale).to(w.dtype)
+    kc0, vc0 = W.to_oracle(t["k_cache"]), W.to_oracle(t["v_cache"])
+    out, err = run_step(t, split_chunk)
+    assert int(err.item()) == 0
+    # append: bit-exact against the oracle's append on the pre-step bytes
+    assert oracle.append_kv(kc0, vc0, W.to_oracle(t["k_new"]), W.to_oracle(t["v_new"]),
+                            t["seq_lens"].cpu().numpy()) == oracle.OK
+    assert W.to_oracle(t["k_cache"]).tobytes() == kc0.tobytes()
+    assert W.to_oracle(t["v_cache"]).tobytes() == vc0.tobytes()
+    ref, rc = oracle_ref(t)
+    assert rc == oracle.OK
+    return compare(out, ref, w.name)
+
+
+# ---------------------------------------------------------------------------
+# the configured workloads at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny-mqa", "mqa-1k", "gqa-70b", "gqa-70b-full", "mqa-32k"])
+def test_workload_full_size(name):
+    print(check_case(W.WORKLOADS[name]), flush=True)
+
+
+@pytest.mark.parametrize("name", ["sweep-g1", "sweep-g8", "sweep-g32"])
+@pytest.mark.parametrize("layer", [0, 31])
+def test_sweep_layers(name, layer):
+    print(check_case(W.WORKLOADS[name], layer=layer), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# shapes, ragged lengths, partitions
+# ---------------------------------------------------------------------------
+
+SHAPES = [
+    # (h, g, d, dtype): every head grouping the kernels distinguish
+    (8, 1, 64, torch.float32), (8, 8, 64, torch.float32), (16, 4, 128, torch.float32),
+    (12, 4, 128, torch.bfloat16), (40, 2, 128, torch.bfloat16), (64, 8, 64, torch.bfloat16),
+    (32, 1, 128, torch.bfloat16), (32, 16, 128, torch.bfloat16), (6, 6, 128, torch.bfloat16),
+    (24, 8, 64, torch.float32), (48, 3, 128, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("h,g,d,dtype", SHAPES)
+def test_shapes_with_ragged_lengths(h, g, d, dtype):
+    # lengths around tile (64) and partition (256) edges, 1 and the capacity
+    lens = [1, 2, 63, 64, 65, 255, 256, 257, 300, 511, 513, 700]
+    w = W.Workload(f"shape-h{h}-g{g}-d{d}", b=len(lens), h=h, g=g, d=d, S=700, dtype=dtype,
+                   seed=77)
+    t = W.make_step(w, DEV)
+    t["seq_lens"] = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    for chunk in (256, 0):
+        out, err = run_step(t, chunk)
+        assert int(err.item()) == 0
+        ref, _ = oracle_ref(t)
+        compare(out, ref, f"{w.name} chunk={chunk}")
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 512, 4096])
+def test_partition_length_sweep(chunk):
+    """Every partition length gives the oracle's result (pins the LSE combine)."""
+    w = W.shrink(W.WORKLOADS["gqa-70b"], b=8)
+    check_case(w, split_chunk=chunk)
+
+
+def test_peaky_softmax():
+    """q scaled by 8: near one-hot weights, large score range."""
+    check_case(W.shrink(W.WORKLOADS["gqa-70b"], b=8), q_scale=8.0)
+    check_case(W.shrink(W.WORKLOADS["mqa-32k"], b=1, S=4096, L=4096), q_scale=8.0)
+
+
+def test_scale_argument_is_used():
+    w = W.shrink(W.WORKLOADS["mqa-1k"], b=2)
+    t = W.make_step(w, DEV)
+    out, _ = run_step(t, scale=0.3)
+    ref, _ = oracle_ref(t, scale=0.3)
+    compare(out, ref, "scale=0.3")
+
+
+# ---------------------------------------------------------------------------
+# invariants on the device
+# ---------------------------------------------------------------------------
+
+def test_rows_past_length_are_never_read():
+    """NaN in every cache row >= L: output finite and bitwise equal to a zero-tail run."""
+    w = W.Workload("tail", b=6, h=16, g=2, d=128, S=1024, dtype=torch.bfloat16, seed=91)
+    t = W.make_step(w, DEV)
+    t["seq_lens"] = torch.tensor([1, 64, 65, 500, 1000, 1024], dtype=torch.int32, device=DEV)
+    run_step(t)  # append first so row L-1 holds k_new
+    lens = t["seq_lens"].cpu().tolist()
+    kz, vz = t["k_cache"].clone(), t["v_cache"].clone()
+    kn, vn = t["k_cache"].clone(), t["v_cache"].clone()
+    for i, L in enumerate(lens):
+        kz[i, :, L:] = 0
+        vz[i, :, L:] = 0
+        kn[i, :, L:] = float("nan")
+        vn[i, :, L:] = float("nan")
+    oz = mqa.decode_attn(t["q"], kz, vz, t["seq_lens"])
+    on = mqa.decode_attn(t["q"], kn, vn, t["seq_lens"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(on).all()
+    assert torch.equal(oz, on)
+
+
+def test_deterministic():
+    w = W.shrink(W.WORKLOADS["gqa-70b"], b=16)
+    t = W.make_step(w, DEV)
+    a = mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"])
+    b = mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_constant_v_and_zero_k():
+    """V = 1 gives 1; K = 0 gives the mean of the first L rows of V."""
+    w = W.Workload("closed", b=4, h=32, g=4, d=128, S=2048, dtype=torch.bfloat16, seed=5)
+    t = W.make_step(w, DEV)
+    t["seq_lens"] = torch.tensor([1, 100, 1500, 2048], dtype=torch.int32, device=DEV)
+    ones = torch.ones_like(t["v_cache"])
+    out = mqa.decode_attn(t["q"], t["k_cache"], ones, t["seq_lens"])
+    torch.cuda.synchronize()
+    assert (out - 1).abs().max().item() <= 1e-6
+    zk = torch.zeros_like(t["k_cache"])
+    out = mqa.decode_attn(t["q"], zk, t["v_cache"], t["seq_lens"])
+    torch.cuda.synchronize()
+    for i, L in enumerate(t["seq_lens"].cpu().tolist()):
+        mean = t["v_cache"][i, :, :L].double().mean(dim=1)          # [g, d]
+        ref = mean.repeat_interleave(w.G, dim=0).cpu().numpy()     # [h, d]
+        got = out[i].double().cpu().numpy()
+        assert np.abs(got - ref).max() <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# append and device-side errors
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_append_bit_exact_with_sentinels(dtype):
+    """Whole-buffer comparison, with sentinel bands before and after each cache."""
+    b, g, S, d = 5, 3, 37, 128
+    n = b * g * S * d
+    band = 4096
+    w = W.Workload("append", b=b, h=g, g=g, d=d, S=S, dtype=dtype, seed=11)
+    t = W.make_step(w, DEV)
+    t["seq_lens"] = torch.tensor([1, 37, 20, 2, 36], dtype=torch.int32, device=DEV)
+    bufs = []
+    for name in ("k_cache", "v_cache"):
+        buf = torch.full((n + 2 * band,), 7.0, dtype=dtype, device=DEV)
+        buf[band:band + n] = t[name].reshape(-1)
+        bufs.append(buf)
+    kview = bufs[0][band:band + n].view(b, g, S, d)
+    vview = bufs[1][band:band + n].view(b, g, S, d)
+    k0, v0 = W.to_oracle(kview), W.to_oracle(vview)
+    before = [W.to_oracle(x) for x in bufs]
+    mqa.append_kv(kview, vview, t["k_new"], t["v_new"], t["seq_lens"])
+    torch.cuda.synchronize()
+    assert oracle.append_kv(k0, v0, W.to_oracle(t["k_new"]), W.to_oracle(t["v_new"]),
+                            t["seq_lens"].cpu().numpy()) == oracle.OK
+    after = [W.to_oracle(x) for x in bufs]
+    for x0, x1, exp in zip(before, after, (k0, v0)):
+        assert x1[:band].tobytes() == x0[:band].tobytes()
+        assert x1[band + n:].tobytes() == x0[band + n:].tobytes()
+        assert x1[band:band + n].tobytes() == exp.reshape(-1).tobytes()
+
+
+def test_out_of_range_lengths_flag_and_nan():
+    w = W.Workload("badlen", b=4, h=8, g=2, d=64, S=100, dtype=torch.bfloat16, seed=3)
+    t = W.make_step(w, DEV)
+    t["seq_lens"] = torch.tensor([50, 0, 101, 100], dtype=torch.int32, device=DEV)
+    kc0 = t["k_cache"].clone()
+    out, err = run_step(t)
+    assert int(err.item()) & mqa.DEVERR_SEQLEN
+    assert torch.isnan(out[1]).all() and torch.isnan(out[2]).all()
+    assert torch.isfinite(out[0]).all() and torch.isfinite(out[3]).all()
+    # append skipped the bad sequences entirely
+    assert torch.equal(t["k_cache"][1], kc0[1]) and torch.equal(t["k_cache"][2], kc0[2])
+    ref, rc = oracle_ref(t)
+    assert rc == oracle.BAD_LEN
+    got = out.double().cpu().numpy()
+    for i in (0, 3):
+        assert np.abs(got[i] - ref[i]).max() <= ATOL

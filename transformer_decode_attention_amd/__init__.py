@@ -1,0 +1,183 @@
+"""Decode attention over a shared-head KV cache on MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libmqa_decode.so`` (declared in
+``include/mqa_decode.h``). Every step of the path runs in the library's HIP
+kernels; this module only checks tensor metadata and marshals pointers,
+sizes and the current HIP stream. PyTorch supplies device memory and streams.
+
+Entry points (same names as the C ABI, without the ``mqa_`` prefix):
+  append_kv(k_cache, v_cache, k_new, v_new, seq_lens, err_flags=None)
+  decode_attn(q, k_cache, v_cache, seq_lens, scale=None, out=None,
+              workspace=None, split_chunk=0, err_flags=None) -> out
+  decode_workspace_bytes(b, h, g, S, d, dtype, split_chunk=0)
+  decode_resolve_chunk(b, h, g, S, d, dtype, split_chunk=0)
+  kv_bytes(layers, g, S, d, dtype_bytes)
+  status_string(status)
+
+There is no CPU fallback: if the library is missing, the first call raises
+ImportError. Build it with ``python -m transformer_decode_attention_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "append_kv", "decode_attn", "decode_workspace_bytes", "decode_resolve_chunk",
+    "kv_bytes", "status_string", "MQAError", "LIB_PATH", "DEVERR_SEQLEN",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa_decode.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)
+F32, BF16 = 0, 1
+DEVERR_SEQLEN = 1
+
+EXPORTS = (
+    "mqa_append_kv", "mqa_decode_workspace_bytes", "mqa_decode_resolve_chunk",
+    "mqa_decode_attn", "mqa_status_string", "mqa_kv_bytes",
+)
+
+
+class MQAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m transformer_decode_attention_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    L.mqa_append_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    L.mqa_append_kv.restype = i32
+    L.mqa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.mqa_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.mqa_decode_resolve_chunk.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.mqa_decode_resolve_chunk.restype = i32
+    L.mqa_decode_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_float,
+                                  vp, vp, ctypes.c_size_t, i32, vp, vp]
+    L.mqa_decode_attn.restype = i32
+    L.mqa_status_string.argtypes = [i32]
+    L.mqa_status_string.restype = ctypes.c_char_p
+    L.mqa_kv_bytes.argtypes = [i32, i32, i64, i32, i32]
+    L.mqa_kv_bytes.restype = ctypes.c_uint64
+    return L
+
+
+_lib_handle: ctypes.CDLL | None = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmqa_decode.so (loaded on first use; raises if missing)."""
+    global _lib_handle
+    if _lib_handle is None:
+        _lib_handle = _load()
+    return _lib_handle
+
+
+def status_string(status: int) -> str:
+    return lib().mqa_status_string(int(status)).decode()
+
+
+def kv_bytes(layers: int, g: int, S: int, d: int, dtype_bytes: int) -> int:
+    return int(lib().mqa_kv_bytes(layers, g, S, d, dtype_bytes))
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return BF16
+    if dt == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {dt} (bfloat16 or float32)")
+
+
+def decode_workspace_bytes(b, h, g, S, d, dtype, split_chunk: int = 0) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(lib().mqa_decode_workspace_bytes(b, h, g, S, d, code, split_chunk))
+
+
+def decode_resolve_chunk(b, h, g, S, d, dtype, split_chunk: int = 0) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(lib().mqa_decode_resolve_chunk(b, h, g, S, d, code, split_chunk))
+
+
+def _ptr(t) -> ctypes.c_void_p | None:
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def append_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+              v_new: torch.Tensor, seq_lens: torch.Tensor,
+              err_flags: torch.Tensor | None = None) -> None:
+    """Write k_new/v_new [b,g,d] into row seq_lens[i]-1 of k_cache/v_cache [b,g,S,d]."""
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new),
+                 ("v_new", v_new), ("seq_lens", seq_lens)):
+        _dev(t, n)
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must both be [b, g, S, d]")
+    b, g, S, d = k_cache.shape
+    if k_new.shape != (b, g, d) or v_new.shape != (b, g, d):
+        raise ValueError("k_new and v_new must be [b, g, d]")
+    if not (k_cache.dtype == v_cache.dtype == k_new.dtype == v_new.dtype):
+        raise TypeError("caches and new rows must share one dtype")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (b,):
+        raise ValueError("seq_lens must be int32 [b]")
+    st = lib().mqa_append_kv(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+                            _ptr(seq_lens), b, g, S, d, _dtype_code(k_cache.dtype),
+                            _ptr(err_flags), _stream(k_cache.device))
+    if st != OK:
+        raise MQAError(st, "mqa_append_kv")
+
+
+def decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                seq_lens: torch.Tensor, scale: float | None = None,
+                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                split_chunk: int = 0, err_flags: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention: q [b,h,d], caches [b,g,S,d], seq_lens int32 [b] -> out fp32 [b,h,d]."""
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
+        _dev(t, n)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [b, h, d]; k_cache and v_cache [b, g, S, d]")
+    b, h, d = q.shape
+    bb, g, S, dd = k_cache.shape
+    if bb != b or dd != d:
+        raise ValueError("q and the caches disagree on b or d")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q and the caches must share one dtype")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (b,):
+        raise ValueError("seq_lens must be int32 [b]")
+    code = _dtype_code(q.dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((b, h, d), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or out.shape != (b, h, d):
+        raise ValueError("out must be float32 [b, h, d]")
+    _dev(out, "out")
+    need = decode_workspace_bytes(b, h, g, S, d, code, split_chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    st = lib().mqa_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), b, h, g,
+                              S, d, code, ctypes.c_float(scale), _ptr(out), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), split_chunk,
+                              _ptr(err_flags), _stream(q.device))
+    if st != OK:
+        raise MQAError(st, "mqa_decode_attn")
+    return out
