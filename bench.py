@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa-70b")
     ap.add_argument("--split-chunk", type=int, default=0)
+    ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto",
+                    help="partition kernel (auto: mqa_decode_attn's own choice)")
     ap.add_argument("--replicas", type=int, default=0,
                     help="distinct cache copies rotated across steps (0: enough for >= 2 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
@@ -87,11 +89,11 @@ def main() -> int:
     steps_in = [W.make_step(w, dev, layer=r) for r in range(reps)]
     lens = steps_in[0]["seq_lens"].cpu().numpy().astype(np.int64)
     chunk = mqa.decode_resolve_chunk(w.b, w.h, w.g, w.S, w.d, w.dtype, args.split_chunk)
-    ws = torch.empty(mqa.decode_workspace_bytes(w.b, w.h, w.g, w.S, w.d, w.dtype, args.split_chunk),
-                     dtype=torch.uint8, device=dev)
+    ws = mqa.decode_workspace(w.b, w.h, w.g, w.S, w.d, w.dtype, dev, args.split_chunk)
     outs = [torch.empty((w.b, w.h, w.d), dtype=torch.float32, device=dev) for _ in range(reps)]
     err = torch.zeros(1, dtype=torch.int32, device=dev)
 
+    kernel = {"auto": mqa.KERNEL_AUTO, "valu": mqa.KERNEL_VALU, "mfma": mqa.KERNEL_MFMA}[args.kernel]
     B = w.elem_bytes
     kv_read = int(sum(2 * w.g * int(L) * w.d * B for L in lens))
     dec_bytes = kv_read + w.b * w.h * w.d * B + w.b * w.h * w.d * 4
@@ -106,7 +108,7 @@ def main() -> int:
         if ev is not None:
             ev[0].record()
         mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], out=outs[r],
-                        workspace=ws, split_chunk=args.split_chunk, err_flags=err)
+                        workspace=ws, split_chunk=args.split_chunk, err_flags=err, kernel=kernel)
         if ev is not None:
             ev[1].record()
 

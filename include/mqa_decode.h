@@ -58,8 +58,20 @@ typedef enum {
 
 typedef enum { MQA_F32 = 0, MQA_BF16 = 1 } mqa_dtype;
 
+/* Which partition kernel computes the attention (see mqa_decode_attn_kernel). */
+typedef enum {
+    MQA_KERNEL_AUTO = 0, /* bf16: matrix cores; fp32: vector ALUs */
+    MQA_KERNEL_VALU = 1, /* vector-ALU kernel (bf16 dot2 / fp32 FMA), any dtype */
+    MQA_KERNEL_MFMA = 2  /* matrix-core kernel, bf16 only */
+} mqa_kernel;
+
 /* Bit ORed into *err_flags by the kernels: some seq_lens[i] outside [1, S]. */
 #define MQA_DEVERR_SEQLEN 1
+
+/* Leading bytes of every decode workspace that hold arrival counters (see
+ * mqa_decode_attn): zero before the workspace's first use, zero again after
+ * every call that completes. */
+#define MQA_WORKSPACE_COUNTER_BYTES (256u * 1024u)
 
 /*
  * Append this step's K/V rows to the cache, bit-exactly.
@@ -107,13 +119,21 @@ int mqa_decode_resolve_chunk(int b, int h, int g, int S, int d, mqa_dtype dt,
  *   scale            : score scale, normally 1/sqrt(d)
  *   out              : [b][h][d] fp32, fully overwritten
  *   workspace        : >= mqa_decode_workspace_bytes(...) bytes of device
- *                      memory, 16-byte aligned; holds per-partition partial
- *                      results; contents on entry are ignored
+ *                      memory, 16-byte aligned. Its first
+ *                      MQA_WORKSPACE_COUNTER_BYTES bytes are arrival counters
+ *                      of the partitions: they must be zero before the
+ *                      workspace is first used (e.g. hipMemset once at
+ *                      allocation), and every call leaves them zero when it
+ *                      completes. The rest holds partial results; its
+ *                      contents on entry are ignored.
  *   split_chunk      : positions per partition, a multiple of 64, or 0 for
  *                      the automatic choice
- * The sequence is cut into partitions of split_chunk positions; each keeps
- * a running max and sum (online softmax) and a log-sum-exp combine merges
- * them. Concurrent calls must not share a workspace.
+ * The sequence is cut into partitions; each keeps a running max and sum
+ * (online softmax) and a log-sum-exp merge combines them. With split_chunk
+ * > 0 the partitions are split_chunk positions long; with 0 the library
+ * chooses, and for bf16 batches of many (sequence, K/V head) pairs it splits
+ * the total work evenly over the compute units whatever the lengths.
+ * Concurrent calls must not share a workspace.
  */
 mqa_status mqa_decode_attn(const void *q, const void *k_cache,
                            const void *v_cache, const int32_t *seq_lens, int b,
@@ -121,6 +141,20 @@ mqa_status mqa_decode_attn(const void *q, const void *k_cache,
                            float scale, float *out, void *workspace,
                            size_t workspace_bytes, int split_chunk,
                            int32_t *err_flags, hipStream_t stream);
+
+/*
+ * mqa_decode_attn with an explicit choice of partition kernel; same arguments,
+ * layouts, workspace and results (to floating-point rounding). MQA_KERNEL_MFMA
+ * with dt = MQA_F32 returns MQA_ERR_UNSUPPORTED. mqa_decode_attn is this call
+ * with MQA_KERNEL_AUTO.
+ */
+mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache,
+                                  const void *v_cache, const int32_t *seq_lens,
+                                  int b, int h, int g, int S, int d,
+                                  mqa_dtype dt, float scale, float *out,
+                                  void *workspace, size_t workspace_bytes,
+                                  int split_chunk, int32_t *err_flags,
+                                  mqa_kernel kernel, hipStream_t stream);
 
 /* Static text for a status code (never NULL). */
 const char *mqa_status_string(mqa_status s);

@@ -41,12 +41,13 @@ def compare(out_gpu: torch.Tensor, ref: np.ndarray, what: str = "") -> dict:
     return stats
 
 
-def run_step(t: dict, split_chunk: int = 0, scale: float | None = None):
+def run_step(t: dict, split_chunk: int = 0, scale: float | None = None,
+             kernel: int = mqa.KERNEL_AUTO):
     """append + decode on the device; returns (out, err_flags)."""
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     mqa.append_kv(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], t["seq_lens"], err_flags=err)
     out = mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], scale=scale,
-                          split_chunk=split_chunk, err_flags=err)
+                          split_chunk=split_chunk, err_flags=err, kernel=kernel)
     torch.cuda.synchronize()
     return out, err
 
@@ -60,13 +61,15 @@ def oracle_ref(t: dict, scale: float | None = None):
     return ref, rc
 
 
-def check_case(w: W.Workload, split_chunk: int = 0, layer: int = 0, q_scale: float = 1.0):
-    print(f"[case] {w.name} b={w.b} h={w.h} g={w.g} d={w.d} S={w.S} chunk={split_chunk}", flush=True)
+def check_case(w: W.Workload, split_chunk: int = 0, layer: int = 0, q_scale: float = 1.0,
+               kernel: int = mqa.KERNEL_AUTO):
+    print(f"[case] {w.name} b={w.b} h={w.h} g={w.g} d={w.d} S={w.S} chunk={split_chunk} "
+          f"kernel={kernel}", flush=True)
     t = W.make_step(w, DEV, layer)
     if q_scale != 1.0:
         t["q"] = (t["q"].float() * q_scale).to(w.dtype)
     kc0, vc0 = W.to_oracle(t["k_cache"]), W.to_oracle(t["v_cache"])
-    out, err = run_step(t, split_chunk)
+    out, err = run_step(t, split_chunk, kernel=kernel)
     assert int(err.item()) == 0
     # append: bit-exact against the oracle's append on the pre-step bytes
     assert oracle.append_kv(kc0, vc0, W.to_oracle(t["k_new"]), W.to_oracle(t["v_new"]),
@@ -106,32 +109,53 @@ SHAPES = [
 ]
 
 
+KERNELS = [mqa.KERNEL_AUTO, mqa.KERNEL_VALU]
+
+
+@pytest.mark.parametrize("kernel", KERNELS, ids=["auto", "valu"])
 @pytest.mark.parametrize("h,g,d,dtype", SHAPES)
-def test_shapes_with_ragged_lengths(h, g, d, dtype):
+def test_shapes_with_ragged_lengths(h, g, d, dtype, kernel):
     # lengths around tile (64) and partition (256) edges, 1 and the capacity
     lens = [1, 2, 63, 64, 65, 255, 256, 257, 300, 511, 513, 700]
     w = W.Workload(f"shape-h{h}-g{g}-d{d}", b=len(lens), h=h, g=g, d=d, S=700, dtype=dtype,
                    seed=77)
     t = W.make_step(w, DEV)
     t["seq_lens"] = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    if kernel == mqa.KERNEL_VALU and dtype == torch.float32:
+        pytest.skip("fp32 always runs the vector-ALU kernel (covered by 'auto')")
     for chunk in (256, 0):
-        out, err = run_step(t, chunk)
+        out, err = run_step(t, chunk, kernel=kernel)
         assert int(err.item()) == 0
         ref, _ = oracle_ref(t)
         compare(out, ref, f"{w.name} chunk={chunk}")
 
 
+@pytest.mark.parametrize("kernel", KERNELS, ids=["auto", "valu"])
 @pytest.mark.parametrize("chunk", [64, 128, 512, 4096])
-def test_partition_length_sweep(chunk):
+def test_partition_length_sweep(chunk, kernel):
     """Every partition length gives the oracle's result (pins the LSE combine)."""
     w = W.shrink(W.WORKLOADS["gqa-70b"], b=8)
-    check_case(w, split_chunk=chunk)
+    check_case(w, split_chunk=chunk, kernel=kernel)
 
 
-def test_peaky_softmax():
-    """q scaled by 8: near one-hot weights, large score range."""
-    check_case(W.shrink(W.WORKLOADS["gqa-70b"], b=8), q_scale=8.0)
-    check_case(W.shrink(W.WORKLOADS["mqa-32k"], b=1, S=4096, L=4096), q_scale=8.0)
+@pytest.mark.parametrize("name", ["gqa-70b", "mqa-32k"])
+def test_vector_alu_kernel_full_size(name):
+    """The vector-ALU kernel on bf16 workloads (the automatic choice there is MFMA)."""
+    print(check_case(W.WORKLOADS[name], kernel=mqa.KERNEL_VALU), flush=True)
+
+
+def test_mfma_kernel_rejects_fp32():
+    w = W.Workload("f32", b=1, h=8, g=1, d=64, S=64, dtype=torch.float32, seed=1)
+    t = W.make_step(w, DEV)
+    with pytest.raises(mqa.MQAError):
+        mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], kernel=mqa.KERNEL_MFMA)
+
+
+@pytest.mark.parametrize("kernel", KERNELS, ids=["auto", "valu"])
+def test_peaky_softmax(kernel):
+    """q scaled by 8: near one-hot weights, large score range (many rescales)."""
+    check_case(W.shrink(W.WORKLOADS["gqa-70b"], b=8), q_scale=8.0, kernel=kernel)
+    check_case(W.shrink(W.WORKLOADS["mqa-32k"], b=1, S=4096, L=4096), q_scale=8.0, kernel=kernel)
 
 
 def test_scale_argument_is_used():
@@ -244,3 +268,81 @@ def test_out_of_range_lengths_flag_and_nan():
     got = out.double().cpu().numpy()
     for i in (0, 3):
         assert np.abs(got[i] - ref[i]).max() <= ATOL
+
+
+# ---------------------------------------------------------------------------
+# balanced schedule (bf16, automatic partitioning): unit boundaries cut by
+# work-group ranges in every way
+# ---------------------------------------------------------------------------
+
+def _check_lens(w: W.Workload, lens, split_chunk=0, kernel=mqa.KERNEL_AUTO):
+    t = W.make_step(w, DEV)
+    t["seq_lens"] = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out, err = run_step(t, split_chunk, kernel=kernel)
+    assert int(err.item()) == 0
+    ref, _ = oracle_ref(t)
+    return compare(out, ref, w.name)
+
+
+def test_many_short_sequences():
+    """Units far smaller than a work-group's range (many units per range)."""
+    gen = torch.Generator().manual_seed(8)
+    lens = torch.randint(1, 101, (1000,), generator=gen).tolist()
+    w = W.Workload("short", b=1000, h=16, g=2, d=128, S=100, dtype=torch.bfloat16, seed=21)
+    _check_lens(w, lens)
+
+
+def test_one_long_sequence_many_pieces():
+    """One long unit among 255 tiny ones: cut into hundreds of pieces."""
+    lens = [1 + (k * 7) % 50 for k in range(255)] + [8192]
+    w = W.Workload("long", b=256, h=16, g=1, d=128, S=8192, dtype=torch.bfloat16, seed=22)
+    _check_lens(w, lens)
+
+
+@pytest.mark.parametrize("h,g,d,b", [(64, 2, 128, 128), (32, 1, 64, 256), (64, 1, 128, 256),
+                                     (128, 2, 128, 128)])
+def test_head_blocks(h, g, d, b):
+    """G = 32 / 64 (several 16-head blocks per work-group) and G = 64 across two groups."""
+    gen = torch.Generator().manual_seed(h + g + b)
+    lens = torch.randint(1, 301, (b,), generator=gen).tolist()
+    w = W.Workload(f"hb-h{h}-g{g}", b=b, h=h, g=g, d=d, S=300, dtype=torch.bfloat16, seed=23)
+    _check_lens(w, lens)
+
+
+@pytest.mark.parametrize("h,g,d", [(64, 1, 128), (32, 1, 64), (128, 2, 128)])
+def test_few_units_many_heads(h, g, d):
+    """Few (sequence, K/V head) units with 32-64 heads each: fixed partitions."""
+    w = W.Workload(f"few-h{h}-g{g}", b=3, h=h, g=g, d=d, S=3000, dtype=torch.bfloat16, seed=25)
+    _check_lens(w, [3000, 1, 1777])
+
+
+def test_large_batch_uses_fixed_partitions():
+    """More sequences than the balanced schedule takes: the fixed partitions serve it."""
+    gen = torch.Generator().manual_seed(9)
+    lens = torch.randint(1, 41, (1100,), generator=gen).tolist()
+    w = W.Workload("b1100", b=1100, h=8, g=1, d=64, S=40, dtype=torch.bfloat16, seed=24)
+    _check_lens(w, lens)
+
+
+def test_workspace_reused_across_shapes_and_kernels():
+    """One workspace for many calls of different shapes and paths: the arrival
+    counters come back to zero after every call, partials never collide."""
+    big = mqa.decode_workspace(256, 64, 8, 4096, 128, torch.bfloat16, DEV)
+    cases = [
+        (W.Workload("r1", b=64, h=64, g=8, d=128, S=2048, dtype=torch.bfloat16, seed=31), 0, mqa.KERNEL_AUTO),
+        (W.Workload("r2", b=256, h=16, g=2, d=64, S=700, dtype=torch.bfloat16, seed=32), 0, mqa.KERNEL_AUTO),
+        (W.Workload("r3", b=8, h=32, g=1, d=128, S=3000, dtype=torch.bfloat16, seed=33), 512, mqa.KERNEL_AUTO),
+        (W.Workload("r4", b=64, h=64, g=8, d=128, S=2048, dtype=torch.bfloat16, seed=34), 0, mqa.KERNEL_VALU),
+    ]
+    for rep in range(2):
+        for w, chunk, kernel in cases:
+            gen = torch.Generator().manual_seed(rep * 100 + w.seed)
+            t = W.make_step(w, DEV)
+            t["seq_lens"] = torch.randint(1, w.S + 1, (w.b,), generator=gen, dtype=torch.int32).to(DEV)
+            out = mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], workspace=big,
+                                  split_chunk=chunk, kernel=kernel)
+            torch.cuda.synchronize()
+            ref, _ = oracle_ref(t)
+            compare(out, ref, f"{w.name} rep {rep}")
+    counters = big[:mqa.WORKSPACE_COUNTER_BYTES]
+    assert int(counters.count_nonzero().item()) == 0

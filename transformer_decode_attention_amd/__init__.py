@@ -10,6 +10,7 @@ Entry points (same names as the C ABI, without the ``mqa_`` prefix):
   decode_attn(q, k_cache, v_cache, seq_lens, scale=None, out=None,
               workspace=None, split_chunk=0, err_flags=None) -> out
   decode_workspace_bytes(b, h, g, S, d, dtype, split_chunk=0)
+  decode_workspace(b, h, g, S, d, dtype, device, split_chunk=0) -> zeroed uint8 tensor
   decode_resolve_chunk(b, h, g, S, d, dtype, split_chunk=0)
   kv_bytes(layers, g, S, d, dtype_bytes)
   status_string(status)
@@ -26,19 +27,22 @@ import os
 import torch
 
 __all__ = [
-    "append_kv", "decode_attn", "decode_workspace_bytes", "decode_resolve_chunk",
+    "append_kv", "decode_attn", "decode_workspace_bytes", "decode_workspace", "decode_resolve_chunk",
     "kv_bytes", "status_string", "MQAError", "LIB_PATH", "DEVERR_SEQLEN",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa_decode.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)
+WORKSPACE_COUNTER_BYTES = 256 * 1024  # MQA_WORKSPACE_COUNTER_BYTES
 F32, BF16 = 0, 1
 DEVERR_SEQLEN = 1
 
+KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
+
 EXPORTS = (
     "mqa_append_kv", "mqa_decode_workspace_bytes", "mqa_decode_resolve_chunk",
-    "mqa_decode_attn", "mqa_status_string", "mqa_kv_bytes",
+    "mqa_decode_attn", "mqa_decode_attn_kernel", "mqa_status_string", "mqa_kv_bytes",
 )
 
 
@@ -63,6 +67,10 @@ def _load() -> ctypes.CDLL:
     L.mqa_decode_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_float,
                                   vp, vp, ctypes.c_size_t, i32, vp, vp]
     L.mqa_decode_attn.restype = i32
+    L.mqa_decode_attn_kernel.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                         ctypes.c_float, vp, vp, ctypes.c_size_t, i32, vp, i32,
+                                         vp]
+    L.mqa_decode_attn_kernel.restype = i32
     L.mqa_status_string.argtypes = [i32]
     L.mqa_status_string.restype = ctypes.c_char_p
     L.mqa_kv_bytes.argtypes = [i32, i32, i64, i32, i32]
@@ -100,6 +108,14 @@ def _dtype_code(dt: torch.dtype) -> int:
 def decode_workspace_bytes(b, h, g, S, d, dtype, split_chunk: int = 0) -> int:
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
     return int(lib().mqa_decode_workspace_bytes(b, h, g, S, d, code, split_chunk))
+
+
+def decode_workspace(b, h, g, S, d, dtype, device, split_chunk: int = 0) -> torch.Tensor:
+    """A workspace for these sizes, zero-filled (its counter region must start at zero)."""
+    n = decode_workspace_bytes(b, h, g, S, d, dtype, split_chunk)
+    if n == 0:
+        raise ValueError("invalid sizes")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def decode_resolve_chunk(b, h, g, S, d, dtype, split_chunk: int = 0) -> int:
@@ -148,8 +164,13 @@ def append_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
 def decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                 seq_lens: torch.Tensor, scale: float | None = None,
                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                split_chunk: int = 0, err_flags: torch.Tensor | None = None) -> torch.Tensor:
-    """Decode attention: q [b,h,d], caches [b,g,S,d], seq_lens int32 [b] -> out fp32 [b,h,d]."""
+                split_chunk: int = 0, err_flags: torch.Tensor | None = None,
+                kernel: int = KERNEL_AUTO) -> torch.Tensor:
+    """Decode attention: q [b,h,d], caches [b,g,S,d], seq_lens int32 [b] -> out fp32 [b,h,d].
+
+    kernel: KERNEL_AUTO (mqa_decode_attn), or KERNEL_VALU / KERNEL_MFMA
+    (mqa_decode_attn_kernel with that choice).
+    """
     for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
         _dev(t, n)
     if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
@@ -170,14 +191,18 @@ def decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     elif out.dtype != torch.float32 or out.shape != (b, h, d):
         raise ValueError("out must be float32 [b, h, d]")
     _dev(out, "out")
-    need = decode_workspace_bytes(b, h, g, S, d, code, split_chunk)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(b, h, g, S, d, code, q.device, split_chunk)
     _dev(workspace, "workspace")
-    st = lib().mqa_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), b, h, g,
-                              S, d, code, ctypes.c_float(scale), _ptr(out), _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), split_chunk,
-                              _ptr(err_flags), _stream(q.device))
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), b, h, g, S, d, code,
+            ctypes.c_float(scale), _ptr(out), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), split_chunk, _ptr(err_flags))
+    if kernel == KERNEL_AUTO:
+        st = lib().mqa_decode_attn(*args, _stream(q.device))
+        where = "mqa_decode_attn"
+    else:
+        st = lib().mqa_decode_attn_kernel(*args, int(kernel), _stream(q.device))
+        where = "mqa_decode_attn_kernel"
     if st != OK:
-        raise MQAError(st, "mqa_decode_attn")
+        raise MQAError(st, where)
     return out

@@ -76,6 +76,12 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16-byte streaming load (read once, not kept in the caches).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4_t load_stream16(const void *p) {
+    return __builtin_nontemporal_load((const u32x4_t *)p);
+}
+
 // 16-byte global -> LDS copy. The LDS destination of lane l is
 // lds_block + 16*l (lds_block is wave-uniform and goes through m0, which is
 // saved and restored around the copy; one wait state separates the m0 write
@@ -97,11 +103,11 @@ __device__ __forceinline__ void dma16(const void *src, uint32_t lds_block) {
         : "memory");
 }
 
-// Wait until at most N vector-memory operations of this wave are pending,
-// then work-group barrier.
+// Wait until at most N vector-memory operations of this wave are pending and
+// its LDS accesses are done, then work-group barrier.
 template <int N>
 __device__ __forceinline__ void vmem_wait_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
 // Work-group barrier after this wave's LDS accesses have completed.
@@ -151,15 +157,21 @@ struct RowsCfg {
     static constexpr int EB = (int)sizeof(T);
     static constexpr int ROW_BYTES = D * EB;          // 128 .. 512
     static constexpr int CPR = ROW_BYTES / 16;        // 16-byte chunks per row
-    static constexpr int ELEMS = 16 / EB;             // elements per chunk
     static constexpr int NW = HPW;                    // waves per work-group
     static constexpr int NT = 64 * NW;
     static constexpr int TILE_BYTES = kTile * ROW_BYTES;
     static constexpr int DMA = TILE_BYTES / 16 / NT;  // DMA loads per lane per K (or V) tile
-    static constexpr int RPW = kTile / NW;            // rows per wave in the P.V phase
-    static constexpr int RPI = 64 / CPR;              // rows covered by one wave-wide 1 KB
-    static constexpr int VROWS = RPW / RPI;           // rows per lane in the P.V phase
     static constexpr int ROW_DW = ROW_BYTES / 4;
+    // P.V phase: each lane owns a VCB-byte column chunk of some rows; 8-byte
+    // chunks keep the 8 heads' accumulators of the bf16 case at 32 registers.
+    static constexpr int VCB = (EB == 2 && HPW == 8) ? 8 : 16;
+    static constexpr int ELEMS = VCB / EB;            // columns per lane
+    static constexpr int CPRV = ROW_BYTES / VCB;      // column chunks per row
+    static constexpr int RPW = kTile / NW;            // rows per wave in the P.V phase
+    static constexpr int RPI = 64 / CPRV;             // rows covered by one wave-wide read
+    static constexpr int VROWS = RPW / RPI;           // rows per lane in the P.V phase
+    // two 8-wave work-groups per compute unit need <= 128 registers per lane
+    static constexpr int WAVES_PER_EU = (HPW == 8 && ROW_BYTES <= 256) ? 4 : 1;
     static_assert(DMA >= 1 && VROWS >= 1, "too many waves for this row size");
     static_assert(NW * HPW * D * 4 <= 2 * 2 * TILE_BYTES, "reduction scratch must fit");
 };
@@ -167,36 +179,79 @@ struct RowsCfg {
 template <typename T, int D, int HPW>
 struct RowsSmem {
     using C = RowsCfg<T, D, HPW>;
-    uint8_t kv[2][2][C::TILE_BYTES];  // [stage][K=0, V=1], rows XOR-swizzled in 16-byte chunks
-    float p[kTile][HPW];              // softmax numerators of the current tile, [row][head]
-    float alpha[HPW];                 // rescale factor of the running sums, per head
+    uint8_t kv[2][2][C::TILE_BYTES];  // [stage][K=0, V=1], rows XOR-swizzled by 16-byte chunk
+    float p[2][kTile][HPW];           // softmax numerators of a tile, [row][head]
+    float alpha[2][HPW];              // rescale factor of the running sums, per head
 };
 
-// Issue the DMA of one 64-row tile of K or V into LDS. Row r, chunk c lands at
-// r*ROW_BYTES + 16*(c ^ (r % CPR)): a 64-lane read of one chunk of 64 rows, or
-// of 64 chunks of 4 rows, touches 64 distinct 16-byte bank groups.
+// Scores more than 2^kSlack above the reference max of a head trigger a
+// rescale of its running sums; below that the reference is kept, so the
+// exponentials stay <= 2^kSlack and most tiles skip the rescale entirely.
+constexpr float kSlack = 8.0f;
+
+// Tile DMA: row r, chunk c of a 64-row tile lands at LDS offset
+// r*ROW_BYTES + 16*(c ^ (r % CPR)), so that a 64-lane read of one chunk of 64
+// rows, or of 64 chunks of 4 rows, touches 64 distinct 16-byte bank groups.
+// Lane `lane` of wave `w` copies, in its r-th instruction, the chunk whose
+// byte offset from the tile's first row is dma_off(w, lane, r).
 template <typename C>
+__device__ __forceinline__ int dma_row(int w, int lane, int r) {
+    return ((w * C::DMA + r) * 64 + lane) / C::CPR;
+}
+template <typename C>
+__device__ __forceinline__ uint32_t dma_off(int w, int lane, int r) {
+    const int slot = (w * C::DMA + r) * 64 + lane;
+    const int row = slot / C::CPR;
+    return (uint32_t)(row * C::ROW_BYTES + (((slot % C::CPR) ^ (row % C::CPR)) << 4));
+}
+
+// 16-byte global -> LDS copy from a wave-uniform base plus a per-lane 32-bit
+// byte offset (same m0 handling as dma16).
+__device__ __forceinline__ void dma16_sv(const void *sbase, uint32_t voff, uint32_t lds_block) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_block), "v"(voff), "s"(sbase)
+        : "memory");
+}
+
+template <typename C, bool TAIL>
 __device__ __forceinline__ void dma_tile(const uint8_t *__restrict__ base, int t0, int S,
-                                         uint8_t *lds_tile, int w, int lane) {
+                                         uint32_t lds_tile, const uint32_t (&off)[C::DMA], int w,
+                                         int lane) {
+    if constexpr (!TAIL) {
+        const uint8_t *tile = base + (size_t)t0 * C::ROW_BYTES;
 #pragma unroll
-    for (int r = 0; r < C::DMA; r++) {
-        const int blk = w * C::DMA + r;  // 1 KB block of the tile written by this instruction
-        const int slot = blk * 64 + lane;
-        const int row = slot / C::CPR;
-        const int chunk = (slot % C::CPR) ^ (row % C::CPR);
-        const int grow = min(t0 + row, S - 1);  // rows past the capacity are never used
-        dma16(base + (size_t)grow * C::ROW_BYTES + chunk * 16, lds_addr(lds_tile + blk * 1024));
+        for (int r = 0; r < C::DMA; r++)
+            dma16_sv(tile, off[r], lds_tile + (w * C::DMA + r) * 1024);
+    } else {
+        // rows past the capacity are clamped to the last row (never used)
+#pragma unroll
+        for (int r = 0; r < C::DMA; r++) {
+            const int row = dma_row<C>(w, lane, r);
+            const int grow = min(t0 + row, S - 1);
+            const uint32_t col = off[r] - (uint32_t)(row * C::ROW_BYTES);
+            dma16(base + (size_t)grow * C::ROW_BYTES + col, lds_tile + (w * C::DMA + r) * 1024);
+        }
     }
 }
 
+template <bool V> struct TailTag { static constexpr bool value = V; };
+
 template <typename T, int D, int HPW>
 __global__ void __launch_bounds__(64 * HPW)
+__attribute__((amdgpu_waves_per_eu(RowsCfg<T, D, HPW>::WAVES_PER_EU, 8)))
 split_rows_kernel(const T *__restrict__ q, const T *__restrict__ kc, const T *__restrict__ vc,
                   const int32_t *__restrict__ seq_lens, int h, int g, int S, int G, int nhc,
                   int chunk, int nsplit, float qk_scale_log2, float *__restrict__ part_o,
                   float2 *__restrict__ part_ml) {
     using C = RowsCfg<T, D, HPW>;
-    __shared__ __attribute__((aligned(16))) RowsSmem<T, D, HPW> sm;
+    __shared__ __attribute__((aligned(1024))) RowsSmem<T, D, HPW> sm;
 
     const int s = blockIdx.x;
     const int j = blockIdx.y / nhc;
@@ -217,7 +272,7 @@ split_rows_kernel(const T *__restrict__ q, const T *__restrict__ kc, const T *__
     const uint8_t *vbase = (const uint8_t *)vc + head_row0 * C::ROW_BYTES;
 
     // Query head scored by this wave (slots past G repeat the last head and
-    // are never written out).
+    // are never written out). Its row stays in scalar registers.
     const int slot_w = hc * HPW + w;
     const int hq_w = j * G + min(slot_w, G - 1);
     const uint32_t *qrow = (const uint32_t *)(q + ((size_t)i * h + hq_w) * D);
@@ -225,37 +280,61 @@ split_rows_kernel(const T *__restrict__ q, const T *__restrict__ kc, const T *__
 #pragma unroll
     for (int x = 0; x < C::ROW_DW; x++) qv[x] = qrow[x];
 
-    // P.V ownership: lane -> (row group rg, 16-byte column chunk cc)
-    const int rg = lane / C::CPR;
-    const int cc = lane % C::CPR;
+    // per-lane constant offsets
+    uint32_t doff[C::DMA];
+#pragma unroll
+    for (int r = 0; r < C::DMA; r++) doff[r] = dma_off<C>(w, lane, r);
+    const uint32_t smem = lds_addr(&sm);
+    const uint32_t kv_base = lds_addr(&sm.kv[0][0][0]);
+    // score phase: lane reads row `lane`, chunk c at koff ^ (c << 4)
+    const uint32_t koff = (uint32_t)(lane * C::ROW_BYTES + ((lane % C::CPR) << 4));
+    // P.V phase: lane -> (row group rg, VCB-byte column chunk cc)
+    const int rg = lane / C::CPRV;
+    const int cc = lane % C::CPRV;
+    constexpr int SUB = 16 / C::VCB;  // column chunks per 16-byte granule
+    uint32_t voff[C::VROWS];
+    int vrow[C::VROWS];
+#pragma unroll
+    for (int r = 0; r < C::VROWS; r++) {
+        vrow[r] = w * C::RPW + r * C::RPI + rg;
+        voff[r] = (uint32_t)(vrow[r] * C::ROW_BYTES + (((cc / SUB) ^ (vrow[r] % C::CPR)) << 4) +
+                             (cc % SUB) * C::VCB);
+    }
 
     float acc[HPW][C::ELEMS];
 #pragma unroll
     for (int a = 0; a < HPW; a++)
 #pragma unroll
         for (int e = 0; e < C::ELEMS; e++) acc[a][e] = 0.f;
-    float m_run = -INFINITY;  // running max of this wave's head (log2 units)
+    float m_ref = -INFINITY;  // reference max of this wave's head (log2 units)
     float l_lane = 0.f;       // this lane's share of the running sum
 
-    dma_tile<C>(kbase, t_begin, S, sm.kv[0][0], w, lane);
-    dma_tile<C>(vbase, t_begin, S, sm.kv[0][1], w, lane);
+    auto stage_k = [&](int st) { return kv_base + (uint32_t)((2 * st) * C::TILE_BYTES); };
+    auto stage_v = [&](int st) { return kv_base + (uint32_t)((2 * st + 1) * C::TILE_BYTES); };
 
-    for (int n = 0; n < ntiles; n++) {
-        const int st = n & 1;
+    auto issue_k = [&](int n, int st) {
         const int t0 = t_begin + n * kTile;
-        // tile n landed everywhere; every wave finished tile n-1
-        vmem_wait_barrier<0>();
-        if (n + 1 < ntiles) {
-            dma_tile<C>(kbase, t0 + kTile, S, sm.kv[st ^ 1][0], w, lane);
-            dma_tile<C>(vbase, t0 + kTile, S, sm.kv[st ^ 1][1], w, lane);
-        }
+        if (t0 + kTile <= S) dma_tile<C, false>(kbase, t0, S, stage_k(st), doff, w, lane);
+        else dma_tile<C, true>(kbase, t0, S, stage_k(st), doff, w, lane);
+    };
+    auto issue_v = [&](int n, int st) {
+        const int t0 = t_begin + n * kTile;
+        if (t0 + kTile <= S) dma_tile<C, false>(vbase, t0, S, stage_v(st), doff, w, lane);
+        else dma_tile<C, true>(vbase, t0, S, stage_v(st), doff, w, lane);
+    };
 
-        // ---- scores: lane = cache row, wave = query head ----
-        const uint8_t *krow = sm.kv[st][0] + lane * C::ROW_BYTES;
+    // Scores of tile n: lane = cache row, wave = query head; online-softmax
+    // bookkeeping; the numerators go to pbuf[n & 1], the head's rescale
+    // factor to alpha[n & 1]. TAIL masks rows >= t_end.
+    auto scores = [&](int n, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        const int t0 = t_begin + n * kTile;
+        const uint8_t *lds = (const uint8_t *)&sm;
+        const uint32_t kb = stage_k(n & 1) - smem + koff;
         float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
         for (int c = 0; c < C::CPR; c++) {
-            const uint4 kk = *(const uint4 *)(krow + ((c ^ (lane % C::CPR)) << 4));
+            const uint4 kk = *(const uint4 *)(lds + (kb ^ (uint32_t)(c << 4)));
             if constexpr (sizeof(T) == 2) {
                 a0 = dot2_bf16(qv[4 * c + 0], kk.x, a0);
                 a1 = dot2_bf16(qv[4 * c + 1], kk.y, a1);
@@ -268,51 +347,92 @@ split_rows_kernel(const T *__restrict__ q, const T *__restrict__ kc, const T *__
                 a3 = fmaf(__uint_as_float(qv[4 * c + 3]), __uint_as_float(kk.w), a3);
             }
         }
-        const bool row_ok = t0 + lane < t_end;
-        const float s2 = row_ok ? ((a0 + a1) + (a2 + a3)) * qk_scale_log2 : -INFINITY;
-        const float m_new = fmaxf(m_run, wave_max(s2));  // finite: row t0 is always valid
-        const float alpha = fast_exp2(m_run - m_new);
-        const float p = fast_exp2(s2 - m_new);
-        l_lane = l_lane * alpha + p;
-        m_run = m_new;
-        sm.p[lane][w] = p;
-        if (lane == 0) sm.alpha[w] = alpha;
-        lds_barrier();
+        float s2 = ((a0 + a1) + (a2 + a3)) * qk_scale_log2;
+        if constexpr (TAIL) s2 = (t0 + lane < t_end) ? s2 : -INFINITY;
+        float alpha = 1.f;
+        // The cross-lane max is needed only when some score passes the
+        // reference by more than the slack (always on the first tile).
+        if (__any(s2 > m_ref + kSlack)) {  // wave-uniform
+            const float mt = wave_max(s2);
+            alpha = fast_exp2(m_ref - mt);
+            m_ref = mt;
+        }
+        const float p = fast_exp2(s2 - m_ref);
+        l_lane = fmaf(l_lane, alpha, p);
+        sm.p[n & 1][lane][w] = p;
+        if (lane == 0) sm.alpha[n & 1][w] = alpha;
+    };
 
-        // ---- P.V: lane owns column chunk cc of rows rg, rg+RPI, ... ----
+    // P.V of tile n: lane owns column chunk cc of rows vrow[0..VROWS).
+    auto pv = [&](int n, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        const int t0 = t_begin + n * kTile;
+        const uint8_t *lds = (const uint8_t *)&sm;
         float al[HPW];
+        bool rescale = false;
 #pragma unroll
-        for (int a = 0; a < HPW; a++) al[a] = sm.alpha[a];
+        for (int a = 0; a < HPW; a++) {
+            al[a] = sm.alpha[n & 1][a];
+            rescale |= al[a] != 1.f;
+        }
+        if (rescale) {  // uniform across the work-group
 #pragma unroll
-        for (int a = 0; a < HPW; a++)
+            for (int a = 0; a < HPW; a++)
 #pragma unroll
-            for (int e = 0; e < C::ELEMS; e++) acc[a][e] *= al[a];
+                for (int e = 0; e < C::ELEMS; e++) acc[a][e] *= al[a];
+        }
+        const uint32_t vb = stage_v(n & 1) - smem;
 #pragma unroll
         for (int r = 0; r < C::VROWS; r++) {
-            const int row = w * C::RPW + r * C::RPI + rg;
-            const uint4 vv =
-                *(const uint4 *)(sm.kv[st][1] + row * C::ROW_BYTES + ((cc ^ (row % C::CPR)) << 4));
             float vf[C::ELEMS];
-            if constexpr (sizeof(T) == 2) {
+            if constexpr (C::VCB == 8) {
+                const uint2 vv = *(const uint2 *)(lds + vb + voff[r]);
+                vf[0] = bf16_lo(vv.x); vf[1] = bf16_hi(vv.x);
+                vf[2] = bf16_lo(vv.y); vf[3] = bf16_hi(vv.y);
+            } else if constexpr (sizeof(T) == 2) {
+                const uint4 vv = *(const uint4 *)(lds + vb + voff[r]);
                 vf[0] = bf16_lo(vv.x); vf[1] = bf16_hi(vv.x);
                 vf[2] = bf16_lo(vv.y); vf[3] = bf16_hi(vv.y);
                 vf[4] = bf16_lo(vv.z); vf[5] = bf16_hi(vv.z);
                 vf[6] = bf16_lo(vv.w); vf[7] = bf16_hi(vv.w);
             } else {
+                const uint4 vv = *(const uint4 *)(lds + vb + voff[r]);
                 vf[0] = __uint_as_float(vv.x); vf[1] = __uint_as_float(vv.y);
                 vf[2] = __uint_as_float(vv.z); vf[3] = __uint_as_float(vv.w);
             }
-            // rows past the end may hold anything (even NaN): never let them in
-            const bool ok = t0 + row < t_end;
+            if constexpr (TAIL) {
+                // rows past the end may hold anything (even NaN): never let them in
+                const bool ok = t0 + vrow[r] < t_end;
 #pragma unroll
-            for (int e = 0; e < C::ELEMS; e++) vf[e] = ok ? vf[e] : 0.f;
+                for (int e = 0; e < C::ELEMS; e++) vf[e] = ok ? vf[e] : 0.f;
+            }
             float pr[HPW];
 #pragma unroll
-            for (int a = 0; a < HPW; a++) pr[a] = sm.p[row][a];
+            for (int a = 0; a < HPW; a++) pr[a] = sm.p[n & 1][vrow[r]][a];
 #pragma unroll
             for (int a = 0; a < HPW; a++)
 #pragma unroll
                 for (int e = 0; e < C::ELEMS; e++) acc[a][e] = fmaf(pr[a], vf[e], acc[a][e]);
+        }
+    };
+
+    // Software pipeline, one barrier per tile. Iteration n: wait for K(n) and
+    // V(n-1) (everything issued in iteration n-1) and for every wave to have
+    // finished iteration n-1; start copying K(n+1) and V(n); scores of tile n;
+    // P.V of tile n-1. Stages are reused two iterations after their copy.
+    const bool last_full = t_begin + ntiles * kTile <= t_end;
+    issue_k(0, 0);
+    for (int n = 0; n <= ntiles; n++) {
+        vmem_wait_barrier<0>();
+        if (n + 1 < ntiles) issue_k(n + 1, (n + 1) & 1);
+        if (n < ntiles) {
+            issue_v(n, n & 1);
+            if (n + 1 < ntiles || last_full) scores(n, TailTag<false>{});
+            else scores(n, TailTag<true>{});
+        }
+        if (n >= 1) {
+            if (n < ntiles || last_full) pv(n - 1, TailTag<false>{});
+            else pv(n - 1, TailTag<true>{});
         }
     }
 
@@ -324,12 +444,12 @@ split_rows_kernel(const T *__restrict__ q, const T *__restrict__ kc, const T *__
         for (int e = 0; e < C::ELEMS; e++) {
             float x = acc[a][e];
 #pragma unroll
-            for (int off = C::CPR; off < 64; off <<= 1) x += __shfl_xor(x, off);
+            for (int off = C::CPRV; off < 64; off <<= 1) x += __shfl_xor(x, off);
             acc[a][e] = x;
         }
     lds_barrier();  // every wave is done with the tiles; reuse them as scratch
     float *red = (float *)&sm.kv[0][0][0];  // [NW][HPW][D]
-    if (lane < C::CPR) {
+    if (lane < C::CPRV) {
 #pragma unroll
         for (int a = 0; a < HPW; a++)
 #pragma unroll
@@ -347,7 +467,557 @@ split_rows_kernel(const T *__restrict__ q, const T *__restrict__ kc, const T *__
     }
     if (lane == 0 && slot_w < G) {
         const size_t hq = (size_t)i * h + j * G + slot_w;
-        part_ml[hq * nsplit + s] = make_float2(m_run, l_tot);
+        part_ml[hq * nsplit + s] = make_float2(m_ref, l_tot);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 partition kernels: matrix cores for both contractions
+// ---------------------------------------------------------------------------
+//
+// Per 32-position step of one wave, with 16 query heads of the group as the
+// 16-wide matrix dimension (padded when fewer than 16):
+//   S^T[pos][head] = K[pos][:] . Q[head][:]     two 16x16x32 bf16 MFMA blocks
+//                                               per 32 d (fp32 accumulate;
+//                                               bf16 products are exact)
+//   O[head][x]    += P[head][pos] V[pos][x]     P split as bf16 hi + lo
+//                                               (two MFMAs, ~2^-17 relative)
+// Lane l (r = l % 16, qd = l / 16) holds S^T rows pos = 4qd+v (v < 4) of each
+// 16-position block for head r: exactly the A-operand slots of P for the
+// P.V MFMA if the 32 positions of a step are numbered
+//   kslot(qd, e) = 4qd + e (e < 4),  16 + 4qd + (e - 4) (e >= 4),
+// so P never moves. V needs a transposed read (8 positions of one column per
+// lane); it goes through a small wave-private LDS buffer with padded rows.
+// Each wave runs its own online softmax over its steps; the waves are merged
+// through LDS at the end of a partition.
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+template <int D>
+struct MfmaCfg {
+    static constexpr int ROW_BYTES = D * 2;
+    static constexpr int KSTEPS = D / 32;            // 32-wide d slices of the score MFMA
+    static constexpr int NB = D / 16;                // 16-column blocks of the P.V MFMA
+    static constexpr int STEP = 32;                  // positions per step
+    static constexpr int NW = 4;                     // waves per work-group
+    static constexpr int CPR = ROW_BYTES / 16;       // 16-byte chunks per row
+    static constexpr int RPI = 64 / CPR;             // rows per wave-wide V load
+    static constexpr int VLOADS = STEP / RPI;        // V loads per lane per step
+    static constexpr int VSTRIDE = ROW_BYTES + 16;   // padded LDS row stride of V
+    static constexpr int VBUF = STEP * VSTRIDE;      // per-wave V staging bytes
+    static constexpr int HB = 16;                    // query heads per matrix block
+    static_assert(NW * HB * (D + 2) * 4 <= NW * VBUF, "merge scratch must fit");
+};
+
+__device__ __forceinline__ int kslot(int qd, int e) { return e < 4 ? 4 * qd + e : 12 + 4 * qd + e; }
+
+// One wave's running state for 16 query heads.
+template <int D>
+struct MfmaState {
+    f32x4_t acc[MfmaCfg<D>::NB];  // O[head 4qd+v][x = 16nb + r], unnormalised
+    float m_ref;                  // reference max of head r (log2 units), equal in the 4 qd lanes
+    float l_lane;                 // this lane's share of head r's running sum
+    __device__ __forceinline__ void reset() {
+#pragma unroll
+        for (int nb = 0; nb < MfmaCfg<D>::NB; nb++) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m_ref = -INFINITY;
+        l_lane = 0.f;
+    }
+};
+
+// Q^T operand of query head `hq`: lane holds Q[hq][32k + 8qd .. +8].
+template <int D>
+__device__ __forceinline__ void load_q_operand(const uint16_t *__restrict__ q, size_t qrow,
+                                               int qd, bf16x8_t (&qop)[MfmaCfg<D>::KSTEPS]) {
+#pragma unroll
+    for (int k = 0; k < MfmaCfg<D>::KSTEPS; k++)
+        qop[k] = *(const bf16x8_t *)(q + qrow * D + 32 * k + 8 * qd);
+}
+
+// K and V of one 32-position step as loaded: K straight into the A operand
+// of the score MFMA, V row-contiguous (16 bytes per lane).
+template <int D>
+struct StepData {
+    bf16x8_t kop[2][MfmaCfg<D>::KSTEPS];
+    u32x4_t vld[MfmaCfg<D>::VLOADS];
+};
+
+// Issue the loads of step [t0, t0+32); rows past the capacity are clamped
+// (and masked later).
+template <int D>
+__device__ __forceinline__ void load_step(const uint8_t *__restrict__ kbase,
+                                          const uint8_t *__restrict__ vbase, int t0, int S,
+                                          int lane, StepData<D> &sd) {
+    using C = MfmaCfg<D>;
+    const int r = lane & 15, qd = lane >> 4;
+    const int vl_row = lane / C::CPR, vl_chunk = lane % C::CPR;
+#pragma unroll
+    for (int pb = 0; pb < 2; pb++) {
+        const int row = min(t0 + 16 * pb + r, S - 1);
+#pragma unroll
+        for (int k = 0; k < C::KSTEPS; k++)
+            sd.kop[pb][k] = __builtin_bit_cast(
+                bf16x8_t, load_stream16(kbase + (size_t)row * C::ROW_BYTES + 64 * k + 16 * qd));
+    }
+#pragma unroll
+    for (int ii = 0; ii < C::VLOADS; ii++) {
+        const int row = min(t0 + ii * C::RPI + vl_row, S - 1);
+        sd.vld[ii] = load_stream16(vbase + (size_t)row * C::ROW_BYTES + 16 * vl_chunk);
+    }
+}
+
+// One 32-position step [t0, t0+32) of one wave from loaded data, rows >=
+// t_end masked; vb is the wave's staging buffer.
+template <int D>
+__device__ __forceinline__ void compute_step(const StepData<D> &sd, int t0, int t_end,
+                                             const bf16x8_t (&qop)[MfmaCfg<D>::KSTEPS],
+                                             MfmaState<D> &st, uint8_t *vb, int lane,
+                                             float qk_scale_log2) {
+    using C = MfmaCfg<D>;
+    const int r = lane & 15, qd = lane >> 4;
+    const int vl_row = lane / C::CPR, vl_chunk = lane % C::CPR;
+    const bool tail = t0 + C::STEP > t_end;
+    const auto &kop = sd.kop;
+    const auto &vld = sd.vld;
+
+    // ---- scores ----
+    f32x4_t sc[2];
+#pragma unroll
+    for (int pb = 0; pb < 2; pb++) {
+        sc[pb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < C::KSTEPS; k++)
+            sc[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[pb][k], qop[k], sc[pb], 0, 0, 0);
+    }
+    float s2[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        s2[e] = sc[e >> 2][e & 3] * qk_scale_log2;
+        if (tail && t0 + kslot(qd, e) >= t_end) s2[e] = -INFINITY;
+    }
+
+    // ---- V into the staging buffer (rows past the end zeroed: they may be NaN) ----
+#pragma unroll
+    for (int ii = 0; ii < C::VLOADS; ii++) {
+        u32x4_t v = vld[ii];
+        if (tail && t0 + ii * C::RPI + vl_row >= t_end) v = u32x4_t{0u, 0u, 0u, 0u};
+        *(u32x4_t *)(vb + (ii * C::RPI + vl_row) * C::VSTRIDE + 16 * vl_chunk) = v;
+    }
+
+    // ---- online softmax for head r ----
+    float smax = s2[0];
+#pragma unroll
+    for (int e = 1; e < 8; e++) smax = fmaxf(smax, s2[e]);
+    if (__any(smax > st.m_ref + kSlack)) {  // wave-uniform
+        float mt = fmaxf(smax, __shfl_xor(smax, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));   // max over the head's 32 positions
+        mt = fmaxf(mt, st.m_ref);
+        const float alpha = fast_exp2(st.m_ref - mt);  // per head r
+        st.m_ref = mt;
+        st.l_lane *= alpha;
+        // acc rows are heads 4qd+v: fetch their factors from lanes 4qd+v
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const float av = __shfl(alpha, 4 * qd + v);
+#pragma unroll
+            for (int nb = 0; nb < C::NB; nb++) st.acc[nb][v] *= av;
+        }
+    }
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        p[e] = fast_exp2(s2[e] - st.m_ref);
+        st.l_lane += p[e];
+    }
+    // P as bf16 hi + lo parts, A operand of the P.V MFMA
+    bf16x8_t phi, plo;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const __bf16 hi = (__bf16)p[e];
+        phi[e] = hi;
+        plo[e] = (__bf16)(p[e] - (float)hi);
+    }
+
+    // ---- P.V ----
+    const uint16_t *vt = (const uint16_t *)(vb + 4 * qd * C::VSTRIDE + 2 * r);
+#pragma unroll
+    for (int nb = 0; nb < C::NB; nb++) {
+        bf16x8_t vop;
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            vop[e] = __builtin_bit_cast(__bf16, vt[(kslot(0, e) * C::VSTRIDE + 32 * nb) / 2]);
+        st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vop, st.acc[nb], 0, 0, 0);
+        st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vop, st.acc[nb], 0, 0, 0);
+    }
+}
+
+// Steps s_begin, s_begin+stride, ... < s_end of one K/V head, with the loads
+// of the next step in flight while this one computes (two register sets,
+// alternating). Past the last step the prefetch reads `idle` instead, one
+// row (ROW_BYTES) this wave has just read and that sits in cache, so every
+// iteration issues the same loads without a second trip to HBM.
+template <int D>
+__device__ __forceinline__ void run_steps(const uint8_t *__restrict__ kbase,
+                                          const uint8_t *__restrict__ vbase,
+                                          const uint8_t *__restrict__ idle, int s_begin,
+                                          int s_end, int stride, int t_end, int S,
+                                          const bf16x8_t (&qop)[MfmaCfg<D>::KSTEPS],
+                                          MfmaState<D> &st, uint8_t *vb, int lane,
+                                          float qk_scale_log2) {
+    using C = MfmaCfg<D>;
+    int stp = s_begin;
+    if (stp >= s_end) return;
+    StepData<D> a, b;
+    load_step<D>(kbase, vbase, stp * C::STEP, S, lane, a);
+    // the prefetch source, chosen without branching (one copy of the loads)
+    auto prefetch = [&](int nx, StepData<D> &sd) {
+        const bool more = nx < s_end;
+        load_step<D>(more ? kbase : idle, more ? vbase : idle, more ? nx * C::STEP : 0,
+                     more ? S : 1, lane, sd);
+    };
+    while (true) {
+        int nx = stp + stride;
+        prefetch(nx, b);
+        compute_step<D>(a, stp * C::STEP, t_end, qop, st, vb, lane, qk_scale_log2);
+        if (nx >= s_end) break;
+        stp = nx;
+        nx = stp + stride;
+        prefetch(nx, a);
+        compute_step<D>(b, stp * C::STEP, t_end, qop, st, vb, lane, qk_scale_log2);
+        if (nx >= s_end) break;
+        stp = nx;
+    }
+}
+
+// Publish one wave's state into the merge scratch (mrg [NW][HB][D], mls [NW][HB][2]).
+template <int D>
+__device__ __forceinline__ void publish_state(const MfmaState<D> &st, float *mrg, float *mls, int w,
+                                              int lane) {
+    using C = MfmaCfg<D>;
+    const int r = lane & 15, qd = lane >> 4;
+    const float l_head = st.l_lane + __shfl_xor(st.l_lane, 16);
+    const float l_tot = l_head + __shfl_xor(l_head, 32);
+#pragma unroll
+    for (int nb = 0; nb < C::NB; nb++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) mrg[(w * C::HB + 4 * qd + v) * D + 16 * nb + r] = st.acc[nb][v];
+    if (qd == 0) {
+        mls[(w * C::HB + r) * 2 + 0] = st.m_ref;
+        mls[(w * C::HB + r) * 2 + 1] = l_tot;
+    }
+}
+
+// Merge waves [w0, w0+nw) of the scratch for head hh, column x:
+// returns the unnormalised O, and (M, l) of the merged state.
+template <int D>
+__device__ __forceinline__ float merge_waves(const float *mrg, const float *mls, int w0, int nw,
+                                             int hh, int x, float &M, float &l) {
+    using C = MfmaCfg<D>;
+    M = -INFINITY;
+    for (int ww = w0; ww < w0 + nw; ww++) M = fmaxf(M, mls[(ww * C::HB + hh) * 2]);
+    float o = 0.f;
+    l = 0.f;
+    for (int ww = w0; ww < w0 + nw; ww++) {
+        const float mw = mls[(ww * C::HB + hh) * 2];
+        const float sc = mw == -INFINITY ? 0.f : fast_exp2(mw - M);  // idle waves weigh 0
+        o = fmaf(sc, mrg[(ww * C::HB + hh) * D + x], o);
+        l = fmaf(sc, mls[(ww * C::HB + hh) * 2 + 1], l);
+    }
+    return o;
+}
+
+// Fixed partitions: one work-group per (partition of split_chunk positions,
+// K/V head, block of 16 query heads, sequence); writes partials for the
+// log-sum-exp combine.
+template <int D>
+__global__ void __launch_bounds__(256)
+split_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
+                  const uint16_t *__restrict__ vc, const int32_t *__restrict__ seq_lens, int h,
+                  int g, int S, int G, int nhb, int chunk, int nsplit, float qk_scale_log2,
+                  float *__restrict__ part_o, float2 *__restrict__ part_ml) {
+    using C = MfmaCfg<D>;
+    __shared__ __attribute__((aligned(16))) uint8_t vbuf[C::NW][C::VBUF];
+
+    const int s = blockIdx.x;
+    const int j = blockIdx.y / nhb;
+    const int hb = blockIdx.y % nhb;
+    const int i = blockIdx.z;
+    const int L = seq_lens[i];
+    if (L < 1 || L > S) return;  // reported by the combine
+    const int t_begin = s * chunk;
+    if (t_begin >= L) return;
+    const int t_end = min(t_begin + chunk, L);
+    const int nsteps = (t_end - t_begin + C::STEP - 1) / C::STEP;
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, qd = lane >> 4;
+
+    const size_t head_row0 = ((size_t)i * g + j) * (size_t)S;
+    const uint8_t *kbase = (const uint8_t *)kc + head_row0 * C::ROW_BYTES;
+    const uint8_t *vbase = (const uint8_t *)vc + head_row0 * C::ROW_BYTES;
+
+    // padded heads reuse the last real one and are never written out
+    bf16x8_t qop[C::KSTEPS];
+    load_q_operand<D>(q, (size_t)i * h + j * G + min(hb * C::HB + r, G - 1), qd, qop);
+
+    MfmaState<D> st;
+    st.reset();
+    // steps of this partition, numbered from the sequence start
+    const uint8_t *idle = (const uint8_t *)(q + ((size_t)i * h + j * G) * D);  // a q row
+    run_steps<D>(kbase, vbase, idle, t_begin / C::STEP + w, t_begin / C::STEP + nsteps, C::NW,
+                 t_end, S, qop, st, vbuf[w], lane, qk_scale_log2);
+
+    __syncthreads();  // every wave is done with its staging buffer
+    float *mrg = (float *)&vbuf[0][0];
+    float *mls = mrg + C::NW * C::HB * D;
+    publish_state<D>(st, mrg, mls, w, lane);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < C::HB * D; idx += 64 * C::NW) {
+        const int hh = idx / D, x = idx % D;
+        if (hb * C::HB + hh >= G) continue;
+        float M, l;
+        const float o = merge_waves<D>(mrg, mls, 0, C::NW, hh, x, M, l);
+        const size_t hrow = (size_t)i * h + j * G + hb * C::HB + hh;
+        part_o[(hrow * nsplit + s) * D + x] = o;
+        if (x == 0) part_ml[hrow * nsplit + s] = make_float2(M, l);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// balanced ("stream-K") schedule for the bf16 kernel
+// ---------------------------------------------------------------------------
+//
+// Work unit u = (sequence i, K/V head j) with n_i = ceil(L_i / 32) steps;
+// units are numbered i-major and their steps laid end to end (T steps in
+// all; sequences with an invalid length contribute none). Work-group w of
+// nwg takes steps [w*T/nwg, (w+1)*T/nwg): equal work whatever the lengths
+// (nwg is cut on the device so that every range holds >= kStreamMinSteps
+// steps). Its waves are split as (block of 16 query heads, sub-stream): with
+// nhb blocks, 4/nhb waves share a block and interleave the steps, so the
+// waves of different blocks read each K/V step at about the same time (the
+// second read comes from L2). A unit entirely inside one range is normalised
+// and written to `out` directly. A unit cut by range boundaries leaves, in
+// each work-group that touches it, a partial (m, l, o) in slot 0 (the range's
+// first segment) or slot 1 (its last) and bumps the unit's arrival counter;
+// the last work-group to arrive merges the pieces, writes `out` and puts the
+// counter back to zero.
+
+constexpr int kStreamMaxSeq = 1024;    // sequences per call on this schedule (prefix sums in LDS)
+constexpr int kStreamMaxWG = 1024;     // work-groups (bounds the workspace)
+constexpr int kStreamMinUnits = 256;   // fewer (sequence, K/V head) units: fixed partitions
+constexpr int kStreamMinSteps = 8;     // steps per work-group range, at least
+constexpr int kStreamMaxUnits = 65536; // arrival counters at the head of the workspace
+constexpr size_t kCounterBytes = (size_t)kStreamMaxUnits * 4;
+static_assert(kCounterBytes == MQA_WORKSPACE_COUNTER_BYTES, "counter region size");
+
+// steps of sequence i (0 for an invalid length)
+__device__ __forceinline__ int seq_steps(int L, int S) { return (L < 1 || L > S) ? 0 : (L + 31) / 32; }
+
+// Exclusive prefix over sequences of units*steps, into pre[0..b]; whole
+// work-group (256 threads). Each thread sums a contiguous run of sequences;
+// the runs are scanned with wave shuffles and the four wave totals added.
+// The host keeps the total below 2^31.
+__device__ __forceinline__ void unit_prefix(const int32_t *__restrict__ seq_lens, int b, int S,
+                                            int units_per_seq, int *pre, int *wtot) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int per = (b + 255) / 256;
+    const int a0 = min(b, t * per), a1 = min(b, a0 + per);
+    int run = 0;
+    for (int a = a0; a < a1; a++) run += seq_steps(seq_lens[a], S);
+    int v = run;  // inclusive scan over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(v, off);
+        if (lane >= off) v += y;
+    }
+    if (lane == 63) wtot[w] = v;
+    __syncthreads();
+    int acc = v - run;
+    for (int k = 0; k < w; k++) acc += wtot[k];
+    acc *= units_per_seq;
+    for (int a = a0; a < a1; a++) {
+        pre[a] = acc;
+        acc += seq_steps(seq_lens[a], S) * units_per_seq;
+    }
+    if (t == 255) pre[b] = acc;
+    __syncthreads();
+}
+
+// Partials of cut units are written and read with agent-coherent accesses
+// (they bypass the per-XCD caches), so only these bytes, not whole caches,
+// need to reach the point of coherence before a unit's arrival count moves.
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(float2 *p, float2 v) {
+    __hip_atomic_store((uint64_t *)p, __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_coherent(const float2 *p) {
+    return __builtin_bit_cast(float2, __hip_atomic_load((const uint64_t *)p, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Work-group owning global step x; the first step of work-group w's range.
+__device__ __forceinline__ int owner_of(int x, int T, int nwg) {
+    return (int)((((long long)x + 1) * nwg - 1) / T);
+}
+__device__ __forceinline__ int range_start(int w, int T, int nwg) {
+    return (int)((long long)T * w / nwg);
+}
+
+// Merge pieces [wf, wl] of one head slot hs, column x; the first owner's
+// piece is in slot slot_f, the others in slot 0. Loads go out eight pieces
+// at a time.
+template <int D>
+__device__ __forceinline__ float merge_pieces(const float *__restrict__ part_o,
+                                              const float2 *__restrict__ part_ml, int wf, int wl,
+                                              int slot_f, int HBT, int hs, int x) {
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    for (int p0 = wf; p0 <= wl; p0 += 8) {
+        float2 e[8];
+        float o[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const int wg = p0 + k;
+            if (wg <= wl) {
+                const size_t prow = ((size_t)wg * 2 + (wg == wf ? slot_f : 0)) * HBT + hs;
+                e[k] = load_coherent(part_ml + prow);
+                o[k] = load_coherent(part_o + prow * D + x);
+            } else {
+                e[k] = make_float2(-INFINITY, 0.f);
+                o[k] = 0.f;
+            }
+        }
+        float Mb = M;
+#pragma unroll
+        for (int k = 0; k < 8; k++) Mb = fmaxf(Mb, e[k].x);
+        const float rs = M == -INFINITY ? 0.f : fast_exp2(M - Mb);
+        num *= rs;
+        den *= rs;
+        M = Mb;
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const float wgt = e[k].x == -INFINITY ? 0.f : fast_exp2(e[k].x - M);
+            num = fmaf(wgt, o[k], num);
+            den = fmaf(wgt, e[k].y, den);
+        }
+    }
+    return num / den;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
+streamk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
+                    const uint16_t *__restrict__ vc, const int32_t *__restrict__ seq_lens, int b,
+                    int h, int g, int S, int G, int nhb, float qk_scale_log2,
+                    float *__restrict__ out, float *__restrict__ part_o,
+                    float2 *__restrict__ part_ml, uint32_t *__restrict__ counters,
+                    int32_t *__restrict__ err) {
+    using C = MfmaCfg<D>;
+    __shared__ __attribute__((aligned(16))) uint8_t vbuf[C::NW][C::VBUF];
+    __shared__ int pre[kStreamMaxSeq + 1];
+    __shared__ int wtot[4];
+    __shared__ int last_flag;
+
+    unit_prefix(seq_lens, b, S, g, pre, wtot);
+    // everything that steers the loops below is wave-uniform: keep it scalar
+    const int T = __builtin_amdgcn_readfirstlane(pre[b]);
+    const int wg = blockIdx.x;
+
+    // sequences with a length out of range: NaN rows and the error flag
+    // (work-group 0, one thread per sequence; such rows are rare)
+    if (wg == 0) {
+        for (int i = threadIdx.x; i < b; i += blockDim.x) {
+            if (pre[i + 1] != pre[i]) continue;
+            for (int idx = 0; idx < h * D; idx++) out[(size_t)i * h * D + idx] = __builtin_nanf("");
+            if (err) atomicOr(err, MQA_DEVERR_SEQLEN);
+        }
+    }
+    const int nwg = max(1, min((int)gridDim.x, T / kStreamMinSteps));
+    if (T == 0 || wg >= nwg) return;  // uniform across the work-group
+    const int x0 = range_start(wg, T, nwg), x1 = range_start(wg + 1, T, nwg);
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, qd = lane >> 4;
+    const int wph = C::NW / nhb;  // waves per head block
+    const int hb = w / wph, sub = w % wph;
+    const int HBT = nhb * C::HB;  // head slots per unit
+
+    int seg = 0;
+    int i = 0;
+    for (int x = x0; x < x1; seg++) {
+        // unit containing step x: sequence i (pre is non-decreasing; advance), head j
+        while (__builtin_amdgcn_readfirstlane(pre[i + 1]) <= x) i++;
+        const int pre_i = __builtin_amdgcn_readfirstlane(pre[i]);
+        const int L = __builtin_amdgcn_readfirstlane(seq_lens[i]);
+        const int n = seq_steps(L, S);
+        const int local = x - pre_i;
+        const int j = local / n;
+        const int s0 = local - j * n;
+        const int s1 = min(n, s0 + (x1 - x));
+
+        const size_t head_row0 = ((size_t)i * g + j) * (size_t)S;
+        const uint8_t *kbase = (const uint8_t *)kc + head_row0 * C::ROW_BYTES;
+        const uint8_t *vbase = (const uint8_t *)vc + head_row0 * C::ROW_BYTES;
+        bf16x8_t qop[C::KSTEPS];
+        load_q_operand<D>(q, (size_t)i * h + j * G + min(hb * C::HB + r, G - 1), qd, qop);
+
+        MfmaState<D> st;
+        st.reset();
+        run_steps<D>(kbase, vbase, (const uint8_t *)(q + ((size_t)i * h + j * G) * D), s0 + sub,
+                     s1, wph, L, S, qop, st, vbuf[w], lane, qk_scale_log2);
+
+        __syncthreads();  // every wave is done with its staging buffer
+        float *mrg = (float *)&vbuf[0][0];
+        float *mls = mrg + C::NW * C::HB * D;
+        publish_state<D>(st, mrg, mls, w, lane);
+        __syncthreads();
+        const bool whole = s0 == 0 && s1 == n;
+        const int slot = seg == 0 ? 0 : 1;
+        for (int idx = threadIdx.x; idx < HBT * D; idx += 64 * C::NW) {
+            const int hs = idx / D, x_ = idx % D;  // head slot within the unit
+            if (hs >= G) continue;
+            float M, l;
+            const float o = merge_waves<D>(mrg, mls, (hs / C::HB) * wph, wph, hs % C::HB, x_, M, l);
+            const size_t hrow = (size_t)i * h + j * G + hs;
+            if (whole) {
+                out[hrow * D + x_] = o / l;
+            } else {
+                const size_t prow = ((size_t)wg * 2 + slot) * HBT + hs;
+                store_coherent(part_o + prow * D + x_, o);
+                if (x_ == 0) store_coherent(part_ml + prow, make_float2(M, l));
+            }
+        }
+        if (!whole) {  // uniform: publish the piece, count arrivals, last one merges
+            const int u0 = pre_i + j * n;
+            const int wf = owner_of(u0, T, nwg), wl = owner_of(u0 + n - 1, T, nwg);
+            __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are done
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                const uint32_t old = atomicAdd(&counters[(size_t)i * g + j], 1u);
+                const bool last = old == (uint32_t)(wl - wf);
+                if (last) atomicExch(&counters[(size_t)i * g + j], 0u);  // ready for the next call
+                last_flag = last;
+            }
+            __syncthreads();
+            if (last_flag) {
+                const int slot_f = range_start(wf, T, nwg) < u0 ? 1 : 0;
+                for (int idx = threadIdx.x; idx < G * D; idx += 64 * C::NW) {
+                    const int hs = idx / D, x_ = idx % D;
+                    out[((size_t)i * h + j * G + hs) * D + x_] =
+                        merge_pieces<D>(part_o, part_ml, wf, wl, slot_f, HBT, hs, x_);
+                }
+            }
+        }
+        __syncthreads();  // scratch reused by the next segment
+        x += s1 - s0;
     }
 }
 
@@ -370,14 +1040,31 @@ combine_kernel(const float *__restrict__ part_o, const float2 *__restrict__ part
     }
     const int n = (L + chunk - 1) / chunk;
     const float2 *ml = part_ml + row * nsplit;
-    float M = -INFINITY;
-    for (int s = 0; s < n; s++) M = fmaxf(M, ml[s].x);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < n; s++) {
-        const float2 e = ml[s];
-        const float wgt = fast_exp2(e.x - M);
-        den = fmaf(wgt, e.y, den);
-        num = fmaf(wgt, part_o[(row * nsplit + s) * D + x], num);
+    const float *po = part_o + row * nsplit * D + x;
+    // online merge, eight partitions' loads in flight at a time
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    for (int s0 = 0; s0 < n; s0 += 8) {
+        float2 e[8];
+        float o[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const bool ok = s0 + k < n;
+            e[k] = ok ? ml[s0 + k] : make_float2(-INFINITY, 0.f);
+            o[k] = ok ? po[(size_t)(s0 + k) * D] : 0.f;
+        }
+        float Mb = M;
+#pragma unroll
+        for (int k = 0; k < 8; k++) Mb = fmaxf(Mb, e[k].x);
+        const float rs = M == -INFINITY ? 0.f : fast_exp2(M - Mb);
+        num *= rs;
+        den *= rs;
+        M = Mb;
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const float wgt = e[k].x == -INFINITY ? 0.f : fast_exp2(e[k].x - M);
+            num = fmaf(wgt, o[k], num);
+            den = fmaf(wgt, e[k].y, den);
+        }
     }
     out[row * D + x] = num / den;
 }
@@ -407,10 +1094,14 @@ mqa_status check_sizes(int b, int h, int g, int S, int d, mqa_dtype dt, int spli
     return MQA_OK;
 }
 
-int resolve_chunk(int b, int h, int g, int S, int split_chunk) {
+// Query heads one work-group scores: bf16 runs on the matrix cores in blocks
+// of 16 heads, fp32 on the vector ALUs in blocks of up to 8.
+int wg_heads(mqa_dtype dt, int G) { return dt == MQA_BF16 ? 16 : heads_per_wg(G); }
+
+int resolve_chunk(int b, int h, int g, int S, mqa_dtype dt, int split_chunk) {
     if (split_chunk > 0) return split_chunk;
     const int G = h / g;
-    const long long groups = (long long)b * g * ((G + heads_per_wg(G) - 1) / heads_per_wg(G));
+    const long long groups = (long long)b * g * ((G + wg_heads(dt, G) - 1) / wg_heads(dt, G));
     const long long want = (kTargetGroups + groups - 1) / groups;  // partitions per group
     long long c = ((long long)S + want - 1) / want;
     c = (c + kTile - 1) / kTile * kTile;
@@ -425,6 +1116,57 @@ size_t workspace_for(int b, int h, int S, int d, int chunk) {
     const size_t rows = (size_t)b * h * nsplit;
     const size_t o_bytes = (rows * d * sizeof(float) + 255) & ~(size_t)255;
     return o_bytes + rows * sizeof(float2);
+}
+
+// The balanced schedule serves bf16 calls with automatic partitioning, up to
+// kStreamMaxSeq sequences and 64 query heads per K/V head.
+// It pays where there are many units (sequence, K/V head) whose lengths
+// differ; with few units every unit would be cut into many pieces and the
+// fixed partitions (merged in parallel by combine_kernel) do better.
+bool use_streamk(int b, int h, int g, int S, mqa_dtype dt, int split_chunk, mqa_kernel kernel) {
+    const int nhb = (h / g + 15) / 16;
+    const long long units = (long long)b * g;
+    if (units * ((S + 31) / 32) >= (1ll << 31)) return false;  // step indices are 32-bit
+    return dt == MQA_BF16 && kernel != MQA_KERNEL_VALU && split_chunk == 0 &&
+           b <= kStreamMaxSeq && units >= kStreamMinUnits && units <= kStreamMaxUnits &&
+           (nhb == 1 || nhb == 2 || nhb == 4);
+}
+
+// [partials o][partials (m, l)]
+size_t streamk_workspace(int h, int g, int d) {
+    const size_t hbt = (size_t)((h / g + 15) / 16) * 16;
+    const size_t rows = (size_t)kStreamMaxWG * 2 * hbt;
+    const size_t o_bytes = (rows * d * sizeof(float) + 255) & ~(size_t)255;
+    return o_bytes + rows * sizeof(float2);
+}
+
+// Workspace: [arrival counters, kCounterBytes][partials of whichever path]
+size_t workspace_need(int b, int h, int g, int S, int d, mqa_dtype dt, int split_chunk,
+                      mqa_kernel kernel) {
+    size_t need = workspace_for(b, h, S, d, resolve_chunk(b, h, g, S, dt, split_chunk));
+    if (use_streamk(b, h, g, S, dt, split_chunk, kernel)) {
+        const size_t sk = streamk_workspace(h, g, d);
+        if (sk > need) need = sk;
+    }
+    return kCounterBytes + need;
+}
+
+// Work-groups of the balanced schedule: two per compute unit (longer ranges
+// mean fewer cut units; the kernel uses fewer when the call has fewer than
+// kStreamMinSteps steps for each).
+int streamk_wgs(int b, int g, int S) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            cus = v;
+    }
+    const long long tmax = (long long)b * g * ((S + 31) / 32);
+    long long n = (tmax + kStreamMinSteps - 1) / kStreamMinSteps;
+    if (n > 2ll * cus) n = 2ll * cus;
+    if (n > kStreamMaxWG) n = kStreamMaxWG;
+    if (n < 1) n = 1;
+    return (int)n;
 }
 
 template <typename T, int D, int HPW>
@@ -475,13 +1217,14 @@ uint64_t mqa_kv_bytes(int layers, int g, int64_t S, int d, int dtype_bytes) {
 
 int mqa_decode_resolve_chunk(int b, int h, int g, int S, int d, mqa_dtype dt, int split_chunk) {
     if (check_sizes(b, h, g, S, d, dt, split_chunk) != MQA_OK) return -1;
-    return resolve_chunk(b, h, g, S, split_chunk);
+    return resolve_chunk(b, h, g, S, dt, split_chunk);
 }
 
 size_t mqa_decode_workspace_bytes(int b, int h, int g, int S, int d, mqa_dtype dt,
                                   int split_chunk) {
     if (check_sizes(b, h, g, S, d, dt, split_chunk) != MQA_OK) return 0;
-    return workspace_for(b, h, S, d, resolve_chunk(b, h, g, S, split_chunk));
+    // enough for every kernel choice of mqa_decode_attn_kernel
+    return workspace_need(b, h, g, S, d, dt, split_chunk, MQA_KERNEL_AUTO);
 }
 
 mqa_status mqa_append_kv(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
@@ -502,30 +1245,67 @@ mqa_status mqa_append_kv(void *k_cache, void *v_cache, const void *k_new, const 
     return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
 }
 
-mqa_status mqa_decode_attn(const void *q, const void *k_cache, const void *v_cache,
-                           const int32_t *seq_lens, int b, int h, int g, int S, int d,
-                           mqa_dtype dt, float scale, float *out, void *workspace,
-                           size_t workspace_bytes, int split_chunk, int32_t *err_flags,
-                           hipStream_t stream) {
+mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *seq_lens, int b, int h, int g, int S, int d,
+                                  mqa_dtype dt, float scale, float *out, void *workspace,
+                                  size_t workspace_bytes, int split_chunk, int32_t *err_flags,
+                                  mqa_kernel kernel, hipStream_t stream) {
     if (!q || !k_cache || !v_cache || !seq_lens || !out) return MQA_ERR_NULL;
     mqa_status st = check_sizes(b, h, g, S, d, dt, split_chunk);
     if (st != MQA_OK) return st;
+    if (kernel != MQA_KERNEL_AUTO && kernel != MQA_KERNEL_VALU && kernel != MQA_KERNEL_MFMA)
+        return MQA_ERR_UNSUPPORTED;
+    if (kernel == MQA_KERNEL_MFMA && dt != MQA_BF16) return MQA_ERR_UNSUPPORTED;
+    const bool use_mfma = dt == MQA_BF16 && kernel != MQA_KERNEL_VALU;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
         return MQA_ERR_ALIGN;
-    const int chunk = resolve_chunk(b, h, g, S, split_chunk);
+    const int chunk = resolve_chunk(b, h, g, S, dt, split_chunk);
     const int nsplit = (S + chunk - 1) / chunk;
-    const size_t need = workspace_for(b, h, S, d, chunk);
+    const size_t need = workspace_need(b, h, g, S, d, dt, split_chunk, kernel);
     if (!workspace || workspace_bytes < need) return MQA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MQA_ERR_ALIGN;
+    const float qs_ = scale * kLog2e;
+
+    if (use_streamk(b, h, g, S, dt, split_chunk, kernel)) {
+        const int G = h / g;
+        const int nhb = (G + 15) / 16;
+        const int nwg = streamk_wgs(b, g, S);
+        const size_t rows = (size_t)kStreamMaxWG * 2 * nhb * 16;
+        const size_t o_bytes = (rows * d * sizeof(float) + 255) & ~(size_t)255;
+        uint32_t *counters = (uint32_t *)workspace;
+        float *po = (float *)((uint8_t *)workspace + kCounterBytes);
+        float2 *pml = (float2 *)((uint8_t *)workspace + kCounterBytes + o_bytes);
+        if (d == 128)
+            hipLaunchKernelGGL(streamk_mfma_kernel<128>, dim3(nwg), dim3(256), 0, stream,
+                               (const uint16_t *)q, (const uint16_t *)k_cache, (const uint16_t *)v_cache,
+                               seq_lens, b, h, g, S, G, nhb, qs_, out, po, pml, counters, err_flags);
+        else
+            hipLaunchKernelGGL(streamk_mfma_kernel<64>, dim3(nwg), dim3(256), 0, stream,
+                               (const uint16_t *)q, (const uint16_t *)k_cache, (const uint16_t *)v_cache,
+                               seq_lens, b, h, g, S, G, nhb, qs_, out, po, pml, counters, err_flags);
+        return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+    }
 
     const size_t rows = (size_t)b * h * nsplit;
-    float *part_o = (float *)workspace;
-    float2 *part_ml =
-        (float2 *)((uint8_t *)workspace + ((rows * d * sizeof(float) + 255) & ~(size_t)255));
+    uint8_t *wsp = (uint8_t *)workspace + kCounterBytes;  // the counters are never touched here
+    float *part_o = (float *)wsp;
+    float2 *part_ml = (float2 *)(wsp + ((rows * d * sizeof(float) + 255) & ~(size_t)255));
     const float qs = scale * kLog2e;
     const int hpw = heads_per_wg(h / g);
 
-    if (dt == MQA_BF16) {
+    if (use_mfma) {
+        const int G = h / g;
+        const int nhb = (G + 15) / 16;
+        dim3 grid(nsplit, g * nhb, b);
+        if (d == 128)
+            hipLaunchKernelGGL(split_mfma_kernel<128>, grid, dim3(256), 0, stream, (const uint16_t *)q,
+                               (const uint16_t *)k_cache, (const uint16_t *)v_cache, seq_lens, h, g, S, G,
+                               nhb, chunk, nsplit, qs, part_o, part_ml);
+        else
+            hipLaunchKernelGGL(split_mfma_kernel<64>, grid, dim3(256), 0, stream, (const uint16_t *)q,
+                               (const uint16_t *)k_cache, (const uint16_t *)v_cache, seq_lens, h, g, S, G,
+                               nhb, chunk, nsplit, qs, part_o, part_ml);
+    } else if (dt == MQA_BF16) {
         if (d == 128) dispatch_rows<uint16_t, 128>(hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream);
         else dispatch_rows<uint16_t, 64>(hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream);
     } else {
@@ -541,6 +1321,16 @@ mqa_status mqa_decode_attn(const void *q, const void *k_cache, const void *v_cac
         hipLaunchKernelGGL(combine_kernel<64>, dim3(h, b), dim3(64), 0, stream, part_o, part_ml,
                            seq_lens, h, S, chunk, nsplit, out, err_flags);
     return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+}
+
+mqa_status mqa_decode_attn(const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *seq_lens, int b, int h, int g, int S, int d,
+                           mqa_dtype dt, float scale, float *out, void *workspace,
+                           size_t workspace_bytes, int split_chunk, int32_t *err_flags,
+                           hipStream_t stream) {
+    return mqa_decode_attn_kernel(q, k_cache, v_cache, seq_lens, b, h, g, S, d, dt, scale, out,
+                                  workspace, workspace_bytes, split_chunk, err_flags,
+                                  MQA_KERNEL_AUTO, stream);
 }
 
 }  // extern "C"
