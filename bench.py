@@ -94,6 +94,7 @@ def main() -> int:
     err = torch.zeros(1, dtype=torch.int32, device=dev)
 
     kernel = {"auto": mqa.KERNEL_AUTO, "valu": mqa.KERNEL_VALU, "mfma": mqa.KERNEL_MFMA}[args.kernel]
+    schedule = mqa.decode_schedule(w.b, w.h, w.g, w.S, w.d, w.dtype, args.split_chunk, kernel)
     B = w.elem_bytes
     kv_read = int(sum(2 * w.g * int(L) * w.d * B for L in lens))
     dec_bytes = kv_read + w.b * w.h * w.d * B + w.b * w.h * w.d * 4
@@ -162,7 +163,8 @@ def main() -> int:
     tf = os.path.join(ROOT, "profiles", f"decode_{w.name}_traffic.json")
     if os.path.exists(tf):
         rec = json.load(open(tf))
-        if rec.get("source_sha") == source_sha() and rec.get("split_chunk", 0) == args.split_chunk:
+        if (rec.get("source_sha") == source_sha() and rec.get("split_chunk", 0) == args.split_chunk
+                and args.kernel == "auto"):
             traffic = rec.get("bytes_per_launch")
 
     result = {
@@ -182,13 +184,15 @@ def main() -> int:
         "data": "synthetic: seeded N(0,1) q/K/V in HBM, no trained weights",
         "config": {"workload": w.name, "b": w.b, "h": w.h, "g": w.g, "d_h": w.d, "capacity": w.S,
                    "seq_lens": "fixed %d" % w.L if w.L else f"U[{w.L_lo},{w.L_hi}] (sum {int(lens.sum())})",
-                   "layers": layers, "split_chunk": chunk, "cache_copies_rotated": reps,
+                   "layers": layers, "schedule": schedule,
+                   "split_chunk": chunk if schedule != "mfma-balanced" else None,
+                   "cache_copies_rotated": reps,
                    "accumulate": "fp32", "out": "fp32"},
         "algorithmic_bytes_per_step": step_bytes,
         "flops_per_step": flops_per_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": "mqa_decode_attn (partition + combine kernels)",
+            "kernel": "mqa_decode_attn launch, schedule " + schedule,
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

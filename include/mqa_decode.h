@@ -156,6 +156,19 @@ mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache,
                                   int split_chunk, int32_t *err_flags,
                                   mqa_kernel kernel, hipStream_t stream);
 
+/* The schedule mqa_decode_attn_kernel runs for these arguments. */
+typedef enum {
+    MQA_SCHEDULE_VALU_PARTITIONS = 0, /* vector-ALU partition kernel + combine kernel */
+    MQA_SCHEDULE_MFMA_PARTITIONS = 1, /* matrix-core partition kernel + combine kernel */
+    MQA_SCHEDULE_MFMA_BALANCED = 2    /* one matrix-core kernel, equal work per
+                                         work-group, in-kernel merge of cut units */
+} mqa_schedule;
+
+/* Which schedule (above) a call with these arguments runs; -1 if the
+ * arguments are invalid. Host only, enqueues nothing. */
+int mqa_decode_schedule(int b, int h, int g, int S, int d, mqa_dtype dt,
+                        int split_chunk, mqa_kernel kernel);
+
 /* Static text for a status code (never NULL). */
 const char *mqa_status_string(mqa_status s);
 

@@ -33,6 +33,19 @@ def test_exports_every_declared_function():
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
 
 
+def test_schedule_choice():
+    # many ragged (sequence, K/V head) units in bf16: the balanced schedule
+    assert mqa.decode_schedule(64, 64, 8, 4096, 128, mqa.BF16) == "mfma-balanced"
+    # few units (MQA, small batch): fixed partitions on the matrix cores
+    assert mqa.decode_schedule(4, 32, 1, 32768, 128, mqa.BF16) == "mfma-partitions"
+    # an explicit partition length, or the vector-ALU kernel, or fp32
+    assert mqa.decode_schedule(64, 64, 8, 4096, 128, mqa.BF16, 512) == "mfma-partitions"
+    assert mqa.decode_schedule(64, 64, 8, 4096, 128, mqa.BF16, 0, mqa.KERNEL_VALU) == "valu-partitions"
+    assert mqa.decode_schedule(1, 8, 1, 129, 64, mqa.F32) == "valu-partitions"
+    with pytest.raises(ValueError):
+        mqa.decode_schedule(1, 8, 1, 129, 64, mqa.F32, 0, mqa.KERNEL_MFMA)
+
+
 def test_status_strings():
     for s in range(7):
         assert mqa.status_string(s)

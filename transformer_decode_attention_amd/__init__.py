@@ -28,7 +28,7 @@ import torch
 
 __all__ = [
     "append_kv", "decode_attn", "decode_workspace_bytes", "decode_workspace", "decode_resolve_chunk",
-    "kv_bytes", "status_string", "MQAError", "LIB_PATH", "DEVERR_SEQLEN",
+    "decode_schedule", "kv_bytes", "status_string", "MQAError", "LIB_PATH", "DEVERR_SEQLEN",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa_decode.so")
@@ -42,8 +42,10 @@ KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
 
 EXPORTS = (
     "mqa_append_kv", "mqa_decode_workspace_bytes", "mqa_decode_resolve_chunk",
-    "mqa_decode_attn", "mqa_decode_attn_kernel", "mqa_status_string", "mqa_kv_bytes",
+    "mqa_decode_attn", "mqa_decode_attn_kernel", "mqa_decode_schedule", "mqa_status_string",
+    "mqa_kv_bytes",
 )
+SCHEDULES = {0: "valu-partitions", 1: "mfma-partitions", 2: "mfma-balanced"}
 
 
 class MQAError(RuntimeError):
@@ -71,6 +73,8 @@ def _load() -> ctypes.CDLL:
                                          ctypes.c_float, vp, vp, ctypes.c_size_t, i32, vp, i32,
                                          vp]
     L.mqa_decode_attn_kernel.restype = i32
+    L.mqa_decode_schedule.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    L.mqa_decode_schedule.restype = i32
     L.mqa_status_string.argtypes = [i32]
     L.mqa_status_string.restype = ctypes.c_char_p
     L.mqa_kv_bytes.argtypes = [i32, i32, i64, i32, i32]
@@ -121,6 +125,15 @@ def decode_workspace(b, h, g, S, d, dtype, device, split_chunk: int = 0) -> torc
 def decode_resolve_chunk(b, h, g, S, d, dtype, split_chunk: int = 0) -> int:
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
     return int(lib().mqa_decode_resolve_chunk(b, h, g, S, d, code, split_chunk))
+
+
+def decode_schedule(b, h, g, S, d, dtype, split_chunk: int = 0, kernel: int = 0) -> str:
+    """Name of the schedule mqa_decode_attn_kernel runs for these arguments."""
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    v = int(lib().mqa_decode_schedule(b, h, g, S, d, code, split_chunk, kernel))
+    if v < 0:
+        raise ValueError("invalid arguments")
+    return SCHEDULES[v]
 
 
 def _ptr(t) -> ctypes.c_void_p | None:

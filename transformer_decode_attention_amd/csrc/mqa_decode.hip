@@ -1215,6 +1215,16 @@ uint64_t mqa_kv_bytes(int layers, int g, int64_t S, int d, int dtype_bytes) {
     return 2ull * (uint64_t)layers * (uint64_t)g * (uint64_t)S * (uint64_t)d * (uint64_t)dtype_bytes;
 }
 
+int mqa_decode_schedule(int b, int h, int g, int S, int d, mqa_dtype dt, int split_chunk,
+                        mqa_kernel kernel) {
+    if (check_sizes(b, h, g, S, d, dt, split_chunk) != MQA_OK) return -1;
+    if (kernel != MQA_KERNEL_AUTO && kernel != MQA_KERNEL_VALU && kernel != MQA_KERNEL_MFMA) return -1;
+    if (kernel == MQA_KERNEL_MFMA && dt != MQA_BF16) return -1;
+    if (use_streamk(b, h, g, S, dt, split_chunk, kernel)) return MQA_SCHEDULE_MFMA_BALANCED;
+    return (dt == MQA_BF16 && kernel != MQA_KERNEL_VALU) ? MQA_SCHEDULE_MFMA_PARTITIONS
+                                                         : MQA_SCHEDULE_VALU_PARTITIONS;
+}
+
 int mqa_decode_resolve_chunk(int b, int h, int g, int S, int d, mqa_dtype dt, int split_chunk) {
     if (check_sizes(b, h, g, S, d, dt, split_chunk) != MQA_OK) return -1;
     return resolve_chunk(b, h, g, S, dt, split_chunk);
