@@ -49,7 +49,8 @@ extern "C" {
 typedef enum {
     MQA_OK = 0,
     MQA_ERR_NULL = 1,        /* a required pointer is NULL */
-    MQA_ERR_SHAPE = 2,       /* a size < 1, or h not a multiple of g */
+    MQA_ERR_SHAPE = 2,       /* a size < 1, h not a multiple of g, b > 65535,
+                                or one K/V head's S rows (S*d*elem) >= 2 GiB */
     MQA_ERR_UNSUPPORTED = 3, /* d not 64/128, unknown dtype, bad split_chunk */
     MQA_ERR_ALIGN = 4,       /* a tensor pointer not 16-byte aligned */
     MQA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
@@ -67,11 +68,6 @@ typedef enum {
 
 /* Bit ORed into *err_flags by the kernels: some seq_lens[i] outside [1, S]. */
 #define MQA_DEVERR_SEQLEN 1
-
-/* Leading bytes of every decode workspace that hold arrival counters (see
- * mqa_decode_attn): zero before the workspace's first use, zero again after
- * every call that completes. */
-#define MQA_WORKSPACE_COUNTER_BYTES (256u * 1024u)
 
 /*
  * Append this step's K/V rows to the cache, bit-exactly.
@@ -119,12 +115,7 @@ int mqa_decode_resolve_chunk(int b, int h, int g, int S, int d, mqa_dtype dt,
  *   scale            : score scale, normally 1/sqrt(d)
  *   out              : [b][h][d] fp32, fully overwritten
  *   workspace        : >= mqa_decode_workspace_bytes(...) bytes of device
- *                      memory, 16-byte aligned. Its first
- *                      MQA_WORKSPACE_COUNTER_BYTES bytes are arrival counters
- *                      of the partitions: they must be zero before the
- *                      workspace is first used (e.g. hipMemset once at
- *                      allocation), and every call leaves them zero when it
- *                      completes. The rest holds partial results; its
+ *                      memory, 16-byte aligned, for partial results; its
  *                      contents on entry are ignored.
  *   split_chunk      : positions per partition, a multiple of 64, or 0 for
  *                      the automatic choice
@@ -160,8 +151,9 @@ mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache,
 typedef enum {
     MQA_SCHEDULE_VALU_PARTITIONS = 0, /* vector-ALU partition kernel + combine kernel */
     MQA_SCHEDULE_MFMA_PARTITIONS = 1, /* matrix-core partition kernel + combine kernel */
-    MQA_SCHEDULE_MFMA_BALANCED = 2    /* one matrix-core kernel, equal work per
-                                         work-group, in-kernel merge of cut units */
+    MQA_SCHEDULE_MFMA_BALANCED = 2    /* matrix-core kernel with equal work per
+                                         compute unit + a merge kernel for the
+                                         units cut between work-groups */
 } mqa_schedule;
 
 /* Which schedule (above) a call with these arguments runs; -1 if the

@@ -104,6 +104,7 @@ def append(**kw):
     (dict(h=6, g=4), mqa.ERR_SHAPE),           # h not a multiple of g
     (dict(b=0), mqa.ERR_SHAPE),
     (dict(S=0), mqa.ERR_SHAPE),
+    (dict(S=1 << 23), mqa.ERR_SHAPE),         # one head's bf16 rows reach 2 GiB
     (dict(d=96), mqa.ERR_UNSUPPORTED),
     (dict(dt=7), mqa.ERR_UNSUPPORTED),
     (dict(chunk=100), mqa.ERR_UNSUPPORTED),

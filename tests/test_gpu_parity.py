@@ -325,9 +325,11 @@ def test_large_batch_uses_fixed_partitions():
 
 
 def test_workspace_reused_across_shapes_and_kernels():
-    """One workspace for many calls of different shapes and paths: the arrival
-    counters come back to zero after every call, partials never collide."""
+    """One workspace for many calls of different shapes and paths; its contents
+    on entry are ignored (it starts as NaN bytes and is refilled between
+    calls), and partials never collide."""
     big = mqa.decode_workspace(256, 64, 8, 4096, 128, torch.bfloat16, DEV)
+    big.fill_(0xFF)  # NaN as float
     cases = [
         (W.Workload("r1", b=64, h=64, g=8, d=128, S=2048, dtype=torch.bfloat16, seed=31), 0, mqa.KERNEL_AUTO),
         (W.Workload("r2", b=256, h=16, g=2, d=64, S=700, dtype=torch.bfloat16, seed=32), 0, mqa.KERNEL_AUTO),
@@ -344,5 +346,4 @@ def test_workspace_reused_across_shapes_and_kernels():
             torch.cuda.synchronize()
             ref, _ = oracle_ref(t)
             compare(out, ref, f"{w.name} rep {rep}")
-    counters = big[:mqa.WORKSPACE_COUNTER_BYTES]
-    assert int(counters.count_nonzero().item()) == 0
+            big.fill_(0xFF if rep == 0 else 0x7F)

@@ -34,7 +34,6 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa_decode.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)
-WORKSPACE_COUNTER_BYTES = 256 * 1024  # MQA_WORKSPACE_COUNTER_BYTES
 F32, BF16 = 0, 1
 DEVERR_SEQLEN = 1
 
@@ -115,11 +114,11 @@ def decode_workspace_bytes(b, h, g, S, d, dtype, split_chunk: int = 0) -> int:
 
 
 def decode_workspace(b, h, g, S, d, dtype, device, split_chunk: int = 0) -> torch.Tensor:
-    """A workspace for these sizes, zero-filled (its counter region must start at zero)."""
+    """A workspace for these sizes (its contents on entry are ignored)."""
     n = decode_workspace_bytes(b, h, g, S, d, dtype, split_chunk)
     if n == 0:
         raise ValueError("invalid sizes")
-    return torch.zeros(n, dtype=torch.uint8, device=device)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def decode_resolve_chunk(b, h, g, S, d, dtype, split_chunk: int = 0) -> int:

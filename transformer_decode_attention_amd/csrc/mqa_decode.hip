@@ -76,10 +76,22 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// 16-byte streaming load (read once, not kept in the caches).
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x4_t load_stream16(const void *p) {
-    return __builtin_nontemporal_load((const u32x4_t *)p);
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 16 bytes
+// Raw buffer descriptor over [base, base + bytes): offsets are 32-bit, the
+// base sits in scalar registers, and a load whose offset is at or past
+// `bytes` returns zeros without a memory access. Word 3 is the raw-buffer
+// format of the gfx9 family.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;  // wave-uniform by construction
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0,
+                                             (int)bytes, 0x00020000);
+}
+// 16 bytes through a descriptor, non-temporal (streamed once)
+__device__ __forceinline__ u32x4_t buffer_stream16(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
 }
 
 // 16-byte global -> LDS copy. The LDS destination of lane l is
@@ -510,6 +522,18 @@ struct MfmaCfg {
     static_assert(NW * HB * (D + 2) * 4 <= NW * VBUF, "merge scratch must fit");
 };
 
+// The lane index as a value the compiler must recompute where it is used:
+// addresses derived from it in rarely taken code are then not hoisted out of
+// the hot loop (where they would hold registers for its whole length).
+__device__ __forceinline__ int opaque_lane(int lane) {
+    asm volatile("" : "+v"(lane));
+    return lane;
+}
+// x of lane src (0..63)
+__device__ __forceinline__ float shfl_from(float x, int src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
+}
+
 __device__ __forceinline__ int kslot(int qd, int e) { return e < 4 ? 4 * qd + e : 12 + 4 * qd + e; }
 
 // One wave's running state for 16 query heads.
@@ -543,28 +567,27 @@ struct StepData {
     u32x4_t vld[MfmaCfg<D>::VLOADS];
 };
 
-// Issue the loads of step [t0, t0+32); rows past the capacity are clamped
-// (and masked later).
+// Issue the loads of step [t0, t0+32) through the descriptors of one K/V
+// head's rows; rows past the descriptors' extent come back as zeros (and are
+// masked later), so a step past the end loads nothing from memory.
 template <int D>
-__device__ __forceinline__ void load_step(const uint8_t *__restrict__ kbase,
-                                          const uint8_t *__restrict__ vbase, int t0, int S,
-                                          int lane, StepData<D> &sd) {
+__device__ __forceinline__ void load_step(rsrc_t krs, rsrc_t vrs, int t0, int lane,
+                                          StepData<D> &sd) {
     using C = MfmaCfg<D>;
     const int r = lane & 15, qd = lane >> 4;
     const int vl_row = lane / C::CPR, vl_chunk = lane % C::CPR;
+    const uint32_t base = (uint32_t)t0 * C::ROW_BYTES;
+    const uint32_t kl = base + r * C::ROW_BYTES + 16 * qd;
+    const uint32_t vl = base + vl_row * C::ROW_BYTES + 16 * vl_chunk;
 #pragma unroll
-    for (int pb = 0; pb < 2; pb++) {
-        const int row = min(t0 + 16 * pb + r, S - 1);
+    for (int pb = 0; pb < 2; pb++)
 #pragma unroll
         for (int k = 0; k < C::KSTEPS; k++)
             sd.kop[pb][k] = __builtin_bit_cast(
-                bf16x8_t, load_stream16(kbase + (size_t)row * C::ROW_BYTES + 64 * k + 16 * qd));
-    }
+                bf16x8_t, buffer_stream16(krs, kl + 16 * pb * C::ROW_BYTES + 64 * k));
 #pragma unroll
-    for (int ii = 0; ii < C::VLOADS; ii++) {
-        const int row = min(t0 + ii * C::RPI + vl_row, S - 1);
-        sd.vld[ii] = load_stream16(vbase + (size_t)row * C::ROW_BYTES + 16 * vl_chunk);
-    }
+    for (int ii = 0; ii < C::VLOADS; ii++)
+        sd.vld[ii] = buffer_stream16(vrs, vl + ii * C::RPI * C::ROW_BYTES);
 }
 
 // One 32-position step [t0, t0+32) of one wave from loaded data, rows >=
@@ -610,8 +633,10 @@ __device__ __forceinline__ void compute_step(const StepData<D> &sd, int t0, int 
 #pragma unroll
     for (int e = 1; e < 8; e++) smax = fmaxf(smax, s2[e]);
     if (__any(smax > st.m_ref + kSlack)) {  // wave-uniform
-        float mt = fmaxf(smax, __shfl_xor(smax, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));   // max over the head's 32 positions
+        // (shuffle addresses built here, not kept live across the whole loop)
+        const int ln = opaque_lane(lane);
+        float mt = fmaxf(smax, shfl_from(smax, ln ^ 16));
+        mt = fmaxf(mt, shfl_from(mt, ln ^ 32));   // max over the head's 32 positions
         mt = fmaxf(mt, st.m_ref);
         const float alpha = fast_exp2(st.m_ref - mt);  // per head r
         st.m_ref = mt;
@@ -619,7 +644,7 @@ __device__ __forceinline__ void compute_step(const StepData<D> &sd, int t0, int 
         // acc rows are heads 4qd+v: fetch their factors from lanes 4qd+v
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-            const float av = __shfl(alpha, 4 * qd + v);
+            const float av = shfl_from(alpha, 4 * (ln >> 4) + v);
 #pragma unroll
             for (int nb = 0; nb < C::NB; nb++) st.acc[nb][v] *= av;
         }
@@ -652,16 +677,13 @@ __device__ __forceinline__ void compute_step(const StepData<D> &sd, int t0, int 
     }
 }
 
-// Steps s_begin, s_begin+stride, ... < s_end of one K/V head, with the loads
-// of the next step in flight while this one computes (two register sets,
-// alternating). Past the last step the prefetch reads `idle` instead, one
-// row (ROW_BYTES) this wave has just read and that sits in cache, so every
-// iteration issues the same loads without a second trip to HBM.
+// Steps s_begin, s_begin+stride, ... < s_end of one K/V head (descriptors
+// over its first L rows), with the loads of the next step in flight while
+// this one computes (two register sets, alternating). Past the last step the
+// prefetch asks for rows past the end, which load nothing.
 template <int D>
-__device__ __forceinline__ void run_steps(const uint8_t *__restrict__ kbase,
-                                          const uint8_t *__restrict__ vbase,
-                                          const uint8_t *__restrict__ idle, int s_begin,
-                                          int s_end, int stride, int t_end, int S,
+__device__ __forceinline__ void run_steps(rsrc_t krs, rsrc_t vrs, int s_begin, int s_end,
+                                          int stride, int t_end, int S,
                                           const bf16x8_t (&qop)[MfmaCfg<D>::KSTEPS],
                                           MfmaState<D> &st, uint8_t *vb, int lane,
                                           float qk_scale_log2) {
@@ -669,12 +691,9 @@ __device__ __forceinline__ void run_steps(const uint8_t *__restrict__ kbase,
     int stp = s_begin;
     if (stp >= s_end) return;
     StepData<D> a, b;
-    load_step<D>(kbase, vbase, stp * C::STEP, S, lane, a);
-    // the prefetch source, chosen without branching (one copy of the loads)
-    auto prefetch = [&](int nx, StepData<D> &sd) {
-        const bool more = nx < s_end;
-        load_step<D>(more ? kbase : idle, more ? vbase : idle, more ? nx * C::STEP : 0,
-                     more ? S : 1, lane, sd);
+    load_step<D>(krs, vrs, stp * C::STEP, lane, a);
+    auto prefetch = [&](int nx, StepData<D> &sd) __attribute__((always_inline)) {
+        load_step<D>(krs, vrs, nx < s_end ? nx * C::STEP : S, lane, sd);
     };
     while (true) {
         int nx = stp + stride;
@@ -755,8 +774,8 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     const int r = lane & 15, qd = lane >> 4;
 
     const size_t head_row0 = ((size_t)i * g + j) * (size_t)S;
-    const uint8_t *kbase = (const uint8_t *)kc + head_row0 * C::ROW_BYTES;
-    const uint8_t *vbase = (const uint8_t *)vc + head_row0 * C::ROW_BYTES;
+    const rsrc_t krs = make_rsrc((const uint8_t *)kc + head_row0 * C::ROW_BYTES, L * C::ROW_BYTES);
+    const rsrc_t vrs = make_rsrc((const uint8_t *)vc + head_row0 * C::ROW_BYTES, L * C::ROW_BYTES);
 
     // padded heads reuse the last real one and are never written out
     bf16x8_t qop[C::KSTEPS];
@@ -765,9 +784,8 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     MfmaState<D> st;
     st.reset();
     // steps of this partition, numbered from the sequence start
-    const uint8_t *idle = (const uint8_t *)(q + ((size_t)i * h + j * G) * D);  // a q row
-    run_steps<D>(kbase, vbase, idle, t_begin / C::STEP + w, t_begin / C::STEP + nsteps, C::NW,
-                 t_end, S, qop, st, vbuf[w], lane, qk_scale_log2);
+    run_steps<D>(krs, vrs, t_begin / C::STEP + w, t_begin / C::STEP + nsteps, C::NW, t_end, S,
+                 qop, st, vbuf[w], lane, qk_scale_log2);
 
     __syncthreads();  // every wave is done with its staging buffer
     float *mrg = (float *)&vbuf[0][0];
@@ -792,75 +810,74 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
 // Work unit u = (sequence i, K/V head j) with n_i = ceil(L_i / 32) steps;
 // units are numbered i-major and their steps laid end to end (T steps in
 // all; sequences with an invalid length contribute none). Work-group w of
-// nwg takes steps [w*T/nwg, (w+1)*T/nwg): equal work whatever the lengths
-// (nwg is cut on the device so that every range holds >= kStreamMinSteps
-// steps). Its waves are split as (block of 16 query heads, sub-stream): with
-// nhb blocks, 4/nhb waves share a block and interleave the steps, so the
-// waves of different blocks read each K/V step at about the same time (the
-// second read comes from L2). A unit entirely inside one range is normalised
-// and written to `out` directly. A unit cut by range boundaries leaves, in
-// each work-group that touches it, a partial (m, l, o) in slot 0 (the range's
-// first segment) or slot 1 (its last) and bumps the unit's arrival counter;
-// the last work-group to arrive merges the pieces, writes `out` and puts the
-// counter back to zero.
+// nwg (one per compute unit) takes steps [w*T/nwg, (w+1)*T/nwg): equal work
+// whatever the lengths (nwg is cut on the device so that every range holds
+// >= kStreamMinSteps steps). Its waves are split into blocks of 16 query
+// heads; with nhb blocks, each block's waves walk the whole range, so the
+// blocks read each K/V step at about the same time (the second read comes
+// from L2). A unit entirely inside one range is normalised and written to
+// `out` directly. A unit cut by range boundaries leaves, for each work-group
+// and head block that touch it, a partial (m, l, o) in slot 0 (the range's
+// first segment) or slot 1 (its last) and bumps the arrival counter of
+// (unit, head block); the last arrival merges the pieces, writes `out` and
+// puts the counter back to zero.
 
 constexpr int kStreamMaxSeq = 1024;    // sequences per call on this schedule (prefix sums in LDS)
 constexpr int kStreamMaxWG = 1024;     // work-groups (bounds the workspace)
 constexpr int kStreamMinUnits = 256;   // fewer (sequence, K/V head) units: fixed partitions
-constexpr int kStreamMinSteps = 8;     // steps per work-group range, at least
-constexpr int kStreamMaxUnits = 65536; // arrival counters at the head of the workspace
-constexpr size_t kCounterBytes = (size_t)kStreamMaxUnits * 4;
-static_assert(kCounterBytes == MQA_WORKSPACE_COUNTER_BYTES, "counter region size");
+constexpr int kStreamMinSteps = 16;    // steps per work-group range, at least
+constexpr int kStreamWaves = 4;        // waves per work-group (one work-group per compute unit)
+constexpr int kRing = 16;              // segment records per head block
 
 // steps of sequence i (0 for an invalid length)
 __device__ __forceinline__ int seq_steps(int L, int S) { return (L < 1 || L > S) ? 0 : (L + 31) / 32; }
 
-// Exclusive prefix over sequences of units*steps, into pre[0..b]; whole
-// work-group (256 threads). Each thread sums a contiguous run of sequences;
-// the runs are scanned with wave shuffles and the four wave totals added.
-// The host keeps the total below 2^31.
+// Exclusive prefixes over sequences, whole work-group (NT threads): steps
+// of units, pre[0..b] (units_per_seq units per valid sequence), and valid
+// sequences, vpre[0..b]. Each thread takes a contiguous run of sequences;
+// the runs are scanned with wave shuffles and the wave totals added. The
+// host keeps the step total below 2^31.
+template <int NT>
 __device__ __forceinline__ void unit_prefix(const int32_t *__restrict__ seq_lens, int b, int S,
-                                            int units_per_seq, int *pre, int *wtot) {
+                                            int units_per_seq, int *pre, int *vpre, int2 *wtot) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int per = (b + 255) / 256;
+    const int per = (b + NT - 1) / NT;
     const int a0 = min(b, t * per), a1 = min(b, a0 + per);
-    int run = 0;
-    for (int a = a0; a < a1; a++) run += seq_steps(seq_lens[a], S);
-    int v = run;  // inclusive scan over the wave
+    int run = 0, vrun = 0;
+    for (int a = a0; a < a1; a++) {
+        const int n = seq_steps(seq_lens[a], S);
+        run += n;
+        vrun += n > 0;
+    }
+    int v = run, vv = vrun;  // inclusive scans over the wave
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(v, off);
-        if (lane >= off) v += y;
+        const int y = __shfl_up(v, off), yy = __shfl_up(vv, off);
+        if (lane >= off) {
+            v += y;
+            vv += yy;
+        }
     }
-    if (lane == 63) wtot[w] = v;
+    if (lane == 63) wtot[w] = make_int2(v, vv);
     __syncthreads();
-    int acc = v - run;
-    for (int k = 0; k < w; k++) acc += wtot[k];
+    int acc = v - run, vacc = vv - vrun;
+    for (int k = 0; k < w; k++) {
+        acc += wtot[k].x;
+        vacc += wtot[k].y;
+    }
     acc *= units_per_seq;
     for (int a = a0; a < a1; a++) {
+        const int n = seq_steps(seq_lens[a], S);
         pre[a] = acc;
-        acc += seq_steps(seq_lens[a], S) * units_per_seq;
+        vpre[a] = vacc;
+        acc += n * units_per_seq;
+        vacc += n > 0;
     }
-    if (t == 255) pre[b] = acc;
+    if (t == NT - 1) {
+        pre[b] = acc;
+        vpre[b] = vacc;
+    }
     __syncthreads();
-}
-
-// Partials of cut units are written and read with agent-coherent accesses
-// (they bypass the per-XCD caches), so only these bytes, not whole caches,
-// need to reach the point of coherence before a unit's arrival count moves.
-__device__ __forceinline__ void store_coherent(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_coherent(float2 *p, float2 v) {
-    __hip_atomic_store((uint64_t *)p, __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float2 load_coherent(const float2 *p) {
-    return __builtin_bit_cast(float2, __hip_atomic_load((const uint64_t *)p, __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT));
 }
 
 // Work-group owning global step x; the first step of work-group w's range.
@@ -871,153 +888,340 @@ __device__ __forceinline__ int range_start(int w, int T, int nwg) {
     return (int)((long long)T * w / nwg);
 }
 
-// Merge pieces [wf, wl] of one head slot hs, column x; the first owner's
-// piece is in slot slot_f, the others in slot 0. Loads go out eight pieces
-// at a time.
-template <int D>
-__device__ __forceinline__ float merge_pieces(const float *__restrict__ part_o,
-                                              const float2 *__restrict__ part_ml, int wf, int wl,
-                                              int slot_f, int HBT, int hs, int x) {
-    float M = -INFINITY, num = 0.f, den = 0.f;
-    for (int p0 = wf; p0 <= wl; p0 += 8) {
-        float2 e[8];
-        float o[8];
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-            const int wg = p0 + k;
-            if (wg <= wl) {
-                const size_t prow = ((size_t)wg * 2 + (wg == wf ? slot_f : 0)) * HBT + hs;
-                e[k] = load_coherent(part_ml + prow);
-                o[k] = load_coherent(part_o + prow * D + x);
-            } else {
-                e[k] = make_float2(-INFINITY, 0.f);
-                o[k] = 0.f;
-            }
-        }
-        float Mb = M;
-#pragma unroll
-        for (int k = 0; k < 8; k++) Mb = fmaxf(Mb, e[k].x);
-        const float rs = M == -INFINITY ? 0.f : fast_exp2(M - Mb);
-        num *= rs;
-        den *= rs;
-        M = Mb;
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-            const float wgt = e[k].x == -INFINITY ? 0.f : fast_exp2(e[k].x - M);
-            num = fmaf(wgt, o[k], num);
-            den = fmaf(wgt, e[k].y, den);
-        }
-    }
-    return num / den;
+// Flags between the waves of one work-group, in LDS. A flag is written after
+// the data it guards has left the wave (lgkmcnt drained), and the data is read
+// only after the flag has been seen; the asm statements also keep the
+// compiler from moving LDS accesses across them.
+__device__ __forceinline__ void lds_drain() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void lds_flag_set(int *f, int v) {
+    __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// (the loops test a wave-uniform copy of the flag, so that they exit uniformly)
+__device__ __forceinline__ void lds_flag_wait(int *f, int v) {
+    while (__builtin_amdgcn_readfirstlane(
+               __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != v)
+        __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
 }
 
+// One work-group per compute unit, kStreamWaves waves. The waves of a head
+// block claim the steps of the range one at a time from a counter in LDS, so
+// a wave that the hardware serves faster simply takes more steps; the loads
+// of a wave's next claimed step are issued before its current step is
+// computed, across unit boundaries too. A wave keeps one running state while
+// its claims stay in one unit. When its next claim leaves the unit it stores
+// the state in its LDS slot and adds (steps done, its bit) to the segment's
+// record; the wave whose addition completes the segment's step count merges
+// the slots named in the record into its own state and writes the result
+// (out, or a partial of a cut unit). No wave waits for another's progress:
+// the only waits are for a slot or a record to be released by a merge, and
+// each is on a segment that ends earlier in the range, so they cannot form a
+// cycle. Which wave computes which step depends on timing, so the rounding
+// of the sums can differ between calls.
 template <int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
+__global__ void __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
 streamk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
                     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seq_lens, int b,
                     int h, int g, int S, int G, int nhb, float qk_scale_log2,
                     float *__restrict__ out, float *__restrict__ part_o,
-                    float2 *__restrict__ part_ml, uint32_t *__restrict__ counters,
+                    float2 *__restrict__ part_ml, int4 *__restrict__ cut_desc,
                     int32_t *__restrict__ err) {
     using C = MfmaCfg<D>;
-    __shared__ __attribute__((aligned(16))) uint8_t vbuf[C::NW][C::VBUF];
-    __shared__ int pre[kStreamMaxSeq + 1];
-    __shared__ int wtot[4];
-    __shared__ int last_flag;
+    constexpr int NW = kStreamWaves;
+    __shared__ __attribute__((aligned(16))) uint8_t vbuf[NW][C::VBUF];
+    __shared__ f32x4_t slot_o[NW][C::NB][64];  // a wave's acc, lane-native order
+    __shared__ float2 slot_ml[NW][C::HB];      // (m, l) per head
+    __shared__ int slot_busy[NW];              // 1 while the slot holds a state not merged yet
+    __shared__ int rec_tag[4][kRing];          // ordinal of the segment the record serves now
+    __shared__ uint32_t rec_val[4][kRing];     // (steps done << 8) | waves (bit per wave of the block)
+    __shared__ int cursor[4];                  // steps of the range claimed so far, per head block
+    __shared__ int first_seq, last_seq;        // sequences holding the range's first and last steps
+    __shared__ int pre[kStreamMaxSeq + 1];     // steps before sequence i
+    __shared__ int vpre[kStreamMaxSeq + 1];    // valid sequences before sequence i
+    __shared__ int2 wtot[NW];
 
-    unit_prefix(seq_lens, b, S, g, pre, wtot);
+    if (threadIdx.x < NW) slot_busy[threadIdx.x] = 0;
+    if (threadIdx.x < 4) cursor[threadIdx.x] = 0;
+    unit_prefix<64 * NW>(seq_lens, b, S, g, pre, vpre, wtot);  // its barriers publish the above
     // everything that steers the loops below is wave-uniform: keep it scalar
     const int T = __builtin_amdgcn_readfirstlane(pre[b]);
     const int wg = blockIdx.x;
+    const int nwg = __builtin_amdgcn_readfirstlane(max(1, min((int)gridDim.x, T / kStreamMinSteps)));
 
     // sequences with a length out of range: NaN rows and the error flag
     // (work-group 0, one thread per sequence; such rows are rare)
     if (wg == 0) {
-        for (int i = threadIdx.x; i < b; i += blockDim.x) {
+        for (int i = threadIdx.x; i < b; i += 64 * NW) {
             if (pre[i + 1] != pre[i]) continue;
             for (int idx = 0; idx < h * D; idx++) out[(size_t)i * h * D + idx] = __builtin_nanf("");
             if (err) atomicOr(err, MQA_DEVERR_SEQLEN);
         }
     }
-    const int nwg = max(1, min((int)gridDim.x, T / kStreamMinSteps));
-    if (T == 0 || wg >= nwg) return;  // uniform across the work-group
+    if (T == 0 || wg >= nwg) {  // uniform across the work-group
+        if (threadIdx.x == 0) cut_desc[wg] = make_int4(-1, 0, 0, 0);
+        return;
+    }
     const int x0 = range_start(wg, T, nwg), x1 = range_start(wg + 1, T, nwg);
+
+    // The range's last segment [xl, x1) is claimed first, then [x0, xl): a
+    // unit cut at x1 is then finished early on both sides of the cut, and
+    // its merge does not fall at the end of the range. Segments are numbered
+    // in claim order (sn: 0 for the last segment, then 1 + ordinal - ordinal
+    // of the first, where the ordinal numbers units with steps densely: valid
+    // sequences before i, times g, plus j). Record e serves the segments with
+    // sn = e mod kRing one after the other, so a segment waits only for an
+    // earlier-claimed one to release its record.
+    for (int i = threadIdx.x; i < b; i += 64 * NW) {
+        if (pre[i] <= x0 && x0 < pre[i + 1]) first_seq = i;
+        if (pre[i] < x1 && x1 <= pre[i + 1]) last_seq = i;
+    }
+    if (threadIdx.x < 4 * kRing) {
+        rec_tag[threadIdx.x / kRing][threadIdx.x % kRing] = threadIdx.x % kRing;
+        rec_val[threadIdx.x / kRing][threadIdx.x % kRing] = 0;
+    }
+    __syncthreads();
+    const int i_first = __builtin_amdgcn_readfirstlane(first_seq);
+    const int i_last = __builtin_amdgcn_readfirstlane(last_seq);
+    const int ord0 = __builtin_amdgcn_readfirstlane(vpre[i_first]) * g +
+                     (x0 - __builtin_amdgcn_readfirstlane(pre[i_first])) /
+                         seq_steps(__builtin_amdgcn_readfirstlane(seq_lens[i_first]), S);
+    const int n_last = seq_steps(__builtin_amdgcn_readfirstlane(seq_lens[i_last]), S);
+    const int p_last = __builtin_amdgcn_readfirstlane(pre[i_last]);
+    const int u0_last = p_last + (x1 - 1 - p_last) / n_last * n_last;  // the last unit's first step
+    const int xl = max(x0, u0_last);
+    const int len_last = x1 - xl;
+    // A unit cut at x1 whose first step is in this range is described for
+    // streamk_combine_kernel: (sequence, K/V head, last range holding a
+    // piece, slot of this range's piece).
+    if (threadIdx.x == 0)
+        cut_desc[wg] = (u0_last >= x0 && u0_last + n_last > x1)
+                           ? make_int4(i_last, (u0_last - p_last) / n_last,
+                                       owner_of(u0_last + n_last - 1, T, nwg), u0_last > x0 ? 1 : 0)
+                           : make_int4(-1, 0, 0, 0);
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, qd = lane >> 4;
-    const int wph = C::NW / nhb;  // waves per head block
-    const int hb = w / wph, sub = w % wph;
+    const int wph = NW / nhb;  // waves per head block
+    const int hb = w / wph, wb = w % wph;
     const int HBT = nhb * C::HB;  // head slots per unit
 
-    int seg = 0;
-    int i = 0;
-    for (int x = x0; x < x1; seg++) {
-        // unit containing step x: sequence i (pre is non-decreasing; advance), head j
-        while (__builtin_amdgcn_readfirstlane(pre[i + 1]) <= x) i++;
-        const int pre_i = __builtin_amdgcn_readfirstlane(pre[i]);
-        const int L = __builtin_amdgcn_readfirstlane(seq_lens[i]);
-        const int n = seq_steps(L, S);
-        const int local = x - pre_i;
-        const int j = local / n;
-        const int s0 = local - j * n;
-        const int s1 = min(n, s0 + (x1 - x));
+    // next step of the range for this head block, in claim order (x1: none left)
+    auto claim = [&]() __attribute__((always_inline)) {
+        int c = 0;
+        if (lane == 0) c = atomicAdd(&cursor[hb], 1);
+        c = __builtin_amdgcn_readfirstlane(__shfl(c, 0));
+        return c >= x1 - x0 ? x1 : c < len_last ? xl + c : x0 + (c - len_last);
+    };
+    // unit holding flat step tt: sequence i_, its length L_ and steps n_, K/V
+    // head j_, first flat step u0_ (claims move forward, but for the one jump
+    // from the last segment back to x0)
+    auto locate = [&](int tt, int &i_, int &L_, int &n_, int &j_, int &u0_)
+                      __attribute__((always_inline)) {
+        if (tt >= u0_ && tt < u0_ + n_) return;
+        if (tt < u0_) i_ = i_first;
+        while (__builtin_amdgcn_readfirstlane(pre[i_ + 1]) <= tt) i_++;
+        L_ = __builtin_amdgcn_readfirstlane(seq_lens[i_]);
+        n_ = seq_steps(L_, S);
+        const int p = __builtin_amdgcn_readfirstlane(pre[i_]);
+        j_ = (tt - p) / n_;
+        u0_ = p + j_ * n_;
+    };
+    // descriptors over the first L_ rows of K/V head (i_, j_)
+    auto kv_rsrc = [&](const uint16_t *base, int i_, int j_, int L_) __attribute__((always_inline)) {
+        return make_rsrc((const uint8_t *)base + ((size_t)i_ * g + j_) * (size_t)S * C::ROW_BYTES,
+                         (uint32_t)L_ * C::ROW_BYTES);
+    };
+    // padded heads reuse the last real one and are never written out
+    auto q_row = [&](int i_, int j_) __attribute__((always_inline)) {
+        return (size_t)i_ * h + j_ * G + min(hb * C::HB + r, G - 1);
+    };
 
-        const size_t head_row0 = ((size_t)i * g + j) * (size_t)S;
-        const uint8_t *kbase = (const uint8_t *)kc + head_row0 * C::ROW_BYTES;
-        const uint8_t *vbase = (const uint8_t *)vc + head_row0 * C::ROW_BYTES;
-        bf16x8_t qop[C::KSTEPS];
-        load_q_operand<D>(q, (size_t)i * h + j * G + min(hb * C::HB + r, G - 1), qd, qop);
+    int t = claim();
+    if (t >= x1) return;  // nothing left for this wave
+    int ci = i_first, cL = 0, cn = 0, cj = 0, cu0 = 0;
+    locate(t, ci, cL, cn, cj, cu0);
+    rsrc_t krs = kv_rsrc(kc, ci, cj, cL), vrs = kv_rsrc(vc, ci, cj, cL);
+    StepData<D> A, B;
+    load_step<D>(krs, vrs, (t - cu0) * C::STEP, lane, A);
+    bf16x8_t qop[C::KSTEPS];
+    load_q_operand<D>(q, q_row(ci, cj), qd, qop);
+    MfmaState<D> st;
+    st.reset();
+    int mine = 0;  // steps of the current unit in this wave's state
 
-        MfmaState<D> st;
-        st.reset();
-        run_steps<D>(kbase, vbase, (const uint8_t *)(q + ((size_t)i * h + j * G) * D), s0 + sub,
-                     s1, wph, L, S, qop, st, vbuf[w], lane, qk_scale_log2);
-
-        __syncthreads();  // every wave is done with its staging buffer
-        float *mrg = (float *)&vbuf[0][0];
-        float *mls = mrg + C::NW * C::HB * D;
-        publish_state<D>(st, mrg, mls, w, lane);
-        __syncthreads();
-        const bool whole = s0 == 0 && s1 == n;
-        const int slot = seg == 0 ? 0 : 1;
-        for (int idx = threadIdx.x; idx < HBT * D; idx += 64 * C::NW) {
-            const int hs = idx / D, x_ = idx % D;  // head slot within the unit
-            if (hs >= G) continue;
-            float M, l;
-            const float o = merge_waves<D>(mrg, mls, (hs / C::HB) * wph, wph, hs % C::HB, x_, M, l);
-            const size_t hrow = (size_t)i * h + j * G + hs;
-            if (whole) {
-                out[hrow * D + x_] = o / l;
-            } else {
-                const size_t prow = ((size_t)wg * 2 + slot) * HBT + hs;
-                store_coherent(part_o + prow * D + x_, o);
-                if (x_ == 0) store_coherent(part_ml + prow, make_float2(M, l));
-            }
+    // this wave is done with the segment (range ∩ unit (ci, cj))
+    auto finish_segment = [&]() __attribute__((always_inline)) {
+        const int lane = opaque_lane(threadIdx.x & 63);
+        const int r = lane & 15, qd = lane >> 4;
+        const int seg_s = max(x0, cu0), seg_e = min(x1, cu0 + cn);
+        const int sn = seg_s == xl ? 0 : __builtin_amdgcn_readfirstlane(vpre[ci]) * g + cj - ord0 + 1;
+        const int e = sn & (kRing - 1);
+        const float l_head = st.l_lane + __shfl_xor(st.l_lane, 16);
+        const float l_tot = l_head + __shfl_xor(l_head, 32);  // head r
+        // rows of acc are heads 4qd+v
+        float Mv[4], Lv[4];
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            Mv[v] = __shfl(st.m_ref, 4 * qd + v);
+            Lv[v] = __shfl(l_tot, 4 * qd + v);
         }
-        if (!whole) {  // uniform: publish the piece, count arrivals, last one merges
-            const int u0 = pre_i + j * n;
-            const int wf = owner_of(u0, T, nwg), wl = owner_of(u0 + n - 1, T, nwg);
-            __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are done
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                const uint32_t old = atomicAdd(&counters[(size_t)i * g + j], 1u);
-                const bool last = old == (uint32_t)(wl - wf);
-                if (last) atomicExch(&counters[(size_t)i * g + j], 0u);  // ready for the next call
-                last_flag = last;
-            }
-            __syncthreads();
-            if (last_flag) {
-                const int slot_f = range_start(wf, T, nwg) < u0 ? 1 : 0;
-                for (int idx = threadIdx.x; idx < G * D; idx += 64 * C::NW) {
-                    const int hs = idx / D, x_ = idx % D;
-                    out[((size_t)i * h + j * G + hs) * D + x_] =
-                        merge_pieces<D>(part_o, part_ml, wf, wl, slot_f, HBT, hs, x_);
+        if (mine == seg_e - seg_s) {  // the whole segment was this wave's: pass the record on
+            lds_flag_wait(&rec_tag[hb][e], sn);
+            if (lane == 0) lds_flag_set(&rec_tag[hb][e], sn + kRing);
+        } else {  // other waves have steps of this segment
+            lds_flag_wait(&slot_busy[w], 0);
+#pragma unroll
+            for (int nb = 0; nb < C::NB; nb++) slot_o[w][nb][lane] = st.acc[nb];
+            if (qd == 0) slot_ml[w][r] = make_float2(st.m_ref, l_tot);
+            if (lane == 0) slot_busy[w] = 1;
+            lds_drain();
+            lds_flag_wait(&rec_tag[hb][e], sn);  // an earlier segment may still hold the record
+            const uint32_t add = ((uint32_t)mine << 8) | (1u << wb);
+            uint32_t old = 0;
+            if (lane == 0) old = atomicAdd(&rec_val[hb][e], add);
+            const uint32_t now_ = __builtin_amdgcn_readfirstlane(__shfl(old, 0)) + add;
+            if ((int)(now_ >> 8) != seg_e - seg_s) return;  // not the last: the state waits in the slot
+            // the last share in: merge the others, release their slots and the record
+            if (lane == 0) slot_busy[w] = 0;
+            for (uint32_t m = now_ & 0xffu & ~(1u << wb); m; m &= m - 1) {
+                const int ww = hb * wph + __builtin_ctz(m);
+                float a_own[4], a_oth[4];
+#pragma unroll
+                for (int v = 0; v < 4; v++) {
+                    const float2 eo = slot_ml[ww][4 * qd + v];
+                    const float Mn = fmaxf(Mv[v], eo.x);
+                    a_own[v] = Mv[v] == -INFINITY ? 0.f : fast_exp2(Mv[v] - Mn);
+                    a_oth[v] = eo.x == -INFINITY ? 0.f : fast_exp2(eo.x - Mn);
+                    Lv[v] = fmaf(Lv[v], a_own[v], a_oth[v] * eo.y);
+                    Mv[v] = Mn;
                 }
+#pragma unroll
+                for (int nb = 0; nb < C::NB; nb++) {
+                    const f32x4_t o = slot_o[ww][nb][lane];
+#pragma unroll
+                    for (int v = 0; v < 4; v++)
+                        st.acc[nb][v] = fmaf(st.acc[nb][v], a_own[v], a_oth[v] * o[v]);
+                }
+                lds_drain();
+                if (lane == 0) lds_flag_set(&slot_busy[ww], 0);
+            }
+            if (lane == 0) {
+                rec_val[hb][e] = 0;
+                lds_drain();
+                lds_flag_set(&rec_tag[hb][e], sn + kRing);
             }
         }
-        __syncthreads();  // scratch reused by the next segment
-        x += s1 - s0;
+        if (seg_s != cu0 || seg_e != cu0 + cn) {
+            // a piece of a cut unit: slot 0 for the range's first segment, 1
+            // for its last; streamk_combine_kernel merges the pieces
+            const int slot = seg_s == x0 ? 0 : 1;
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const int hs = hb * C::HB + 4 * qd + v;
+                if (hs >= G) continue;
+                const size_t prow = ((size_t)wg * 2 + slot) * HBT + hs;
+#pragma unroll
+                for (int nb = 0; nb < C::NB; nb++) part_o[prow * D + 16 * nb + r] = st.acc[nb][v];
+                if (r == 0) part_ml[prow] = make_float2(Mv[v], Lv[v]);
+            }
+            return;
+        }
+        // a whole unit: its rows, normalised
+        const size_t row0 = (size_t)ci * h + cj * G;  // first query head of the unit
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const int hs = hb * C::HB + 4 * qd + v;
+            if (hs >= G) continue;
+            const float inv = 1.f / Lv[v];
+#pragma unroll
+            for (int nb = 0; nb < C::NB; nb++)
+                out[(row0 + hs) * D + 16 * nb + r] = st.acc[nb][v] * inv;
+        }
+    };
+
+    // one step: claim and prefetch the next, compute this one, close the
+    // segment if the next claim leaves it
+    auto body = [&](StepData<D> &now, StepData<D> &later) __attribute__((always_inline)) -> bool {
+        const int tn = claim();
+        const bool more = tn < x1;
+        int ni = ci, nL = cL, nn = cn, nj = cj, nu0 = cu0;
+        if (more) locate(tn, ni, nL, nn, nj, nu0);
+        const bool next_unit = more && nu0 != cu0;
+        const rsrc_t nks = next_unit ? kv_rsrc(kc, ni, nj, nL) : krs;
+        const rsrc_t nvs = next_unit ? kv_rsrc(vc, ni, nj, nL) : vrs;
+        // nothing left: rows past the end, which load nothing
+        load_step<D>(nks, nvs, more ? (tn - nu0) * C::STEP : S, lane, later);
+        compute_step<D>(now, (t - cu0) * C::STEP, cL, qop, st, vbuf[w], lane, qk_scale_log2);
+        mine++;
+        // the next unit's q, in flight during the segment's close
+        if (next_unit) load_q_operand<D>(q, q_row(ni, nj), qd, qop);
+        if (!more || next_unit) {
+            finish_segment();
+            st.reset();
+            mine = 0;
+        }
+        if (!more) return false;
+        krs = nks;
+        vrs = nvs;
+        // wave-uniform; said explicitly so that the loop state stays scalar
+        t = __builtin_amdgcn_readfirstlane(tn);
+        ci = __builtin_amdgcn_readfirstlane(ni);
+        cL = __builtin_amdgcn_readfirstlane(nL);
+        cn = __builtin_amdgcn_readfirstlane(nn);
+        cj = __builtin_amdgcn_readfirstlane(nj);
+        cu0 = __builtin_amdgcn_readfirstlane(nu0);
+        return true;
+    };
+    while (body(A, B) && body(B, A)) {
+    }
+}
+
+// Units cut between ranges, after streamk_mfma_kernel: block w merges the
+// pieces of the unit described by cut_desc[w] (the first range's piece in
+// its slot cut_desc[w].w, the following ranges' pieces in slot 0) and writes
+// its rows of `out`. The pieces go in range order, so the merge is the same
+// every call.
+template <int D>
+__global__ void __launch_bounds__(256)
+streamk_combine_kernel(const float *__restrict__ part_o, const float2 *__restrict__ part_ml,
+                       const int4 *__restrict__ cut_desc, int h, int G, int HBT,
+                       float *__restrict__ out) {
+    const int wf = blockIdx.x;
+    const int4 dsc = cut_desc[wf];
+    if (dsc.x < 0) return;
+    const int wl = dsc.z, slot_f = dsc.w;
+    const size_t row0 = (size_t)dsc.x * h + (size_t)dsc.y * G;  // first query head of the unit
+    constexpr int C4 = D / 4;                                     // float4 columns per row
+    for (int idx = threadIdx.x; idx < G * C4; idx += 256) {
+        const int hs = idx / C4, c = (idx % C4) * 4;
+        float M = -INFINITY, den = 0.f;
+        f32x4_t num = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int p0 = wf; p0 <= wl; p0 += 4) {  // four pieces' loads in flight at a time
+            float2 e[4];
+            f32x4_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const int p = p0 + k;
+                const size_t prow = ((size_t)p * 2 + (p == wf ? slot_f : 0)) * HBT + hs;
+                e[k] = p <= wl ? part_ml[prow] : make_float2(-INFINITY, 0.f);
+                o[k] = p <= wl ? *(const f32x4_t *)(part_o + prow * D + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+            float Mb = M;
+#pragma unroll
+            for (int k = 0; k < 4; k++) Mb = fmaxf(Mb, e[k].x);
+            const float rs = M == -INFINITY ? 0.f : fast_exp2(M - Mb);
+            num *= rs;
+            den *= rs;
+            M = Mb;
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const float wgt = e[k].x == -INFINITY ? 0.f : fast_exp2(e[k].x - M);
+                num += wgt * o[k];
+                den = fmaf(wgt, e[k].y, den);
+            }
+        }
+        *(f32x4_t *)(out + (row0 + hs) * D + c) = num * (1.f / den);
     }
 }
 
@@ -1091,6 +1295,8 @@ mqa_status check_sizes(int b, int h, int g, int S, int d, mqa_dtype dt, int spli
     if (d != 64 && d != 128) return MQA_ERR_UNSUPPORTED;
     if (dt != MQA_F32 && dt != MQA_BF16) return MQA_ERR_UNSUPPORTED;
     if (split_chunk < 0 || split_chunk % kTile != 0) return MQA_ERR_UNSUPPORTED;
+    // one K/V head's S rows stay below 2 GiB: kernels address them with 32-bit offsets
+    if ((long long)S * d * (dt == MQA_BF16 ? 2 : 4) >= (1ll << 31)) return MQA_ERR_SHAPE;
     return MQA_OK;
 }
 
@@ -1128,32 +1334,41 @@ bool use_streamk(int b, int h, int g, int S, mqa_dtype dt, int split_chunk, mqa_
     const long long units = (long long)b * g;
     if (units * ((S + 31) / 32) >= (1ll << 31)) return false;  // step indices are 32-bit
     return dt == MQA_BF16 && kernel != MQA_KERNEL_VALU && split_chunk == 0 &&
-           b <= kStreamMaxSeq && units >= kStreamMinUnits && units <= kStreamMaxUnits &&
+           b <= kStreamMaxSeq && units >= kStreamMinUnits &&
            (nhb == 1 || nhb == 2 || nhb == 4);
 }
 
-// [partials o][partials (m, l)]
-size_t streamk_workspace(int h, int g, int d) {
+// Balanced-schedule workspace: [partials o][partials (m, l)][cut-unit
+// descriptors], each part 256-byte aligned; two pieces per work-group.
+struct StreamkLayout {
+    size_t o_bytes, ml_off, desc_off, total;
+};
+StreamkLayout streamk_layout(int h, int g, int d) {
     const size_t hbt = (size_t)((h / g + 15) / 16) * 16;
     const size_t rows = (size_t)kStreamMaxWG * 2 * hbt;
-    const size_t o_bytes = (rows * d * sizeof(float) + 255) & ~(size_t)255;
-    return o_bytes + rows * sizeof(float2);
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    StreamkLayout L;
+    L.o_bytes = up(rows * d * sizeof(float));
+    L.ml_off = L.o_bytes;
+    L.desc_off = L.ml_off + up(rows * sizeof(float2));
+    L.total = L.desc_off + kStreamMaxWG * sizeof(int4);
+    return L;
 }
 
-// Workspace: [arrival counters, kCounterBytes][partials of whichever path]
+// Workspace bytes: the larger of the two paths' needs (the same workspace
+// serves every kernel choice)
 size_t workspace_need(int b, int h, int g, int S, int d, mqa_dtype dt, int split_chunk,
                       mqa_kernel kernel) {
     size_t need = workspace_for(b, h, S, d, resolve_chunk(b, h, g, S, dt, split_chunk));
     if (use_streamk(b, h, g, S, dt, split_chunk, kernel)) {
-        const size_t sk = streamk_workspace(h, g, d);
+        const size_t sk = streamk_layout(h, g, d).total;
         if (sk > need) need = sk;
     }
-    return kCounterBytes + need;
+    return need;
 }
 
-// Work-groups of the balanced schedule: two per compute unit (longer ranges
-// mean fewer cut units; the kernel uses fewer when the call has fewer than
-// kStreamMinSteps steps for each).
+// Work-groups of the balanced schedule: one per compute unit (the kernel
+// uses fewer when the call has fewer than kStreamMinSteps steps for each).
 int streamk_wgs(int b, int g, int S) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
@@ -1163,7 +1378,7 @@ int streamk_wgs(int b, int g, int S) {
     }
     const long long tmax = (long long)b * g * ((S + 31) / 32);
     long long n = (tmax + kStreamMinSteps - 1) / kStreamMinSteps;
-    if (n > 2ll * cus) n = 2ll * cus;
+    if (n > cus) n = cus;
     if (n > kStreamMaxWG) n = kStreamMaxWG;
     if (n < 1) n = 1;
     return (int)n;
@@ -1280,24 +1495,28 @@ mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache, const void
         const int G = h / g;
         const int nhb = (G + 15) / 16;
         const int nwg = streamk_wgs(b, g, S);
-        const size_t rows = (size_t)kStreamMaxWG * 2 * nhb * 16;
-        const size_t o_bytes = (rows * d * sizeof(float) + 255) & ~(size_t)255;
-        uint32_t *counters = (uint32_t *)workspace;
-        float *po = (float *)((uint8_t *)workspace + kCounterBytes);
-        float2 *pml = (float2 *)((uint8_t *)workspace + kCounterBytes + o_bytes);
-        if (d == 128)
-            hipLaunchKernelGGL(streamk_mfma_kernel<128>, dim3(nwg), dim3(256), 0, stream,
+        const StreamkLayout L = streamk_layout(h, g, d);
+        float *po = (float *)workspace;
+        float2 *pml = (float2 *)((uint8_t *)workspace + L.ml_off);
+        int4 *desc = (int4 *)((uint8_t *)workspace + L.desc_off);
+        if (d == 128) {
+            hipLaunchKernelGGL(streamk_mfma_kernel<128>, dim3(nwg), dim3(64 * kStreamWaves), 0, stream,
                                (const uint16_t *)q, (const uint16_t *)k_cache, (const uint16_t *)v_cache,
-                               seq_lens, b, h, g, S, G, nhb, qs_, out, po, pml, counters, err_flags);
-        else
-            hipLaunchKernelGGL(streamk_mfma_kernel<64>, dim3(nwg), dim3(256), 0, stream,
+                               seq_lens, b, h, g, S, G, nhb, qs_, out, po, pml, desc, err_flags);
+            hipLaunchKernelGGL(streamk_combine_kernel<128>, dim3(nwg), dim3(256), 0, stream, po, pml,
+                               desc, h, G, nhb * 16, out);
+        } else {
+            hipLaunchKernelGGL(streamk_mfma_kernel<64>, dim3(nwg), dim3(64 * kStreamWaves), 0, stream,
                                (const uint16_t *)q, (const uint16_t *)k_cache, (const uint16_t *)v_cache,
-                               seq_lens, b, h, g, S, G, nhb, qs_, out, po, pml, counters, err_flags);
+                               seq_lens, b, h, g, S, G, nhb, qs_, out, po, pml, desc, err_flags);
+            hipLaunchKernelGGL(streamk_combine_kernel<64>, dim3(nwg), dim3(256), 0, stream, po, pml,
+                               desc, h, G, nhb * 16, out);
+        }
         return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
     }
 
     const size_t rows = (size_t)b * h * nsplit;
-    uint8_t *wsp = (uint8_t *)workspace + kCounterBytes;  // the counters are never touched here
+    uint8_t *wsp = (uint8_t *)workspace;
     float *part_o = (float *)wsp;
     float2 *part_ml = (float2 *)(wsp + ((rows * d * sizeof(float) + 255) & ~(size_t)255));
     const float qs = scale * kLog2e;
