@@ -839,13 +839,16 @@ __device__ __forceinline__ int seq_steps(int L, int S) { return (L < 1 || L > S)
 // host keeps the step total below 2^31.
 template <int NT>
 __device__ __forceinline__ void unit_prefix(const int32_t *__restrict__ seq_lens, int b, int S,
-                                            int units_per_seq, int *pre, int *vpre, int2 *wtot) {
+                                            int units_per_seq, int *pre, int *vpre, int *lens,
+                                            int2 *wtot) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int per = (b + NT - 1) / NT;
     const int a0 = min(b, t * per), a1 = min(b, a0 + per);
     int run = 0, vrun = 0;
     for (int a = a0; a < a1; a++) {
-        const int n = seq_steps(seq_lens[a], S);
+        const int L = seq_lens[a];
+        lens[a] = L;  // kept in LDS for the rest of the kernel
+        const int n = seq_steps(L, S);
         run += n;
         vrun += n > 0;
     }
@@ -867,7 +870,7 @@ __device__ __forceinline__ void unit_prefix(const int32_t *__restrict__ seq_lens
     }
     acc *= units_per_seq;
     for (int a = a0; a < a1; a++) {
-        const int n = seq_steps(seq_lens[a], S);
+        const int n = seq_steps(lens[a], S);
         pre[a] = acc;
         vpre[a] = vacc;
         acc += n * units_per_seq;
@@ -904,7 +907,10 @@ __device__ __forceinline__ void lds_flag_wait(int *f, int v) {
     asm volatile("" ::: "memory");
 }
 
-// One work-group per compute unit, kStreamWaves waves. The waves of a head
+// One work-group per compute unit, NW waves (four: with 2 steps in flight per
+// wave that is ~32 MB in flight on the chip, several times what the memory
+// needs to stay busy; more waves only lengthen the queues, measured slower).
+// The waves of a head
 // block claim the steps of the range one at a time from a counter in LDS, so
 // a wave that the hardware serves faster simply takes more steps; the loads
 // of a wave's next claimed step are issued before its current step is
@@ -918,8 +924,8 @@ __device__ __forceinline__ void lds_flag_wait(int *f, int v) {
 // each is on a segment that ends earlier in the range, so they cannot form a
 // cycle. Which wave computes which step depends on timing, so the rounding
 // of the sums can differ between calls.
-template <int D>
-__global__ void __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 8)))
 streamk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
                     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seq_lens, int b,
                     int h, int g, int S, int G, int nhb, float qk_scale_log2,
@@ -927,7 +933,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
                     float2 *__restrict__ part_ml, int4 *__restrict__ cut_desc,
                     int32_t *__restrict__ err) {
     using C = MfmaCfg<D>;
-    constexpr int NW = kStreamWaves;
+    static_assert(NW == 4 || NW == 8, "waves per work-group (the segment records hold 8 bits)");
     __shared__ __attribute__((aligned(16))) uint8_t vbuf[NW][C::VBUF];
     __shared__ f32x4_t slot_o[NW][C::NB][64];  // a wave's acc, lane-native order
     __shared__ float2 slot_ml[NW][C::HB];      // (m, l) per head
@@ -938,11 +944,12 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
     __shared__ int first_seq, last_seq;        // sequences holding the range's first and last steps
     __shared__ int pre[kStreamMaxSeq + 1];     // steps before sequence i
     __shared__ int vpre[kStreamMaxSeq + 1];    // valid sequences before sequence i
+    __shared__ int lens[kStreamMaxSeq];        // seq_lens
     __shared__ int2 wtot[NW];
 
     if (threadIdx.x < NW) slot_busy[threadIdx.x] = 0;
     if (threadIdx.x < 4) cursor[threadIdx.x] = 0;
-    unit_prefix<64 * NW>(seq_lens, b, S, g, pre, vpre, wtot);  // its barriers publish the above
+    unit_prefix<64 * NW>(seq_lens, b, S, g, pre, vpre, lens, wtot);  // its barriers publish the above
     // everything that steers the loops below is wave-uniform: keep it scalar
     const int T = __builtin_amdgcn_readfirstlane(pre[b]);
     const int wg = blockIdx.x;
@@ -984,8 +991,8 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
     const int i_last = __builtin_amdgcn_readfirstlane(last_seq);
     const int ord0 = __builtin_amdgcn_readfirstlane(vpre[i_first]) * g +
                      (x0 - __builtin_amdgcn_readfirstlane(pre[i_first])) /
-                         seq_steps(__builtin_amdgcn_readfirstlane(seq_lens[i_first]), S);
-    const int n_last = seq_steps(__builtin_amdgcn_readfirstlane(seq_lens[i_last]), S);
+                         seq_steps(__builtin_amdgcn_readfirstlane(lens[i_first]), S);
+    const int n_last = seq_steps(__builtin_amdgcn_readfirstlane(lens[i_last]), S);
     const int p_last = __builtin_amdgcn_readfirstlane(pre[i_last]);
     const int u0_last = p_last + (x1 - 1 - p_last) / n_last * n_last;  // the last unit's first step
     const int xl = max(x0, u0_last);
@@ -1021,7 +1028,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
         if (tt >= u0_ && tt < u0_ + n_) return;
         if (tt < u0_) i_ = i_first;
         while (__builtin_amdgcn_readfirstlane(pre[i_ + 1]) <= tt) i_++;
-        L_ = __builtin_amdgcn_readfirstlane(seq_lens[i_]);
+        L_ = __builtin_amdgcn_readfirstlane(lens[i_]);
         n_ = seq_steps(L_, S);
         const int p = __builtin_amdgcn_readfirstlane(pre[i_]);
         j_ = (tt - p) / n_;
@@ -1177,52 +1184,77 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
     }
 }
 
-// Units cut between ranges, after streamk_mfma_kernel: block w merges the
-// pieces of the unit described by cut_desc[w] (the first range's piece in
-// its slot cut_desc[w].w, the following ranges' pieces in slot 0) and writes
-// its rows of `out`. The pieces go in range order, so the merge is the same
-// every call.
-template <int D>
+// Units cut between ranges, after streamk_mfma_kernel: block (w, y) merges
+// head slots HPB*y .. HPB*y+HPB-1 of the unit described by cut_desc[w] (the
+// first range's piece in its slot cut_desc[w].w, the following ranges'
+// pieces in slot 0) and writes those rows of `out`. Threads are (head slot,
+// piece lane, four columns); piece lane k merges pieces w+k, w+k+PL, ...
+// (four loads in flight at a time) and the lanes are merged in order through
+// LDS, so the result is the same every call. Many head slots per block suit
+// units cut into few pieces, many piece lanes units cut into many.
+template <int D, int HPB>
 __global__ void __launch_bounds__(256)
 streamk_combine_kernel(const float *__restrict__ part_o, const float2 *__restrict__ part_ml,
                        const int4 *__restrict__ cut_desc, int h, int G, int HBT,
                        float *__restrict__ out) {
+    constexpr int C4 = D / 4;               // float4 columns per row
+    constexpr int PL = 256 / (HPB * C4);    // piece lanes per head slot
+    constexpr int BATCH = 4;
+    static_assert(PL >= 1 && HPB * PL * C4 == 256, "block shape");
+    __shared__ f32x4_t s_num[HPB][PL][C4];
+    __shared__ float2 s_md[HPB][PL][C4];
     const int wf = blockIdx.x;
     const int4 dsc = cut_desc[wf];
-    if (dsc.x < 0) return;
+    if (dsc.x < 0) return;  // uniform over the block
     const int wl = dsc.z, slot_f = dsc.w;
-    const size_t row0 = (size_t)dsc.x * h + (size_t)dsc.y * G;  // first query head of the unit
-    constexpr int C4 = D / 4;                                     // float4 columns per row
-    for (int idx = threadIdx.x; idx < G * C4; idx += 256) {
-        const int hs = idx / C4, c = (idx % C4) * 4;
-        float M = -INFINITY, den = 0.f;
-        f32x4_t num = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int p0 = wf; p0 <= wl; p0 += 4) {  // four pieces' loads in flight at a time
-            float2 e[4];
-            f32x4_t o[4];
+    const int hh = threadIdx.x / (PL * C4), pl = (threadIdx.x / C4) % PL, c4 = threadIdx.x % C4;
+    const int hs = blockIdx.y * HPB + hh;
+    const bool live_row = hs < G;
+    float M = -INFINITY, den = 0.f;
+    f32x4_t num = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int p0 = wf + pl; live_row && p0 <= wl; p0 += BATCH * PL) {
+        float2 e[BATCH];
+        f32x4_t o[BATCH];
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-                const int p = p0 + k;
-                const size_t prow = ((size_t)p * 2 + (p == wf ? slot_f : 0)) * HBT + hs;
-                e[k] = p <= wl ? part_ml[prow] : make_float2(-INFINITY, 0.f);
-                o[k] = p <= wl ? *(const f32x4_t *)(part_o + prow * D + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-            }
-            float Mb = M;
-#pragma unroll
-            for (int k = 0; k < 4; k++) Mb = fmaxf(Mb, e[k].x);
-            const float rs = M == -INFINITY ? 0.f : fast_exp2(M - Mb);
-            num *= rs;
-            den *= rs;
-            M = Mb;
-#pragma unroll
-            for (int k = 0; k < 4; k++) {
-                const float wgt = e[k].x == -INFINITY ? 0.f : fast_exp2(e[k].x - M);
-                num += wgt * o[k];
-                den = fmaf(wgt, e[k].y, den);
-            }
+        for (int k = 0; k < BATCH; k++) {
+            const int p = p0 + k * PL;
+            const size_t prow = ((size_t)p * 2 + (p == wf ? slot_f : 0)) * HBT + hs;
+            const bool live = p <= wl;
+            e[k] = live ? part_ml[prow] : make_float2(-INFINITY, 0.f);
+            o[k] = live ? *(const f32x4_t *)(part_o + prow * D + 4 * c4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        *(f32x4_t *)(out + (row0 + hs) * D + c) = num * (1.f / den);
+        float Mb = M;
+#pragma unroll
+        for (int k = 0; k < BATCH; k++) Mb = fmaxf(Mb, e[k].x);
+        const float rs = M == -INFINITY ? 0.f : fast_exp2(M - Mb);
+        num *= rs;
+        den *= rs;
+        M = Mb;
+#pragma unroll
+        for (int k = 0; k < BATCH; k++) {
+            const float wgt = e[k].x == -INFINITY ? 0.f : fast_exp2(e[k].x - M);
+            num += wgt * o[k];
+            den = fmaf(wgt, e[k].y, den);
+        }
     }
+    if (PL > 1) {
+        s_num[hh][pl][c4] = num;
+        s_md[hh][pl][c4] = make_float2(M, den);
+        __syncthreads();
+        if (pl != 0) return;
+        for (int k = 1; k < PL; k++) {
+            const float2 md = s_md[hh][k][c4];
+            const float Mn = fmaxf(M, md.x);
+            const float a0 = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+            const float a1 = md.x == -INFINITY ? 0.f : fast_exp2(md.x - Mn);
+            num = num * a0 + a1 * s_num[hh][k][c4];
+            den = den * a0 + a1 * md.y;
+            M = Mn;
+        }
+    }
+    if (!live_row) return;
+    const size_t row = (size_t)dsc.x * h + (size_t)dsc.y * G + hs;
+    *(f32x4_t *)(out + row * D + 4 * c4) = num * (1.f / den);
 }
 
 // ---------------------------------------------------------------------------
@@ -1369,13 +1401,17 @@ size_t workspace_need(int b, int h, int g, int S, int d, mqa_dtype dt, int split
 
 // Work-groups of the balanced schedule: one per compute unit (the kernel
 // uses fewer when the call has fewer than kStreamMinSteps steps for each).
-int streamk_wgs(int b, int g, int S) {
+int streamk_cus() {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
         int v = 0;
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
             cus = v;
     }
+    return cus;
+}
+int streamk_wgs(int b, int g, int S) {
+    const int cus = streamk_cus();
     const long long tmax = (long long)b * g * ((S + 31) / 32);
     long long n = (tmax + kStreamMinSteps - 1) / kStreamMinSteps;
     if (n > cus) n = cus;
@@ -1499,18 +1535,26 @@ mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache, const void
         float *po = (float *)workspace;
         float2 *pml = (float2 *)((uint8_t *)workspace + L.ml_off);
         int4 *desc = (int4 *)((uint8_t *)workspace + L.desc_off);
+        auto launch = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3(nwg), dim3(64 * kStreamWaves), 0, stream, (const uint16_t *)q,
+                               (const uint16_t *)k_cache, (const uint16_t *)v_cache, seq_lens, b, h, g,
+                               S, G, nhb, qs_, out, po, pml, desc, err_flags);
+        };
+        // pieces per cut unit: ~2 when there are more units than work-groups,
+        // ~nwg/units when each unit spans many ranges
+        const bool many_pieces = (long long)b * g * 4 < nwg;
+        auto combine = [&](auto kern, int hpb) {
+            hipLaunchKernelGGL(kern, dim3(nwg, (G + hpb - 1) / hpb), dim3(256), 0, stream, po, pml,
+                               desc, h, G, nhb * 16, out);
+        };
         if (d == 128) {
-            hipLaunchKernelGGL(streamk_mfma_kernel<128>, dim3(nwg), dim3(64 * kStreamWaves), 0, stream,
-                               (const uint16_t *)q, (const uint16_t *)k_cache, (const uint16_t *)v_cache,
-                               seq_lens, b, h, g, S, G, nhb, qs_, out, po, pml, desc, err_flags);
-            hipLaunchKernelGGL(streamk_combine_kernel<128>, dim3(nwg), dim3(256), 0, stream, po, pml,
-                               desc, h, G, nhb * 16, out);
+            launch(streamk_mfma_kernel<128, kStreamWaves>);
+            if (many_pieces) combine(streamk_combine_kernel<128, 1>, 1);
+            else combine(streamk_combine_kernel<128, 8>, 8);
         } else {
-            hipLaunchKernelGGL(streamk_mfma_kernel<64>, dim3(nwg), dim3(64 * kStreamWaves), 0, stream,
-                               (const uint16_t *)q, (const uint16_t *)k_cache, (const uint16_t *)v_cache,
-                               seq_lens, b, h, g, S, G, nhb, qs_, out, po, pml, desc, err_flags);
-            hipLaunchKernelGGL(streamk_combine_kernel<64>, dim3(nwg), dim3(256), 0, stream, po, pml,
-                               desc, h, G, nhb * 16, out);
+            launch(streamk_mfma_kernel<64, kStreamWaves>);
+            if (many_pieces) combine(streamk_combine_kernel<64, 1>, 1);
+            else combine(streamk_combine_kernel<64, 16>, 16);
         }
         return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
     }
