@@ -1310,7 +1310,17 @@ combine_kernel(const float *__restrict__ part_o, const float2 *__restrict__ part
 // ---------------------------------------------------------------------------
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kTargetGroups = 2048;  // aim for ~8 partitions per compute unit
+// Compute units of the current device (256 on MI355X; also the answer when
+// no device is visible, for the host-only queries).
+int device_cus() {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            cus = v;
+    }
+    return cus;
+}
 
 int heads_per_wg(int G) {
     int hpw = 1;
@@ -1336,14 +1346,17 @@ mqa_status check_sizes(int b, int h, int g, int S, int d, mqa_dtype dt, int spli
 // of 16 heads, fp32 on the vector ALUs in blocks of up to 8.
 int wg_heads(mqa_dtype dt, int G) { return dt == MQA_BF16 ? 16 : heads_per_wg(G); }
 
+// Automatic partition length: about one work-group per compute unit (each
+// work-group's waves then stream tens of steps; measured best for MQA at
+// 32K context, the 32-layer sweeps and short contexts alike — more, shorter
+// partitions only add start-up latency and combine work).
 int resolve_chunk(int b, int h, int g, int S, mqa_dtype dt, int split_chunk) {
     if (split_chunk > 0) return split_chunk;
     const int G = h / g;
     const long long groups = (long long)b * g * ((G + wg_heads(dt, G) - 1) / wg_heads(dt, G));
-    const long long want = (kTargetGroups + groups - 1) / groups;  // partitions per group
+    const long long want = (device_cus() + groups - 1) / groups;  // partitions per group
     long long c = ((long long)S + want - 1) / want;
     c = (c + kTile - 1) / kTile * kTile;
-    if (c < 256) c = 256;
     const long long cap = ((long long)S + kTile - 1) / kTile * kTile;
     if (c > cap) c = cap;
     return (int)c;
@@ -1401,17 +1414,8 @@ size_t workspace_need(int b, int h, int g, int S, int d, mqa_dtype dt, int split
 
 // Work-groups of the balanced schedule: one per compute unit (the kernel
 // uses fewer when the call has fewer than kStreamMinSteps steps for each).
-int streamk_cus() {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            cus = v;
-    }
-    return cus;
-}
 int streamk_wgs(int b, int g, int S) {
-    const int cus = streamk_cus();
+    const int cus = device_cus();
     const long long tmax = (long long)b * g * ((S + 31) / 32);
     long long n = (tmax + kStreamMinSteps - 1) / kStreamMinSteps;
     if (n > cus) n = cus;
