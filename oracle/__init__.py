@@ -13,7 +13,8 @@ module is ctypes marshalling over numpy arrays only. Element type codes:
 Sources, cited by page title and section:
   [GQA notes] ybb.press "分组查询注意力（GQA）与多查询注意力（MQA）深度实战",
               §一/§七 (KV bytes), §四/§五 (grouped math), §八 (cache write).
-  [MQA blog]  nanhubrain.csdn.net MQA article §2.2 (append on the sequence axis).
+  [MQA blog]  nanhubrain.csdn.net MQA article §2.2 (append on the sequence axis),
+              §3.3 (paged cache, 16 tokens per page).
 """
 from __future__ import annotations
 
@@ -28,6 +29,7 @@ BF16 = 1
 OK = 0
 BAD_LEN = 1
 BAD_SHAPE = 2
+BAD_PAGE = 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
@@ -65,6 +67,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_partial.restype = None
         L.oracle_lse_combine.argtypes = [i32, vp, vp, vp, i32, vp]
         L.oracle_lse_combine.restype = None
+        L.oracle_decode_attn_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                               i32, i32, i32, ctypes.c_float, vp, i32]
+        L.oracle_decode_attn_paged.restype = i32
+        L.oracle_append_kv_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                             i32, i32]
+        L.oracle_append_kv_paged.restype = i32
         L.oracle_kv_bytes.argtypes = [i32, i32, ctypes.c_int64, i32, i32]
         L.oracle_kv_bytes.restype = ctypes.c_uint64
         _lib = L
@@ -121,6 +129,42 @@ def decode_attn(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                                   _ptr(sl), b, h, g, S, d, dt, ctypes.c_float(scale),
                                   _ptr(out), _ptr(alpha), int(nthreads))
     return out, alpha, rc
+
+
+def decode_attn_paged(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray,
+                      block_table: np.ndarray, seq_lens: np.ndarray, scale: float,
+                      nthreads: int = 1):
+    """Decode attention over a paged cache, in double.
+
+    q: [b, h, d]; k_pages, v_pages: [num_pages, g, page_size, d]; block_table:
+    [b, max_pages] int32 page ids; seq_lens: [b]. Returns (out [b, h, d], status).
+    """
+    b, h, d = q.shape
+    num_pages, g, P, _ = k_pages.shape
+    max_pages = block_table.shape[1]
+    dt = _dtype_code(k_pages)
+    assert _dtype_code(q) == dt and _dtype_code(v_pages) == dt
+    out = np.empty((b, h, d), np.float64)
+    bt = _c(block_table.astype(np.int32))
+    sl = _c(seq_lens.astype(np.int32))
+    rc = lib().oracle_decode_attn_paged(_ptr(_c(q)), _ptr(_c(k_pages)), _ptr(_c(v_pages)),
+                                        _ptr(bt), _ptr(sl), b, h, g, P, max_pages, num_pages,
+                                        d, dt, ctypes.c_float(scale), _ptr(out), int(nthreads))
+    return out, rc
+
+
+def append_kv_paged(k_pages: np.ndarray, v_pages: np.ndarray, k_new: np.ndarray,
+                    v_new: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarray) -> int:
+    """In place: row (L-1) % page_size of page block_table[i][(L-1) // page_size]
+    of every K/V head of sequence i gets k_new/v_new. Returns the status bits."""
+    assert k_pages.flags.c_contiguous and v_pages.flags.c_contiguous
+    num_pages, g, P, d = k_pages.shape
+    b = k_new.shape[0]
+    bt = _c(block_table.astype(np.int32))
+    sl = _c(seq_lens.astype(np.int32))
+    return lib().oracle_append_kv_paged(_ptr(k_pages), _ptr(v_pages), _ptr(_c(k_new)),
+                                        _ptr(_c(v_new)), _ptr(bt), _ptr(sl), b, g, P,
+                                        bt.shape[1], num_pages, d, _dtype_code(k_pages))
 
 
 def mha_per_head(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:

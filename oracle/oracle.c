@@ -62,7 +62,20 @@ typedef struct {
     double *out, *alpha;
     int row_begin, row_end; /* rows are i*h + hq */
     int flags;
+    /* paged cache (block_table != NULL): position t of sequence i is row
+     * t % page_size of page block_table[i * max_pages + t / page_size] */
+    const int32_t *block_table;
+    int page_size, max_pages, num_pages;
 } decode_job;
+
+/* Element index of K/V row (sequence i, K/V head j, position t), or -1 when
+ * the page holding it is not a valid page id. */
+static long long kv_row(const decode_job *J, int i, int j, int t) {
+    if (!J->block_table) return (((long long)i * J->g + j) * J->S + t) * J->d;
+    int page = J->block_table[(size_t)i * J->max_pages + t / J->page_size];
+    if (page < 0 || page >= J->num_pages) return -1;
+    return (((long long)page * J->g + j) * J->page_size + t % J->page_size) * J->d;
+}
 
 static void decode_row(decode_job *J, int row) {
     int i = row / J->h, hq = row % J->h;
@@ -77,15 +90,21 @@ static void decode_row(decode_job *J, int row) {
         return;
     }
     size_t qoff = (size_t)row * d;
-    size_t kvoff = ((size_t)i * J->g + j) * (size_t)S * d;
+    for (int t = 0; t < L; t++) {
+        if (kv_row(J, i, j, t) < 0) { /* a position on an invalid page */
+            for (int x = 0; x < d; x++) o[x] = NAN;
+            J->flags |= ORACLE_BAD_PAGE;
+            return;
+        }
+    }
 
     double *s = (double *)malloc(sizeof(double) * (size_t)L);
     /* score_t = (Q_i . K_j,t) * scale */
     for (int t = 0; t < L; t++) {
         double dot = 0.0;
+        size_t kr = (size_t)kv_row(J, i, j, t);
         for (int x = 0; x < d; x++)
-            dot += elem(J->q, qoff + x, J->dtype) *
-                   elem(J->k, kvoff + (size_t)t * d + x, J->dtype);
+            dot += elem(J->q, qoff + x, J->dtype) * elem(J->k, kr + x, J->dtype);
         s[t] = J->scale * dot;
     }
     /* alpha_t = softmax_t(score); subtracting the max leaves it unchanged */
@@ -102,7 +121,7 @@ static void decode_row(decode_job *J, int row) {
     for (int x = 0; x < d; x++) {
         double acc = 0.0;
         for (int t = 0; t < L; t++)
-            acc += s[t] * elem(J->v, kvoff + (size_t)t * d + x, J->dtype);
+            acc += s[t] * elem(J->v, (size_t)kv_row(J, i, j, t) + x, J->dtype);
         o[x] = acc;
     }
     if (J->alpha) {
@@ -118,22 +137,18 @@ static void *decode_worker(void *arg) {
     return NULL;
 }
 
-int oracle_decode_attn(const void *q, const void *k, const void *v,
-                       const int32_t *seq_lens, int b, int h, int g, int S,
-                       int d, int dtype, float scale, double *out,
-                       double *alpha, int nthreads) {
-    if (b < 1 || h < 1 || g < 1 || S < 1 || d < 1 || h % g != 0)
-        return ORACLE_BAD_SHAPE;
-    int rows = b * h;
+/* Run the rows of a job template over nthreads POSIX threads. */
+static int run_decode(const decode_job *tmpl, int nthreads) {
+    int rows = tmpl->b * tmpl->h;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > rows) nthreads = rows;
     decode_job *jobs = (decode_job *)calloc((size_t)nthreads, sizeof(decode_job));
     pthread_t *tid = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
     for (int w = 0; w < nthreads; w++) {
-        decode_job J = {q, k, v, seq_lens, b, h, g, S, d, dtype, (double)scale,
-                        out, alpha, (int)((long)rows * w / nthreads),
-                        (int)((long)rows * (w + 1) / nthreads), 0};
-        jobs[w] = J;
+        jobs[w] = *tmpl;
+        jobs[w].row_begin = (int)((long)rows * w / nthreads);
+        jobs[w].row_end = (int)((long)rows * (w + 1) / nthreads);
+        jobs[w].flags = 0;
     }
     for (int w = 1; w < nthreads; w++)
         pthread_create(&tid[w], NULL, decode_worker, &jobs[w]);
@@ -145,6 +160,60 @@ int oracle_decode_attn(const void *q, const void *k, const void *v,
     }
     free(jobs);
     free(tid);
+    return rc;
+}
+
+int oracle_decode_attn(const void *q, const void *k, const void *v,
+                       const int32_t *seq_lens, int b, int h, int g, int S,
+                       int d, int dtype, float scale, double *out,
+                       double *alpha, int nthreads) {
+    if (b < 1 || h < 1 || g < 1 || S < 1 || d < 1 || h % g != 0)
+        return ORACLE_BAD_SHAPE;
+    decode_job J = {q, k, v, seq_lens, b, h, g, S, d, dtype, (double)scale,
+                    out, alpha, 0, 0, 0, NULL, 0, 0, 0};
+    return run_decode(&J, nthreads);
+}
+
+int oracle_decode_attn_paged(const void *q, const void *k_pages,
+                             const void *v_pages, const int32_t *block_table,
+                             const int32_t *seq_lens, int b, int h, int g,
+                             int page_size, int max_pages, int num_pages, int d,
+                             int dtype, float scale, double *out, int nthreads) {
+    if (b < 1 || h < 1 || g < 1 || d < 1 || h % g != 0 || page_size < 1 ||
+        max_pages < 1 || num_pages < 1)
+        return ORACLE_BAD_SHAPE;
+    decode_job J = {q, k_pages, v_pages, seq_lens, b, h, g, page_size * max_pages, d,
+                    dtype, (double)scale, out, NULL, 0, 0, 0, block_table, page_size,
+                    max_pages, num_pages};
+    return run_decode(&J, nthreads);
+}
+
+int oracle_append_kv_paged(void *k_pages, void *v_pages, const void *k_new,
+                           const void *v_new, const int32_t *block_table,
+                           const int32_t *seq_lens, int b, int g, int page_size,
+                           int max_pages, int num_pages, int d, int dtype) {
+    if (b < 1 || g < 1 || d < 1 || page_size < 1 || max_pages < 1 || num_pages < 1)
+        return ORACLE_BAD_SHAPE;
+    int rc = ORACLE_OK;
+    size_t row = (size_t)d * elem_bytes(dtype);
+    for (int i = 0; i < b; i++) {
+        int L = seq_lens[i];
+        if (L < 1 || L > page_size * max_pages) {
+            rc |= ORACLE_BAD_LEN;
+            continue;
+        }
+        int page = block_table[(size_t)i * max_pages + (L - 1) / page_size];
+        if (page < 0 || page >= num_pages) {
+            rc |= ORACLE_BAD_PAGE;
+            continue;
+        }
+        for (int j = 0; j < g; j++) {
+            size_t dst = (((size_t)page * g + j) * page_size + (size_t)((L - 1) % page_size)) * row;
+            size_t src = ((size_t)i * g + j) * row;
+            memcpy((char *)k_pages + dst, (const char *)k_new + src, row);
+            memcpy((char *)v_pages + dst, (const char *)v_new + src, row);
+        }
+    }
     return rc;
 }
 

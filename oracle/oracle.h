@@ -13,7 +13,7 @@
  *               §一 (KV bytes), §四 (GQA grouping), §五 (math form), §七 (h/g),
  *               §八 (reference implementation: cache write, repeat_interleave).
  *  [MQA blog]   nanhubrain.csdn.net MQA article, §2.2 (concat of the new K/V on
- *               the sequence axis).
+ *               the sequence axis), §3.3 (paged cache, 16 tokens per page).
  *  [MQA concept] compassingai.com "多查詢注意力", 技術原理 / "KV Cache 結構與
  *               視訊記憶體佔用對比" (per-layer byte counts).
  *
@@ -40,7 +40,7 @@ enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
 /* Return bits. ORACLE_BAD_LEN: some seq_lens[i] outside [1, S]; those rows
  * are left alone by append and set to NaN by decode. ORACLE_BAD_SHAPE: h not a
  * multiple of g, or a size < 1; nothing is written. */
-enum { ORACLE_OK = 0, ORACLE_BAD_LEN = 1, ORACLE_BAD_SHAPE = 2 };
+enum { ORACLE_OK = 0, ORACLE_BAD_LEN = 1, ORACLE_BAD_SHAPE = 2, ORACLE_BAD_PAGE = 4 };
 
 /* Cache append: row seq_lens[i]-1 of every K/V head j of sequence i receives
  * k_new[i][j][:] / v_new[i][j][:], byte for byte. [MQA blog] §2.2;
@@ -58,6 +58,25 @@ int oracle_decode_attn(const void *q, const void *k, const void *v,
                        const int32_t *seq_lens, int b, int h, int g, int S,
                        int d, int dtype, float scale, double *out,
                        double *alpha, int nthreads);
+
+/* Paged cache ([MQA blog] §3.3: the cache cut into fixed-size pages, 16
+ * tokens by default; [GQA notes] §十 item 12: ragged batches managed with
+ * pages): K/V live in pages k_pages, v_pages [num_pages][g][page_size][d];
+ * position t of sequence i is row t % page_size of page
+ * block_table[i][t / page_size] (block_table [b][max_pages], int32).
+ * Decode is the plain definition above over the positions t < L_i looked up
+ * this way; a row that reads a page id outside [0, num_pages) is NaN and
+ * ORACLE_BAD_PAGE is returned. Append writes row (L_i-1) % page_size of page
+ * block_table[i][(L_i-1) / page_size]. Capacity is page_size * max_pages. */
+int oracle_decode_attn_paged(const void *q, const void *k_pages,
+                             const void *v_pages, const int32_t *block_table,
+                             const int32_t *seq_lens, int b, int h, int g,
+                             int page_size, int max_pages, int num_pages, int d,
+                             int dtype, float scale, double *out, int nthreads);
+int oracle_append_kv_paged(void *k_pages, void *v_pages, const void *k_new,
+                           const void *v_new, const int32_t *block_table,
+                           const int32_t *seq_lens, int b, int g, int page_size,
+                           int max_pages, int num_pages, int d, int dtype);
 
 /* Textbook multi-head attention for one sequence, one K/V head per query
  * head (no sharing): q [h][d], K and V [h][L][d], all double.

@@ -158,6 +158,106 @@ def test_g_equals_h_is_per_head_mha():
     np.testing.assert_allclose(out[0], ref, rtol=1e-12, atol=1e-14)
 
 
+# ---- paged cache ([MQA blog] §3.3: fixed-size pages, 16 tokens by default) ----
+
+def _paged_from_contiguous(k, v, P, rng, extra_pages=5, share_prefix=False):
+    """Scatter a contiguous cache [b, g, S, d] into randomly numbered pages of P
+    rows (numpy indexing only); unused pages hold NaN."""
+    b, g, S, d = k.shape
+    maxp = -(-S // P)
+    num = b * maxp + extra_pages
+    ids = rng.permutation(num)[: b * maxp].reshape(b, maxp).astype(np.int32)
+    if share_prefix:  # sequence 1 reuses sequence 0's first page
+        ids[1, 0] = ids[0, 0]
+    nan = np.float32("nan") if k.dtype == np.float32 else np.uint16(0x7FC0)
+    kp = np.full((num, g, P, d), nan, k.dtype)
+    vp = np.full((num, g, P, d), nan, v.dtype)
+    for i in range(b):
+        for p in range(maxp):
+            rows = min(P, S - p * P)
+            kp[ids[i, p], :, :rows] = k[i, :, p * P: p * P + rows]
+            vp[ids[i, p], :, :rows] = v[i, :, p * P: p * P + rows]
+    return kp, vp, ids
+
+
+@pytest.mark.parametrize("P,h,g", [(16, 8, 2), (1, 4, 1), (7, 6, 3), (32, 8, 8)])
+def test_paged_matches_gathered_sdpa(P, h, g):
+    """Paged oracle = torch SDPA (float64) over the cache gathered back from
+    random page numbers, and bitwise = the contiguous oracle."""
+    rng = np.random.default_rng(P * 100 + h)
+    b, S, d = 3, 70, 64
+    q, k, v = randn(b, h, d, scale=2.0), randn(b, g, S, d), randn(b, g, S, d)
+    lens = np.array([70, 17, 45], np.int32)
+    kp, vp, bt = _paged_from_contiguous(k, v, P, rng)
+    out, rc = oracle.decode_attn_paged(q, kp, vp, bt, lens, 0.125)
+    assert rc == oracle.OK
+    ref = sdpa_ref(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), lens, 0.125)
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+    flat, _, _ = oracle.decode_attn(q, k, v, lens, 0.125)
+    assert np.array_equal(out, flat)
+
+
+def test_paged_shared_prefix_page():
+    """Two sequences may share a page (a common prefix): each reads it as its own."""
+    rng = np.random.default_rng(5)
+    b, h, g, S, d, P = 2, 4, 2, 48, 32, 16
+    q, k, v = randn(b, h, d), randn(b, g, S, d), randn(b, g, S, d)
+    k[1, :, :P], v[1, :, :P] = k[0, :, :P], v[0, :, :P]
+    kp, vp, bt = _paged_from_contiguous(k, v, P, rng, share_prefix=True)
+    lens = np.array([48, 40], np.int32)
+    out, rc = oracle.decode_attn_paged(q, kp, vp, bt, lens, 0.2)
+    assert rc == oracle.OK
+    flat, _, _ = oracle.decode_attn(q, k, v, lens, 0.2)
+    assert np.array_equal(out, flat)
+
+
+def test_paged_entries_past_length_are_not_read():
+    """Block-table entries past ceil(L/P) may be anything (here -1 and huge ids)."""
+    rng = np.random.default_rng(6)
+    b, h, g, S, d, P = 2, 4, 1, 64, 32, 16
+    q, k, v = randn(b, h, d), randn(b, g, S, d), randn(b, g, S, d)
+    kp, vp, bt = _paged_from_contiguous(k, v, P, rng)
+    lens = np.array([17, 33], np.int32)
+    bt[0, 2:] = -1
+    bt[1, 3:] = 1 << 30
+    out, rc = oracle.decode_attn_paged(q, kp, vp, bt, lens, 0.2)
+    assert rc == oracle.OK and np.isfinite(out).all()
+    flat, _, _ = oracle.decode_attn(q, k, v, lens, 0.2)
+    assert np.array_equal(out, flat)
+
+
+def test_paged_bad_page_is_flagged():
+    """A page id outside [0, num_pages) among the attended positions: that
+    sequence's rows are NaN and the status says so; the others are untouched."""
+    rng = np.random.default_rng(7)
+    b, h, g, S, d, P = 2, 4, 2, 32, 16, 16
+    q, k, v = randn(b, h, d), randn(b, g, S, d), randn(b, g, S, d)
+    kp, vp, bt = _paged_from_contiguous(k, v, P, rng)
+    bt[1, 1] = kp.shape[0]
+    lens = np.array([32, 20], np.int32)
+    out, rc = oracle.decode_attn_paged(q, kp, vp, bt, lens, 0.25)
+    assert rc & oracle.BAD_PAGE
+    assert np.isnan(out[1]).all() and np.isfinite(out[0]).all()
+
+
+def test_paged_append_writes_one_row():
+    rng = np.random.default_rng(8)
+    b, g, S, d, P = 3, 2, 40, 16, 16
+    k, v = randn(b, g, S, d), randn(b, g, S, d)
+    kp, vp, bt = _paged_from_contiguous(k, v, P, rng, extra_pages=2)
+    kn, vn = randn(b, g, d), randn(b, g, d)
+    lens = np.array([1, 16, 40], np.int32)
+    kp0, vp0 = kp.copy(), vp.copy()
+    assert oracle.append_kv_paged(kp, vp, kn, vn, bt, lens) == oracle.OK
+    for i, L in enumerate(lens):
+        page, row = bt[i, (L - 1) // P], (L - 1) % P
+        assert np.array_equal(kp[page, :, row], kn[i]) and np.array_equal(vp[page, :, row], vn[i])
+        kp0[page, :, row], vp0[page, :, row] = kn[i], vn[i]
+    assert np.array_equal(kp, kp0, equal_nan=True) and np.array_equal(vp, vp0, equal_nan=True)
+    bt[0, 0] = -3
+    assert oracle.append_kv_paged(kp, vp, kn, vn, bt, lens) & oracle.BAD_PAGE
+
+
 @pytest.mark.parametrize("h,g", [(8, 2), (12, 3), (16, 4)])
 def test_group_map_is_repeat_interleave(h, g):
     """[GQA notes] §八: K/V heads repeated with repeat_interleave onto the query heads."""
@@ -303,7 +403,9 @@ MUTANTS = {
     "scale dropped": ("s[t] = J->scale * dot;", "s[t] = dot;"),
     "attended length off by one": ("for (int t = 0; t < L; t++) {\n        double dot", "for (int t = 0; t < L - 1; t++) {\n        double dot"),
     "no normalisation": ("for (int t = 0; t < L; t++) s[t] /= Z;", ""),
-    "key and value swapped": ("elem(J->v, kvoff + (size_t)t * d + x, J->dtype);\n        o[x]", "elem(J->k, kvoff + (size_t)t * d + x, J->dtype);\n        o[x]"),
+    "key and value swapped": ("elem(J->v, (size_t)kv_row(J, i, j, t) + x, J->dtype);\n        o[x]", "elem(J->k, (size_t)kv_row(J, i, j, t) + x, J->dtype);\n        o[x]"),
+    "page looked up one position late": ("(size_t)i * J->max_pages + t / J->page_size]", "(size_t)i * J->max_pages + (t + 1) / J->page_size]"),
+    "row within the page ignored": ("J->page_size + t % J->page_size) * J->d", "J->page_size) * J->d"),
     "query index transposed": ("elem(J->q, qoff + x, J->dtype)", "elem(J->q, (size_t)x * J->h + hq, J->dtype)"),
 }
 
@@ -326,13 +428,14 @@ def test_planted_mistakes_are_caught(tmp_path, name, monkeypatch):
     mutant = ctypes.CDLL(so)
     real = oracle.lib()
     # reuse the argument declarations of the real library
-    for fn in ("oracle_decode_attn", "oracle_mha_per_head"):
+    for fn in ("oracle_decode_attn", "oracle_mha_per_head", "oracle_decode_attn_paged"):
         getattr(mutant, fn).argtypes = getattr(real, fn).argtypes
         getattr(mutant, fn).restype = getattr(real, fn).restype
     monkeypatch.setattr(oracle, "_lib", mutant)
     caught = []
     for pin in (test_hand_example, lambda: test_matches_torch_sdpa(12, 4),
-                lambda: test_matches_torch_sdpa(8, 8)):
+                lambda: test_matches_torch_sdpa(8, 8),
+                lambda: test_paged_matches_gathered_sdpa(16, 8, 2)):
         try:
             pin()
         except AssertionError:
