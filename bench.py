@@ -18,7 +18,12 @@ Algorithmic bytes per decode launch and layer: the K and V rows attended
 2*b*g*d*B read and the same written. Bytes the method avoids (the h/g times
 larger MHA cache) are not counted.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+With --page-size P the cache is paged (pages of P rows in a shuffled pool,
+one int32 block table per batch): mqa_append_kv_paged + mqa_decode_attn_paged,
+whose algorithmic bytes add the block-table entries read (sum_i ceil(L_i/P)*4,
+and 4*b for the append).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--page-size P]
 """
 from __future__ import annotations
 
@@ -55,6 +60,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="wall-clock budget of the CPU-oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="paged KV cache with pages of this many rows (0: contiguous cache)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -86,30 +93,61 @@ def main() -> int:
     print(f"[bench] workload {w.name}: b={w.b} h={w.h} g={w.g} d={w.d} S={w.S} layers={layers} "
           f"copies={reps} ({reps * cache_bytes / 2**30:.2f} GiB of cache)", file=sys.stderr, flush=True)
 
-    steps_in = [W.make_step(w, dev, layer=r) for r in range(reps)]
+    P = args.page_size
+    if P:
+        if args.kernel == "valu":
+            print("the paged path runs the matrix-core kernels only", file=sys.stderr)
+            return 2
+        steps_in = []
+        for r in range(reps):
+            t = W.make_paged_step(w, dev, page_size=P, layer=r)
+            del t["k_cache"], t["v_cache"]  # the pages hold the cache
+            steps_in.append(t)
+        cap = steps_in[0]["capacity"]
+        maxp = cap // P
+        ws = torch.empty(mqa.decode_paged_workspace_bytes(w.b, w.h, w.g, P, maxp, w.d, w.dtype,
+                                                          args.split_chunk),
+                         dtype=torch.uint8, device=dev)
+    else:
+        steps_in = [W.make_step(w, dev, layer=r) for r in range(reps)]
+        cap = w.S
+        ws = mqa.decode_workspace(w.b, w.h, w.g, w.S, w.d, w.dtype, dev, args.split_chunk)
     lens = steps_in[0]["seq_lens"].cpu().numpy().astype(np.int64)
-    chunk = mqa.decode_resolve_chunk(w.b, w.h, w.g, w.S, w.d, w.dtype, args.split_chunk)
-    ws = mqa.decode_workspace(w.b, w.h, w.g, w.S, w.d, w.dtype, dev, args.split_chunk)
+    chunk = mqa.decode_resolve_chunk(w.b, w.h, w.g, cap, w.d, w.dtype, args.split_chunk)
     outs = [torch.empty((w.b, w.h, w.d), dtype=torch.float32, device=dev) for _ in range(reps)]
     err = torch.zeros(1, dtype=torch.int32, device=dev)
 
     kernel = {"auto": mqa.KERNEL_AUTO, "valu": mqa.KERNEL_VALU, "mfma": mqa.KERNEL_MFMA}[args.kernel]
-    schedule = mqa.decode_schedule(w.b, w.h, w.g, w.S, w.d, w.dtype, args.split_chunk, kernel)
+    schedule = mqa.decode_schedule(w.b, w.h, w.g, cap, w.d, w.dtype, args.split_chunk, kernel)
     B = w.elem_bytes
     kv_read = int(sum(2 * w.g * int(L) * w.d * B for L in lens))
     dec_bytes = kv_read + w.b * w.h * w.d * B + w.b * w.h * w.d * 4
     app_bytes = 2 * (2 * w.b * w.g * w.d * B)
+    if P:
+        dec_bytes += 4 * int(sum(-(-int(L) // P) for L in lens))
+        app_bytes += 4 * w.b
     per_layer = dec_bytes + app_bytes
     step_bytes = per_layer * layers
     flops_per_step = 4 * w.h * int(lens.sum()) * w.d * layers
 
     def layer_call(r, ev=None):
         t = steps_in[r]
-        mqa.append_kv(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], t["seq_lens"], err_flags=err)
+        if P:
+            mqa.append_kv_paged(t["k_pages"], t["v_pages"], t["k_new"], t["v_new"],
+                                t["block_table"], t["seq_lens"], err_flags=err)
+        else:
+            mqa.append_kv(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], t["seq_lens"],
+                          err_flags=err)
         if ev is not None:
             ev[0].record()
-        mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], out=outs[r],
-                        workspace=ws, split_chunk=args.split_chunk, err_flags=err, kernel=kernel)
+        if P:
+            mqa.decode_attn_paged(t["q"], t["k_pages"], t["v_pages"], t["block_table"],
+                                  t["seq_lens"], out=outs[r], workspace=ws,
+                                  split_chunk=args.split_chunk, err_flags=err)
+        else:
+            mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], out=outs[r],
+                            workspace=ws, split_chunk=args.split_chunk, err_flags=err,
+                            kernel=kernel)
         if ev is not None:
             ev[1].record()
 
@@ -160,7 +198,8 @@ def main() -> int:
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = dec_bytes / (dec_ms_avg * 1e-3) / 1e9
     traffic = None
-    tf = os.path.join(ROOT, "profiles", f"decode_{w.name}_traffic.json")
+    tag = w.name + (f"-paged{P}" if P else "")
+    tf = os.path.join(ROOT, "profiles", f"decode_{tag}_traffic.json")
     if os.path.exists(tf):
         rec = json.load(open(tf))
         if (rec.get("source_sha") == source_sha() and rec.get("split_chunk", 0) == args.split_chunk
@@ -185,6 +224,7 @@ def main() -> int:
         "config": {"workload": w.name, "b": w.b, "h": w.h, "g": w.g, "d_h": w.d, "capacity": w.S,
                    "seq_lens": "fixed %d" % w.L if w.L else f"U[{w.L_lo},{w.L_hi}] (sum {int(lens.sum())})",
                    "layers": layers, "schedule": schedule,
+                   "kv_layout": f"paged, {P}-row pages" if P else "contiguous",
                    "split_chunk": chunk if schedule != "mfma-balanced" else None,
                    "cache_copies_rotated": reps,
                    "accumulate": "fp32", "out": "fp32"},
@@ -192,7 +232,8 @@ def main() -> int:
         "flops_per_step": flops_per_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": "mqa_decode_attn launch, schedule " + schedule,
+            "kernel": ("mqa_decode_attn_paged" if P else "mqa_decode_attn")
+                      + " launch, schedule " + schedule,
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
@@ -205,13 +246,14 @@ def main() -> int:
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, steps_in[0], lens, per_layer, layers, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, steps_in[0], lens, per_layer, layers,
+                                              args.cpu_seconds, P)
 
     print(json.dumps(result), flush=True)
     return 0
 
 
-def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s):
+def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0):
     """The oracle (plain double loops) on the host cores, one layer's step."""
     import numpy as np
 
@@ -219,21 +261,32 @@ def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s):
     import workloads as W
 
     nthreads = max(1, min(16, os.cpu_count() or 1))
-    args = [W.to_oracle(t["q"]), W.to_oracle(t["k_cache"]), W.to_oracle(t["v_cache"])]
     scale = float(np.float32(1.0 / math.sqrt(w.d)))
     lens32 = lens.astype(np.int32)
+    q = W.to_oracle(t["q"])
+    if page_size:
+        kp, vp = W.to_oracle(t["k_pages"]), W.to_oracle(t["v_pages"])
+        bt = t["block_table"].cpu().numpy()
+
+        def run(n):
+            oracle.decode_attn_paged(q[:n].copy(), kp, vp, bt[:n].copy(), lens32[:n], scale,
+                                     nthreads=nthreads)
+    else:
+        kc, vc = W.to_oracle(t["k_cache"]), W.to_oracle(t["v_cache"])
+
+        def run(n):
+            oracle.decode_attn(q[:n].copy(), kc[:n].copy(), vc[:n].copy(), lens32[:n], scale,
+                               nthreads=nthreads)
     # bounded sample: the first sequences of the batch, sized to the budget
     # from a one-sequence probe
     t0 = time.perf_counter()
-    oracle.decode_attn(args[0][:1].copy(), args[1][:1].copy(), args[2][:1].copy(), lens32[:1],
-                       scale, nthreads=nthreads)
+    run(1)
     one = max(time.perf_counter() - t0, 1e-4) / max(int(lens32[0]), 1)  # s per position
     nb = 1
     while nb < w.b and one * int(lens32[:nb + 1].sum()) * 1.0 <= budget_s:
         nb += 1
-    sub = [a[:nb].copy() for a in args]
     t0 = time.perf_counter()
-    oracle.decode_attn(sub[0], sub[1], sub[2], lens32[:nb], scale, nthreads=nthreads)
+    run(nb)
     dt = time.perf_counter() - t0
     B = w.elem_bytes
     sample_bytes = int(sum(2 * w.g * int(L) * w.d * B for L in lens32[:nb])) + nb * w.h * w.d * (B + 4)

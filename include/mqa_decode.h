@@ -66,8 +66,10 @@ typedef enum {
     MQA_KERNEL_MFMA = 2  /* matrix-core kernel, bf16 only */
 } mqa_kernel;
 
-/* Bit ORed into *err_flags by the kernels: some seq_lens[i] outside [1, S]. */
+/* Bits ORed into *err_flags by the kernels: some seq_lens[i] outside [1, S];
+ * some position of a paged call on a page id outside [0, num_pages). */
 #define MQA_DEVERR_SEQLEN 1
+#define MQA_DEVERR_PAGE 2
 
 /*
  * Append this step's K/V rows to the cache, bit-exactly.
@@ -160,6 +162,46 @@ typedef enum {
  * arguments are invalid. Host only, enqueues nothing. */
 int mqa_decode_schedule(int b, int h, int g, int S, int d, mqa_dtype dt,
                         int split_chunk, mqa_kernel kernel);
+
+/*
+ * Paged KV cache. [MQA blog] §3.3 (the cache cut into fixed-size pages, 16
+ * tokens by default); [GQA notes] §十 item 12 (ragged batches managed with
+ * pages rather than padding).
+ *
+ *   k_pages, v_pages : [num_pages][g][page_size][d] of dt
+ *   block_table      : [b][max_pages] int32 device: the page ids of sequence
+ *                      i in position order; position t of sequence i is row
+ *                      t % page_size of page block_table[i][t / page_size].
+ *                      Entries past the length are never read; pages may be
+ *                      shared between sequences (a common prefix).
+ * Capacity S = page_size * max_pages; seq_lens as above (post-append).
+ * page_size is a positive multiple of 16. The decode is bf16 only
+ * (MQA_F32 returns MQA_ERR_UNSUPPORTED) and runs the matrix-core kernels.
+ * A position on a page id outside [0, num_pages) gives NaN rows for its
+ * sequence's query heads of that K/V head (decode) or skips the row (append)
+ * and ORs MQA_DEVERR_PAGE into *err_flags.
+ */
+mqa_status mqa_append_kv_paged(void *k_pages, void *v_pages, const void *k_new,
+                               const void *v_new, const int32_t *block_table,
+                               const int32_t *seq_lens, int b, int g,
+                               int page_size, int max_pages, int num_pages,
+                               int d, mqa_dtype dt, int32_t *err_flags,
+                               hipStream_t stream);
+
+/* Bytes of workspace mqa_decode_attn_paged needs (0: invalid arguments). */
+size_t mqa_decode_paged_workspace_bytes(int b, int h, int g, int page_size,
+                                        int max_pages, int d, mqa_dtype dt,
+                                        int split_chunk);
+
+/* Decode attention (as mqa_decode_attn) over a paged cache. */
+mqa_status mqa_decode_attn_paged(const void *q, const void *k_pages,
+                                 const void *v_pages, const int32_t *block_table,
+                                 const int32_t *seq_lens, int b, int h, int g,
+                                 int page_size, int max_pages, int num_pages,
+                                 int d, mqa_dtype dt, float scale, float *out,
+                                 void *workspace, size_t workspace_bytes,
+                                 int split_chunk, int32_t *err_flags,
+                                 hipStream_t stream);
 
 /* Static text for a status code (never NULL). */
 const char *mqa_status_string(mqa_status s);

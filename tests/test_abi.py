@@ -146,3 +146,35 @@ def test_product_path_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "oracle_" not in text and "liboracle" not in text, f
+
+
+def paged_decode(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, b=2, h=8, g=2, P=16, maxp=4, num=8,
+             d=128, dt=mqa.BF16, scale=0.088, out=FAKE, ws=FAKE, ws_bytes=1 << 30, chunk=0)
+    a.update(kw)
+    return mqa.lib().mqa_decode_attn_paged(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["b"],
+                                           a["h"], a["g"], a["P"], a["maxp"], a["num"], a["d"],
+                                           a["dt"], ctypes.c_float(a["scale"]), a["out"], a["ws"],
+                                           a["ws_bytes"], a["chunk"], None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bt=None), mqa.ERR_NULL),
+    (dict(P=8), mqa.ERR_SHAPE),            # pages are multiples of 16 rows
+    (dict(P=24), mqa.ERR_SHAPE),
+    (dict(maxp=0), mqa.ERR_SHAPE),
+    (dict(num=0), mqa.ERR_SHAPE),
+    (dict(h=6, g=4), mqa.ERR_SHAPE),
+    (dict(dt=mqa.F32), mqa.ERR_UNSUPPORTED),  # paged reads run the bf16 matrix-core kernels
+    (dict(d=96), mqa.ERR_UNSUPPORTED),
+    (dict(v=MISALIGNED), mqa.ERR_ALIGN),
+    (dict(ws_bytes=16), mqa.ERR_WORKSPACE),
+])
+def test_paged_decode_rejects_bad_arguments_before_launch(kw, status):
+    assert paged_decode(**kw) == status
+
+
+def test_paged_workspace_bytes():
+    n = mqa.decode_paged_workspace_bytes(64, 64, 8, 16, 256, 128, mqa.BF16)
+    assert n == mqa.decode_workspace_bytes(64, 64, 8, 16 * 256, 128, mqa.BF16)
+    assert mqa.decode_paged_workspace_bytes(64, 64, 8, 24, 256, 128, mqa.BF16) == 0

@@ -10,8 +10,12 @@ Entry points (same names as the C ABI, without the ``mqa_`` prefix):
   decode_attn(q, k_cache, v_cache, seq_lens, scale=None, out=None,
               workspace=None, split_chunk=0, err_flags=None) -> out
   decode_workspace_bytes(b, h, g, S, d, dtype, split_chunk=0)
-  decode_workspace(b, h, g, S, d, dtype, device, split_chunk=0) -> zeroed uint8 tensor
+  decode_workspace(b, h, g, S, d, dtype, device, split_chunk=0) -> uint8 tensor
   decode_resolve_chunk(b, h, g, S, d, dtype, split_chunk=0)
+  append_kv_paged(k_pages, v_pages, k_new, v_new, block_table, seq_lens, err_flags=None)
+  decode_attn_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, out=None,
+                    workspace=None, split_chunk=0, err_flags=None) -> out
+  decode_paged_workspace_bytes(b, h, g, page_size, max_pages, d, dtype, split_chunk=0)
   kv_bytes(layers, g, S, d, dtype_bytes)
   status_string(status)
 
@@ -29,6 +33,7 @@ import torch
 __all__ = [
     "append_kv", "decode_attn", "decode_workspace_bytes", "decode_workspace", "decode_resolve_chunk",
     "decode_schedule", "kv_bytes", "status_string", "MQAError", "LIB_PATH", "DEVERR_SEQLEN",
+    "DEVERR_PAGE", "append_kv_paged", "decode_attn_paged", "decode_paged_workspace_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa_decode.so")
@@ -36,13 +41,15 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa_deco
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)
 F32, BF16 = 0, 1
 DEVERR_SEQLEN = 1
+DEVERR_PAGE = 2
 
 KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
 
 EXPORTS = (
     "mqa_append_kv", "mqa_decode_workspace_bytes", "mqa_decode_resolve_chunk",
     "mqa_decode_attn", "mqa_decode_attn_kernel", "mqa_decode_schedule", "mqa_status_string",
-    "mqa_kv_bytes",
+    "mqa_kv_bytes", "mqa_append_kv_paged", "mqa_decode_paged_workspace_bytes",
+    "mqa_decode_attn_paged",
 )
 SCHEDULES = {0: "valu-partitions", 1: "mfma-partitions", 2: "mfma-balanced"}
 
@@ -78,6 +85,14 @@ def _load() -> ctypes.CDLL:
     L.mqa_status_string.restype = ctypes.c_char_p
     L.mqa_kv_bytes.argtypes = [i32, i32, i64, i32, i32]
     L.mqa_kv_bytes.restype = ctypes.c_uint64
+    L.mqa_append_kv_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                      vp, vp]
+    L.mqa_append_kv_paged.restype = i32
+    L.mqa_decode_paged_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    L.mqa_decode_paged_workspace_bytes.restype = ctypes.c_size_t
+    L.mqa_decode_attn_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                        i32, ctypes.c_float, vp, vp, ctypes.c_size_t, i32, vp, vp]
+    L.mqa_decode_attn_paged.restype = i32
     return L
 
 
@@ -217,4 +232,82 @@ def decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         where = "mqa_decode_attn_kernel"
     if st != OK:
         raise MQAError(st, where)
+    return out
+
+
+# ---- paged cache: pages [num_pages, g, page_size, d], block_table int32 [b, max_pages] ----
+
+def _check_pages(k_pages, v_pages, block_table, seq_lens):
+    for n, t in (("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table),
+                 ("seq_lens", seq_lens)):
+        _dev(t, n)
+    if k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages and v_pages must both be [num_pages, g, page_size, d]")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous int32 [b, max_pages]")
+    b = block_table.shape[0]
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (b,):
+        raise ValueError("seq_lens must be int32 [b]")
+    return k_pages.shape, b, block_table.shape[1]
+
+
+def append_kv_paged(k_pages: torch.Tensor, v_pages: torch.Tensor, k_new: torch.Tensor,
+                    v_new: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                    err_flags: torch.Tensor | None = None) -> None:
+    """Write k_new/v_new [b,g,d] into row (L-1) % page_size of page block_table[i][(L-1) // page_size]."""
+    (num_pages, g, P, d), b, max_pages = _check_pages(k_pages, v_pages, block_table, seq_lens)
+    for n, t in (("k_new", k_new), ("v_new", v_new)):
+        _dev(t, n)
+    if k_new.shape != (b, g, d) or v_new.shape != (b, g, d):
+        raise ValueError("k_new and v_new must be [b, g, d]")
+    if not (k_pages.dtype == v_pages.dtype == k_new.dtype == v_new.dtype):
+        raise TypeError("pages and new rows must share one dtype")
+    st = lib().mqa_append_kv_paged(_ptr(k_pages), _ptr(v_pages), _ptr(k_new), _ptr(v_new),
+                                   _ptr(block_table), _ptr(seq_lens), b, g, P, max_pages,
+                                   num_pages, d, _dtype_code(k_pages.dtype), _ptr(err_flags),
+                                   _stream(k_pages.device))
+    if st != OK:
+        raise MQAError(st, "mqa_append_kv_paged")
+
+
+def decode_paged_workspace_bytes(b, h, g, page_size, max_pages, d, dtype, split_chunk: int = 0) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(lib().mqa_decode_paged_workspace_bytes(b, h, g, page_size, max_pages, d, code,
+                                                      split_chunk))
+
+
+def decode_attn_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                      block_table: torch.Tensor, seq_lens: torch.Tensor,
+                      scale: float | None = None, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, split_chunk: int = 0,
+                      err_flags: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention over a paged cache -> out fp32 [b,h,d]."""
+    (num_pages, g, P, d), b, max_pages = _check_pages(k_pages, v_pages, block_table, seq_lens)
+    _dev(q, "q")
+    if q.dim() != 3 or q.shape[0] != b or q.shape[2] != d:
+        raise ValueError("q must be [b, h, d] matching the pages and the block table")
+    if not (q.dtype == k_pages.dtype == v_pages.dtype):
+        raise TypeError("q and the pages must share one dtype")
+    h = q.shape[1]
+    code = _dtype_code(q.dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((b, h, d), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or out.shape != (b, h, d):
+        raise ValueError("out must be float32 [b, h, d]")
+    _dev(out, "out")
+    if workspace is None:
+        n = decode_paged_workspace_bytes(b, h, g, P, max_pages, d, code, split_chunk)
+        if n == 0:
+            raise ValueError("invalid sizes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    st = lib().mqa_decode_attn_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                     _ptr(seq_lens), b, h, g, P, max_pages, num_pages, d, code,
+                                     ctypes.c_float(scale), _ptr(out), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), split_chunk,
+                                     _ptr(err_flags), _stream(q.device))
+    if st != OK:
+        raise MQAError(st, "mqa_decode_attn_paged")
     return out

@@ -160,6 +160,41 @@ __global__ void append_kv_kernel(uint8_t *__restrict__ kc, uint8_t *__restrict__
     *(uint4 *)(dp + dst) = *(const uint4 *)(s + src);
 }
 
+// Paged cache: the row goes to row (L-1) % P of page block_table[i][(L-1) / P]
+// of pages [num_pages][g][P][d]. A page id outside [0, num_pages) is skipped
+// and flagged.
+__global__ void append_kv_paged_kernel(uint8_t *__restrict__ kp, uint8_t *__restrict__ vp,
+                                       const uint8_t *__restrict__ kn, const uint8_t *__restrict__ vn,
+                                       const int32_t *__restrict__ block_table,
+                                       const int32_t *__restrict__ seq_lens, int b, int g, int P,
+                                       int max_pages, int num_pages, int row_bytes,
+                                       int32_t *__restrict__ err) {
+    const int cpr = row_bytes >> 4;
+    const long long total = 2ll * b * g * cpr;
+    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= total) return;
+    const int c = (int)(t % cpr);
+    const long long ij = (t / cpr) % ((long long)b * g);
+    const int which = (int)(t / ((long long)cpr * b * g));
+    const int i = (int)(ij / g), j = (int)(ij % g);
+    const bool first = c == 0 && which == 0 && j == 0;
+    const int L = seq_lens[i];
+    if (L < 1 || L > P * max_pages) {
+        if (first && err) atomicOr(err, MQA_DEVERR_SEQLEN);
+        return;
+    }
+    const int page = block_table[(size_t)i * max_pages + (L - 1) / P];
+    if (page < 0 || page >= num_pages) {
+        if (first && err) atomicOr(err, MQA_DEVERR_PAGE);
+        return;
+    }
+    const size_t src = (size_t)ij * row_bytes + (size_t)c * 16;
+    const size_t dst = (((size_t)page * g + j) * P + (size_t)((L - 1) % P)) * row_bytes + (size_t)c * 16;
+    const uint8_t *s = which ? vn : kn;
+    uint8_t *dp = which ? vp : kp;
+    *(uint4 *)(dp + dst) = *(const uint4 *)(s + src);
+}
+
 // ---------------------------------------------------------------------------
 // split kernel: one wave per query head in the score phase, one lane per row
 // ---------------------------------------------------------------------------
@@ -567,27 +602,131 @@ struct StepData {
     u32x4_t vld[MfmaCfg<D>::VLOADS];
 };
 
-// Issue the loads of step [t0, t0+32) through the descriptors of one K/V
-// head's rows; rows past the descriptors' extent come back as zeros (and are
-// masked later), so a step past the end loads nothing from memory.
+// Where the K/V rows of one 32-position step come from: for each 16-row half,
+// a buffer descriptor and the byte offset of the half's first row in it.
+// Rows past a descriptor's extent come back as zeros without a memory access
+// (and are masked later), so a step past the end loads nothing.
+struct StepSrc {
+    rsrc_t k[2], v[2];
+    uint32_t off[2];
+};
+
+// Contiguous cache [b][g][S][d]: both halves in the head's S rows, the
+// descriptors' extent the sequence length.
 template <int D>
-__device__ __forceinline__ void load_step(rsrc_t krs, rsrc_t vrs, int t0, int lane,
-                                          StepData<D> &sd) {
+struct ContigKV {
+    static constexpr bool kPaged = false;
+    static constexpr int kStage = 1;
+    const uint8_t *k, *v;
+    int g, S;
+    __device__ __forceinline__ StepSrc step(int i, int j, int L, int t0, bool &) const {
+        constexpr uint32_t RB = MfmaCfg<D>::ROW_BYTES;
+        const size_t head = ((size_t)i * g + j) * (size_t)S * RB;
+        const rsrc_t kr = make_rsrc(k + head, (uint32_t)L * RB);
+        const rsrc_t vr = make_rsrc(v + head, (uint32_t)L * RB);
+        return StepSrc{{kr, kr}, {vr, vr}, {(uint32_t)t0 * RB, (uint32_t)(t0 + 16) * RB}};
+    }
+    __device__ __forceinline__ StepSrc none() const {
+        const rsrc_t z = make_rsrc(k, 0);
+        return StepSrc{{z, z}, {z, z}, {0u, 0u}};
+    }
+};
+
+// Paged cache: pages [num_pages][g][P][d], position t of sequence i in row
+// t % P of page block_table[i][t / P] ([MQA blog] §3.3). P is a multiple of
+// 16, so each half of a step lies in one page. A referenced page id outside
+// [0, num_pages) reads nothing and sets `bad`. The kernels stage the page ids
+// of their steps in LDS (up to kStage entries, two per step) before the
+// first step, so that no table lookup sits between a claim and its loads.
+template <int D>
+struct PagedKV {
+    static constexpr bool kPaged = true;
+    static constexpr int kStage = 4096;
+    const uint8_t *k, *v;
+    const int32_t *bt;
+    int g, P, max_pages, num_pages;
+    // page id of position `row` of sequence i (-1 at or past L)
+    __device__ __forceinline__ int page_id(int i, int row, int L) const {
+        return row < L ? bt[(size_t)i * max_pages + row / P] : -1;
+    }
+    // the step at t0 of K/V head j, its halves in pages id0 and id1
+    __device__ __forceinline__ StepSrc step_ids(int j, int L, int t0, int id0, int id1,
+                                                bool &bad) const {
+        constexpr uint32_t RB = MfmaCfg<D>::ROW_BYTES;
+        StepSrc s;
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++) {
+            const int row = t0 + 16 * hf;
+            const int pid = hf ? id1 : id0;
+            const bool ok = row < L && pid >= 0 && pid < num_pages;
+            bad |= row < L && !ok;
+            // the extent stops at the sequence's length, so rows of the page
+            // past it (stale or never written) are never read: they load as 0
+            const uint32_t rows = ok ? (uint32_t)min(P, L - row / P * P) : 0u;
+            const size_t page = ((size_t)(ok ? pid : 0) * g + j) * (size_t)P * RB;
+            s.k[hf] = make_rsrc(k + page, rows * RB);
+            s.v[hf] = make_rsrc(v + page, rows * RB);
+            s.off[hf] = (uint32_t)(row % P) * RB;
+        }
+        return s;
+    }
+    __device__ __forceinline__ StepSrc none() const {
+        const rsrc_t z = make_rsrc(k, 0);
+        return StepSrc{{z, z}, {z, z}, {0u, 0u}};
+    }
+};
+
+// Stage the page ids of entries 0..n-1 into pg (where(e, i, row, L): entry
+// e is position row of sequence i, of length L), whole work-group, four
+// lookups in flight per thread; the caller's barrier publishes them.
+template <int NT, class KV, class Where>
+__device__ __forceinline__ void stage_page_ids(const KV &kv, int *pg, int n, Where where) {
+    for (int e0 = threadIdx.x; e0 < n; e0 += 4 * NT) {
+        int id[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const int e = e0 + k * NT;
+            id[k] = -1;
+            if (e < n) {
+                int i, row, L;
+                where(e, i, row, L);
+                id[k] = kv.page_id(i, row, L);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+            if (e0 + k * NT < n) pg[e0 + k * NT] = id[k];
+    }
+}
+
+// Issue the loads of one step.
+template <int D>
+__device__ __forceinline__ void load_step(const StepSrc &src, int lane, StepData<D> &sd) {
     using C = MfmaCfg<D>;
     const int r = lane & 15, qd = lane >> 4;
     const int vl_row = lane / C::CPR, vl_chunk = lane % C::CPR;
-    const uint32_t base = (uint32_t)t0 * C::ROW_BYTES;
-    const uint32_t kl = base + r * C::ROW_BYTES + 16 * qd;
-    const uint32_t vl = base + vl_row * C::ROW_BYTES + 16 * vl_chunk;
+    const uint32_t kl = r * C::ROW_BYTES + 16 * qd;
+    const uint32_t vl = vl_row * C::ROW_BYTES + 16 * vl_chunk;
 #pragma unroll
     for (int pb = 0; pb < 2; pb++)
 #pragma unroll
         for (int k = 0; k < C::KSTEPS; k++)
             sd.kop[pb][k] = __builtin_bit_cast(
-                bf16x8_t, buffer_stream16(krs, kl + 16 * pb * C::ROW_BYTES + 64 * k));
+                bf16x8_t, buffer_stream16(src.k[pb], src.off[pb] + kl + 64 * k));
 #pragma unroll
-    for (int ii = 0; ii < C::VLOADS; ii++)
-        sd.vld[ii] = buffer_stream16(vrs, vl + ii * C::RPI * C::ROW_BYTES);
+    for (int ii = 0; ii < C::VLOADS; ii++) {
+        constexpr int H = 16 / C::RPI;  // V loads per half
+        sd.vld[ii] = buffer_stream16(src.v[ii / H],
+                                     src.off[ii / H] + vl + (ii % H) * C::RPI * C::ROW_BYTES);
+    }
+}
+
+// A step that read an invalid page: its unit's results become NaN (the state's
+// sum is NaN, which every merge carries) and the error flag is raised.
+template <int D>
+__device__ __forceinline__ void poison_state(MfmaState<D> &st, int32_t *err, int lane) {
+    st.l_lane = __builtin_nanf("");
+    if (err && lane == 0) atomicOr(err, MQA_DEVERR_PAGE);
 }
 
 // One 32-position step [t0, t0+32) of one wave from loaded data, rows >=
@@ -677,33 +816,39 @@ __device__ __forceinline__ void compute_step(const StepData<D> &sd, int t0, int 
     }
 }
 
-// Steps s_begin, s_begin+stride, ... < s_end of one K/V head (descriptors
-// over its first L rows), with the loads of the next step in flight while
-// this one computes (two register sets, alternating). Past the last step the
-// prefetch asks for rows past the end, which load nothing.
-template <int D>
-__device__ __forceinline__ void run_steps(rsrc_t krs, rsrc_t vrs, int s_begin, int s_end,
-                                          int stride, int t_end, int S,
+// Steps s_begin, s_begin+stride, ... < s_end (src(step, bad) gives where a
+// step's rows are), with the loads of the next step in flight while this
+// one computes (two register sets, alternating). Past the last step the
+// prefetch asks for nothing.
+template <int D, class Src>
+__device__ __forceinline__ void run_steps(const Src &src, const StepSrc &nothing, int s_begin,
+                                          int s_end, int stride, int t_end,
                                           const bf16x8_t (&qop)[MfmaCfg<D>::KSTEPS],
                                           MfmaState<D> &st, uint8_t *vb, int lane,
-                                          float qk_scale_log2) {
+                                          float qk_scale_log2, int32_t *err) {
     using C = MfmaCfg<D>;
     int stp = s_begin;
     if (stp >= s_end) return;
     StepData<D> a, b;
-    load_step<D>(krs, vrs, stp * C::STEP, lane, a);
+    bool bad = false, bad_n = false;
+    load_step<D>(src(stp, bad), lane, a);
     auto prefetch = [&](int nx, StepData<D> &sd) __attribute__((always_inline)) {
-        load_step<D>(krs, vrs, nx < s_end ? nx * C::STEP : S, lane, sd);
+        bad_n = false;
+        load_step<D>(nx < s_end ? src(nx, bad_n) : nothing, lane, sd);
     };
     while (true) {
         int nx = stp + stride;
         prefetch(nx, b);
         compute_step<D>(a, stp * C::STEP, t_end, qop, st, vb, lane, qk_scale_log2);
+        if (bad) poison_state<D>(st, err, lane);
+        bad = bad_n;
         if (nx >= s_end) break;
         stp = nx;
         nx = stp + stride;
         prefetch(nx, a);
         compute_step<D>(b, stp * C::STEP, t_end, qop, st, vb, lane, qk_scale_log2);
+        if (bad) poison_state<D>(st, err, lane);
+        bad = bad_n;
         if (nx >= s_end) break;
         stp = nx;
     }
@@ -749,14 +894,15 @@ __device__ __forceinline__ float merge_waves(const float *mrg, const float *mls,
 // Fixed partitions: one work-group per (partition of split_chunk positions,
 // K/V head, block of 16 query heads, sequence); writes partials for the
 // log-sum-exp combine.
-template <int D>
+template <int D, class KV>
 __global__ void __launch_bounds__(256)
-split_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
-                  const uint16_t *__restrict__ vc, const int32_t *__restrict__ seq_lens, int h,
-                  int g, int S, int G, int nhb, int chunk, int nsplit, float qk_scale_log2,
-                  float *__restrict__ part_o, float2 *__restrict__ part_ml) {
+split_mfma_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__restrict__ seq_lens,
+                  int h, int g, int S, int G, int nhb, int chunk, int nsplit, float qk_scale_log2,
+                  float *__restrict__ part_o, float2 *__restrict__ part_ml,
+                  int32_t *__restrict__ err) {
     using C = MfmaCfg<D>;
     __shared__ __attribute__((aligned(16))) uint8_t vbuf[C::NW][C::VBUF];
+    __shared__ int pg[KV::kStage];  // paged: the page ids of the partition's steps
 
     const int s = blockIdx.x;
     const int j = blockIdx.y / nhb;
@@ -773,19 +919,44 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, qd = lane >> 4;
 
-    const size_t head_row0 = ((size_t)i * g + j) * (size_t)S;
-    const rsrc_t krs = make_rsrc((const uint8_t *)kc + head_row0 * C::ROW_BYTES, L * C::ROW_BYTES);
-    const rsrc_t vrs = make_rsrc((const uint8_t *)vc + head_row0 * C::ROW_BYTES, L * C::ROW_BYTES);
-
     // padded heads reuse the last real one and are never written out
     bf16x8_t qop[C::KSTEPS];
     load_q_operand<D>(q, (size_t)i * h + j * G + min(hb * C::HB + r, G - 1), qd, qop);
 
+    // steps of this partition, numbered from the sequence start
+    const int s0 = t_begin / C::STEP;
+    const int ne = KV::kPaged ? min(2 * nsteps, KV::kStage) : 0;
+    if constexpr (KV::kPaged) {
+        stage_page_ids<256>(kv, pg, ne, [&](int e, int &i_, int &row, int &L_) {
+            i_ = i;
+            row = t_begin + 16 * e;
+            L_ = L;
+        });
+        __syncthreads();
+    }
+    auto src = [&](int stp, bool &bad) __attribute__((always_inline)) {
+        const int t0 = stp * C::STEP;
+        if constexpr (KV::kPaged) {
+            const int e = 2 * (stp - s0);
+            int id0, id1;
+            if (e < ne) {
+                id0 = pg[e];
+                id1 = pg[e + 1];
+            } else {  // past what LDS holds: look the ids up
+                id0 = kv.page_id(i, t0, L);
+                id1 = kv.page_id(i, t0 + 16, L);
+            }
+            return kv.step_ids(j, L, t0, __builtin_amdgcn_readfirstlane(id0),
+                               __builtin_amdgcn_readfirstlane(id1), bad);
+        } else {
+            return kv.step(i, j, L, t0, bad);
+        }
+    };
+
     MfmaState<D> st;
     st.reset();
-    // steps of this partition, numbered from the sequence start
-    run_steps<D>(krs, vrs, t_begin / C::STEP + w, t_begin / C::STEP + nsteps, C::NW, t_end, S,
-                 qop, st, vbuf[w], lane, qk_scale_log2);
+    run_steps<D>(src, kv.none(), s0 + w, s0 + nsteps, C::NW, t_end, qop, st, vbuf[w], lane,
+                 qk_scale_log2, err);
 
     __syncthreads();  // every wave is done with its staging buffer
     float *mrg = (float *)&vbuf[0][0];
@@ -818,9 +989,9 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
 // from L2). A unit entirely inside one range is normalised and written to
 // `out` directly. A unit cut by range boundaries leaves, for each work-group
 // and head block that touch it, a partial (m, l, o) in slot 0 (the range's
-// first segment) or slot 1 (its last) and bumps the arrival counter of
-// (unit, head block); the last arrival merges the pieces, writes `out` and
-// puts the counter back to zero.
+// first segment) or slot 1 (its last) and a description of the cut
+// (cut_desc); streamk_combine_kernel, launched next, merges the pieces and
+// writes `out`.
 
 constexpr int kStreamMaxSeq = 1024;    // sequences per call on this schedule (prefix sums in LDS)
 constexpr int kStreamMaxWG = 1024;     // work-groups (bounds the workspace)
@@ -924,10 +1095,10 @@ __device__ __forceinline__ void lds_flag_wait(int *f, int v) {
 // each is on a segment that ends earlier in the range, so they cannot form a
 // cycle. Which wave computes which step depends on timing, so the rounding
 // of the sums can differ between calls.
-template <int D, int NW>
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 8)))
-streamk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
-                    const uint16_t *__restrict__ vc, const int32_t *__restrict__ seq_lens, int b,
+template <int D, int NW, class KV>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV::kPaged ? 1 : 2, 8)))
+streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
+                    const int32_t *__restrict__ seq_lens, int b,
                     int h, int g, int S, int G, int nhb, float qk_scale_log2,
                     float *__restrict__ out, float *__restrict__ part_o,
                     float2 *__restrict__ part_ml, int4 *__restrict__ cut_desc,
@@ -946,6 +1117,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
     __shared__ int vpre[kStreamMaxSeq + 1];    // valid sequences before sequence i
     __shared__ int lens[kStreamMaxSeq];        // seq_lens
     __shared__ int2 wtot[NW];
+    __shared__ int pg[KV::kStage];             // paged: the page ids of the range's steps
 
     if (threadIdx.x < NW) slot_busy[threadIdx.x] = 0;
     if (threadIdx.x < 4) cursor[threadIdx.x] = 0;
@@ -969,6 +1141,25 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
         return;
     }
     const int x0 = range_start(wg, T, nwg), x1 = range_start(wg + 1, T, nwg);
+
+    // paged: the page ids of both halves of the range's steps, in step order
+    // (entry 2 (x - x0) + half), published by the barrier below
+    const int ne = KV::kPaged ? min(2 * (x1 - x0), KV::kStage) : 0;
+    if constexpr (KV::kPaged)
+        stage_page_ids<64 * NW>(kv, pg, ne, [&](int e, int &i_, int &row, int &L_) {
+            const int tt = x0 + (e >> 1);
+            int lo = 0, hi = b;  // pre[lo] <= tt < pre[hi] (pre[b] = T > tt)
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (pre[mid] <= tt)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+            i_ = lo;
+            L_ = lens[lo];
+            row = (tt - pre[lo]) % seq_steps(L_, S) * C::STEP + 16 * (e & 1);
+        });
 
     // The range's last segment [xl, x1) is claimed first, then [x0, xl): a
     // unit cut at x1 is then finished early on both sides of the cut, and
@@ -1034,23 +1225,38 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
         j_ = (tt - p) / n_;
         u0_ = p + j_ * n_;
     };
-    // descriptors over the first L_ rows of K/V head (i_, j_)
-    auto kv_rsrc = [&](const uint16_t *base, int i_, int j_, int L_) __attribute__((always_inline)) {
-        return make_rsrc((const uint8_t *)base + ((size_t)i_ * g + j_) * (size_t)S * C::ROW_BYTES,
-                         (uint32_t)L_ * C::ROW_BYTES);
-    };
     // padded heads reuse the last real one and are never written out
     auto q_row = [&](int i_, int j_) __attribute__((always_inline)) {
         return (size_t)i_ * h + j_ * G + min(hb * C::HB + r, G - 1);
+    };
+    // where the rows of flat step tt (of unit (i_, j_), first step u0_) are
+    auto src_of = [&](int i_, int j_, int L_, int u0_, int tt, bool &bad)
+                      __attribute__((always_inline)) {
+        const int t0 = (tt - u0_) * C::STEP;
+        if constexpr (KV::kPaged) {
+            const int e = 2 * (tt - x0);
+            int id0, id1;
+            if (e < ne) {
+                id0 = pg[e];
+                id1 = pg[e + 1];
+            } else {  // past what LDS holds: look the ids up
+                id0 = kv.page_id(i_, t0, L_);
+                id1 = kv.page_id(i_, t0 + 16, L_);
+            }
+            return kv.step_ids(j_, L_, t0, __builtin_amdgcn_readfirstlane(id0),
+                               __builtin_amdgcn_readfirstlane(id1), bad);
+        } else {
+            return kv.step(i_, j_, L_, t0, bad);
+        }
     };
 
     int t = claim();
     if (t >= x1) return;  // nothing left for this wave
     int ci = i_first, cL = 0, cn = 0, cj = 0, cu0 = 0;
     locate(t, ci, cL, cn, cj, cu0);
-    rsrc_t krs = kv_rsrc(kc, ci, cj, cL), vrs = kv_rsrc(vc, ci, cj, cL);
+    bool bad_now = false;  // the current step read an invalid page
     StepData<D> A, B;
-    load_step<D>(krs, vrs, (t - cu0) * C::STEP, lane, A);
+    load_step<D>(src_of(ci, cj, cL, cu0, t, bad_now), lane, A);
     bf16x8_t qop[C::KSTEPS];
     load_q_operand<D>(q, q_row(ci, cj), qd, qop);
     MfmaState<D> st;
@@ -1155,11 +1361,12 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
         int ni = ci, nL = cL, nn = cn, nj = cj, nu0 = cu0;
         if (more) locate(tn, ni, nL, nn, nj, nu0);
         const bool next_unit = more && nu0 != cu0;
-        const rsrc_t nks = next_unit ? kv_rsrc(kc, ni, nj, nL) : krs;
-        const rsrc_t nvs = next_unit ? kv_rsrc(vc, ni, nj, nL) : vrs;
-        // nothing left: rows past the end, which load nothing
-        load_step<D>(nks, nvs, more ? (tn - nu0) * C::STEP : S, lane, later);
+        bool bad_next = false;
+        // nothing left: a step that loads nothing
+        load_step<D>(more ? src_of(ni, nj, nL, nu0, tn, bad_next) : kv.none(), lane, later);
         compute_step<D>(now, (t - cu0) * C::STEP, cL, qop, st, vbuf[w], lane, qk_scale_log2);
+        if (bad_now) poison_state<D>(st, err, lane);
+        bad_now = bad_next;
         mine++;
         // the next unit's q, in flight during the segment's close
         if (next_unit) load_q_operand<D>(q, q_row(ni, nj), qd, qop);
@@ -1169,8 +1376,6 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
             mine = 0;
         }
         if (!more) return false;
-        krs = nks;
-        vrs = nvs;
         // wave-uniform; said explicitly so that the loop state stays scalar
         t = __builtin_amdgcn_readfirstlane(tn);
         ci = __builtin_amdgcn_readfirstlane(ni);
@@ -1448,6 +1653,47 @@ void dispatch_rows(int hpw, const void *q, const void *k, const void *v, const i
     }
 }
 
+// The matrix-core paths (bf16) for one K/V source: the balanced schedule
+// (+ its cut-unit merge) or fixed partitions (+ the log-sum-exp combine).
+template <int D, class KV>
+mqa_status run_mfma(const KV &kv, const void *q, const int32_t *seq_lens, int b, int h, int g,
+                    int S, float qs, float *out, void *workspace, int chunk, int nsplit,
+                    bool balanced, int32_t *err_flags, hipStream_t stream) {
+    const int G = h / g;
+    const int nhb = (G + 15) / 16;
+    if (balanced) {
+        const int nwg = streamk_wgs(b, g, S);
+        const StreamkLayout L = streamk_layout(h, g, D);
+        float *po = (float *)workspace;
+        float2 *pml = (float2 *)((uint8_t *)workspace + L.ml_off);
+        int4 *desc = (int4 *)((uint8_t *)workspace + L.desc_off);
+        hipLaunchKernelGGL((streamk_mfma_kernel<D, kStreamWaves, KV>), dim3(nwg), dim3(64 * kStreamWaves),
+                           0, stream, (const uint16_t *)q, kv, seq_lens, b, h, g, S, G, nhb, qs, out,
+                           po, pml, desc, err_flags);
+        // pieces per cut unit: ~2 when there are more units than work-groups,
+        // ~nwg/units when each unit spans many ranges
+        constexpr int HPB = 256 / (D / 4);  // head slots per block with one piece lane
+        if ((long long)b * g * 4 < nwg)
+            hipLaunchKernelGGL((streamk_combine_kernel<D, 1>), dim3(nwg, G), dim3(256), 0, stream, po,
+                               pml, desc, h, G, nhb * 16, out);
+        else
+            hipLaunchKernelGGL((streamk_combine_kernel<D, HPB>), dim3(nwg, (G + HPB - 1) / HPB),
+                               dim3(256), 0, stream, po, pml, desc, h, G, nhb * 16, out);
+        return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+    }
+    const size_t rows = (size_t)b * h * nsplit;
+    float *part_o = (float *)workspace;
+    float2 *part_ml =
+        (float2 *)((uint8_t *)workspace + ((rows * D * sizeof(float) + 255) & ~(size_t)255));
+    hipLaunchKernelGGL((split_mfma_kernel<D, KV>), dim3(nsplit, g * nhb, b), dim3(256), 0, stream,
+                       (const uint16_t *)q, kv, seq_lens, h, g, S, G, nhb, chunk, nsplit, qs, part_o,
+                       part_ml, err_flags);
+    if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
+    hipLaunchKernelGGL(combine_kernel<D>, dim3(h, b), dim3(D), 0, stream, part_o, part_ml, seq_lens, h,
+                       S, chunk, nsplit, out, err_flags);
+    return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1531,38 +1777,6 @@ mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache, const void
     if (!aligned16(workspace)) return MQA_ERR_ALIGN;
     const float qs_ = scale * kLog2e;
 
-    if (use_streamk(b, h, g, S, dt, split_chunk, kernel)) {
-        const int G = h / g;
-        const int nhb = (G + 15) / 16;
-        const int nwg = streamk_wgs(b, g, S);
-        const StreamkLayout L = streamk_layout(h, g, d);
-        float *po = (float *)workspace;
-        float2 *pml = (float2 *)((uint8_t *)workspace + L.ml_off);
-        int4 *desc = (int4 *)((uint8_t *)workspace + L.desc_off);
-        auto launch = [&](auto kern) {
-            hipLaunchKernelGGL(kern, dim3(nwg), dim3(64 * kStreamWaves), 0, stream, (const uint16_t *)q,
-                               (const uint16_t *)k_cache, (const uint16_t *)v_cache, seq_lens, b, h, g,
-                               S, G, nhb, qs_, out, po, pml, desc, err_flags);
-        };
-        // pieces per cut unit: ~2 when there are more units than work-groups,
-        // ~nwg/units when each unit spans many ranges
-        const bool many_pieces = (long long)b * g * 4 < nwg;
-        auto combine = [&](auto kern, int hpb) {
-            hipLaunchKernelGGL(kern, dim3(nwg, (G + hpb - 1) / hpb), dim3(256), 0, stream, po, pml,
-                               desc, h, G, nhb * 16, out);
-        };
-        if (d == 128) {
-            launch(streamk_mfma_kernel<128, kStreamWaves>);
-            if (many_pieces) combine(streamk_combine_kernel<128, 1>, 1);
-            else combine(streamk_combine_kernel<128, 8>, 8);
-        } else {
-            launch(streamk_mfma_kernel<64, kStreamWaves>);
-            if (many_pieces) combine(streamk_combine_kernel<64, 1>, 1);
-            else combine(streamk_combine_kernel<64, 16>, 16);
-        }
-        return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
-    }
-
     const size_t rows = (size_t)b * h * nsplit;
     uint8_t *wsp = (uint8_t *)workspace;
     float *part_o = (float *)wsp;
@@ -1571,17 +1785,13 @@ mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache, const void
     const int hpw = heads_per_wg(h / g);
 
     if (use_mfma) {
-        const int G = h / g;
-        const int nhb = (G + 15) / 16;
-        dim3 grid(nsplit, g * nhb, b);
+        const bool bal = use_streamk(b, h, g, S, dt, split_chunk, kernel);
+        const uint8_t *kb = (const uint8_t *)k_cache, *vb = (const uint8_t *)v_cache;
         if (d == 128)
-            hipLaunchKernelGGL(split_mfma_kernel<128>, grid, dim3(256), 0, stream, (const uint16_t *)q,
-                               (const uint16_t *)k_cache, (const uint16_t *)v_cache, seq_lens, h, g, S, G,
-                               nhb, chunk, nsplit, qs, part_o, part_ml);
-        else
-            hipLaunchKernelGGL(split_mfma_kernel<64>, grid, dim3(256), 0, stream, (const uint16_t *)q,
-                               (const uint16_t *)k_cache, (const uint16_t *)v_cache, seq_lens, h, g, S, G,
-                               nhb, chunk, nsplit, qs, part_o, part_ml);
+            return run_mfma<128>(ContigKV<128>{kb, vb, g, S}, q, seq_lens, b, h, g, S, qs_, out,
+                                 workspace, chunk, nsplit, bal, err_flags, stream);
+        return run_mfma<64>(ContigKV<64>{kb, vb, g, S}, q, seq_lens, b, h, g, S, qs_, out, workspace,
+                            chunk, nsplit, bal, err_flags, stream);
     } else if (dt == MQA_BF16) {
         if (d == 128) dispatch_rows<uint16_t, 128>(hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream);
         else dispatch_rows<uint16_t, 64>(hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream);
@@ -1608,6 +1818,74 @@ mqa_status mqa_decode_attn(const void *q, const void *k_cache, const void *v_cac
     return mqa_decode_attn_kernel(q, k_cache, v_cache, seq_lens, b, h, g, S, d, dt, scale, out,
                                   workspace, workspace_bytes, split_chunk, err_flags,
                                   MQA_KERNEL_AUTO, stream);
+}
+
+// ---- paged cache ----
+
+namespace {
+mqa_status check_paged(int b, int h, int g, int P, int max_pages, int num_pages, int d,
+                       mqa_dtype dt, int split_chunk) {
+    if (P < 16 || P % 16 != 0 || max_pages < 1 || num_pages < 1) return MQA_ERR_SHAPE;
+    if ((long long)P * max_pages > (1ll << 30)) return MQA_ERR_SHAPE;
+    const mqa_status st = check_sizes(b, h, g, P * max_pages, d, dt, split_chunk);
+    if (st != MQA_OK) return st;
+    if (dt != MQA_BF16) return MQA_ERR_UNSUPPORTED;  // paged reads: matrix-core kernels, bf16
+    return MQA_OK;
+}
+}  // namespace
+
+mqa_status mqa_append_kv_paged(void *k_pages, void *v_pages, const void *k_new, const void *v_new,
+                               const int32_t *block_table, const int32_t *seq_lens, int b, int g,
+                               int page_size, int max_pages, int num_pages, int d, mqa_dtype dt,
+                               int32_t *err_flags, hipStream_t stream) {
+    if (!k_pages || !v_pages || !k_new || !v_new || !block_table || !seq_lens) return MQA_ERR_NULL;
+    if (page_size < 1 || max_pages < 1 || num_pages < 1) return MQA_ERR_SHAPE;
+    const mqa_status st = check_sizes(b, g, g, page_size * max_pages, d, dt, 0);
+    if (st != MQA_OK) return st;
+    if (!aligned16(k_pages) || !aligned16(v_pages) || !aligned16(k_new) || !aligned16(v_new))
+        return MQA_ERR_ALIGN;
+    const int row_bytes = d * (dt == MQA_BF16 ? 2 : 4);
+    const long long total = 2ll * b * g * (row_bytes / 16);
+    hipLaunchKernelGGL(append_kv_paged_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       stream, (uint8_t *)k_pages, (uint8_t *)v_pages, (const uint8_t *)k_new,
+                       (const uint8_t *)v_new, block_table, seq_lens, b, g, page_size, max_pages,
+                       num_pages, row_bytes, err_flags);
+    return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+}
+
+size_t mqa_decode_paged_workspace_bytes(int b, int h, int g, int page_size, int max_pages, int d,
+                                        mqa_dtype dt, int split_chunk) {
+    if (check_paged(b, h, g, page_size, max_pages, 1, d, dt, split_chunk) != MQA_OK) return 0;
+    return workspace_need(b, h, g, page_size * max_pages, d, dt, split_chunk, MQA_KERNEL_MFMA);
+}
+
+mqa_status mqa_decode_attn_paged(const void *q, const void *k_pages, const void *v_pages,
+                                 const int32_t *block_table, const int32_t *seq_lens, int b, int h,
+                                 int g, int page_size, int max_pages, int num_pages, int d,
+                                 mqa_dtype dt, float scale, float *out, void *workspace,
+                                 size_t workspace_bytes, int split_chunk, int32_t *err_flags,
+                                 hipStream_t stream) {
+    if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !out) return MQA_ERR_NULL;
+    const mqa_status st = check_paged(b, h, g, page_size, max_pages, num_pages, d, dt, split_chunk);
+    if (st != MQA_OK) return st;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(out))
+        return MQA_ERR_ALIGN;
+    const int S = page_size * max_pages;
+    const int chunk = resolve_chunk(b, h, g, S, dt, split_chunk);
+    const int nsplit = (S + chunk - 1) / chunk;
+    if (!workspace || workspace_bytes < workspace_need(b, h, g, S, d, dt, split_chunk, MQA_KERNEL_MFMA))
+        return MQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MQA_ERR_ALIGN;
+    const bool bal = use_streamk(b, h, g, S, dt, split_chunk, MQA_KERNEL_MFMA);
+    const float qs = scale * kLog2e;
+    const uint8_t *kb = (const uint8_t *)k_pages, *vb = (const uint8_t *)v_pages;
+    if (d == 128)
+        return run_mfma<128>(PagedKV<128>{kb, vb, block_table, g, page_size, max_pages, num_pages}, q,
+                             seq_lens, b, h, g, S, qs, out, workspace, chunk, nsplit, bal, err_flags,
+                             stream);
+    return run_mfma<64>(PagedKV<64>{kb, vb, block_table, g, page_size, max_pages, num_pages}, q,
+                        seq_lens, b, h, g, S, qs, out, workspace, chunk, nsplit, bal, err_flags,
+                        stream);
 }
 
 }  // extern "C"

@@ -24,6 +24,11 @@ whole cache capacity is filled; the step's append then overwrites row L_i-1.
 seq_lens holds the post-append lengths. Seeds: base = 1000 * k for the k-th
 configuration; streams q +1, k_cache +2, v_cache +3, k_new +4, v_new +5,
 seq_lens +6 (a CPU generator), layer l adds 100 * l.
+
+Paged variants (make_paged_step): the same values scattered into pages of
+page_size rows with page ids drawn as a random permutation (CPU generator,
+stream +7) of b * ceil(S / page_size) + extra_pages pages; pages no sequence
+uses hold NaN.
 """
 from __future__ import annotations
 
@@ -118,3 +123,39 @@ def to_oracle(t: torch.Tensor):
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view("uint16")
     return t.numpy()
+
+
+def make_paged_step(w: Workload, device="cpu", page_size: int = 16, layer: int = 0,
+                    extra_pages: int = 3, share_prefix: bool = False) -> dict:
+    """make_step's values in a paged layout.
+
+    Returns the make_step dict plus k_pages/v_pages [num_pages, g, page_size, d],
+    block_table int32 [b, max_pages] and the capacity page_size * max_pages.
+    With share_prefix, sequence 1 uses sequence 0's first page (its first
+    page_size rows are set equal to sequence 0's before the scatter).
+    """
+    t = make_step(w, device, layer)
+    b, g, S, d = t["k_cache"].shape
+    P = page_size
+    maxp = -(-S // P)
+    num = b * maxp + extra_pages
+    gen = torch.Generator().manual_seed(w.seed + 100 * layer + 7)
+    ids = torch.randperm(num, generator=gen)[: b * maxp].view(b, maxp).to(torch.int32)
+    if share_prefix and b > 1:
+        ids[1, 0] = ids[0, 0]
+        for name in ("k_cache", "v_cache"):
+            t[name][1, :, :P] = t[name][0, :, :P]
+    pages = {}
+    for name in ("k_cache", "v_cache"):
+        c = t[name]
+        padded = torch.full((b, g, maxp * P, d), float("nan"), dtype=c.dtype, device=device)
+        padded[:, :, :S] = c
+        per_page = padded.view(b, g, maxp, P, d).permute(0, 2, 1, 3, 4).reshape(b * maxp, g, P, d)
+        dst = torch.full((num, g, P, d), float("nan"), dtype=c.dtype, device=device)
+        dst[ids.view(-1).long().to(device)] = per_page
+        pages[name] = dst
+    t["k_pages"], t["v_pages"] = pages["k_cache"], pages["v_cache"]
+    t["block_table"] = ids.to(device)
+    t["page_size"] = P
+    t["capacity"] = maxp * P
+    return t
