@@ -15,6 +15,8 @@ Sources, cited by page title and section:
               §一/§七 (KV bytes), §四/§五 (grouped math), §八 (cache write).
   [MQA blog]  nanhubrain.csdn.net MQA article §2.2 (append on the sequence axis),
               §3.3 (paged cache, 16 tokens per page).
+  [GQA notes] §十 item 10 (the causal mask stays per query position when several
+              query tokens attend at once).
 """
 from __future__ import annotations
 
@@ -73,6 +75,18 @@ def lib() -> ctypes.CDLL:
         L.oracle_append_kv_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                              i32, i32]
         L.oracle_append_kv_paged.restype = i32
+        L.oracle_append_kv_multi.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32]
+        L.oracle_append_kv_multi.restype = i32
+        L.oracle_decode_attn_multi.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                               i32, ctypes.c_float, vp, vp, i32]
+        L.oracle_decode_attn_multi.restype = i32
+        L.oracle_decode_attn_paged_multi.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                     i32, i32, i32, i32, i32, ctypes.c_float,
+                                                     vp, i32]
+        L.oracle_decode_attn_paged_multi.restype = i32
+        L.oracle_append_kv_paged_multi.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                   i32, i32, i32, i32]
+        L.oracle_append_kv_paged_multi.restype = i32
         L.oracle_kv_bytes.argtypes = [i32, i32, ctypes.c_int64, i32, i32]
         L.oracle_kv_bytes.restype = ctypes.c_uint64
         _lib = L
@@ -165,6 +179,73 @@ def append_kv_paged(k_pages: np.ndarray, v_pages: np.ndarray, k_new: np.ndarray,
     return lib().oracle_append_kv_paged(_ptr(k_pages), _ptr(v_pages), _ptr(_c(k_new)),
                                         _ptr(_c(v_new)), _ptr(bt), _ptr(sl), b, g, P,
                                         bt.shape[1], num_pages, d, _dtype_code(k_pages))
+
+
+def append_kv_multi(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray,
+                    v_new: np.ndarray, seq_lens: np.ndarray) -> int:
+    """In place: token tau of k_new/v_new [b, T, g, d] goes to position
+    seq_lens[i]-T+tau of every K/V head of sequence i. Returns the status bits."""
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    b, g, S, d = k_cache.shape
+    T = k_new.shape[1]
+    sl = _c(seq_lens.astype(np.int32))
+    return lib().oracle_append_kv_multi(_ptr(k_cache), _ptr(v_cache), _ptr(_c(k_new)),
+                                        _ptr(_c(v_new)), _ptr(sl), b, T, g, S, d,
+                                        _dtype_code(k_cache))
+
+
+def decode_attn_multi(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                      seq_lens: np.ndarray, scale: float, want_alpha: bool = False,
+                      nthreads: int = 1):
+    """T query tokens per sequence with the causal mask, in double.
+
+    q: [b, T, h, d] (token tau at position seq_lens[i]-T+tau); k_cache, v_cache:
+    [b, g, S, d]. Returns (out [b, T, h, d] float64, alpha [b, T, h, S] or None, status).
+    """
+    b, T, h, d = q.shape
+    _, g, S, _ = k_cache.shape
+    dt = _dtype_code(k_cache)
+    assert _dtype_code(q) == dt and _dtype_code(v_cache) == dt
+    out = np.empty((b, T, h, d), np.float64)
+    alpha = np.empty((b, T, h, S), np.float64) if want_alpha else None
+    sl = _c(seq_lens.astype(np.int32))
+    rc = lib().oracle_decode_attn_multi(_ptr(_c(q)), _ptr(_c(k_cache)), _ptr(_c(v_cache)),
+                                        _ptr(sl), b, T, h, g, S, d, dt, ctypes.c_float(scale),
+                                        _ptr(out), _ptr(alpha), int(nthreads))
+    return out, alpha, rc
+
+
+def decode_attn_paged_multi(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray,
+                            block_table: np.ndarray, seq_lens: np.ndarray, scale: float,
+                            nthreads: int = 1):
+    """decode_attn_multi over a paged cache. Returns (out [b, T, h, d], status)."""
+    b, T, h, d = q.shape
+    num_pages, g, P, _ = k_pages.shape
+    dt = _dtype_code(k_pages)
+    assert _dtype_code(q) == dt and _dtype_code(v_pages) == dt
+    out = np.empty((b, T, h, d), np.float64)
+    bt = _c(block_table.astype(np.int32))
+    sl = _c(seq_lens.astype(np.int32))
+    rc = lib().oracle_decode_attn_paged_multi(_ptr(_c(q)), _ptr(_c(k_pages)),
+                                              _ptr(_c(v_pages)), _ptr(bt), _ptr(sl), b, T, h,
+                                              g, P, bt.shape[1], num_pages, d, dt,
+                                              ctypes.c_float(scale), _ptr(out), int(nthreads))
+    return out, rc
+
+
+def append_kv_paged_multi(k_pages: np.ndarray, v_pages: np.ndarray, k_new: np.ndarray,
+                          v_new: np.ndarray, block_table: np.ndarray,
+                          seq_lens: np.ndarray) -> int:
+    """append_kv_multi into a paged cache. Returns the status bits."""
+    assert k_pages.flags.c_contiguous and v_pages.flags.c_contiguous
+    num_pages, g, P, d = k_pages.shape
+    b, T = k_new.shape[:2]
+    bt = _c(block_table.astype(np.int32))
+    sl = _c(seq_lens.astype(np.int32))
+    return lib().oracle_append_kv_paged_multi(_ptr(k_pages), _ptr(v_pages), _ptr(_c(k_new)),
+                                              _ptr(_c(v_new)), _ptr(bt), _ptr(sl), b, T, g,
+                                              P, bt.shape[1], num_pages, d,
+                                              _dtype_code(k_pages))
 
 
 def mha_per_head(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:

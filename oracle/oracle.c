@@ -29,27 +29,36 @@ static double elem(const void *base, size_t idx, int dtype) {
 
 static size_t elem_bytes(int dtype) { return dtype == ORACLE_F32 ? 4u : 2u; }
 
-int oracle_append_kv(void *k_cache, void *v_cache, const void *k_new,
-                     const void *v_new, const int32_t *seq_lens, int b, int g,
-                     int S, int d, int dtype) {
-    if (b < 1 || g < 1 || S < 1 || d < 1) return ORACLE_BAD_SHAPE;
+int oracle_append_kv_multi(void *k_cache, void *v_cache, const void *k_new,
+                           const void *v_new, const int32_t *seq_lens, int b,
+                           int T, int g, int S, int d, int dtype) {
+    if (b < 1 || T < 1 || g < 1 || S < 1 || d < 1) return ORACLE_BAD_SHAPE;
     int rc = ORACLE_OK;
     size_t eb = elem_bytes(dtype);
     size_t row = (size_t)d * eb;
     for (int i = 0; i < b; i++) {
         int L = seq_lens[i];
-        if (L < 1 || L > S) { /* never truncate or wrap silently */
+        if (L < T || L > S) { /* never truncate or wrap silently */
             rc |= ORACLE_BAD_LEN;
             continue;
         }
-        for (int j = 0; j < g; j++) {
-            size_t dst = (((size_t)i * g + j) * S + (size_t)(L - 1)) * row;
-            size_t src = ((size_t)i * g + j) * row;
-            memcpy((char *)k_cache + dst, (const char *)k_new + src, row);
-            memcpy((char *)v_cache + dst, (const char *)v_new + src, row);
-        }
+        /* token tau of this step is position L - T + tau */
+        for (int tau = 0; tau < T; tau++)
+            for (int j = 0; j < g; j++) {
+                size_t dst = (((size_t)i * g + j) * S + (size_t)(L - T + tau)) * row;
+                size_t src = (((size_t)i * T + tau) * g + j) * row;
+                memcpy((char *)k_cache + dst, (const char *)k_new + src, row);
+                memcpy((char *)v_cache + dst, (const char *)v_new + src, row);
+            }
     }
     return rc;
+}
+
+int oracle_append_kv(void *k_cache, void *v_cache, const void *k_new,
+                     const void *v_new, const int32_t *seq_lens, int b, int g,
+                     int S, int d, int dtype) {
+    return oracle_append_kv_multi(k_cache, v_cache, k_new, v_new, seq_lens, b, 1,
+                                  g, S, d, dtype);
 }
 
 /* ---- decode attention: one (sequence, query head) row ---------------- */
@@ -57,10 +66,10 @@ int oracle_append_kv(void *k_cache, void *v_cache, const void *k_new,
 typedef struct {
     const void *q, *k, *v;
     const int32_t *seq_lens;
-    int b, h, g, S, d, dtype;
+    int b, T, h, g, S, d, dtype; /* T query tokens per sequence */
     double scale;
     double *out, *alpha;
-    int row_begin, row_end; /* rows are i*h + hq */
+    int row_begin, row_end; /* rows are (i*T + tau)*h + hq */
     int flags;
     /* paged cache (block_table != NULL): position t of sequence i is row
      * t % page_size of page block_table[i * max_pages + t / page_size] */
@@ -78,19 +87,24 @@ static long long kv_row(const decode_job *J, int i, int j, int t) {
 }
 
 static void decode_row(decode_job *J, int row) {
-    int i = row / J->h, hq = row % J->h;
+    int hq = row % J->h, it = row / J->h;
+    int i = it / J->T, tau = it % J->T;
     int d = J->d, S = J->S;
     int G = J->h / J->g;      /* query heads per K/V head */
     int j = hq / G;           /* [GQA notes] §五: j = i // (h/g) */
     int L = J->seq_lens[i];
     double *o = J->out + (size_t)row * d;
-    if (L < 1 || L > S) {
+    if (L < J->T || L > S) {
         for (int x = 0; x < d; x++) o[x] = NAN;
         J->flags |= ORACLE_BAD_LEN;
         return;
     }
+    /* The step's T tokens are positions L-T .. L-1; token tau sees the
+     * positions up to its own, t <= L-T+tau (the causal mask is applied per
+     * query position, shared K/V or not: [GQA notes] §十 item 10). */
+    int A = L - J->T + 1 + tau;
     size_t qoff = (size_t)row * d;
-    for (int t = 0; t < L; t++) {
+    for (int t = 0; t < A; t++) {
         if (kv_row(J, i, j, t) < 0) { /* a position on an invalid page */
             for (int x = 0; x < d; x++) o[x] = NAN;
             J->flags |= ORACLE_BAD_PAGE;
@@ -98,9 +112,9 @@ static void decode_row(decode_job *J, int row) {
         }
     }
 
-    double *s = (double *)malloc(sizeof(double) * (size_t)L);
+    double *s = (double *)malloc(sizeof(double) * (size_t)A);
     /* score_t = (Q_i . K_j,t) * scale */
-    for (int t = 0; t < L; t++) {
+    for (int t = 0; t < A; t++) {
         double dot = 0.0;
         size_t kr = (size_t)kv_row(J, i, j, t);
         for (int x = 0; x < d; x++)
@@ -109,24 +123,24 @@ static void decode_row(decode_job *J, int row) {
     }
     /* alpha_t = softmax_t(score); subtracting the max leaves it unchanged */
     double m = s[0];
-    for (int t = 1; t < L; t++)
+    for (int t = 1; t < A; t++)
         if (s[t] > m) m = s[t];
     double Z = 0.0;
-    for (int t = 0; t < L; t++) {
+    for (int t = 0; t < A; t++) {
         s[t] = exp(s[t] - m);
         Z += s[t];
     }
-    for (int t = 0; t < L; t++) s[t] /= Z;
+    for (int t = 0; t < A; t++) s[t] /= Z;
     /* O_i = sum_t alpha_t V_j,t */
     for (int x = 0; x < d; x++) {
         double acc = 0.0;
-        for (int t = 0; t < L; t++)
+        for (int t = 0; t < A; t++)
             acc += s[t] * elem(J->v, (size_t)kv_row(J, i, j, t) + x, J->dtype);
         o[x] = acc;
     }
     if (J->alpha) {
         double *a = J->alpha + (size_t)row * S;
-        for (int t = 0; t < S; t++) a[t] = t < L ? s[t] : 0.0;
+        for (int t = 0; t < S; t++) a[t] = t < A ? s[t] : 0.0;
     }
     free(s);
 }
@@ -139,7 +153,7 @@ static void *decode_worker(void *arg) {
 
 /* Run the rows of a job template over nthreads POSIX threads. */
 static int run_decode(const decode_job *tmpl, int nthreads) {
-    int rows = tmpl->b * tmpl->h;
+    int rows = tmpl->b * tmpl->T * tmpl->h;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > rows) nthreads = rows;
     decode_job *jobs = (decode_job *)calloc((size_t)nthreads, sizeof(decode_job));
@@ -163,14 +177,37 @@ static int run_decode(const decode_job *tmpl, int nthreads) {
     return rc;
 }
 
+int oracle_decode_attn_multi(const void *q, const void *k, const void *v,
+                             const int32_t *seq_lens, int b, int T, int h, int g,
+                             int S, int d, int dtype, float scale, double *out,
+                             double *alpha, int nthreads) {
+    if (b < 1 || T < 1 || h < 1 || g < 1 || S < 1 || d < 1 || h % g != 0)
+        return ORACLE_BAD_SHAPE;
+    decode_job J = {q, k, v, seq_lens, b, T, h, g, S, d, dtype, (double)scale,
+                    out, alpha, 0, 0, 0, NULL, 0, 0, 0};
+    return run_decode(&J, nthreads);
+}
+
 int oracle_decode_attn(const void *q, const void *k, const void *v,
                        const int32_t *seq_lens, int b, int h, int g, int S,
                        int d, int dtype, float scale, double *out,
                        double *alpha, int nthreads) {
-    if (b < 1 || h < 1 || g < 1 || S < 1 || d < 1 || h % g != 0)
+    return oracle_decode_attn_multi(q, k, v, seq_lens, b, 1, h, g, S, d, dtype,
+                                    scale, out, alpha, nthreads);
+}
+
+int oracle_decode_attn_paged_multi(const void *q, const void *k_pages,
+                                   const void *v_pages, const int32_t *block_table,
+                                   const int32_t *seq_lens, int b, int T, int h,
+                                   int g, int page_size, int max_pages,
+                                   int num_pages, int d, int dtype, float scale,
+                                   double *out, int nthreads) {
+    if (b < 1 || T < 1 || h < 1 || g < 1 || d < 1 || h % g != 0 || page_size < 1 ||
+        max_pages < 1 || num_pages < 1)
         return ORACLE_BAD_SHAPE;
-    decode_job J = {q, k, v, seq_lens, b, h, g, S, d, dtype, (double)scale,
-                    out, alpha, 0, 0, 0, NULL, 0, 0, 0};
+    decode_job J = {q, k_pages, v_pages, seq_lens, b, T, h, g, page_size * max_pages,
+                    d, dtype, (double)scale, out, NULL, 0, 0, 0, block_table,
+                    page_size, max_pages, num_pages};
     return run_decode(&J, nthreads);
 }
 
@@ -179,42 +216,52 @@ int oracle_decode_attn_paged(const void *q, const void *k_pages,
                              const int32_t *seq_lens, int b, int h, int g,
                              int page_size, int max_pages, int num_pages, int d,
                              int dtype, float scale, double *out, int nthreads) {
-    if (b < 1 || h < 1 || g < 1 || d < 1 || h % g != 0 || page_size < 1 ||
-        max_pages < 1 || num_pages < 1)
+    return oracle_decode_attn_paged_multi(q, k_pages, v_pages, block_table, seq_lens,
+                                          b, 1, h, g, page_size, max_pages,
+                                          num_pages, d, dtype, scale, out, nthreads);
+}
+
+int oracle_append_kv_paged_multi(void *k_pages, void *v_pages, const void *k_new,
+                                 const void *v_new, const int32_t *block_table,
+                                 const int32_t *seq_lens, int b, int T, int g,
+                                 int page_size, int max_pages, int num_pages, int d,
+                                 int dtype) {
+    if (b < 1 || T < 1 || g < 1 || d < 1 || page_size < 1 || max_pages < 1 ||
+        num_pages < 1)
         return ORACLE_BAD_SHAPE;
-    decode_job J = {q, k_pages, v_pages, seq_lens, b, h, g, page_size * max_pages, d,
-                    dtype, (double)scale, out, NULL, 0, 0, 0, block_table, page_size,
-                    max_pages, num_pages};
-    return run_decode(&J, nthreads);
+    int rc = ORACLE_OK;
+    size_t row = (size_t)d * elem_bytes(dtype);
+    for (int i = 0; i < b; i++) {
+        int L = seq_lens[i];
+        if (L < T || L > page_size * max_pages) {
+            rc |= ORACLE_BAD_LEN;
+            continue;
+        }
+        for (int tau = 0; tau < T; tau++) {
+            int t = L - T + tau; /* position of token tau */
+            int page = block_table[(size_t)i * max_pages + t / page_size];
+            if (page < 0 || page >= num_pages) {
+                rc |= ORACLE_BAD_PAGE;
+                continue;
+            }
+            for (int j = 0; j < g; j++) {
+                size_t dst = (((size_t)page * g + j) * page_size + (size_t)(t % page_size)) * row;
+                size_t src = (((size_t)i * T + tau) * g + j) * row;
+                memcpy((char *)k_pages + dst, (const char *)k_new + src, row);
+                memcpy((char *)v_pages + dst, (const char *)v_new + src, row);
+            }
+        }
+    }
+    return rc;
 }
 
 int oracle_append_kv_paged(void *k_pages, void *v_pages, const void *k_new,
                            const void *v_new, const int32_t *block_table,
                            const int32_t *seq_lens, int b, int g, int page_size,
                            int max_pages, int num_pages, int d, int dtype) {
-    if (b < 1 || g < 1 || d < 1 || page_size < 1 || max_pages < 1 || num_pages < 1)
-        return ORACLE_BAD_SHAPE;
-    int rc = ORACLE_OK;
-    size_t row = (size_t)d * elem_bytes(dtype);
-    for (int i = 0; i < b; i++) {
-        int L = seq_lens[i];
-        if (L < 1 || L > page_size * max_pages) {
-            rc |= ORACLE_BAD_LEN;
-            continue;
-        }
-        int page = block_table[(size_t)i * max_pages + (L - 1) / page_size];
-        if (page < 0 || page >= num_pages) {
-            rc |= ORACLE_BAD_PAGE;
-            continue;
-        }
-        for (int j = 0; j < g; j++) {
-            size_t dst = (((size_t)page * g + j) * page_size + (size_t)((L - 1) % page_size)) * row;
-            size_t src = ((size_t)i * g + j) * row;
-            memcpy((char *)k_pages + dst, (const char *)k_new + src, row);
-            memcpy((char *)v_pages + dst, (const char *)v_new + src, row);
-        }
-    }
-    return rc;
+    return oracle_append_kv_paged_multi(k_pages, v_pages, k_new, v_new, block_table,
+                                        seq_lens, b, 1, g, page_size, max_pages,
+                                        num_pages, d, dtype);
 }
 
 /* ---- textbook MHA, one K/V per query head ----------------------------- */

@@ -21,11 +21,11 @@
  * the upper 16 bits of a binary32 (decoded exactly by a 16-bit shift).
  *
  * Layouts (row-major, last index fastest):
- *   q        [b][h][d]
+ *   q        [b][h][d]        ([b][T][h][d] for T query tokens per sequence)
  *   k, v     [b][g][S][d]     (S = capacity; rows >= seq_lens[i] are unused)
- *   k/v_new  [b][g][d]
- *   out      [b][h][d]        (double)
- *   alpha    [b][h][S]        (double, optional attention weights)
+ *   k/v_new  [b][g][d]        ([b][T][g][d])
+ *   out      [b][h][d]        (double; [b][T][h][d])
+ *   alpha    [b][h][S]        (double, optional attention weights; [b][T][h][S])
  */
 #ifndef ORACLE_DECODE_ATTN_H
 #define ORACLE_DECODE_ATTN_H
@@ -37,7 +37,8 @@ extern "C" {
 
 enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
 
-/* Return bits. ORACLE_BAD_LEN: some seq_lens[i] outside [1, S]; those rows
+/* Return bits. ORACLE_BAD_LEN: some seq_lens[i] outside [1, S] ([T, S] with T
+ * query tokens); those rows
  * are left alone by append and set to NaN by decode. ORACLE_BAD_SHAPE: h not a
  * multiple of g, or a size < 1; nothing is written. */
 enum { ORACLE_OK = 0, ORACLE_BAD_LEN = 1, ORACLE_BAD_SHAPE = 2, ORACLE_BAD_PAGE = 4 };
@@ -77,6 +78,33 @@ int oracle_append_kv_paged(void *k_pages, void *v_pages, const void *k_new,
                            const void *v_new, const int32_t *block_table,
                            const int32_t *seq_lens, int b, int g, int page_size,
                            int max_pages, int num_pages, int d, int dtype);
+
+/* T query tokens per sequence (a draft of several tokens verified at once,
+ * or a chunk of a prompt): the step's tokens are positions L_i-T .. L_i-1
+ * (seq_lens counts them), token tau attends positions t <= L_i-T+tau only,
+ * since the causal mask is applied per query position whether K/V are shared
+ * or not ([GQA notes] §十 item 10; the §八 reference code writes T rows at
+ * once). Rows of q and out are (i*T + tau)*h + hq. seq_lens[i] < T is a bad
+ * length. Append writes token tau of k_new/v_new [b][T][g][d] to position
+ * L_i-T+tau. T = 1 is the functions above, which call these. */
+int oracle_append_kv_multi(void *k_cache, void *v_cache, const void *k_new,
+                           const void *v_new, const int32_t *seq_lens, int b,
+                           int T, int g, int S, int d, int dtype);
+int oracle_decode_attn_multi(const void *q, const void *k, const void *v,
+                             const int32_t *seq_lens, int b, int T, int h, int g,
+                             int S, int d, int dtype, float scale, double *out,
+                             double *alpha, int nthreads);
+int oracle_decode_attn_paged_multi(const void *q, const void *k_pages,
+                                   const void *v_pages, const int32_t *block_table,
+                                   const int32_t *seq_lens, int b, int T, int h,
+                                   int g, int page_size, int max_pages,
+                                   int num_pages, int d, int dtype, float scale,
+                                   double *out, int nthreads);
+int oracle_append_kv_paged_multi(void *k_pages, void *v_pages, const void *k_new,
+                                 const void *v_new, const int32_t *block_table,
+                                 const int32_t *seq_lens, int b, int T, int g,
+                                 int page_size, int max_pages, int num_pages, int d,
+                                 int dtype);
 
 /* Textbook multi-head attention for one sequence, one K/V head per query
  * head (no sharing): q [h][d], K and V [h][L][d], all double.

@@ -395,14 +395,134 @@ def test_indivisible_heads_rejected():
 
 
 # ---------------------------------------------------------------------------
+# T query tokens per sequence with the causal mask ([GQA notes] §十 item 10)
+# ---------------------------------------------------------------------------
+
+def _causal_sdpa_last_rows(q_tok, k, v, L, scale, rng):
+    """torch SDPA (float64) with is_causal=True over a full L-query problem whose
+    last T query rows are q_tok [T, h, d] (the first L-T rows are arbitrary):
+    row p of a causal L x L attention sees positions <= p, so the last T rows
+    are the step's tokens at positions L-T .. L-1. k, v [g, >=L, d]."""
+    T, h, d = q_tok.shape
+    g = k.shape[0]
+    qf = np.concatenate([rng.standard_normal((L - T, h, d)), q_tok], axis=0)  # [L, h, d]
+    qt = torch.from_numpy(np.ascontiguousarray(qf.transpose(1, 0, 2))).view(1, h, L, d)
+    kt = torch.from_numpy(np.ascontiguousarray(k[:, :L])).view(1, g, L, d)
+    vt = torch.from_numpy(np.ascontiguousarray(v[:, :L])).view(1, g, L, d)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale, is_causal=True,
+                                                         enable_gqa=(g != h))
+    return o.view(h, L, d).numpy().transpose(1, 0, 2)[L - T:]  # [T, h, d]
+
+
+@pytest.mark.parametrize("T,h,g", [(4, 8, 2), (3, 6, 6), (5, 8, 1)])
+def test_multi_matches_causal_sdpa(T, h, g):
+    """T tokens per sequence = the last T rows of torch's causal SDPA over the
+    whole sequence (float64), for L > T and L = T (the whole prompt at once)."""
+    rng = np.random.default_rng(T * 10 + h + g)
+    b, S, d = 3, 40, 64
+    q, k, v = randn(b, T, h, d, scale=2.0), randn(b, g, S, d), randn(b, g, S, d)
+    lens = np.array([40, T, 23], np.int32)
+    out, _, rc = oracle.decode_attn_multi(q, k, v, lens, 0.125)
+    assert rc == oracle.OK
+    for i in range(b):
+        ref = _causal_sdpa_last_rows(q[i].astype(np.float64), k[i].astype(np.float64),
+                                     v[i].astype(np.float64), int(lens[i]), 0.125, rng)
+        np.testing.assert_allclose(out[i], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_multi_token_is_single_decode_over_its_prefix():
+    """Token tau of a T-token step = the one-token decode (pinned above) of that
+    token over the first L-T+1+tau positions; T = 1 is the one-token decode."""
+    b, T, h, g, S, d = 2, 4, 8, 2, 30, 64
+    q, k, v = randn(b, T, h, d), randn(b, g, S, d), randn(b, g, S, d)
+    lens = np.array([30, 9], np.int32)
+    out, _, rc = oracle.decode_attn_multi(q, k, v, lens, 0.125)
+    assert rc == oracle.OK
+    for tau in range(T):
+        one, _, _ = oracle.decode_attn(np.ascontiguousarray(q[:, tau]), k, v, lens - T + 1 + tau, 0.125)
+        np.testing.assert_array_equal(out[:, tau], one)
+    one_tok, _, _ = oracle.decode_attn_multi(q[:, :1].copy(), k, v, lens, 0.125)
+    flat, _, _ = oracle.decode_attn(np.ascontiguousarray(q[:, 0]), k, v, lens, 0.125)
+    assert np.array_equal(one_tok[:, 0], flat)
+
+
+def test_multi_weights_vanish_past_each_tokens_position():
+    b, T, h, g, S, d = 1, 3, 4, 1, 12, 64
+    q, k, v = randn(b, T, h, d), randn(b, g, S, d), randn(b, g, S, d)
+    L = 10
+    _, alpha, _ = oracle.decode_attn_multi(q, k, v, np.array([L], np.int32), 0.125, want_alpha=True)
+    for tau in range(T):
+        A = L - T + 1 + tau
+        np.testing.assert_allclose(alpha[0, tau].sum(axis=-1), 1.0, rtol=1e-12)
+        assert (alpha[0, tau, :, A:] == 0).all() and (alpha[0, tau, :, A - 1] > 0).all()
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_append_multi_writes_t_rows_per_head(bf16):
+    b, T, g, S, d = 3, 3, 2, 10, 64
+    kc, vc = randn(b, g, S, d), randn(b, g, S, d)
+    kn, vn = randn(b, T, g, d), randn(b, T, g, d)
+    if bf16:
+        kc, vc, kn, vn = bf16_bits(kc), bf16_bits(vc), bf16_bits(kn), bf16_bits(vn)
+    lens = np.array([3, 10, 7], np.int32)
+    k2, v2 = kc.copy(), vc.copy()
+    assert oracle.append_kv_multi(k2, v2, kn, vn, lens) == oracle.OK
+    ek, ev = kc.copy(), vc.copy()
+    for i in range(b):
+        for tau in range(T):
+            ek[i, :, lens[i] - T + tau] = kn[i, tau]
+            ev[i, :, lens[i] - T + tau] = vn[i, tau]
+    assert k2.tobytes() == ek.tobytes() and v2.tobytes() == ev.tobytes()
+
+
+def test_multi_length_below_t_is_flagged():
+    b, T, g, S, d = 2, 4, 1, 8, 64
+    kc, vc = randn(b, g, S, d), randn(b, g, S, d)
+    kn, vn = randn(b, T, g, d), randn(b, T, g, d)
+    lens = np.array([3, 8], np.int32)
+    k2, v2 = kc.copy(), vc.copy()
+    assert oracle.append_kv_multi(k2, v2, kn, vn, lens) == oracle.BAD_LEN
+    np.testing.assert_array_equal(k2[0], kc[0])
+    out, _, rc = oracle.decode_attn_multi(randn(b, T, 2, d), kc, vc, lens, 0.125)
+    assert rc == oracle.BAD_LEN
+    assert np.isnan(out[0]).all() and np.isfinite(out[1]).all()
+
+
+def test_paged_multi_matches_contiguous_multi():
+    """Paged T-token decode = the contiguous one on the gathered cache (bitwise);
+    the paged append writes T rows that may straddle a page boundary."""
+    rng = np.random.default_rng(77)
+    b, T, h, g, S, d, P = 3, 5, 8, 2, 48, 64, 16
+    q, k, v = randn(b, T, h, d), randn(b, g, S, d), randn(b, g, S, d)
+    lens = np.array([48, 18, 5], np.int32)  # 18: tokens at 13..17 straddle pages 0 and 1
+    kp, vp, bt = _paged_from_contiguous(k, v, P, rng)
+    out, rc = oracle.decode_attn_paged_multi(q, kp, vp, bt, lens, 0.125)
+    assert rc == oracle.OK
+    flat, _, _ = oracle.decode_attn_multi(q, k, v, lens, 0.125)
+    assert np.array_equal(out, flat)
+    kn, vn = randn(b, T, g, d), randn(b, T, g, d)
+    assert oracle.append_kv_paged_multi(kp, vp, kn, vn, bt, lens) == oracle.OK
+    assert oracle.append_kv_multi(k, v, kn, vn, lens) == oracle.OK
+    for i in range(b):
+        for t in range(int(lens[i])):
+            page, row = bt[i, t // P], t % P
+            np.testing.assert_array_equal(kp[page, :, row], k[i, :, t])
+            np.testing.assert_array_equal(vp[page, :, row], v[i, :, t])
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: each mutant of the oracle's source must fail a pin above
 # ---------------------------------------------------------------------------
 
 MUTANTS = {
     "group map i % g": ("int j = hq / G;", "int j = hq % J->g;"),
     "scale dropped": ("s[t] = J->scale * dot;", "s[t] = dot;"),
-    "attended length off by one": ("for (int t = 0; t < L; t++) {\n        double dot", "for (int t = 0; t < L - 1; t++) {\n        double dot"),
-    "no normalisation": ("for (int t = 0; t < L; t++) s[t] /= Z;", ""),
+    "attended length off by one": ("for (int t = 0; t < A; t++) {\n        double dot", "for (int t = 0; t < A - 1; t++) {\n        double dot"),
+    "causal mask dropped": ("int A = L - J->T + 1 + tau;", "int A = L;"),
+    "token order reversed": ("int A = L - J->T + 1 + tau;", "int A = L - tau;"),
+    "every token uses the first token's query": ("size_t qoff = (size_t)row * d;", "size_t qoff = ((size_t)i * J->T * J->h + hq) * d;"),
+    "appended tokens reversed": ("* S + (size_t)(L - T + tau)) * row;", "* S + (size_t)(L - 1 - tau)) * row;"),
+    "no normalisation": ("for (int t = 0; t < A; t++) s[t] /= Z;", ""),
     "key and value swapped": ("elem(J->v, (size_t)kv_row(J, i, j, t) + x, J->dtype);\n        o[x]", "elem(J->k, (size_t)kv_row(J, i, j, t) + x, J->dtype);\n        o[x]"),
     "page looked up one position late": ("(size_t)i * J->max_pages + t / J->page_size]", "(size_t)i * J->max_pages + (t + 1) / J->page_size]"),
     "row within the page ignored": ("J->page_size + t % J->page_size) * J->d", "J->page_size) * J->d"),
@@ -428,14 +548,18 @@ def test_planted_mistakes_are_caught(tmp_path, name, monkeypatch):
     mutant = ctypes.CDLL(so)
     real = oracle.lib()
     # reuse the argument declarations of the real library
-    for fn in ("oracle_decode_attn", "oracle_mha_per_head", "oracle_decode_attn_paged"):
+    for fn in ("oracle_decode_attn", "oracle_mha_per_head", "oracle_decode_attn_paged",
+               "oracle_decode_attn_multi", "oracle_decode_attn_paged_multi",
+               "oracle_append_kv_multi", "oracle_append_kv_paged_multi"):
         getattr(mutant, fn).argtypes = getattr(real, fn).argtypes
         getattr(mutant, fn).restype = getattr(real, fn).restype
     monkeypatch.setattr(oracle, "_lib", mutant)
     caught = []
     for pin in (test_hand_example, lambda: test_matches_torch_sdpa(12, 4),
                 lambda: test_matches_torch_sdpa(8, 8),
-                lambda: test_paged_matches_gathered_sdpa(16, 8, 2)):
+                lambda: test_paged_matches_gathered_sdpa(16, 8, 2),
+                lambda: test_multi_matches_causal_sdpa(4, 8, 2),
+                lambda: test_append_multi_writes_t_rows_per_head(False)):
         try:
             pin()
         except AssertionError:
