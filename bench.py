@@ -23,7 +23,12 @@ one int32 block table per batch): mqa_append_kv_paged + mqa_decode_attn_paged,
 whose algorithmic bytes add the block-table entries read (sum_i ceil(L_i/P)*4,
 and 4*b for the append).
 
+With --tokens T each sequence brings T query tokens per step (a draft of T
+tokens verified at once, causal mask): mqa_append_kv_multi + mqa_decode_attn_multi
+(or their paged forms); q and out are T times larger, the K/V bytes the same.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--page-size P]
+                       [--tokens T]
 """
 from __future__ import annotations
 
@@ -62,6 +67,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--page-size", type=int, default=0,
                     help="paged KV cache with pages of this many rows (0: contiguous cache)")
+    ap.add_argument("--tokens", type=int, default=1,
+                    help="query tokens per sequence per step (causal; 1: plain decode)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -94,60 +101,68 @@ def main() -> int:
           f"copies={reps} ({reps * cache_bytes / 2**30:.2f} GiB of cache)", file=sys.stderr, flush=True)
 
     P = args.page_size
-    if P:
-        if args.kernel == "valu":
-            print("the paged path runs the matrix-core kernels only", file=sys.stderr)
-            return 2
-        steps_in = []
-        for r in range(reps):
+    T = args.tokens
+    if (P or T > 1) and args.kernel == "valu":
+        print("paged and multi-token calls run the matrix-core kernels only", file=sys.stderr)
+        return 2
+    steps_in = []
+    for r in range(reps):
+        if T > 1:
+            t = W.make_multi_step(w, dev, T=T, layer=r, page_size=P)
+        elif P:
             t = W.make_paged_step(w, dev, page_size=P, layer=r)
+        else:
+            t = W.make_step(w, dev, layer=r)
+        if P:
             del t["k_cache"], t["v_cache"]  # the pages hold the cache
-            steps_in.append(t)
-        cap = steps_in[0]["capacity"]
-        maxp = cap // P
-        ws = torch.empty(mqa.decode_paged_workspace_bytes(w.b, w.h, w.g, P, maxp, w.d, w.dtype,
-                                                          args.split_chunk),
-                         dtype=torch.uint8, device=dev)
-    else:
-        steps_in = [W.make_step(w, dev, layer=r) for r in range(reps)]
-        cap = w.S
-        ws = mqa.decode_workspace(w.b, w.h, w.g, w.S, w.d, w.dtype, dev, args.split_chunk)
+        steps_in.append(t)
+    cap = steps_in[0]["capacity"] if P else w.S
+    ws = torch.empty(mqa.decode_multi_workspace_bytes(w.b, T, w.h, w.g, cap, w.d, w.dtype,
+                                                      args.split_chunk),
+                     dtype=torch.uint8, device=dev)
     lens = steps_in[0]["seq_lens"].cpu().numpy().astype(np.int64)
     chunk = mqa.decode_resolve_chunk(w.b, w.h, w.g, cap, w.d, w.dtype, args.split_chunk)
-    outs = [torch.empty((w.b, w.h, w.d), dtype=torch.float32, device=dev) for _ in range(reps)]
+    oshape = (w.b, T, w.h, w.d) if T > 1 else (w.b, w.h, w.d)
+    outs = [torch.empty(oshape, dtype=torch.float32, device=dev) for _ in range(reps)]
     err = torch.zeros(1, dtype=torch.int32, device=dev)
 
     kernel = {"auto": mqa.KERNEL_AUTO, "valu": mqa.KERNEL_VALU, "mfma": mqa.KERNEL_MFMA}[args.kernel]
-    schedule = mqa.decode_schedule(w.b, w.h, w.g, cap, w.d, w.dtype, args.split_chunk, kernel)
+    if T > 1:
+        schedule = mqa.decode_multi_schedule(w.b, T, w.h, w.g, cap, w.d, w.dtype, args.split_chunk)
+    else:
+        schedule = mqa.decode_schedule(w.b, w.h, w.g, cap, w.d, w.dtype, args.split_chunk, kernel)
     B = w.elem_bytes
     kv_read = int(sum(2 * w.g * int(L) * w.d * B for L in lens))
-    dec_bytes = kv_read + w.b * w.h * w.d * B + w.b * w.h * w.d * 4
-    app_bytes = 2 * (2 * w.b * w.g * w.d * B)
+    dec_bytes = kv_read + w.b * T * w.h * w.d * B + w.b * T * w.h * w.d * 4
+    app_bytes = 2 * (2 * w.b * T * w.g * w.d * B)
     if P:
         dec_bytes += 4 * int(sum(-(-int(L) // P) for L in lens))
-        app_bytes += 4 * w.b
+        app_bytes += 4 * w.b * T
     per_layer = dec_bytes + app_bytes
     step_bytes = per_layer * layers
-    flops_per_step = 4 * w.h * int(lens.sum()) * w.d * layers
+    # token tau of a sequence of length L attends L - T + 1 + tau positions
+    flops_per_step = 4 * w.h * w.d * layers * int(sum(T * (int(L) - T + 1) + T * (T - 1) // 2
+                                                      for L in lens))
 
     def layer_call(r, ev=None):
         t = steps_in[r]
+        kw = dict(out=outs[r], workspace=ws, split_chunk=args.split_chunk, err_flags=err)
         if P:
-            mqa.append_kv_paged(t["k_pages"], t["v_pages"], t["k_new"], t["v_new"],
-                                t["block_table"], t["seq_lens"], err_flags=err)
+            pages = (t["k_pages"], t["v_pages"])
+            append = mqa.append_kv_paged_multi if T > 1 else mqa.append_kv_paged
+            append(*pages, t["k_new"], t["v_new"], t["block_table"], t["seq_lens"], err_flags=err)
         else:
-            mqa.append_kv(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], t["seq_lens"],
-                          err_flags=err)
+            append = mqa.append_kv_multi if T > 1 else mqa.append_kv
+            append(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], t["seq_lens"], err_flags=err)
         if ev is not None:
             ev[0].record()
         if P:
-            mqa.decode_attn_paged(t["q"], t["k_pages"], t["v_pages"], t["block_table"],
-                                  t["seq_lens"], out=outs[r], workspace=ws,
-                                  split_chunk=args.split_chunk, err_flags=err)
+            decode = mqa.decode_attn_paged_multi if T > 1 else mqa.decode_attn_paged
+            decode(t["q"], *pages, t["block_table"], t["seq_lens"], **kw)
+        elif T > 1:
+            mqa.decode_attn_multi(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], **kw)
         else:
-            mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], out=outs[r],
-                            workspace=ws, split_chunk=args.split_chunk, err_flags=err,
-                            kernel=kernel)
+            mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], kernel=kernel, **kw)
         if ev is not None:
             ev[1].record()
 
@@ -198,7 +213,7 @@ def main() -> int:
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = dec_bytes / (dec_ms_avg * 1e-3) / 1e9
     traffic = None
-    tag = w.name + (f"-paged{P}" if P else "")
+    tag = w.name + (f"-paged{P}" if P else "") + (f"-t{T}" if T > 1 else "")
     tf = os.path.join(ROOT, "profiles", f"decode_{tag}_traffic.json")
     if os.path.exists(tf):
         rec = json.load(open(tf))
@@ -225,6 +240,7 @@ def main() -> int:
                    "seq_lens": "fixed %d" % w.L if w.L else f"U[{w.L_lo},{w.L_hi}] (sum {int(lens.sum())})",
                    "layers": layers, "schedule": schedule,
                    "kv_layout": f"paged, {P}-row pages" if P else "contiguous",
+                   "query_tokens": T,
                    "split_chunk": chunk if schedule != "mfma-balanced" else None,
                    "cache_copies_rotated": reps,
                    "accumulate": "fp32", "out": "fp32"},
@@ -232,7 +248,7 @@ def main() -> int:
         "flops_per_step": flops_per_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("mqa_decode_attn_paged" if P else "mqa_decode_attn")
+            "kernel": ("mqa_decode_attn" + ("_paged" if P else "") + ("_multi" if T > 1 else ""))
                       + " launch, schedule " + schedule,
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
@@ -247,13 +263,13 @@ def main() -> int:
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, steps_in[0], lens, per_layer, layers,
-                                              args.cpu_seconds, P)
+                                              args.cpu_seconds, P, T)
 
     print(json.dumps(result), flush=True)
     return 0
 
 
-def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0):
+def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1):
     """The oracle (plain double loops) on the host cores, one layer's step."""
     import numpy as np
 
@@ -267,16 +283,16 @@ def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0):
     if page_size:
         kp, vp = W.to_oracle(t["k_pages"]), W.to_oracle(t["v_pages"])
         bt = t["block_table"].cpu().numpy()
+        paged = oracle.decode_attn_paged_multi if T > 1 else oracle.decode_attn_paged
 
         def run(n):
-            oracle.decode_attn_paged(q[:n].copy(), kp, vp, bt[:n].copy(), lens32[:n], scale,
-                                     nthreads=nthreads)
+            paged(q[:n].copy(), kp, vp, bt[:n].copy(), lens32[:n], scale, nthreads=nthreads)
     else:
         kc, vc = W.to_oracle(t["k_cache"]), W.to_oracle(t["v_cache"])
+        flat = oracle.decode_attn_multi if T > 1 else oracle.decode_attn
 
         def run(n):
-            oracle.decode_attn(q[:n].copy(), kc[:n].copy(), vc[:n].copy(), lens32[:n], scale,
-                               nthreads=nthreads)
+            flat(q[:n].copy(), kc[:n].copy(), vc[:n].copy(), lens32[:n], scale, nthreads=nthreads)
     # bounded sample: the first sequences of the batch, sized to the budget
     # from a one-sequence probe
     t0 = time.perf_counter()
@@ -289,7 +305,7 @@ def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0):
     run(nb)
     dt = time.perf_counter() - t0
     B = w.elem_bytes
-    sample_bytes = int(sum(2 * w.g * int(L) * w.d * B for L in lens32[:nb])) + nb * w.h * w.d * (B + 4)
+    sample_bytes = int(sum(2 * w.g * int(L) * w.d * B for L in lens32[:nb])) + nb * T * w.h * w.d * (B + 4)
     gbs = sample_bytes / dt / 1e9
     return {
         "value": round(gbs, 4),

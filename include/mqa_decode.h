@@ -203,6 +203,67 @@ mqa_status mqa_decode_attn_paged(const void *q, const void *k_pages,
                                  int split_chunk, int32_t *err_flags,
                                  hipStream_t stream);
 
+/*
+ * Several query tokens per sequence (T >= 1): a draft of T tokens verified in
+ * one step, or a chunk of a prompt. [GQA notes] §八 (its reference code writes
+ * the T new rows of the cache at once and attends them together) and §十
+ * item 10 (the causal mask stays per query position when K/V heads are
+ * shared).
+ *
+ *   q        : [b][T][h][d] of dt; token tau of sequence i sits at position
+ *              seq_lens[i] - T + tau (seq_lens counts the T new tokens)
+ *   k_new, v_new : [b][T][g][d] of dt; the append writes token tau to
+ *              cache position seq_lens[i] - T + tau
+ *   out      : [b][T][h][d] fp32; token tau attends positions
+ *              t <= seq_lens[i] - T + tau (the causal mask)
+ * A sequence with seq_lens[i] outside [T, S] is handled as an invalid length
+ * (skipped by the append, NaN rows, MQA_DEVERR_SEQLEN). T must be in [1, S];
+ * T = 1 is exactly mqa_append_kv / mqa_decode_attn (and the _paged calls).
+ * For T > 1 the decode is bf16 only (MQA_F32: MQA_ERR_UNSUPPORTED) and runs
+ * the matrix-core kernels. The workspace is
+ * mqa_decode_multi_workspace_bytes() bytes, with S the capacity
+ * (page_size * max_pages for a paged cache); the paged calls take their
+ * arguments as in the paged section above.
+ */
+mqa_status mqa_append_kv_multi(void *k_cache, void *v_cache, const void *k_new,
+                               const void *v_new, const int32_t *seq_lens,
+                               int b, int T, int g, int S, int d, mqa_dtype dt,
+                               int32_t *err_flags, hipStream_t stream);
+
+size_t mqa_decode_multi_workspace_bytes(int b, int T, int h, int g, int S, int d,
+                                        mqa_dtype dt, int split_chunk);
+
+/* The schedule (mqa_schedule) a T-token call runs; -1: invalid arguments. */
+int mqa_decode_multi_schedule(int b, int T, int h, int g, int S, int d,
+                              mqa_dtype dt, int split_chunk);
+
+mqa_status mqa_decode_attn_multi(const void *q, const void *k_cache,
+                                 const void *v_cache, const int32_t *seq_lens,
+                                 int b, int T, int h, int g, int S, int d,
+                                 mqa_dtype dt, float scale, float *out,
+                                 void *workspace, size_t workspace_bytes,
+                                 int split_chunk, int32_t *err_flags,
+                                 hipStream_t stream);
+
+mqa_status mqa_append_kv_paged_multi(void *k_pages, void *v_pages,
+                                     const void *k_new, const void *v_new,
+                                     const int32_t *block_table,
+                                     const int32_t *seq_lens, int b, int T,
+                                     int g, int page_size, int max_pages,
+                                     int num_pages, int d, mqa_dtype dt,
+                                     int32_t *err_flags, hipStream_t stream);
+
+mqa_status mqa_decode_attn_paged_multi(const void *q, const void *k_pages,
+                                       const void *v_pages,
+                                       const int32_t *block_table,
+                                       const int32_t *seq_lens, int b, int T,
+                                       int h, int g, int page_size,
+                                       int max_pages, int num_pages, int d,
+                                       mqa_dtype dt, float scale, float *out,
+                                       void *workspace, size_t workspace_bytes,
+                                       int split_chunk, int32_t *err_flags,
+                                       hipStream_t stream);
+
 /* Static text for a status code (never NULL). */
 const char *mqa_status_string(mqa_status s);
 

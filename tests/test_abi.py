@@ -178,3 +178,53 @@ def test_paged_workspace_bytes():
     n = mqa.decode_paged_workspace_bytes(64, 64, 8, 16, 256, 128, mqa.BF16)
     assert n == mqa.decode_workspace_bytes(64, 64, 8, 16 * 256, 128, mqa.BF16)
     assert mqa.decode_paged_workspace_bytes(64, 64, 8, 24, 256, 128, mqa.BF16) == 0
+
+
+def multi_decode(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, b=2, T=4, h=8, g=2, S=64, d=128, dt=mqa.BF16,
+             scale=0.088, out=FAKE, ws=FAKE, ws_bytes=1 << 30, chunk=0)
+    a.update(kw)
+    return mqa.lib().mqa_decode_attn_multi(a["q"], a["k"], a["v"], a["lens"], a["b"], a["T"],
+                                           a["h"], a["g"], a["S"], a["d"], a["dt"],
+                                           ctypes.c_float(a["scale"]), a["out"], a["ws"],
+                                           a["ws_bytes"], a["chunk"], None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), mqa.ERR_NULL),
+    (dict(T=0), mqa.ERR_SHAPE),
+    (dict(T=65), mqa.ERR_SHAPE),             # more tokens than the capacity
+    (dict(dt=mqa.F32), mqa.ERR_UNSUPPORTED),  # several tokens: matrix-core kernels, bf16
+    (dict(h=6, g=4), mqa.ERR_SHAPE),
+    (dict(out=MISALIGNED), mqa.ERR_ALIGN),
+    (dict(ws_bytes=16), mqa.ERR_WORKSPACE),
+])
+def test_multi_decode_rejects_bad_arguments_before_launch(kw, status):
+    assert multi_decode(**kw) == status
+
+
+def test_multi_append_rejects_bad_arguments_before_launch():
+    L = mqa.lib()
+    assert L.mqa_append_kv_multi(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 0, 2, 64, 128, mqa.BF16, None,
+                                 None) == mqa.ERR_SHAPE
+    assert L.mqa_append_kv_multi(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 65, 2, 64, 128, mqa.BF16, None,
+                                 None) == mqa.ERR_SHAPE
+    assert L.mqa_append_kv_multi(FAKE, None, FAKE, FAKE, FAKE, 2, 4, 2, 64, 128, mqa.BF16, None,
+                                 None) == mqa.ERR_NULL
+
+
+def test_multi_workspace_and_schedule():
+    # T = 1 is the one-token call
+    assert mqa.decode_multi_workspace_bytes(64, 1, 64, 8, 4096, 128, mqa.BF16) == \
+        mqa.decode_workspace_bytes(64, 64, 8, 4096, 128, mqa.BF16)
+    assert mqa.decode_multi_schedule(64, 1, 64, 8, 4096, 128, mqa.BF16) == "mfma-balanced"
+    # T tokens of G heads: T*G query rows per K/V head; up to 64 on the balanced schedule
+    assert mqa.decode_multi_schedule(64, 4, 64, 8, 4096, 128, mqa.BF16) == "mfma-balanced"
+    assert mqa.decode_multi_schedule(64, 8, 64, 8, 4096, 128, mqa.BF16) == "mfma-balanced"
+    assert mqa.decode_multi_schedule(64, 9, 64, 8, 4096, 128, mqa.BF16) == "mfma-partitions"
+    assert mqa.decode_multi_schedule(8, 4, 32, 1, 1024, 128, mqa.BF16) == "mfma-partitions"
+    assert mqa.decode_multi_workspace_bytes(64, 4, 64, 8, 4096, 128, mqa.F32) == 0
+    n1 = mqa.decode_multi_workspace_bytes(8, 1, 32, 1, 1024, 128, mqa.BF16, 256)
+    n4 = mqa.decode_multi_workspace_bytes(8, 4, 32, 1, 1024, 128, mqa.BF16, 256)
+    assert n1 == 8 * 32 * 4 * (128 * 4 + 8)  # partials (o, m, l) of 4 partitions per row
+    assert n4 == 4 * n1                        # one set per query token

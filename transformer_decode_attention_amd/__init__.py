@@ -16,6 +16,12 @@ Entry points (same names as the C ABI, without the ``mqa_`` prefix):
   decode_attn_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, out=None,
                     workspace=None, split_chunk=0, err_flags=None) -> out
   decode_paged_workspace_bytes(b, h, g, page_size, max_pages, d, dtype, split_chunk=0)
+  append_kv_multi(k_cache, v_cache, k_new, v_new, seq_lens, err_flags=None)
+  decode_attn_multi(q, k_cache, v_cache, seq_lens, ...) -> out      (q [b, T, h, d])
+  append_kv_paged_multi(k_pages, v_pages, k_new, v_new, block_table, seq_lens, err_flags=None)
+  decode_attn_paged_multi(q, k_pages, v_pages, block_table, seq_lens, ...) -> out
+  decode_multi_workspace_bytes(b, T, h, g, S, d, dtype, split_chunk=0)
+  decode_multi_schedule(b, T, h, g, S, d, dtype, split_chunk=0)
   kv_bytes(layers, g, S, d, dtype_bytes)
   status_string(status)
 
@@ -34,6 +40,8 @@ __all__ = [
     "append_kv", "decode_attn", "decode_workspace_bytes", "decode_workspace", "decode_resolve_chunk",
     "decode_schedule", "kv_bytes", "status_string", "MQAError", "LIB_PATH", "DEVERR_SEQLEN",
     "DEVERR_PAGE", "append_kv_paged", "decode_attn_paged", "decode_paged_workspace_bytes",
+    "append_kv_multi", "decode_attn_multi", "append_kv_paged_multi", "decode_attn_paged_multi",
+    "decode_multi_workspace_bytes", "decode_multi_schedule",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa_decode.so")
@@ -49,7 +57,9 @@ EXPORTS = (
     "mqa_append_kv", "mqa_decode_workspace_bytes", "mqa_decode_resolve_chunk",
     "mqa_decode_attn", "mqa_decode_attn_kernel", "mqa_decode_schedule", "mqa_status_string",
     "mqa_kv_bytes", "mqa_append_kv_paged", "mqa_decode_paged_workspace_bytes",
-    "mqa_decode_attn_paged",
+    "mqa_decode_attn_paged", "mqa_append_kv_multi", "mqa_decode_multi_workspace_bytes",
+    "mqa_decode_multi_schedule", "mqa_decode_attn_multi", "mqa_append_kv_paged_multi",
+    "mqa_decode_attn_paged_multi",
 )
 SCHEDULES = {0: "valu-partitions", 1: "mfma-partitions", 2: "mfma-balanced"}
 
@@ -93,6 +103,22 @@ def _load() -> ctypes.CDLL:
     L.mqa_decode_attn_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                         i32, ctypes.c_float, vp, vp, ctypes.c_size_t, i32, vp, vp]
     L.mqa_decode_attn_paged.restype = i32
+    L.mqa_append_kv_multi.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
+    L.mqa_append_kv_multi.restype = i32
+    L.mqa_decode_multi_workspace_bytes.argtypes = [i32] * 8
+    L.mqa_decode_multi_workspace_bytes.restype = ctypes.c_size_t
+    L.mqa_decode_multi_schedule.argtypes = [i32] * 8
+    L.mqa_decode_multi_schedule.restype = i32
+    L.mqa_decode_attn_multi.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                        ctypes.c_float, vp, vp, ctypes.c_size_t, i32, vp, vp]
+    L.mqa_decode_attn_multi.restype = i32
+    L.mqa_append_kv_paged_multi.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                            i32, i32, i32, vp, vp]
+    L.mqa_append_kv_paged_multi.restype = i32
+    L.mqa_decode_attn_paged_multi.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                              i32, i32, i32, ctypes.c_float, vp, vp,
+                                              ctypes.c_size_t, i32, vp, vp]
+    L.mqa_decode_attn_paged_multi.restype = i32
     return L
 
 
@@ -310,4 +336,136 @@ def decode_attn_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Ten
                                      _ptr(err_flags), _stream(q.device))
     if st != OK:
         raise MQAError(st, "mqa_decode_attn_paged")
+    return out
+
+
+# ---- several query tokens per sequence (q [b, T, h, d], causal) ----
+
+def decode_multi_workspace_bytes(b, T, h, g, S, d, dtype, split_chunk: int = 0) -> int:
+    """Workspace bytes of a T-token decode (S: capacity, page_size * max_pages when paged)."""
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(lib().mqa_decode_multi_workspace_bytes(b, T, h, g, S, d, code, split_chunk))
+
+
+def decode_multi_schedule(b, T, h, g, S, d, dtype, split_chunk: int = 0) -> str:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    v = int(lib().mqa_decode_multi_schedule(b, T, h, g, S, d, code, split_chunk))
+    if v < 0:
+        raise ValueError("invalid arguments")
+    return SCHEDULES[v]
+
+
+def append_kv_multi(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+                    v_new: torch.Tensor, seq_lens: torch.Tensor,
+                    err_flags: torch.Tensor | None = None) -> None:
+    """Token tau of k_new/v_new [b, T, g, d] -> cache position seq_lens[i] - T + tau."""
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new), ("v_new", v_new),
+                 ("seq_lens", seq_lens)):
+        _dev(t, n)
+    b, g, S, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or k_new.dim() != 4 or k_new.shape[0] != b \
+            or k_new.shape[2:] != (g, d) or v_new.shape != k_new.shape:
+        raise ValueError("caches [b, g, S, d] and new rows [b, T, g, d] must match")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (b,):
+        raise ValueError("seq_lens must be int32 [b]")
+    if not (k_cache.dtype == v_cache.dtype == k_new.dtype == v_new.dtype):
+        raise TypeError("caches and new rows must share one dtype")
+    st = lib().mqa_append_kv_multi(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+                                   _ptr(seq_lens), b, k_new.shape[1], g, S, d,
+                                   _dtype_code(k_cache.dtype), _ptr(err_flags),
+                                   _stream(k_cache.device))
+    if st != OK:
+        raise MQAError(st, "mqa_append_kv_multi")
+
+
+def _multi_out(q, out, workspace, nbytes):
+    b, T, h, d = q.shape
+    if out is None:
+        out = torch.empty((b, T, h, d), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or out.shape != (b, T, h, d):
+        raise ValueError("out must be float32 [b, T, h, d]")
+    _dev(out, "out")
+    if workspace is None:
+        if nbytes == 0:
+            raise ValueError("invalid sizes")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    return out, workspace
+
+
+def decode_attn_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      seq_lens: torch.Tensor, scale: float | None = None,
+                      out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                      split_chunk: int = 0, err_flags: torch.Tensor | None = None) -> torch.Tensor:
+    """T query tokens per sequence with the causal mask -> out fp32 [b, T, h, d]."""
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
+        _dev(t, n)
+    b, g, S, d = k_cache.shape
+    if q.dim() != 4 or q.shape[0] != b or q.shape[3] != d or v_cache.shape != k_cache.shape:
+        raise ValueError("q [b, T, h, d] and caches [b, g, S, d] must match")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (b,):
+        raise ValueError("seq_lens must be int32 [b]")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q and the caches must share one dtype")
+    T, h = q.shape[1], q.shape[2]
+    code = _dtype_code(q.dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, workspace = _multi_out(q, out, workspace,
+                                decode_multi_workspace_bytes(b, T, h, g, S, d, code, split_chunk))
+    st = lib().mqa_decode_attn_multi(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), b, T,
+                                     h, g, S, d, code, ctypes.c_float(scale), _ptr(out),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     split_chunk, _ptr(err_flags), _stream(q.device))
+    if st != OK:
+        raise MQAError(st, "mqa_decode_attn_multi")
+    return out
+
+
+def append_kv_paged_multi(k_pages: torch.Tensor, v_pages: torch.Tensor, k_new: torch.Tensor,
+                          v_new: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                          err_flags: torch.Tensor | None = None) -> None:
+    """append_kv_multi into a paged cache."""
+    (num_pages, g, P, d), b, max_pages = _check_pages(k_pages, v_pages, block_table, seq_lens)
+    for n, t in (("k_new", k_new), ("v_new", v_new)):
+        _dev(t, n)
+    if k_new.dim() != 4 or k_new.shape[0] != b or k_new.shape[2:] != (g, d) \
+            or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [b, T, g, d]")
+    if not (k_pages.dtype == v_pages.dtype == k_new.dtype == v_new.dtype):
+        raise TypeError("pages and new rows must share one dtype")
+    st = lib().mqa_append_kv_paged_multi(_ptr(k_pages), _ptr(v_pages), _ptr(k_new), _ptr(v_new),
+                                         _ptr(block_table), _ptr(seq_lens), b, k_new.shape[1], g,
+                                         P, max_pages, num_pages, d, _dtype_code(k_pages.dtype),
+                                         _ptr(err_flags), _stream(k_pages.device))
+    if st != OK:
+        raise MQAError(st, "mqa_append_kv_paged_multi")
+
+
+def decode_attn_paged_multi(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                            block_table: torch.Tensor, seq_lens: torch.Tensor,
+                            scale: float | None = None, out: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None, split_chunk: int = 0,
+                            err_flags: torch.Tensor | None = None) -> torch.Tensor:
+    """decode_attn_multi over a paged cache -> out fp32 [b, T, h, d]."""
+    (num_pages, g, P, d), b, max_pages = _check_pages(k_pages, v_pages, block_table, seq_lens)
+    _dev(q, "q")
+    if q.dim() != 4 or q.shape[0] != b or q.shape[3] != d:
+        raise ValueError("q must be [b, T, h, d] matching the pages and the block table")
+    if not (q.dtype == k_pages.dtype == v_pages.dtype):
+        raise TypeError("q and the pages must share one dtype")
+    T, h = q.shape[1], q.shape[2]
+    code = _dtype_code(q.dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, workspace = _multi_out(q, out, workspace,
+                                decode_multi_workspace_bytes(b, T, h, g, P * max_pages, d, code,
+                                                             split_chunk))
+    st = lib().mqa_decode_attn_paged_multi(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                           _ptr(seq_lens), b, T, h, g, P, max_pages, num_pages, d,
+                                           code, ctypes.c_float(scale), _ptr(out), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           split_chunk, _ptr(err_flags), _stream(q.device))
+    if st != OK:
+        raise MQAError(st, "mqa_decode_attn_paged_multi")
     return out

@@ -135,63 +135,77 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // append
 // ---------------------------------------------------------------------------
 
-// Thread t copies one 16-byte chunk: t -> (tensor K/V, sequence i, head j, chunk c).
+// Where thread t of an append works: one 16-byte chunk c of token tau of
+// K/V head j of sequence i, in tensor `which` (0: K, 1: V).
+struct AppendSlot {
+    int c, j, tau, i, which;
+    __device__ AppendSlot(long long t, int cpr, int b, int T, int g) {
+        c = (int)(t % cpr);
+        t /= cpr;
+        j = (int)(t % g);
+        t /= g;
+        tau = (int)(t % T);
+        t /= T;
+        i = (int)(t % b);
+        which = (int)(t / b);
+    }
+    __device__ bool first() const { return c == 0 && j == 0 && tau == 0 && which == 0; }
+};
+
+// Token tau of the step's T (k_new/v_new [b][T][g][d]) goes to position
+// L - T + tau of its K/V head ([MQA blog] §2.2; [GQA notes] §八 writes the T
+// rows at once); lengths outside [T, S] are skipped and flagged.
 __global__ void append_kv_kernel(uint8_t *__restrict__ kc, uint8_t *__restrict__ vc,
                                  const uint8_t *__restrict__ kn, const uint8_t *__restrict__ vn,
-                                 const int32_t *__restrict__ seq_lens, int b, int g, int S,
+                                 const int32_t *__restrict__ seq_lens, int b, int T, int g, int S,
                                  int row_bytes, int32_t *__restrict__ err) {
     const int cpr = row_bytes >> 4;
-    const long long total = 2ll * b * g * cpr;
+    const long long total = 2ll * b * T * g * cpr;
     const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= total) return;
-    const int c = (int)(t % cpr);
-    const long long ij = (t / cpr) % ((long long)b * g);
-    const int which = (int)(t / ((long long)cpr * b * g));
-    const int i = (int)(ij / g);
-    const int L = seq_lens[i];
-    if (L < 1 || L > S) {
-        if (c == 0 && which == 0 && (ij % g) == 0 && err) atomicOr(err, MQA_DEVERR_SEQLEN);
+    const AppendSlot a(t, cpr, b, T, g);
+    const int L = seq_lens[a.i];
+    if (L < T || L > S) {
+        if (a.first() && err) atomicOr(err, MQA_DEVERR_SEQLEN);
         return;
     }
-    const size_t src = (size_t)ij * row_bytes + (size_t)c * 16;
-    const size_t dst = ((size_t)ij * S + (size_t)(L - 1)) * row_bytes + (size_t)c * 16;
-    const uint8_t *s = which ? vn : kn;
-    uint8_t *dp = which ? vc : kc;
+    const size_t src = (((size_t)a.i * T + a.tau) * g + a.j) * row_bytes + (size_t)a.c * 16;
+    const size_t dst = (((size_t)a.i * g + a.j) * S + (size_t)(L - T + a.tau)) * row_bytes +
+                       (size_t)a.c * 16;
+    const uint8_t *s = a.which ? vn : kn;
+    uint8_t *dp = a.which ? vc : kc;
     *(uint4 *)(dp + dst) = *(const uint4 *)(s + src);
 }
 
-// Paged cache: the row goes to row (L-1) % P of page block_table[i][(L-1) / P]
-// of pages [num_pages][g][P][d]. A page id outside [0, num_pages) is skipped
-// and flagged.
+// Paged cache: position p = L - T + tau goes to row p % P of page
+// block_table[i][p / P] of pages [num_pages][g][P][d]. A page id outside
+// [0, num_pages) is skipped and flagged.
 __global__ void append_kv_paged_kernel(uint8_t *__restrict__ kp, uint8_t *__restrict__ vp,
                                        const uint8_t *__restrict__ kn, const uint8_t *__restrict__ vn,
                                        const int32_t *__restrict__ block_table,
-                                       const int32_t *__restrict__ seq_lens, int b, int g, int P,
-                                       int max_pages, int num_pages, int row_bytes,
+                                       const int32_t *__restrict__ seq_lens, int b, int T, int g,
+                                       int P, int max_pages, int num_pages, int row_bytes,
                                        int32_t *__restrict__ err) {
     const int cpr = row_bytes >> 4;
-    const long long total = 2ll * b * g * cpr;
+    const long long total = 2ll * b * T * g * cpr;
     const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= total) return;
-    const int c = (int)(t % cpr);
-    const long long ij = (t / cpr) % ((long long)b * g);
-    const int which = (int)(t / ((long long)cpr * b * g));
-    const int i = (int)(ij / g), j = (int)(ij % g);
-    const bool first = c == 0 && which == 0 && j == 0;
-    const int L = seq_lens[i];
-    if (L < 1 || L > P * max_pages) {
-        if (first && err) atomicOr(err, MQA_DEVERR_SEQLEN);
+    const AppendSlot a(t, cpr, b, T, g);
+    const int L = seq_lens[a.i];
+    if (L < T || L > P * max_pages) {
+        if (a.first() && err) atomicOr(err, MQA_DEVERR_SEQLEN);
         return;
     }
-    const int page = block_table[(size_t)i * max_pages + (L - 1) / P];
+    const int pos = L - T + a.tau;
+    const int page = block_table[(size_t)a.i * max_pages + pos / P];
     if (page < 0 || page >= num_pages) {
-        if (first && err) atomicOr(err, MQA_DEVERR_PAGE);
+        if (a.c == 0 && a.j == 0 && a.which == 0 && err) atomicOr(err, MQA_DEVERR_PAGE);
         return;
     }
-    const size_t src = (size_t)ij * row_bytes + (size_t)c * 16;
-    const size_t dst = (((size_t)page * g + j) * P + (size_t)((L - 1) % P)) * row_bytes + (size_t)c * 16;
-    const uint8_t *s = which ? vn : kn;
-    uint8_t *dp = which ? vp : kp;
+    const size_t src = (((size_t)a.i * T + a.tau) * g + a.j) * row_bytes + (size_t)a.c * 16;
+    const size_t dst = (((size_t)page * g + a.j) * P + (size_t)(pos % P)) * row_bytes + (size_t)a.c * 16;
+    const uint8_t *s = a.which ? vn : kn;
+    uint8_t *dp = a.which ? vp : kp;
     *(uint4 *)(dp + dst) = *(const uint4 *)(s + src);
 }
 
@@ -723,40 +737,53 @@ __device__ __forceinline__ void load_step(const StepSrc &src, int lane, StepData
 
 // A step that read an invalid page: its unit's results become NaN (the state's
 // sum is NaN, which every merge carries) and the error flag is raised.
-template <int D>
-__device__ __forceinline__ void poison_state(MfmaState<D> &st, int32_t *err, int lane) {
-    st.l_lane = __builtin_nanf("");
+template <int D, int NHB>
+__device__ __forceinline__ void poison_state(MfmaState<D> (&st)[NHB], int32_t *err, int lane) {
+#pragma unroll
+    for (int hb = 0; hb < NHB; hb++) st[hb].l_lane = __builtin_nanf("");
     if (err && lane == 0) atomicOr(err, MQA_DEVERR_PAGE);
 }
 
 // One 32-position step [t0, t0+32) of one wave from loaded data, rows >=
-// t_end masked; vb is the wave's staging buffer.
-template <int D>
-__device__ __forceinline__ void compute_step(const StepData<D> &sd, int t0, int t_end,
-                                             const bf16x8_t (&qop)[MfmaCfg<D>::KSTEPS],
-                                             MfmaState<D> &st, uint8_t *vb, int lane,
+// t_end masked; vb is the wave's staging buffer. The wave computes NHB blocks
+// of 16 query rows against the same K and V registers (block b: its q
+// operand qop[b] and state st[b]), so the K/V bytes are loaded once for all
+// of them. MULTI (several query tokens per sequence): query row r of block b
+// also stops at its own t_row[b] (its token's causal end, per lane, <=
+// t_end); t_lo is the smallest t_row of the wave. A row can then have no
+// position in a step, so exponentials of masked scores are set to 0 (not
+// exp2(-inf - -inf)).
+template <int D, bool MULTI, int NHB>
+__device__ __forceinline__ void compute_step(const StepData<D> &sd, int t0, int t_end, int t_lo,
+                                             const int (&t_row)[NHB],
+                                             const bf16x8_t (&qop)[NHB][MfmaCfg<D>::KSTEPS],
+                                             MfmaState<D> (&st)[NHB], uint8_t *vb, int lane,
                                              float qk_scale_log2) {
     using C = MfmaCfg<D>;
     const int r = lane & 15, qd = lane >> 4;
     const int vl_row = lane / C::CPR, vl_chunk = lane % C::CPR;
-    const bool tail = t0 + C::STEP > t_end;
+    const bool tail = t0 + C::STEP > (MULTI ? t_lo : t_end);
     const auto &kop = sd.kop;
     const auto &vld = sd.vld;
 
     // ---- scores ----
-    f32x4_t sc[2];
+    float s2[NHB][8];
 #pragma unroll
-    for (int pb = 0; pb < 2; pb++) {
-        sc[pb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int hb = 0; hb < NHB; hb++) {
+        f32x4_t sc[2];
 #pragma unroll
-        for (int k = 0; k < C::KSTEPS; k++)
-            sc[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[pb][k], qop[k], sc[pb], 0, 0, 0);
-    }
-    float s2[8];
+        for (int pb = 0; pb < 2; pb++) {
+            sc[pb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-        s2[e] = sc[e >> 2][e & 3] * qk_scale_log2;
-        if (tail && t0 + kslot(qd, e) >= t_end) s2[e] = -INFINITY;
+            for (int k = 0; k < C::KSTEPS; k++)
+                sc[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[pb][k], qop[hb][k], sc[pb], 0,
+                                                                 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            s2[hb][e] = sc[e >> 2][e & 3] * qk_scale_log2;
+            if (tail && t0 + kslot(qd, e) >= (MULTI ? t_row[hb] : t_end)) s2[hb][e] = -INFINITY;
+        }
     }
 
     // ---- V into the staging buffer (rows past the end zeroed: they may be NaN) ----
@@ -767,43 +794,50 @@ __device__ __forceinline__ void compute_step(const StepData<D> &sd, int t0, int 
         *(u32x4_t *)(vb + (ii * C::RPI + vl_row) * C::VSTRIDE + 16 * vl_chunk) = v;
     }
 
-    // ---- online softmax for head r ----
-    float smax = s2[0];
+    // ---- online softmax for head r of each block ----
+    bf16x8_t phi[NHB], plo[NHB];
 #pragma unroll
-    for (int e = 1; e < 8; e++) smax = fmaxf(smax, s2[e]);
-    if (__any(smax > st.m_ref + kSlack)) {  // wave-uniform
-        // (shuffle addresses built here, not kept live across the whole loop)
-        const int ln = opaque_lane(lane);
-        float mt = fmaxf(smax, shfl_from(smax, ln ^ 16));
-        mt = fmaxf(mt, shfl_from(mt, ln ^ 32));   // max over the head's 32 positions
-        mt = fmaxf(mt, st.m_ref);
-        const float alpha = fast_exp2(st.m_ref - mt);  // per head r
-        st.m_ref = mt;
-        st.l_lane *= alpha;
-        // acc rows are heads 4qd+v: fetch their factors from lanes 4qd+v
+    for (int hb = 0; hb < NHB; hb++) {
+        MfmaState<D> &sb = st[hb];
+        float smax = s2[hb][0];
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-            const float av = shfl_from(alpha, 4 * (ln >> 4) + v);
+        for (int e = 1; e < 8; e++) smax = fmaxf(smax, s2[hb][e]);
+        if (__any(smax > sb.m_ref + kSlack)) {  // wave-uniform
+            // (shuffle addresses built here, not kept live across the whole loop)
+            const int ln = opaque_lane(lane);
+            float mt = fmaxf(smax, shfl_from(smax, ln ^ 16));
+            mt = fmaxf(mt, shfl_from(mt, ln ^ 32));   // max over the head's 32 positions
+            mt = fmaxf(mt, sb.m_ref);
+            // per head r (several tokens: a row that has seen no position yet
+            // keeps its empty state; exp2(-inf - -inf) would be NaN)
+            const float alpha = (MULTI && mt == -INFINITY) ? 1.f : fast_exp2(sb.m_ref - mt);
+            sb.m_ref = mt;
+            sb.l_lane *= alpha;
+            // acc rows are heads 4qd+v: fetch their factors from lanes 4qd+v
 #pragma unroll
-            for (int nb = 0; nb < C::NB; nb++) st.acc[nb][v] *= av;
+            for (int v = 0; v < 4; v++) {
+                const float av = shfl_from(alpha, 4 * (ln >> 4) + v);
+#pragma unroll
+                for (int nb = 0; nb < C::NB; nb++) sb.acc[nb][v] *= av;
+            }
+        }
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            p[e] = fast_exp2(s2[hb][e] - sb.m_ref);
+            if constexpr (MULTI) p[e] = s2[hb][e] == -INFINITY ? 0.f : p[e];
+            sb.l_lane += p[e];
+        }
+        // P as bf16 hi + lo parts, A operand of the P.V MFMA
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const __bf16 hi = (__bf16)p[e];
+            phi[hb][e] = hi;
+            plo[hb][e] = (__bf16)(p[e] - (float)hi);
         }
     }
-    float p[8];
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-        p[e] = fast_exp2(s2[e] - st.m_ref);
-        st.l_lane += p[e];
-    }
-    // P as bf16 hi + lo parts, A operand of the P.V MFMA
-    bf16x8_t phi, plo;
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-        const __bf16 hi = (__bf16)p[e];
-        phi[e] = hi;
-        plo[e] = (__bf16)(p[e] - (float)hi);
-    }
 
-    // ---- P.V ----
+    // ---- P.V (one V operand for every block) ----
     const uint16_t *vt = (const uint16_t *)(vb + 4 * qd * C::VSTRIDE + 2 * r);
 #pragma unroll
     for (int nb = 0; nb < C::NB; nb++) {
@@ -811,20 +845,42 @@ __device__ __forceinline__ void compute_step(const StepData<D> &sd, int t0, int 
 #pragma unroll
         for (int e = 0; e < 8; e++)
             vop[e] = __builtin_bit_cast(__bf16, vt[(kslot(0, e) * C::VSTRIDE + 32 * nb) / 2]);
-        st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vop, st.acc[nb], 0, 0, 0);
-        st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vop, st.acc[nb], 0, 0, 0);
+#pragma unroll
+        for (int hb = 0; hb < NHB; hb++) {
+            st[hb].acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[hb], vop, st[hb].acc[nb], 0, 0, 0);
+            st[hb].acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[hb], vop, st[hb].acc[nb], 0, 0, 0);
+        }
     }
 }
+
+// Query rows of a unit (sequence i, K/V head j). With T query tokens per
+// sequence (MULTI) a unit has R = T * Gh rows, row rho = tau * Gh + head,
+// q and out are [b][T][h][d], and token tau (position L - T + tau) sees the
+// positions t <= L - T + tau: the causal mask stays per query position when
+// K/V heads are shared ([GQA notes] §十 item 10). Otherwise R = Gh and every
+// row sees t < L.
+template <bool MULTI>
+struct QRows {
+    int T, Gh, h;
+    __device__ __forceinline__ int tok(int rho) const { return MULTI ? rho / Gh : 0; }
+    __device__ __forceinline__ size_t row(int i, int j, int rho) const {
+        if constexpr (MULTI)
+            return ((size_t)i * T + rho / Gh) * h + (size_t)j * Gh + rho % Gh;
+        else
+            return (size_t)i * h + (size_t)j * Gh + rho;
+    }
+};
 
 // Steps s_begin, s_begin+stride, ... < s_end (src(step, bad) gives where a
 // step's rows are), with the loads of the next step in flight while this
 // one computes (two register sets, alternating). Past the last step the
 // prefetch asks for nothing.
-template <int D, class Src>
+template <int D, bool MULTI, int NHB, class Src>
 __device__ __forceinline__ void run_steps(const Src &src, const StepSrc &nothing, int s_begin,
-                                          int s_end, int stride, int t_end,
-                                          const bf16x8_t (&qop)[MfmaCfg<D>::KSTEPS],
-                                          MfmaState<D> &st, uint8_t *vb, int lane,
+                                          int s_end, int stride, int t_end, int t_lo,
+                                          const int (&t_row)[NHB],
+                                          const bf16x8_t (&qop)[NHB][MfmaCfg<D>::KSTEPS],
+                                          MfmaState<D> (&st)[NHB], uint8_t *vb, int lane,
                                           float qk_scale_log2, int32_t *err) {
     using C = MfmaCfg<D>;
     int stp = s_begin;
@@ -839,14 +895,16 @@ __device__ __forceinline__ void run_steps(const Src &src, const StepSrc &nothing
     while (true) {
         int nx = stp + stride;
         prefetch(nx, b);
-        compute_step<D>(a, stp * C::STEP, t_end, qop, st, vb, lane, qk_scale_log2);
+        compute_step<D, MULTI, NHB>(a, stp * C::STEP, t_end, t_lo, t_row, qop, st, vb, lane,
+                                    qk_scale_log2);
         if (bad) poison_state<D>(st, err, lane);
         bad = bad_n;
         if (nx >= s_end) break;
         stp = nx;
         nx = stp + stride;
         prefetch(nx, a);
-        compute_step<D>(b, stp * C::STEP, t_end, qop, st, vb, lane, qk_scale_log2);
+        compute_step<D, MULTI, NHB>(b, stp * C::STEP, t_end, t_lo, t_row, qop, st, vb, lane,
+                                    qk_scale_log2);
         if (bad) poison_state<D>(st, err, lane);
         bad = bad_n;
         if (nx >= s_end) break;
@@ -892,24 +950,24 @@ __device__ __forceinline__ float merge_waves(const float *mrg, const float *mls,
 }
 
 // Fixed partitions: one work-group per (partition of split_chunk positions,
-// K/V head, block of 16 query heads, sequence); writes partials for the
-// log-sum-exp combine.
-template <int D, class KV>
+// K/V head, group of NHB blocks of 16 query rows, sequence); writes partials
+// for the log-sum-exp combine (partial row (i*g + j)*R + rho).
+template <int D, class KV, bool MULTI, int NHB>
 __global__ void __launch_bounds__(256)
 split_mfma_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__restrict__ seq_lens,
-                  int h, int g, int S, int G, int nhb, int chunk, int nsplit, float qk_scale_log2,
-                  float *__restrict__ part_o, float2 *__restrict__ part_ml,
+                  const QRows<MULTI> qr, int g, int S, int R, int ngroups, int chunk, int nsplit,
+                  float qk_scale_log2, float *__restrict__ part_o, float2 *__restrict__ part_ml,
                   int32_t *__restrict__ err) {
     using C = MfmaCfg<D>;
     __shared__ __attribute__((aligned(16))) uint8_t vbuf[C::NW][C::VBUF];
     __shared__ int pg[KV::kStage];  // paged: the page ids of the partition's steps
 
     const int s = blockIdx.x;
-    const int j = blockIdx.y / nhb;
-    const int hb = blockIdx.y % nhb;
+    const int j = blockIdx.y / ngroups;
+    const int hg = blockIdx.y % ngroups;  // blocks hg*NHB .. hg*NHB+NHB-1
     const int i = blockIdx.z;
     const int L = seq_lens[i];
-    if (L < 1 || L > S) return;  // reported by the combine
+    if (L < qr.T || L > S) return;  // reported by the combine
     const int t_begin = s * chunk;
     if (t_begin >= L) return;
     const int t_end = min(t_begin + chunk, L);
@@ -919,9 +977,16 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, qd = lane >> 4;
 
-    // padded heads reuse the last real one and are never written out
-    bf16x8_t qop[C::KSTEPS];
-    load_q_operand<D>(q, (size_t)i * h + j * G + min(hb * C::HB + r, G - 1), qd, qop);
+    // padded rows reuse the last real one and are never written out
+    bf16x8_t qop[NHB][C::KSTEPS];
+    int t_row[NHB];  // causal ends (several tokens): this lane's row in each block
+#pragma unroll
+    for (int b = 0; b < NHB; b++) {
+        const int rho = min((hg * NHB + b) * C::HB + r, R - 1);
+        load_q_operand<D>(q, qr.row(i, j, rho), qd, qop[b]);
+        t_row[b] = min(t_end, L - qr.T + 1 + qr.tok(rho));
+    }
+    const int t_lo = min(t_end, L - qr.T + 1);  // the earliest of the wave
 
     // steps of this partition, numbered from the sequence start
     const int s0 = t_begin / C::STEP;
@@ -953,24 +1018,30 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
         }
     };
 
-    MfmaState<D> st;
-    st.reset();
-    run_steps<D>(src, kv.none(), s0 + w, s0 + nsteps, C::NW, t_end, qop, st, vbuf[w], lane,
-                 qk_scale_log2, err);
+    MfmaState<D> st[NHB];
+#pragma unroll
+    for (int b = 0; b < NHB; b++) st[b].reset();
+    run_steps<D, MULTI, NHB>(src, kv.none(), s0 + w, s0 + nsteps, C::NW, t_end, t_lo, t_row, qop,
+                             st, vbuf[w], lane, qk_scale_log2, err);
 
-    __syncthreads();  // every wave is done with its staging buffer
+    // merge the waves' states block by block through the staging buffers
     float *mrg = (float *)&vbuf[0][0];
     float *mls = mrg + C::NW * C::HB * D;
-    publish_state<D>(st, mrg, mls, w, lane);
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < C::HB * D; idx += 64 * C::NW) {
-        const int hh = idx / D, x = idx % D;
-        if (hb * C::HB + hh >= G) continue;
-        float M, l;
-        const float o = merge_waves<D>(mrg, mls, 0, C::NW, hh, x, M, l);
-        const size_t hrow = (size_t)i * h + j * G + hb * C::HB + hh;
-        part_o[(hrow * nsplit + s) * D + x] = o;
-        if (x == 0) part_ml[hrow * nsplit + s] = make_float2(M, l);
+#pragma unroll
+    for (int b = 0; b < NHB; b++) {
+        const int hb = hg * NHB + b;
+        __syncthreads();  // every wave is done with the buffers
+        publish_state<D>(st[b], mrg, mls, w, lane);
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < C::HB * D; idx += 64 * C::NW) {
+            const int hh = idx / D, x = idx % D;
+            if (hb * C::HB + hh >= R) continue;
+            float M, l;
+            const float o = merge_waves<D>(mrg, mls, 0, C::NW, hh, x, M, l);
+            const size_t hrow = ((size_t)i * g + j) * R + hb * C::HB + hh;
+            part_o[(hrow * nsplit + s) * D + x] = o;
+            if (x == 0) part_ml[hrow * nsplit + s] = make_float2(M, l);
+        }
     }
 }
 
@@ -1000,8 +1071,11 @@ constexpr int kStreamMinSteps = 16;    // steps per work-group range, at least
 constexpr int kStreamWaves = 4;        // waves per work-group (one work-group per compute unit)
 constexpr int kRing = 16;              // segment records per head block
 
-// steps of sequence i (0 for an invalid length)
-__device__ __forceinline__ int seq_steps(int L, int S) { return (L < 1 || L > S) ? 0 : (L + 31) / 32; }
+// steps of sequence i (0 for an invalid length: below the T tokens of the
+// step, or past the capacity)
+__device__ __forceinline__ int seq_steps(int L, int S, int T) {
+    return (L < T || L > S) ? 0 : (L + 31) / 32;
+}
 
 // Exclusive prefixes over sequences, whole work-group (NT threads): steps
 // of units, pre[0..b] (units_per_seq units per valid sequence), and valid
@@ -1010,8 +1084,8 @@ __device__ __forceinline__ int seq_steps(int L, int S) { return (L < 1 || L > S)
 // host keeps the step total below 2^31.
 template <int NT>
 __device__ __forceinline__ void unit_prefix(const int32_t *__restrict__ seq_lens, int b, int S,
-                                            int units_per_seq, int *pre, int *vpre, int *lens,
-                                            int2 *wtot) {
+                                            int T, int units_per_seq, int *pre, int *vpre,
+                                            int *lens, int2 *wtot) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int per = (b + NT - 1) / NT;
     const int a0 = min(b, t * per), a1 = min(b, a0 + per);
@@ -1019,7 +1093,7 @@ __device__ __forceinline__ void unit_prefix(const int32_t *__restrict__ seq_lens
     for (int a = a0; a < a1; a++) {
         const int L = seq_lens[a];
         lens[a] = L;  // kept in LDS for the rest of the kernel
-        const int n = seq_steps(L, S);
+        const int n = seq_steps(L, S, T);
         run += n;
         vrun += n > 0;
     }
@@ -1041,7 +1115,7 @@ __device__ __forceinline__ void unit_prefix(const int32_t *__restrict__ seq_lens
     }
     acc *= units_per_seq;
     for (int a = a0; a < a1; a++) {
-        const int n = seq_steps(lens[a], S);
+        const int n = seq_steps(lens[a], S, T);
         pre[a] = acc;
         vpre[a] = vacc;
         acc += n * units_per_seq;
@@ -1095,23 +1169,24 @@ __device__ __forceinline__ void lds_flag_wait(int *f, int v) {
 // each is on a segment that ends earlier in the range, so they cannot form a
 // cycle. Which wave computes which step depends on timing, so the rounding
 // of the sums can differ between calls.
-template <int D, int NW, class KV>
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV::kPaged ? 1 : 2, 8)))
+template <int D, int NW, class KV, bool MULTI, int NHB>
+__global__ void __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu((KV::kPaged || NHB > 1) ? 1 : 2, 8)))
 streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
-                    const int32_t *__restrict__ seq_lens, int b,
-                    int h, int g, int S, int G, int nhb, float qk_scale_log2,
+                    const int32_t *__restrict__ seq_lens, int b, const QRows<MULTI> qr,
+                    int g, int S, int R, int ngroups, float qk_scale_log2,
                     float *__restrict__ out, float *__restrict__ part_o,
                     float2 *__restrict__ part_ml, int4 *__restrict__ cut_desc,
                     int32_t *__restrict__ err) {
     using C = MfmaCfg<D>;
     static_assert(NW == 4 || NW == 8, "waves per work-group (the segment records hold 8 bits)");
     __shared__ __attribute__((aligned(16))) uint8_t vbuf[NW][C::VBUF];
-    __shared__ f32x4_t slot_o[NW][C::NB][64];  // a wave's acc, lane-native order
-    __shared__ float2 slot_ml[NW][C::HB];      // (m, l) per head
+    __shared__ f32x4_t slot_o[NW][NHB][C::NB][64];  // a wave's acc, lane-native order
+    __shared__ float2 slot_ml[NW][NHB][C::HB];      // (m, l) per head
     __shared__ int slot_busy[NW];              // 1 while the slot holds a state not merged yet
     __shared__ int rec_tag[4][kRing];          // ordinal of the segment the record serves now
     __shared__ uint32_t rec_val[4][kRing];     // (steps done << 8) | waves (bit per wave of the block)
-    __shared__ int cursor[4];                  // steps of the range claimed so far, per head block
+    __shared__ int cursor[4];                  // steps of the range claimed so far, per head group
     __shared__ int first_seq, last_seq;        // sequences holding the range's first and last steps
     __shared__ int pre[kStreamMaxSeq + 1];     // steps before sequence i
     __shared__ int vpre[kStreamMaxSeq + 1];    // valid sequences before sequence i
@@ -1121,7 +1196,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
 
     if (threadIdx.x < NW) slot_busy[threadIdx.x] = 0;
     if (threadIdx.x < 4) cursor[threadIdx.x] = 0;
-    unit_prefix<64 * NW>(seq_lens, b, S, g, pre, vpre, lens, wtot);  // its barriers publish the above
+    unit_prefix<64 * NW>(seq_lens, b, S, qr.T, g, pre, vpre, lens, wtot);  // its barriers publish the above
     // everything that steers the loops below is wave-uniform: keep it scalar
     const int T = __builtin_amdgcn_readfirstlane(pre[b]);
     const int wg = blockIdx.x;
@@ -1130,9 +1205,10 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
     // sequences with a length out of range: NaN rows and the error flag
     // (work-group 0, one thread per sequence; such rows are rare)
     if (wg == 0) {
+        const int n_row = qr.T * qr.h * D;  // out of one sequence: [T][h][d]
         for (int i = threadIdx.x; i < b; i += 64 * NW) {
             if (pre[i + 1] != pre[i]) continue;
-            for (int idx = 0; idx < h * D; idx++) out[(size_t)i * h * D + idx] = __builtin_nanf("");
+            for (int idx = 0; idx < n_row; idx++) out[(size_t)i * n_row + idx] = __builtin_nanf("");
             if (err) atomicOr(err, MQA_DEVERR_SEQLEN);
         }
     }
@@ -1158,7 +1234,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
             }
             i_ = lo;
             L_ = lens[lo];
-            row = (tt - pre[lo]) % seq_steps(L_, S) * C::STEP + 16 * (e & 1);
+            row = (tt - pre[lo]) % seq_steps(L_, S, qr.T) * C::STEP + 16 * (e & 1);
         });
 
     // The range's last segment [xl, x1) is claimed first, then [x0, xl): a
@@ -1182,8 +1258,8 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
     const int i_last = __builtin_amdgcn_readfirstlane(last_seq);
     const int ord0 = __builtin_amdgcn_readfirstlane(vpre[i_first]) * g +
                      (x0 - __builtin_amdgcn_readfirstlane(pre[i_first])) /
-                         seq_steps(__builtin_amdgcn_readfirstlane(lens[i_first]), S);
-    const int n_last = seq_steps(__builtin_amdgcn_readfirstlane(lens[i_last]), S);
+                         seq_steps(__builtin_amdgcn_readfirstlane(lens[i_first]), S, qr.T);
+    const int n_last = seq_steps(__builtin_amdgcn_readfirstlane(lens[i_last]), S, qr.T);
     const int p_last = __builtin_amdgcn_readfirstlane(pre[i_last]);
     const int u0_last = p_last + (x1 - 1 - p_last) / n_last * n_last;  // the last unit's first step
     const int xl = max(x0, u0_last);
@@ -1200,9 +1276,17 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, qd = lane >> 4;
-    const int wph = NW / nhb;  // waves per head block
+    // The unit's query rows are cut into blocks of 16 and the blocks into
+    // ngroups groups of NHB; a wave computes all blocks of its group against
+    // each step it loads, and the waves of a group share the range's steps.
+    const int wph = NW / ngroups;  // waves per head group
     const int hb = w / wph, wb = w % wph;
-    const int HBT = nhb * C::HB;  // head slots per unit
+    const int HBT = (R + C::HB - 1) / C::HB * C::HB;  // head slots per unit
+    // this lane's query row in each block (padded rows reuse the last real
+    // one and are never written out) and its token
+    int tau[NHB];
+#pragma unroll
+    for (int k = 0; k < NHB; k++) tau[k] = qr.tok(min((hb * NHB + k) * C::HB + r, R - 1));
 
     // next step of the range for this head block, in claim order (x1: none left)
     auto claim = [&]() __attribute__((always_inline)) {
@@ -1220,14 +1304,15 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
         if (tt < u0_) i_ = i_first;
         while (__builtin_amdgcn_readfirstlane(pre[i_ + 1]) <= tt) i_++;
         L_ = __builtin_amdgcn_readfirstlane(lens[i_]);
-        n_ = seq_steps(L_, S);
+        n_ = seq_steps(L_, S, qr.T);
         const int p = __builtin_amdgcn_readfirstlane(pre[i_]);
         j_ = (tt - p) / n_;
         u0_ = p + j_ * n_;
     };
-    // padded heads reuse the last real one and are never written out
-    auto q_row = [&](int i_, int j_) __attribute__((always_inline)) {
-        return (size_t)i_ * h + j_ * G + min(hb * C::HB + r, G - 1);
+    auto load_q = [&](int i_, int j_, bf16x8_t (&qo)[NHB][C::KSTEPS]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < NHB; k++)
+            load_q_operand<D>(q, qr.row(i_, j_, min((hb * NHB + k) * C::HB + r, R - 1)), qd, qo[k]);
     };
     // where the rows of flat step tt (of unit (i_, j_), first step u0_) are
     auto src_of = [&](int i_, int j_, int L_, int u0_, int tt, bool &bad)
@@ -1257,10 +1342,11 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
     bool bad_now = false;  // the current step read an invalid page
     StepData<D> A, B;
     load_step<D>(src_of(ci, cj, cL, cu0, t, bad_now), lane, A);
-    bf16x8_t qop[C::KSTEPS];
-    load_q_operand<D>(q, q_row(ci, cj), qd, qop);
-    MfmaState<D> st;
-    st.reset();
+    bf16x8_t qop[NHB][C::KSTEPS];
+    load_q(ci, cj, qop);
+    MfmaState<D> st[NHB];
+#pragma unroll
+    for (int k = 0; k < NHB; k++) st[k].reset();
     int mine = 0;  // steps of the current unit in this wave's state
 
     // this wave is done with the segment (range ∩ unit (ci, cj))
@@ -1270,14 +1356,17 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
         const int seg_s = max(x0, cu0), seg_e = min(x1, cu0 + cn);
         const int sn = seg_s == xl ? 0 : __builtin_amdgcn_readfirstlane(vpre[ci]) * g + cj - ord0 + 1;
         const int e = sn & (kRing - 1);
-        const float l_head = st.l_lane + __shfl_xor(st.l_lane, 16);
-        const float l_tot = l_head + __shfl_xor(l_head, 32);  // head r
-        // rows of acc are heads 4qd+v
-        float Mv[4], Lv[4];
+        // rows of acc are heads 4qd+v of each block
+        float Mv[NHB][4], Lv[NHB][4], l_tot[NHB];
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-            Mv[v] = __shfl(st.m_ref, 4 * qd + v);
-            Lv[v] = __shfl(l_tot, 4 * qd + v);
+        for (int k = 0; k < NHB; k++) {
+            const float l_head = st[k].l_lane + __shfl_xor(st[k].l_lane, 16);
+            l_tot[k] = l_head + __shfl_xor(l_head, 32);  // head r
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                Mv[k][v] = __shfl(st[k].m_ref, 4 * qd + v);
+                Lv[k][v] = __shfl(l_tot[k], 4 * qd + v);
+            }
         }
         if (mine == seg_e - seg_s) {  // the whole segment was this wave's: pass the record on
             lds_flag_wait(&rec_tag[hb][e], sn);
@@ -1285,8 +1374,11 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
         } else {  // other waves have steps of this segment
             lds_flag_wait(&slot_busy[w], 0);
 #pragma unroll
-            for (int nb = 0; nb < C::NB; nb++) slot_o[w][nb][lane] = st.acc[nb];
-            if (qd == 0) slot_ml[w][r] = make_float2(st.m_ref, l_tot);
+            for (int k = 0; k < NHB; k++) {
+#pragma unroll
+                for (int nb = 0; nb < C::NB; nb++) slot_o[w][k][nb][lane] = st[k].acc[nb];
+                if (qd == 0) slot_ml[w][k][r] = make_float2(st[k].m_ref, l_tot[k]);
+            }
             if (lane == 0) slot_busy[w] = 1;
             lds_drain();
             lds_flag_wait(&rec_tag[hb][e], sn);  // an earlier segment may still hold the record
@@ -1299,22 +1391,25 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
             if (lane == 0) slot_busy[w] = 0;
             for (uint32_t m = now_ & 0xffu & ~(1u << wb); m; m &= m - 1) {
                 const int ww = hb * wph + __builtin_ctz(m);
-                float a_own[4], a_oth[4];
 #pragma unroll
-                for (int v = 0; v < 4; v++) {
-                    const float2 eo = slot_ml[ww][4 * qd + v];
-                    const float Mn = fmaxf(Mv[v], eo.x);
-                    a_own[v] = Mv[v] == -INFINITY ? 0.f : fast_exp2(Mv[v] - Mn);
-                    a_oth[v] = eo.x == -INFINITY ? 0.f : fast_exp2(eo.x - Mn);
-                    Lv[v] = fmaf(Lv[v], a_own[v], a_oth[v] * eo.y);
-                    Mv[v] = Mn;
-                }
+                for (int k = 0; k < NHB; k++) {
+                    float a_own[4], a_oth[4];
 #pragma unroll
-                for (int nb = 0; nb < C::NB; nb++) {
-                    const f32x4_t o = slot_o[ww][nb][lane];
+                    for (int v = 0; v < 4; v++) {
+                        const float2 eo = slot_ml[ww][k][4 * qd + v];
+                        const float Mn = fmaxf(Mv[k][v], eo.x);
+                        a_own[v] = Mv[k][v] == -INFINITY ? 0.f : fast_exp2(Mv[k][v] - Mn);
+                        a_oth[v] = eo.x == -INFINITY ? 0.f : fast_exp2(eo.x - Mn);
+                        Lv[k][v] = fmaf(Lv[k][v], a_own[v], a_oth[v] * eo.y);
+                        Mv[k][v] = Mn;
+                    }
 #pragma unroll
-                    for (int v = 0; v < 4; v++)
-                        st.acc[nb][v] = fmaf(st.acc[nb][v], a_own[v], a_oth[v] * o[v]);
+                    for (int nb = 0; nb < C::NB; nb++) {
+                        const f32x4_t o = slot_o[ww][k][nb][lane];
+#pragma unroll
+                        for (int v = 0; v < 4; v++)
+                            st[k].acc[nb][v] = fmaf(st[k].acc[nb][v], a_own[v], a_oth[v] * o[v]);
+                    }
                 }
                 lds_drain();
                 if (lane == 0) lds_flag_set(&slot_busy[ww], 0);
@@ -1330,27 +1425,32 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
             // for its last; streamk_combine_kernel merges the pieces
             const int slot = seg_s == x0 ? 0 : 1;
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const int hs = hb * C::HB + 4 * qd + v;
-                if (hs >= G) continue;
-                const size_t prow = ((size_t)wg * 2 + slot) * HBT + hs;
+            for (int k = 0; k < NHB; k++)
 #pragma unroll
-                for (int nb = 0; nb < C::NB; nb++) part_o[prow * D + 16 * nb + r] = st.acc[nb][v];
-                if (r == 0) part_ml[prow] = make_float2(Mv[v], Lv[v]);
-            }
+                for (int v = 0; v < 4; v++) {
+                    const int hs = (hb * NHB + k) * C::HB + 4 * qd + v;
+                    if (hs >= R) continue;
+                    const size_t prow = ((size_t)wg * 2 + slot) * HBT + hs;
+#pragma unroll
+                    for (int nb = 0; nb < C::NB; nb++)
+                        part_o[prow * D + 16 * nb + r] = st[k].acc[nb][v];
+                    if (r == 0) part_ml[prow] = make_float2(Mv[k][v], Lv[k][v]);
+                }
             return;
         }
         // a whole unit: its rows, normalised
-        const size_t row0 = (size_t)ci * h + cj * G;  // first query head of the unit
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-            const int hs = hb * C::HB + 4 * qd + v;
-            if (hs >= G) continue;
-            const float inv = 1.f / Lv[v];
+        for (int k = 0; k < NHB; k++)
 #pragma unroll
-            for (int nb = 0; nb < C::NB; nb++)
-                out[(row0 + hs) * D + 16 * nb + r] = st.acc[nb][v] * inv;
-        }
+            for (int v = 0; v < 4; v++) {
+                const int hs = (hb * NHB + k) * C::HB + 4 * qd + v;
+                if (hs >= R) continue;
+                const float inv = 1.f / Lv[k][v];
+                const size_t orow = qr.row(ci, cj, hs);
+#pragma unroll
+                for (int nb = 0; nb < C::NB; nb++)
+                    out[orow * D + 16 * nb + r] = st[k].acc[nb][v] * inv;
+            }
     };
 
     // one step: claim and prefetch the next, compute this one, close the
@@ -1364,15 +1464,22 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
         bool bad_next = false;
         // nothing left: a step that loads nothing
         load_step<D>(more ? src_of(ni, nj, nL, nu0, tn, bad_next) : kv.none(), lane, later);
-        compute_step<D>(now, (t - cu0) * C::STEP, cL, qop, st, vbuf[w], lane, qk_scale_log2);
+        // causal ends of several tokens: this lane's row in each block, the
+        // wave's earliest
+        int t_row[NHB];
+#pragma unroll
+        for (int k = 0; k < NHB; k++) t_row[k] = cL - qr.T + 1 + tau[k];
+        compute_step<D, MULTI, NHB>(now, (t - cu0) * C::STEP, cL, cL - qr.T + 1, t_row, qop, st,
+                                    vbuf[w], lane, qk_scale_log2);
         if (bad_now) poison_state<D>(st, err, lane);
         bad_now = bad_next;
         mine++;
         // the next unit's q, in flight during the segment's close
-        if (next_unit) load_q_operand<D>(q, q_row(ni, nj), qd, qop);
+        if (next_unit) load_q(ni, nj, qop);
         if (!more || next_unit) {
             finish_segment();
-            st.reset();
+#pragma unroll
+            for (int k = 0; k < NHB; k++) st[k].reset();
             mine = 0;
         }
         if (!more) return false;
@@ -1400,7 +1507,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
 template <int D, int HPB>
 __global__ void __launch_bounds__(256)
 streamk_combine_kernel(const float *__restrict__ part_o, const float2 *__restrict__ part_ml,
-                       const int4 *__restrict__ cut_desc, int h, int G, int HBT,
+                       const int4 *__restrict__ cut_desc, const QRows<true> qr, int R, int HBT,
                        float *__restrict__ out) {
     constexpr int C4 = D / 4;               // float4 columns per row
     constexpr int PL = 256 / (HPB * C4);    // piece lanes per head slot
@@ -1414,7 +1521,7 @@ streamk_combine_kernel(const float *__restrict__ part_o, const float2 *__restric
     const int wl = dsc.z, slot_f = dsc.w;
     const int hh = threadIdx.x / (PL * C4), pl = (threadIdx.x / C4) % PL, c4 = threadIdx.x % C4;
     const int hs = blockIdx.y * HPB + hh;
-    const bool live_row = hs < G;
+    const bool live_row = hs < R;
     float M = -INFINITY, den = 0.f;
     f32x4_t num = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int p0 = wf + pl; live_row && p0 <= wl; p0 += BATCH * PL) {
@@ -1458,7 +1565,7 @@ streamk_combine_kernel(const float *__restrict__ part_o, const float2 *__restric
         }
     }
     if (!live_row) return;
-    const size_t row = (size_t)dsc.x * h + (size_t)dsc.y * G + hs;
+    const size_t row = qr.row(dsc.x, dsc.y, hs);
     *(f32x4_t *)(out + row * D + 4 * c4) = num * (1.f / den);
 }
 
@@ -1466,17 +1573,20 @@ streamk_combine_kernel(const float *__restrict__ part_o, const float2 *__restric
 // combine: out = sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s over live partitions
 // ---------------------------------------------------------------------------
 
+// Block (k, i): partial row i*T*h + k (k = j*R + rho: K/V head j, query row
+// rho of the unit), written to out row qr.row(i, j, rho).
 template <int D>
 __global__ void __launch_bounds__(D)
 combine_kernel(const float *__restrict__ part_o, const float2 *__restrict__ part_ml,
-               const int32_t *__restrict__ seq_lens, int h, int S, int chunk, int nsplit,
-               float *__restrict__ out, int32_t *__restrict__ err) {
-    const int hq = blockIdx.x, i = blockIdx.y, x = threadIdx.x;
-    const size_t row = (size_t)i * h + hq;
+               const int32_t *__restrict__ seq_lens, const QRows<true> qr, int R, int S, int chunk,
+               int nsplit, float *__restrict__ out, int32_t *__restrict__ err) {
+    const int k = blockIdx.x, i = blockIdx.y, x = threadIdx.x;
+    const size_t row = (size_t)i * qr.T * qr.h + k;
+    const size_t orow = qr.row(i, k / R, k % R);
     const int L = seq_lens[i];
-    if (L < 1 || L > S) {
-        out[row * D + x] = __builtin_nanf("");
-        if (hq == 0 && x == 0 && err) atomicOr(err, MQA_DEVERR_SEQLEN);
+    if (L < qr.T || L > S) {
+        out[orow * D + x] = __builtin_nanf("");
+        if (k == 0 && x == 0 && err) atomicOr(err, MQA_DEVERR_SEQLEN);
         return;
     }
     const int n = (L + chunk - 1) / chunk;
@@ -1507,7 +1617,7 @@ combine_kernel(const float *__restrict__ part_o, const float2 *__restrict__ part
             den = fmaf(wgt, e[k].y, den);
         }
     }
-    out[row * D + x] = num / den;
+    out[orow * D + x] = num / den;
 }
 
 // ---------------------------------------------------------------------------
@@ -1555,10 +1665,27 @@ int wg_heads(mqa_dtype dt, int G) { return dt == MQA_BF16 ? 16 : heads_per_wg(G)
 // work-group's waves then stream tens of steps; measured best for MQA at
 // 32K context, the 32-layer sweeps and short contexts alike — more, shorter
 // partitions only add start-up latency and combine work).
-int resolve_chunk(int b, int h, int g, int S, mqa_dtype dt, int split_chunk) {
+// Query rows R of a (sequence, K/V head) unit on the matrix cores: blocks of
+// 16 rows; a wave computes blk_per_wave (NHB) blocks against each K/V step
+// it loads (two once there is more than one: the K/V registers then serve
+// 32 rows), and the unit's blocks form `groups` such groups.
+struct RowBlocks {
+    int blocks, per_wave, groups;
+};
+RowBlocks row_blocks(int R) {
+    RowBlocks rb;
+    rb.blocks = (R + 15) / 16;
+    rb.per_wave = rb.blocks > 1 ? 2 : 1;
+    rb.groups = (rb.blocks + rb.per_wave - 1) / rb.per_wave;
+    return rb;
+}
+
+// (T query tokens: T*h/g query rows per (sequence, K/V head).)
+int resolve_chunk(int b, int h, int g, int S, mqa_dtype dt, int split_chunk, int T = 1) {
     if (split_chunk > 0) return split_chunk;
-    const int G = h / g;
-    const long long groups = (long long)b * g * ((G + wg_heads(dt, G) - 1) / wg_heads(dt, G));
+    const int G = T * (h / g);
+    const long long groups = (long long)b * g *
+        (dt == MQA_BF16 ? row_blocks(G).groups : (G + wg_heads(dt, G) - 1) / wg_heads(dt, G));
     const long long want = (device_cus() + groups - 1) / groups;  // partitions per group
     long long c = ((long long)S + want - 1) / want;
     c = (c + kTile - 1) / kTile * kTile;
@@ -1579,13 +1706,14 @@ size_t workspace_for(int b, int h, int S, int d, int chunk) {
 // It pays where there are many units (sequence, K/V head) whose lengths
 // differ; with few units every unit would be cut into many pieces and the
 // fixed partitions (merged in parallel by combine_kernel) do better.
-bool use_streamk(int b, int h, int g, int S, mqa_dtype dt, int split_chunk, mqa_kernel kernel) {
-    const int nhb = (h / g + 15) / 16;
+bool use_streamk(int b, int h, int g, int S, mqa_dtype dt, int split_chunk, mqa_kernel kernel,
+                 int T = 1) {
+    const int ngr = row_blocks(T * (h / g)).groups;
     const long long units = (long long)b * g;
     if (units * ((S + 31) / 32) >= (1ll << 31)) return false;  // step indices are 32-bit
     return dt == MQA_BF16 && kernel != MQA_KERNEL_VALU && split_chunk == 0 &&
            b <= kStreamMaxSeq && units >= kStreamMinUnits &&
-           (nhb == 1 || nhb == 2 || nhb == 4);
+           (ngr == 1 || ngr == 2 || ngr == 4);
 }
 
 // Balanced-schedule workspace: [partials o][partials (m, l)][cut-unit
@@ -1593,8 +1721,8 @@ bool use_streamk(int b, int h, int g, int S, mqa_dtype dt, int split_chunk, mqa_
 struct StreamkLayout {
     size_t o_bytes, ml_off, desc_off, total;
 };
-StreamkLayout streamk_layout(int h, int g, int d) {
-    const size_t hbt = (size_t)((h / g + 15) / 16) * 16;
+StreamkLayout streamk_layout(int h, int g, int d, int T = 1) {
+    const size_t hbt = (size_t)((T * (h / g) + 15) / 16) * 16;
     const size_t rows = (size_t)kStreamMaxWG * 2 * hbt;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     StreamkLayout L;
@@ -1608,10 +1736,10 @@ StreamkLayout streamk_layout(int h, int g, int d) {
 // Workspace bytes: the larger of the two paths' needs (the same workspace
 // serves every kernel choice)
 size_t workspace_need(int b, int h, int g, int S, int d, mqa_dtype dt, int split_chunk,
-                      mqa_kernel kernel) {
-    size_t need = workspace_for(b, h, S, d, resolve_chunk(b, h, g, S, dt, split_chunk));
-    if (use_streamk(b, h, g, S, dt, split_chunk, kernel)) {
-        const size_t sk = streamk_layout(h, g, d).total;
+                      mqa_kernel kernel, int T = 1) {
+    size_t need = workspace_for(b, T * h, S, d, resolve_chunk(b, h, g, S, dt, split_chunk, T));
+    if (use_streamk(b, h, g, S, dt, split_chunk, kernel, T)) {
+        const size_t sk = streamk_layout(h, g, d, T).total;
         if (sk > need) need = sk;
     }
     return need;
@@ -1655,43 +1783,73 @@ void dispatch_rows(int hpw, const void *q, const void *k, const void *v, const i
 
 // The matrix-core paths (bf16) for one K/V source: the balanced schedule
 // (+ its cut-unit merge) or fixed partitions (+ the log-sum-exp combine).
-template <int D, class KV>
-mqa_status run_mfma(const KV &kv, const void *q, const int32_t *seq_lens, int b, int h, int g,
-                    int S, float qs, float *out, void *workspace, int chunk, int nsplit,
-                    bool balanced, int32_t *err_flags, hipStream_t stream) {
-    const int G = h / g;
-    const int nhb = (G + 15) / 16;
+// T query tokens per sequence (T > 1: the causal variant of the kernels).
+template <int D, class KV, bool MULTI, int NHB>
+mqa_status run_mfma_rows(const KV &kv, const void *q, const int32_t *seq_lens, int b, int T,
+                         int h, int g, int S, float qs, float *out, void *workspace, int chunk,
+                         int nsplit, bool balanced, int32_t *err_flags, hipStream_t stream) {
+    const int Gh = h / g, R = T * Gh;
+    const int nhb = (R + 15) / 16;
+    const int ngroups = (nhb + NHB - 1) / NHB;
+    const QRows<MULTI> qr{T, Gh, h};
+    const QRows<true> qc{T, Gh, h};
     if (balanced) {
         const int nwg = streamk_wgs(b, g, S);
-        const StreamkLayout L = streamk_layout(h, g, D);
+        const StreamkLayout L = streamk_layout(h, g, D, T);
         float *po = (float *)workspace;
         float2 *pml = (float2 *)((uint8_t *)workspace + L.ml_off);
         int4 *desc = (int4 *)((uint8_t *)workspace + L.desc_off);
-        hipLaunchKernelGGL((streamk_mfma_kernel<D, kStreamWaves, KV>), dim3(nwg), dim3(64 * kStreamWaves),
-                           0, stream, (const uint16_t *)q, kv, seq_lens, b, h, g, S, G, nhb, qs, out,
-                           po, pml, desc, err_flags);
+        hipLaunchKernelGGL((streamk_mfma_kernel<D, kStreamWaves, KV, MULTI, NHB>), dim3(nwg),
+                           dim3(64 * kStreamWaves), 0, stream, (const uint16_t *)q, kv, seq_lens, b,
+                           qr, g, S, R, ngroups, qs, out, po, pml, desc, err_flags);
         // pieces per cut unit: ~2 when there are more units than work-groups,
         // ~nwg/units when each unit spans many ranges
         constexpr int HPB = 256 / (D / 4);  // head slots per block with one piece lane
         if ((long long)b * g * 4 < nwg)
-            hipLaunchKernelGGL((streamk_combine_kernel<D, 1>), dim3(nwg, G), dim3(256), 0, stream, po,
-                               pml, desc, h, G, nhb * 16, out);
+            hipLaunchKernelGGL((streamk_combine_kernel<D, 1>), dim3(nwg, R), dim3(256), 0, stream, po,
+                               pml, desc, qc, R, nhb * 16, out);
         else
-            hipLaunchKernelGGL((streamk_combine_kernel<D, HPB>), dim3(nwg, (G + HPB - 1) / HPB),
-                               dim3(256), 0, stream, po, pml, desc, h, G, nhb * 16, out);
+            hipLaunchKernelGGL((streamk_combine_kernel<D, HPB>), dim3(nwg, (R + HPB - 1) / HPB),
+                               dim3(256), 0, stream, po, pml, desc, qc, R, nhb * 16, out);
         return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
     }
-    const size_t rows = (size_t)b * h * nsplit;
+    const size_t rows = (size_t)b * T * h * nsplit;
     float *part_o = (float *)workspace;
     float2 *part_ml =
         (float2 *)((uint8_t *)workspace + ((rows * D * sizeof(float) + 255) & ~(size_t)255));
-    hipLaunchKernelGGL((split_mfma_kernel<D, KV>), dim3(nsplit, g * nhb, b), dim3(256), 0, stream,
-                       (const uint16_t *)q, kv, seq_lens, h, g, S, G, nhb, chunk, nsplit, qs, part_o,
-                       part_ml, err_flags);
+    hipLaunchKernelGGL((split_mfma_kernel<D, KV, MULTI, NHB>), dim3(nsplit, g * ngroups, b),
+                       dim3(256), 0, stream, (const uint16_t *)q, kv, seq_lens, qr, g, S, R, ngroups,
+                       chunk, nsplit, qs, part_o, part_ml, err_flags);
     if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
-    hipLaunchKernelGGL(combine_kernel<D>, dim3(h, b), dim3(D), 0, stream, part_o, part_ml, seq_lens, h,
-                       S, chunk, nsplit, out, err_flags);
+    hipLaunchKernelGGL(combine_kernel<D>, dim3(T * h, b), dim3(D), 0, stream, part_o, part_ml,
+                       seq_lens, qc, R, S, chunk, nsplit, out, err_flags);
     return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+}
+
+template <int D, class KV>
+mqa_status run_mfma(const KV &kv, const void *q, const int32_t *seq_lens, int b, int T, int h,
+                    int g, int S, float qs, float *out, void *workspace, int chunk, int nsplit,
+                    bool balanced, int32_t *err_flags, hipStream_t stream) {
+    const bool two = row_blocks(T * (h / g)).per_wave == 2;
+    if (T > 1) {
+        if (two)
+            return run_mfma_rows<D, KV, true, 2>(kv, q, seq_lens, b, T, h, g, S, qs, out, workspace,
+                                                 chunk, nsplit, balanced, err_flags, stream);
+        return run_mfma_rows<D, KV, true, 1>(kv, q, seq_lens, b, T, h, g, S, qs, out, workspace,
+                                             chunk, nsplit, balanced, err_flags, stream);
+    }
+    if (two)
+        return run_mfma_rows<D, KV, false, 2>(kv, q, seq_lens, b, 1, h, g, S, qs, out, workspace,
+                                              chunk, nsplit, balanced, err_flags, stream);
+    return run_mfma_rows<D, KV, false, 1>(kv, q, seq_lens, b, 1, h, g, S, qs, out, workspace,
+                                          chunk, nsplit, balanced, err_flags, stream);
+}
+
+// T-token calls: T in [1, S]; beyond one token only the bf16 matrix-core path
+mqa_status check_tokens(int T, int h, int S, mqa_dtype dt) {
+    if (T < 1 || T > S || (T > 1 && (long long)T * h > (1ll << 24))) return MQA_ERR_SHAPE;
+    if (T > 1 && dt != MQA_BF16) return MQA_ERR_UNSUPPORTED;
+    return MQA_OK;
 }
 
 }  // namespace
@@ -1738,22 +1896,31 @@ size_t mqa_decode_workspace_bytes(int b, int h, int g, int S, int d, mqa_dtype d
     return workspace_need(b, h, g, S, d, dt, split_chunk, MQA_KERNEL_AUTO);
 }
 
-mqa_status mqa_append_kv(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
-                         const int32_t *seq_lens, int b, int g, int S, int d, mqa_dtype dt,
-                         int32_t *err_flags, hipStream_t stream) {
+mqa_status mqa_append_kv_multi(void *k_cache, void *v_cache, const void *k_new,
+                               const void *v_new, const int32_t *seq_lens, int b, int T, int g,
+                               int S, int d, mqa_dtype dt, int32_t *err_flags, hipStream_t stream) {
     if (!k_cache || !v_cache || !k_new || !v_new || !seq_lens) return MQA_ERR_NULL;
     mqa_status st = check_sizes(b, g, g, S, d, dt, 0);
     if (st != MQA_OK) return st;
+    if (T < 1 || T > S) return MQA_ERR_SHAPE;
     if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
         return MQA_ERR_ALIGN;
     const int row_bytes = d * (dt == MQA_BF16 ? 2 : 4);
-    const long long total = 2ll * b * g * (row_bytes / 16);
+    const long long total = 2ll * b * T * g * (row_bytes / 16);
     const int threads = 256;
     const long long blocks = (total + threads - 1) / threads;
+    if (blocks > 0x7fffffffll) return MQA_ERR_SHAPE;
     hipLaunchKernelGGL(append_kv_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
                        (uint8_t *)k_cache, (uint8_t *)v_cache, (const uint8_t *)k_new,
-                       (const uint8_t *)v_new, seq_lens, b, g, S, row_bytes, err_flags);
+                       (const uint8_t *)v_new, seq_lens, b, T, g, S, row_bytes, err_flags);
     return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+}
+
+mqa_status mqa_append_kv(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                         const int32_t *seq_lens, int b, int g, int S, int d, mqa_dtype dt,
+                         int32_t *err_flags, hipStream_t stream) {
+    return mqa_append_kv_multi(k_cache, v_cache, k_new, v_new, seq_lens, b, 1, g, S, d, dt,
+                               err_flags, stream);
 }
 
 mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache, const void *v_cache,
@@ -1775,23 +1942,22 @@ mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache, const void
     const size_t need = workspace_need(b, h, g, S, d, dt, split_chunk, kernel);
     if (!workspace || workspace_bytes < need) return MQA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MQA_ERR_ALIGN;
-    const float qs_ = scale * kLog2e;
+    const float qs = scale * kLog2e;
 
     const size_t rows = (size_t)b * h * nsplit;
     uint8_t *wsp = (uint8_t *)workspace;
     float *part_o = (float *)wsp;
     float2 *part_ml = (float2 *)(wsp + ((rows * d * sizeof(float) + 255) & ~(size_t)255));
-    const float qs = scale * kLog2e;
     const int hpw = heads_per_wg(h / g);
 
     if (use_mfma) {
         const bool bal = use_streamk(b, h, g, S, dt, split_chunk, kernel);
         const uint8_t *kb = (const uint8_t *)k_cache, *vb = (const uint8_t *)v_cache;
         if (d == 128)
-            return run_mfma<128>(ContigKV<128>{kb, vb, g, S}, q, seq_lens, b, h, g, S, qs_, out,
+            return run_mfma<128>(ContigKV<128>{kb, vb, g, S}, q, seq_lens, b, 1, h, g, S, qs, out,
                                  workspace, chunk, nsplit, bal, err_flags, stream);
-        return run_mfma<64>(ContigKV<64>{kb, vb, g, S}, q, seq_lens, b, h, g, S, qs_, out, workspace,
-                            chunk, nsplit, bal, err_flags, stream);
+        return run_mfma<64>(ContigKV<64>{kb, vb, g, S}, q, seq_lens, b, 1, h, g, S, qs, out,
+                            workspace, chunk, nsplit, bal, err_flags, stream);
     } else if (dt == MQA_BF16) {
         if (d == 128) dispatch_rows<uint16_t, 128>(hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream);
         else dispatch_rows<uint16_t, 64>(hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream);
@@ -1801,12 +1967,13 @@ mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache, const void
         else dispatch_rows<float, 64>(hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream);
     }
     if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
+    const QRows<true> qc{1, h / g, h};
     if (d == 128)
         hipLaunchKernelGGL(combine_kernel<128>, dim3(h, b), dim3(128), 0, stream, part_o, part_ml,
-                           seq_lens, h, S, chunk, nsplit, out, err_flags);
+                           seq_lens, qc, h / g, S, chunk, nsplit, out, err_flags);
     else
         hipLaunchKernelGGL(combine_kernel<64>, dim3(h, b), dim3(64), 0, stream, part_o, part_ml,
-                           seq_lens, h, S, chunk, nsplit, out, err_flags);
+                           seq_lens, qc, h / g, S, chunk, nsplit, out, err_flags);
     return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
 }
 
@@ -1818,6 +1985,54 @@ mqa_status mqa_decode_attn(const void *q, const void *k_cache, const void *v_cac
     return mqa_decode_attn_kernel(q, k_cache, v_cache, seq_lens, b, h, g, S, d, dt, scale, out,
                                   workspace, workspace_bytes, split_chunk, err_flags,
                                   MQA_KERNEL_AUTO, stream);
+}
+
+// ---- several query tokens per sequence ----
+
+size_t mqa_decode_multi_workspace_bytes(int b, int T, int h, int g, int S, int d, mqa_dtype dt,
+                                        int split_chunk) {
+    if (T == 1) return mqa_decode_workspace_bytes(b, h, g, S, d, dt, split_chunk);
+    if (check_sizes(b, h, g, S, d, dt, split_chunk) != MQA_OK) return 0;
+    if (check_tokens(T, h, S, dt) != MQA_OK) return 0;
+    return workspace_need(b, h, g, S, d, dt, split_chunk, MQA_KERNEL_MFMA, T);
+}
+
+int mqa_decode_multi_schedule(int b, int T, int h, int g, int S, int d, mqa_dtype dt,
+                              int split_chunk) {
+    if (T == 1) return mqa_decode_schedule(b, h, g, S, d, dt, split_chunk, MQA_KERNEL_AUTO);
+    if (check_sizes(b, h, g, S, d, dt, split_chunk) != MQA_OK) return -1;
+    if (check_tokens(T, h, S, dt) != MQA_OK) return -1;
+    return use_streamk(b, h, g, S, dt, split_chunk, MQA_KERNEL_MFMA, T) ? MQA_SCHEDULE_MFMA_BALANCED
+                                                                         : MQA_SCHEDULE_MFMA_PARTITIONS;
+}
+
+mqa_status mqa_decode_attn_multi(const void *q, const void *k_cache, const void *v_cache,
+                                 const int32_t *seq_lens, int b, int T, int h, int g, int S, int d,
+                                 mqa_dtype dt, float scale, float *out, void *workspace,
+                                 size_t workspace_bytes, int split_chunk, int32_t *err_flags,
+                                 hipStream_t stream) {
+    if (T == 1)
+        return mqa_decode_attn(q, k_cache, v_cache, seq_lens, b, h, g, S, d, dt, scale, out,
+                               workspace, workspace_bytes, split_chunk, err_flags, stream);
+    if (!q || !k_cache || !v_cache || !seq_lens || !out) return MQA_ERR_NULL;
+    mqa_status st = check_sizes(b, h, g, S, d, dt, split_chunk);
+    if (st != MQA_OK) return st;
+    if ((st = check_tokens(T, h, S, dt)) != MQA_OK) return st;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return MQA_ERR_ALIGN;
+    const int chunk = resolve_chunk(b, h, g, S, dt, split_chunk, T);
+    const int nsplit = (S + chunk - 1) / chunk;
+    if (!workspace || workspace_bytes < workspace_need(b, h, g, S, d, dt, split_chunk, MQA_KERNEL_MFMA, T))
+        return MQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MQA_ERR_ALIGN;
+    const bool bal = use_streamk(b, h, g, S, dt, split_chunk, MQA_KERNEL_MFMA, T);
+    const float qs = scale * kLog2e;
+    const uint8_t *kb = (const uint8_t *)k_cache, *vb = (const uint8_t *)v_cache;
+    if (d == 128)
+        return run_mfma<128>(ContigKV<128>{kb, vb, g, S}, q, seq_lens, b, T, h, g, S, qs, out,
+                             workspace, chunk, nsplit, bal, err_flags, stream);
+    return run_mfma<64>(ContigKV<64>{kb, vb, g, S}, q, seq_lens, b, T, h, g, S, qs, out, workspace,
+                        chunk, nsplit, bal, err_flags, stream);
 }
 
 // ---- paged cache ----
@@ -1834,23 +2049,35 @@ mqa_status check_paged(int b, int h, int g, int P, int max_pages, int num_pages,
 }
 }  // namespace
 
+mqa_status mqa_append_kv_paged_multi(void *k_pages, void *v_pages, const void *k_new,
+                                     const void *v_new, const int32_t *block_table,
+                                     const int32_t *seq_lens, int b, int T, int g, int page_size,
+                                     int max_pages, int num_pages, int d, mqa_dtype dt,
+                                     int32_t *err_flags, hipStream_t stream) {
+    if (!k_pages || !v_pages || !k_new || !v_new || !block_table || !seq_lens) return MQA_ERR_NULL;
+    if (page_size < 1 || max_pages < 1 || num_pages < 1) return MQA_ERR_SHAPE;
+    if ((long long)page_size * max_pages > (1ll << 30)) return MQA_ERR_SHAPE;
+    const mqa_status st = check_sizes(b, g, g, page_size * max_pages, d, dt, 0);
+    if (st != MQA_OK) return st;
+    if (T < 1 || T > page_size * max_pages) return MQA_ERR_SHAPE;
+    if (!aligned16(k_pages) || !aligned16(v_pages) || !aligned16(k_new) || !aligned16(v_new))
+        return MQA_ERR_ALIGN;
+    const int row_bytes = d * (dt == MQA_BF16 ? 2 : 4);
+    const long long total = 2ll * b * T * g * (row_bytes / 16);
+    if ((total + 255) / 256 > 0x7fffffffll) return MQA_ERR_SHAPE;
+    hipLaunchKernelGGL(append_kv_paged_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       stream, (uint8_t *)k_pages, (uint8_t *)v_pages, (const uint8_t *)k_new,
+                       (const uint8_t *)v_new, block_table, seq_lens, b, T, g, page_size, max_pages,
+                       num_pages, row_bytes, err_flags);
+    return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+}
+
 mqa_status mqa_append_kv_paged(void *k_pages, void *v_pages, const void *k_new, const void *v_new,
                                const int32_t *block_table, const int32_t *seq_lens, int b, int g,
                                int page_size, int max_pages, int num_pages, int d, mqa_dtype dt,
                                int32_t *err_flags, hipStream_t stream) {
-    if (!k_pages || !v_pages || !k_new || !v_new || !block_table || !seq_lens) return MQA_ERR_NULL;
-    if (page_size < 1 || max_pages < 1 || num_pages < 1) return MQA_ERR_SHAPE;
-    const mqa_status st = check_sizes(b, g, g, page_size * max_pages, d, dt, 0);
-    if (st != MQA_OK) return st;
-    if (!aligned16(k_pages) || !aligned16(v_pages) || !aligned16(k_new) || !aligned16(v_new))
-        return MQA_ERR_ALIGN;
-    const int row_bytes = d * (dt == MQA_BF16 ? 2 : 4);
-    const long long total = 2ll * b * g * (row_bytes / 16);
-    hipLaunchKernelGGL(append_kv_paged_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                       stream, (uint8_t *)k_pages, (uint8_t *)v_pages, (const uint8_t *)k_new,
-                       (const uint8_t *)v_new, block_table, seq_lens, b, g, page_size, max_pages,
-                       num_pages, row_bytes, err_flags);
-    return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+    return mqa_append_kv_paged_multi(k_pages, v_pages, k_new, v_new, block_table, seq_lens, b, 1,
+                                     g, page_size, max_pages, num_pages, d, dt, err_flags, stream);
 }
 
 size_t mqa_decode_paged_workspace_bytes(int b, int h, int g, int page_size, int max_pages, int d,
@@ -1859,33 +2086,46 @@ size_t mqa_decode_paged_workspace_bytes(int b, int h, int g, int page_size, int 
     return workspace_need(b, h, g, page_size * max_pages, d, dt, split_chunk, MQA_KERNEL_MFMA);
 }
 
+mqa_status mqa_decode_attn_paged_multi(const void *q, const void *k_pages, const void *v_pages,
+                                       const int32_t *block_table, const int32_t *seq_lens, int b,
+                                       int T, int h, int g, int page_size, int max_pages,
+                                       int num_pages, int d, mqa_dtype dt, float scale, float *out,
+                                       void *workspace, size_t workspace_bytes, int split_chunk,
+                                       int32_t *err_flags, hipStream_t stream) {
+    if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !out) return MQA_ERR_NULL;
+    mqa_status st = check_paged(b, h, g, page_size, max_pages, num_pages, d, dt, split_chunk);
+    if (st != MQA_OK) return st;
+    const int S = page_size * max_pages;
+    if ((st = check_tokens(T, h, S, dt)) != MQA_OK) return st;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(out))
+        return MQA_ERR_ALIGN;
+    const int chunk = resolve_chunk(b, h, g, S, dt, split_chunk, T);
+    const int nsplit = (S + chunk - 1) / chunk;
+    if (!workspace ||
+        workspace_bytes < workspace_need(b, h, g, S, d, dt, split_chunk, MQA_KERNEL_MFMA, T))
+        return MQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MQA_ERR_ALIGN;
+    const bool bal = use_streamk(b, h, g, S, dt, split_chunk, MQA_KERNEL_MFMA, T);
+    const float qs = scale * kLog2e;
+    const uint8_t *kb = (const uint8_t *)k_pages, *vb = (const uint8_t *)v_pages;
+    if (d == 128)
+        return run_mfma<128>(PagedKV<128>{kb, vb, block_table, g, page_size, max_pages, num_pages}, q,
+                             seq_lens, b, T, h, g, S, qs, out, workspace, chunk, nsplit, bal,
+                             err_flags, stream);
+    return run_mfma<64>(PagedKV<64>{kb, vb, block_table, g, page_size, max_pages, num_pages}, q,
+                        seq_lens, b, T, h, g, S, qs, out, workspace, chunk, nsplit, bal, err_flags,
+                        stream);
+}
+
 mqa_status mqa_decode_attn_paged(const void *q, const void *k_pages, const void *v_pages,
                                  const int32_t *block_table, const int32_t *seq_lens, int b, int h,
                                  int g, int page_size, int max_pages, int num_pages, int d,
                                  mqa_dtype dt, float scale, float *out, void *workspace,
                                  size_t workspace_bytes, int split_chunk, int32_t *err_flags,
                                  hipStream_t stream) {
-    if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !out) return MQA_ERR_NULL;
-    const mqa_status st = check_paged(b, h, g, page_size, max_pages, num_pages, d, dt, split_chunk);
-    if (st != MQA_OK) return st;
-    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(out))
-        return MQA_ERR_ALIGN;
-    const int S = page_size * max_pages;
-    const int chunk = resolve_chunk(b, h, g, S, dt, split_chunk);
-    const int nsplit = (S + chunk - 1) / chunk;
-    if (!workspace || workspace_bytes < workspace_need(b, h, g, S, d, dt, split_chunk, MQA_KERNEL_MFMA))
-        return MQA_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return MQA_ERR_ALIGN;
-    const bool bal = use_streamk(b, h, g, S, dt, split_chunk, MQA_KERNEL_MFMA);
-    const float qs = scale * kLog2e;
-    const uint8_t *kb = (const uint8_t *)k_pages, *vb = (const uint8_t *)v_pages;
-    if (d == 128)
-        return run_mfma<128>(PagedKV<128>{kb, vb, block_table, g, page_size, max_pages, num_pages}, q,
-                             seq_lens, b, h, g, S, qs, out, workspace, chunk, nsplit, bal, err_flags,
-                             stream);
-    return run_mfma<64>(PagedKV<64>{kb, vb, block_table, g, page_size, max_pages, num_pages}, q,
-                        seq_lens, b, h, g, S, qs, out, workspace, chunk, nsplit, bal, err_flags,
-                        stream);
+    return mqa_decode_attn_paged_multi(q, k_pages, v_pages, block_table, seq_lens, b, 1, h, g,
+                                       page_size, max_pages, num_pages, d, dt, scale, out,
+                                       workspace, workspace_bytes, split_chunk, err_flags, stream);
 }
 
 }  // extern "C"

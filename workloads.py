@@ -25,6 +25,10 @@ seq_lens holds the post-append lengths. Seeds: base = 1000 * k for the k-th
 configuration; streams q +1, k_cache +2, v_cache +3, k_new +4, v_new +5,
 seq_lens +6 (a CPU generator), layer l adds 100 * l.
 
+Several query tokens per sequence (make_multi_step): q [b, T, h, d] and
+k_new/v_new [b, T, g, d] drawn like the one-token ones (streams +8, +9, +10),
+lengths raised to at least T.
+
 Paged variants (make_paged_step): the same values scattered into pages of
 page_size rows with page ids drawn as a random permutation (CPU generator,
 stream +7) of b * ceil(S / page_size) + extra_pages pages; pages no sequence
@@ -158,4 +162,22 @@ def make_paged_step(w: Workload, device="cpu", page_size: int = 16, layer: int =
     t["block_table"] = ids.to(device)
     t["page_size"] = P
     t["capacity"] = maxp * P
+    return t
+
+
+def make_multi_step(w: Workload, device="cpu", T: int = 4, layer: int = 0,
+                    page_size: int = 0) -> dict:
+    """A step with T query tokens per sequence (a verified draft, a prompt chunk).
+
+    The make_step (or make_paged_step, page_size > 0) dict with q [b, T, h, d],
+    k_new/v_new [b, T, g, d], and seq_lens (post-append, so counting the T new
+    tokens) raised to at least T.
+    """
+    t = make_paged_step(w, device, page_size, layer) if page_size else make_step(w, device, layer)
+    base = w.seed + 100 * layer
+    t["q"] = _normal((w.b, T, w.h, w.d), base + 8, w.dtype, device)
+    t["k_new"] = _normal((w.b, T, w.g, w.d), base + 9, w.dtype, device)
+    t["v_new"] = _normal((w.b, T, w.g, w.d), base + 10, w.dtype, device)
+    t["seq_lens"] = torch.clamp(t["seq_lens"], min=T)
+    t["T"] = T
     return t
