@@ -553,6 +553,9 @@ split_rows_kernel(const T *__restrict__ q, const T *__restrict__ kc, const T *__
 // through LDS at the end of a partition.
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 template <int D>
@@ -565,7 +568,7 @@ struct MfmaCfg {
     static constexpr int CPR = ROW_BYTES / 16;       // 16-byte chunks per row
     static constexpr int RPI = 64 / CPR;             // rows per wave-wide V load
     static constexpr int VLOADS = STEP / RPI;        // V loads per lane per step
-    static constexpr int VSTRIDE = ROW_BYTES + 16;   // padded LDS row stride of V
+    static constexpr int VSTRIDE = ROW_BYTES + 32;   // padded LDS row stride of V (see compute_step)
     static constexpr int VBUF = STEP * VSTRIDE;      // per-wave V staging bytes
     static constexpr int HB = 16;                    // query heads per matrix block
     static_assert(NW * HB * (D + 2) * 4 <= NW * VBUF, "merge scratch must fit");
@@ -838,13 +841,24 @@ __device__ __forceinline__ void compute_step(const StepData<D> &sd, int t0, int 
     }
 
     // ---- P.V (one V operand for every block) ----
-    const uint16_t *vt = (const uint16_t *)(vb + 4 * qd * C::VSTRIDE + 2 * r);
+    // The B operand wants lane (r, qd) to hold V[kslot(qd, e)][16nb + r],
+    // e = 0..7: eight positions of one column, where the staging buffer holds
+    // rows. The LDS transpose read gives each lane of a 16-lane group the
+    // transpose of what the group loads: lane j gets element j%4 of the
+    // 8-byte chunk of group lane 4i + j/4, for i = 0..3 (measured on the
+    // device). So lane r of group qd loads row p0 + r/4, columns 16nb +
+    // 4(r%4) .. +3, and receives column 16nb + r of rows p0 .. p0+3; two such
+    // reads (p0 = 4qd and 16 + 4qd) cover the eight positions. The row stride
+    // (ROW_BYTES + 32) puts the four rows of a read in distinct banks.
+    const uint8_t *vt = vb + (4 * qd + (r >> 2)) * C::VSTRIDE + 8 * (r & 3);
 #pragma unroll
     for (int nb = 0; nb < C::NB; nb++) {
-        bf16x8_t vop;
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-            vop[e] = __builtin_bit_cast(__bf16, vt[(kslot(0, e) * C::VSTRIDE + 32 * nb) / 2]);
+        const i16x4_t v_lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4 *)(const lds_u8 *)(vt + 32 * nb));
+        const i16x4_t v_hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4 *)(const lds_u8 *)(vt + 16 * C::VSTRIDE + 32 * nb));
+        const bf16x8_t vop = __builtin_bit_cast(
+            bf16x8_t, (i16x8_t){v_lo[0], v_lo[1], v_lo[2], v_lo[3], v_hi[0], v_hi[1], v_hi[2], v_hi[3]});
 #pragma unroll
         for (int hb = 0; hb < NHB; hb++) {
             st[hb].acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[hb], vop, st[hb].acc[nb], 0, 0, 0);
@@ -872,10 +886,11 @@ struct QRows {
 };
 
 // Steps s_begin, s_begin+stride, ... < s_end (src(step, bad) gives where a
-// step's rows are), with the loads of the next step in flight while this
-// one computes (two register sets, alternating). Past the last step the
-// prefetch asks for nothing.
-template <int D, bool MULTI, int NHB, class Src>
+// step's rows are), with the loads of the next NBUF-1 steps in flight while
+// one computes (NBUF register sets in rotation; the loop is unrolled by NBUF
+// so that each set keeps fixed registers). Past the last step a prefetch
+// asks for nothing.
+template <int D, bool MULTI, int NHB, int NBUF, class Src>
 __device__ __forceinline__ void run_steps(const Src &src, const StepSrc &nothing, int s_begin,
                                           int s_end, int stride, int t_end, int t_lo,
                                           const int (&t_row)[NHB],
@@ -883,32 +898,31 @@ __device__ __forceinline__ void run_steps(const Src &src, const StepSrc &nothing
                                           MfmaState<D> (&st)[NHB], uint8_t *vb, int lane,
                                           float qk_scale_log2, int32_t *err) {
     using C = MfmaCfg<D>;
+    static_assert(NBUF >= 2, "at least one step in flight");
     int stp = s_begin;
     if (stp >= s_end) return;
-    StepData<D> a, b;
-    bool bad = false, bad_n = false;
-    load_step<D>(src(stp, bad), lane, a);
-    auto prefetch = [&](int nx, StepData<D> &sd) __attribute__((always_inline)) {
-        bad_n = false;
-        load_step<D>(nx < s_end ? src(nx, bad_n) : nothing, lane, sd);
-    };
+    StepData<D> buf[NBUF];
+    bool bad[NBUF];
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; k++) {
+        const int sk = stp + k * stride;
+        bad[k] = false;
+        load_step<D>(sk < s_end ? src(sk, bad[k]) : nothing, lane, buf[k]);
+    }
     while (true) {
-        int nx = stp + stride;
-        prefetch(nx, b);
-        compute_step<D, MULTI, NHB>(a, stp * C::STEP, t_end, t_lo, t_row, qop, st, vb, lane,
-                                    qk_scale_log2);
-        if (bad) poison_state<D>(st, err, lane);
-        bad = bad_n;
-        if (nx >= s_end) break;
-        stp = nx;
-        nx = stp + stride;
-        prefetch(nx, a);
-        compute_step<D, MULTI, NHB>(b, stp * C::STEP, t_end, t_lo, t_row, qop, st, vb, lane,
-                                    qk_scale_log2);
-        if (bad) poison_state<D>(st, err, lane);
-        bad = bad_n;
-        if (nx >= s_end) break;
-        stp = nx;
+#pragma unroll
+        for (int k = 0; k < NBUF; k++) {
+            // the step NBUF-1 ahead, into the set computed last
+            const int kn = (k + NBUF - 1) % NBUF;
+            const int sn = stp + (NBUF - 1) * stride;
+            bad[kn] = false;
+            load_step<D>(sn < s_end ? src(sn, bad[kn]) : nothing, lane, buf[kn]);
+            compute_step<D, MULTI, NHB>(buf[k], stp * C::STEP, t_end, t_lo, t_row, qop, st, vb,
+                                        lane, qk_scale_log2);
+            if (bad[k]) poison_state<D>(st, err, lane);
+            stp += stride;
+            if (stp >= s_end) return;
+        }
     }
 }
 
@@ -1021,8 +1035,8 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
     MfmaState<D> st[NHB];
 #pragma unroll
     for (int b = 0; b < NHB; b++) st[b].reset();
-    run_steps<D, MULTI, NHB>(src, kv.none(), s0 + w, s0 + nsteps, C::NW, t_end, t_lo, t_row, qop,
-                             st, vbuf[w], lane, qk_scale_log2, err);
+    run_steps<D, MULTI, NHB, 2>(src, kv.none(), s0 + w, s0 + nsteps, C::NW, t_end, t_lo, t_row,
+                                qop, st, vbuf[w], lane, qk_scale_log2, err);
 
     // merge the waves' states block by block through the staging buffers
     float *mrg = (float *)&vbuf[0][0];
@@ -1171,7 +1185,7 @@ __device__ __forceinline__ void lds_flag_wait(int *f, int v) {
 // of the sums can differ between calls.
 template <int D, int NW, class KV, bool MULTI, int NHB>
 __global__ void __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu((KV::kPaged || NHB > 1) ? 1 : 2, 8)))
+__attribute__((amdgpu_waves_per_eu(1, 8)))
 streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
                     const int32_t *__restrict__ seq_lens, int b, const QRows<MULTI> qr,
                     int g, int S, int R, int ngroups, float qk_scale_log2,
@@ -1574,50 +1588,73 @@ streamk_combine_kernel(const float *__restrict__ part_o, const float2 *__restric
 // ---------------------------------------------------------------------------
 
 // Block (k, i): partial row i*T*h + k (k = j*R + rho: K/V head j, query row
-// rho of the unit), written to out row qr.row(i, j, rho).
+// rho of the unit), written to out row qr.row(i, j, rho). Threads are (piece
+// lane, four columns); piece lane pl merges partitions pl, pl+PL, ... (four
+// loads in flight at a time) and the lanes are merged in order through LDS,
+// so the result is the same every call.
 template <int D>
-__global__ void __launch_bounds__(D)
+__global__ void __launch_bounds__(256)
 combine_kernel(const float *__restrict__ part_o, const float2 *__restrict__ part_ml,
                const int32_t *__restrict__ seq_lens, const QRows<true> qr, int R, int S, int chunk,
                int nsplit, float *__restrict__ out, int32_t *__restrict__ err) {
-    const int k = blockIdx.x, i = blockIdx.y, x = threadIdx.x;
+    constexpr int C4 = D / 4;           // float4 columns per row
+    constexpr int PL = 256 / C4;        // piece lanes
+    constexpr int BATCH = 4;
+    __shared__ f32x4_t s_num[PL][C4];
+    __shared__ float2 s_md[PL][C4];
+    const int k = blockIdx.x, i = blockIdx.y;
+    const int pl = threadIdx.x / C4, c4 = threadIdx.x % C4;
     const size_t row = (size_t)i * qr.T * qr.h + k;
     const size_t orow = qr.row(i, k / R, k % R);
     const int L = seq_lens[i];
-    if (L < qr.T || L > S) {
-        out[orow * D + x] = __builtin_nanf("");
-        if (k == 0 && x == 0 && err) atomicOr(err, MQA_DEVERR_SEQLEN);
+    if (L < qr.T || L > S) {  // uniform over the block
+        if (pl == 0) *(f32x4_t *)(out + orow * D + 4 * c4) = f32x4_t{1.f, 1.f, 1.f, 1.f} * __builtin_nanf("");
+        if (k == 0 && threadIdx.x == 0 && err) atomicOr(err, MQA_DEVERR_SEQLEN);
         return;
     }
     const int n = (L + chunk - 1) / chunk;
     const float2 *ml = part_ml + row * nsplit;
-    const float *po = part_o + row * nsplit * D + x;
-    // online merge, eight partitions' loads in flight at a time
-    float M = -INFINITY, num = 0.f, den = 0.f;
-    for (int s0 = 0; s0 < n; s0 += 8) {
-        float2 e[8];
-        float o[8];
+    const float *po = part_o + row * nsplit * D + 4 * c4;
+    float M = -INFINITY, den = 0.f;
+    f32x4_t num = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int p0 = pl; p0 < n; p0 += BATCH * PL) {
+        float2 e[BATCH];
+        f32x4_t o[BATCH];
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
-            const bool ok = s0 + k < n;
-            e[k] = ok ? ml[s0 + k] : make_float2(-INFINITY, 0.f);
-            o[k] = ok ? po[(size_t)(s0 + k) * D] : 0.f;
+        for (int kk = 0; kk < BATCH; kk++) {
+            const int p = p0 + kk * PL;
+            const bool ok = p < n;
+            e[kk] = ok ? ml[p] : make_float2(-INFINITY, 0.f);
+            o[kk] = ok ? *(const f32x4_t *)(po + (size_t)p * D) : f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
         float Mb = M;
 #pragma unroll
-        for (int k = 0; k < 8; k++) Mb = fmaxf(Mb, e[k].x);
+        for (int kk = 0; kk < BATCH; kk++) Mb = fmaxf(Mb, e[kk].x);
         const float rs = M == -INFINITY ? 0.f : fast_exp2(M - Mb);
         num *= rs;
         den *= rs;
         M = Mb;
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
-            const float wgt = e[k].x == -INFINITY ? 0.f : fast_exp2(e[k].x - M);
-            num = fmaf(wgt, o[k], num);
-            den = fmaf(wgt, e[k].y, den);
+        for (int kk = 0; kk < BATCH; kk++) {
+            const float wgt = e[kk].x == -INFINITY ? 0.f : fast_exp2(e[kk].x - M);
+            num += wgt * o[kk];
+            den = fmaf(wgt, e[kk].y, den);
         }
     }
-    out[orow * D + x] = num / den;
+    s_num[pl][c4] = num;
+    s_md[pl][c4] = make_float2(M, den);
+    __syncthreads();
+    if (pl != 0) return;
+    for (int kk = 1; kk < PL; kk++) {
+        const float2 md = s_md[kk][c4];
+        const float Mn = fmaxf(M, md.x);
+        const float a0 = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+        const float a1 = md.x == -INFINITY ? 0.f : fast_exp2(md.x - Mn);
+        num = num * a0 + a1 * s_num[kk][c4];
+        den = den * a0 + a1 * md.y;
+        M = Mn;
+    }
+    *(f32x4_t *)(out + orow * D + 4 * c4) = num * (1.f / den);
 }
 
 // ---------------------------------------------------------------------------
@@ -1821,7 +1858,7 @@ mqa_status run_mfma_rows(const KV &kv, const void *q, const int32_t *seq_lens, i
                        dim3(256), 0, stream, (const uint16_t *)q, kv, seq_lens, qr, g, S, R, ngroups,
                        chunk, nsplit, qs, part_o, part_ml, err_flags);
     if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
-    hipLaunchKernelGGL(combine_kernel<D>, dim3(T * h, b), dim3(D), 0, stream, part_o, part_ml,
+    hipLaunchKernelGGL(combine_kernel<D>, dim3(T * h, b), dim3(256), 0, stream, part_o, part_ml,
                        seq_lens, qc, R, S, chunk, nsplit, out, err_flags);
     return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
 }
@@ -1969,10 +2006,10 @@ mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache, const void
     if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
     const QRows<true> qc{1, h / g, h};
     if (d == 128)
-        hipLaunchKernelGGL(combine_kernel<128>, dim3(h, b), dim3(128), 0, stream, part_o, part_ml,
+        hipLaunchKernelGGL(combine_kernel<128>, dim3(h, b), dim3(256), 0, stream, part_o, part_ml,
                            seq_lens, qc, h / g, S, chunk, nsplit, out, err_flags);
     else
-        hipLaunchKernelGGL(combine_kernel<64>, dim3(h, b), dim3(64), 0, stream, part_o, part_ml,
+        hipLaunchKernelGGL(combine_kernel<64>, dim3(h, b), dim3(256), 0, stream, part_o, part_ml,
                            seq_lens, qc, h / g, S, chunk, nsplit, out, err_flags);
     return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
 }
