@@ -16,7 +16,7 @@ Sources, cited by page title and section:
   [MQA blog]  nanhubrain.csdn.net MQA article §2.2 (append on the sequence axis),
               §3.3 (paged cache, 16 tokens per page).
   [GQA notes] §十 item 10 (the causal mask stays per query position when several
-              query tokens attend at once).
+              query tokens attend at once), §十 item 7 (a quantised KV cache).
 """
 from __future__ import annotations
 
@@ -28,6 +28,7 @@ import numpy as np
 
 F32 = 0
 BF16 = 1
+FP8_E4M3 = 2
 OK = 0
 BAD_LEN = 1
 BAD_SHAPE = 2
@@ -87,6 +88,21 @@ def lib() -> ctypes.CDLL:
         L.oracle_append_kv_paged_multi.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                                    i32, i32, i32, i32]
         L.oracle_append_kv_paged_multi.restype = i32
+        L.oracle_fp8_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_fp8_e4m3_decode.restype = ctypes.c_double
+        L.oracle_fp8_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_fp8_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_decode_attn_fp8.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                             i32, ctypes.c_float, vp, i32]
+        L.oracle_decode_attn_fp8.restype = i32
+        L.oracle_decode_attn_paged_fp8.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                                   i32, i32, i32, i32, i32, ctypes.c_float, vp, i32]
+        L.oracle_decode_attn_paged_fp8.restype = i32
+        L.oracle_append_kv_fp8.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32]
+        L.oracle_append_kv_fp8.restype = i32
+        L.oracle_append_kv_paged_fp8.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32,
+                                                 i32, i32, i32, i32]
+        L.oracle_append_kv_paged_fp8.restype = i32
         L.oracle_kv_bytes.argtypes = [i32, i32, ctypes.c_int64, i32, i32]
         L.oracle_kv_bytes.restype = ctypes.c_uint64
         _lib = L
@@ -246,6 +262,94 @@ def append_kv_paged_multi(k_pages: np.ndarray, v_pages: np.ndarray, k_new: np.nd
                                               _ptr(_c(v_new)), _ptr(bt), _ptr(sl), b, T, g,
                                               P, bt.shape[1], num_pages, d,
                                               _dtype_code(k_pages))
+
+
+# ---- fp8 e4m3 cache with per-K/V-head scales ([GQA notes] §十 item 7) ----
+
+def fp8_decode(code: int) -> float:
+    """Value of one e4m3 code (OCP E4M3FN)."""
+    return float(lib().oracle_fp8_e4m3_decode(int(code)))
+
+
+def fp8_encode(x: float) -> int:
+    """e4m3 code of a float32 value: nearest, ties to even, saturating at +-448."""
+    return int(lib().oracle_fp8_e4m3_encode(float(np.float32(x))))
+
+
+def _f32(a):
+    return _c(np.asarray(a, np.float32))
+
+
+def decode_attn_fp8(q: np.ndarray, k_codes: np.ndarray, v_codes: np.ndarray,
+                    k_scale: np.ndarray, v_scale: np.ndarray, seq_lens: np.ndarray,
+                    scale: float, nthreads: int = 1):
+    """Decode attention over an fp8 cache (values code * scale[j]), in double.
+
+    q: [b, h, d] or [b, T, h, d] (float32 or bf16 bits); k_codes, v_codes:
+    [b, g, S, d] uint8; k_scale, v_scale: [g]. Returns (out shaped like q, status).
+    """
+    q4 = q if q.ndim == 4 else q[:, None]
+    b, T, h, d = q4.shape
+    _, g, S, _ = k_codes.shape
+    assert k_codes.dtype == np.uint8 and v_codes.dtype == np.uint8
+    out = np.empty((b, T, h, d), np.float64)
+    sl = _c(seq_lens.astype(np.int32))
+    rc = lib().oracle_decode_attn_fp8(_ptr(_c(q4)), _dtype_code(q4), _ptr(_c(k_codes)),
+                                      _ptr(_c(v_codes)), _ptr(_f32(k_scale)), _ptr(_f32(v_scale)),
+                                      _ptr(sl), b, T, h, g, S, d, ctypes.c_float(scale), _ptr(out),
+                                      int(nthreads))
+    return (out if q.ndim == 4 else out[:, 0]), rc
+
+
+def decode_attn_paged_fp8(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray,
+                          k_scale: np.ndarray, v_scale: np.ndarray, block_table: np.ndarray,
+                          seq_lens: np.ndarray, scale: float, nthreads: int = 1):
+    """decode_attn_fp8 over a paged cache [num_pages, g, page_size, d] of codes."""
+    q4 = q if q.ndim == 4 else q[:, None]
+    b, T, h, d = q4.shape
+    num_pages, g, P, _ = k_pages.shape
+    out = np.empty((b, T, h, d), np.float64)
+    bt = _c(block_table.astype(np.int32))
+    sl = _c(seq_lens.astype(np.int32))
+    rc = lib().oracle_decode_attn_paged_fp8(_ptr(_c(q4)), _dtype_code(q4), _ptr(_c(k_pages)),
+                                            _ptr(_c(v_pages)), _ptr(_f32(k_scale)),
+                                            _ptr(_f32(v_scale)), _ptr(bt), _ptr(sl), b, T, h, g,
+                                            P, bt.shape[1], num_pages, d, ctypes.c_float(scale),
+                                            _ptr(out), int(nthreads))
+    return (out if q.ndim == 4 else out[:, 0]), rc
+
+
+def append_kv_fp8(k_codes: np.ndarray, v_codes: np.ndarray, k_new: np.ndarray,
+                  v_new: np.ndarray, k_scale: np.ndarray, v_scale: np.ndarray,
+                  seq_lens: np.ndarray) -> int:
+    """In place: the new rows ([b, g, d] or [b, T, g, d], float32 or bf16 bits)
+    quantised with the head's scale into positions L-T .. L-1. Returns the status."""
+    assert k_codes.flags.c_contiguous and v_codes.flags.c_contiguous
+    kn = k_new if k_new.ndim == 4 else k_new[:, None]
+    vn = v_new if v_new.ndim == 4 else v_new[:, None]
+    b, g, S, d = k_codes.shape
+    T = kn.shape[1]
+    sl = _c(seq_lens.astype(np.int32))
+    return lib().oracle_append_kv_fp8(_ptr(k_codes), _ptr(v_codes), _ptr(_c(kn)), _ptr(_c(vn)),
+                                      _dtype_code(kn), _ptr(_f32(k_scale)), _ptr(_f32(v_scale)),
+                                      _ptr(sl), b, T, g, S, d)
+
+
+def append_kv_paged_fp8(k_pages: np.ndarray, v_pages: np.ndarray, k_new: np.ndarray,
+                        v_new: np.ndarray, k_scale: np.ndarray, v_scale: np.ndarray,
+                        block_table: np.ndarray, seq_lens: np.ndarray) -> int:
+    """append_kv_fp8 into a paged cache."""
+    assert k_pages.flags.c_contiguous and v_pages.flags.c_contiguous
+    kn = k_new if k_new.ndim == 4 else k_new[:, None]
+    vn = v_new if v_new.ndim == 4 else v_new[:, None]
+    num_pages, g, P, d = k_pages.shape
+    b, T = kn.shape[:2]
+    bt = _c(block_table.astype(np.int32))
+    sl = _c(seq_lens.astype(np.int32))
+    return lib().oracle_append_kv_paged_fp8(_ptr(k_pages), _ptr(v_pages), _ptr(_c(kn)),
+                                            _ptr(_c(vn)), _dtype_code(kn), _ptr(_f32(k_scale)),
+                                            _ptr(_f32(v_scale)), _ptr(bt), _ptr(sl), b, T, g, P,
+                                            bt.shape[1], num_pages, d)
 
 
 def mha_per_head(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:

@@ -12,8 +12,39 @@
 #include <stdlib.h>
 #include <string.h>
 
+/* fp8 e4m3 (OCP "E4M3FN"): sign, 4 exponent bits (bias 7), 3 mantissa bits;
+ * exponent 0 holds the subnormals m/8 * 2^-6; S.1111.111 is NaN and there is
+ * no infinity, so the largest finite value is 1.75 * 2^8 = 448. */
+double oracle_fp8_e4m3_decode(uint8_t c) {
+    int e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    double v = e == 0 ? (m / 8.0) * ldexp(1.0, -6) : (1.0 + m / 8.0) * ldexp(1.0, e - 7);
+    return (c & 0x80) ? -v : v;
+}
+
+/* Nearest e4m3 value, ties to the even code; magnitudes at or above 448
+ * saturate to +-448 (a finite input never becomes NaN); NaN stays NaN. */
+uint8_t oracle_fp8_e4m3_encode(float f) {
+    uint8_t sign = signbit(f) ? 0x80 : 0;
+    float a = fabsf(f);
+    if (isnan(f)) return sign | 0x7F;
+    if (a >= 448.0f) return sign | 0x7E;
+    if (a < 0.015625f) /* below 2^-6: the multiples of 2^-9 (8 * 2^-9 is 2^-6, code 8) */
+        return sign | (uint8_t)nearbyintf(a * 512.0f);
+    int e;
+    float fr = frexpf(a, &e);             /* a = fr * 2^e, fr in [0.5, 1) */
+    int sm = (int)nearbyintf(fr * 16.0f); /* 8 + mantissa, rounded: 8 .. 16 */
+    int E = e - 1 + 7;                    /* biased exponent of 2^(e-1) */
+    if (sm == 16) {
+        sm = 8;
+        E += 1;
+    }
+    return sign | (uint8_t)((E << 3) | (sm - 8));
+}
+
 /* Read element idx of a buffer of the given type, widened exactly to double. */
 static double elem(const void *base, size_t idx, int dtype) {
+    if (dtype == ORACLE_FP8_E4M3) return oracle_fp8_e4m3_decode(((const uint8_t *)base)[idx]);
     if (dtype == ORACLE_F32) {
         float f;
         memcpy(&f, (const char *)base + 4 * idx, 4);
@@ -27,7 +58,9 @@ static double elem(const void *base, size_t idx, int dtype) {
     return (double)f;
 }
 
-static size_t elem_bytes(int dtype) { return dtype == ORACLE_F32 ? 4u : 2u; }
+static size_t elem_bytes(int dtype) {
+    return dtype == ORACLE_F32 ? 4u : dtype == ORACLE_FP8_E4M3 ? 1u : 2u;
+}
 
 int oracle_append_kv_multi(void *k_cache, void *v_cache, const void *k_new,
                            const void *v_new, const int32_t *seq_lens, int b,
@@ -66,7 +99,7 @@ int oracle_append_kv(void *k_cache, void *v_cache, const void *k_new,
 typedef struct {
     const void *q, *k, *v;
     const int32_t *seq_lens;
-    int b, T, h, g, S, d, dtype; /* T query tokens per sequence */
+    int b, T, h, g, S, d, dtype; /* T query tokens per sequence; dtype: K and V */
     double scale;
     double *out, *alpha;
     int row_begin, row_end; /* rows are (i*T + tau)*h + hq */
@@ -75,6 +108,10 @@ typedef struct {
      * t % page_size of page block_table[i * max_pages + t / page_size] */
     const int32_t *block_table;
     int page_size, max_pages, num_pages;
+    /* element type of q; per-K/V-head dequantisation scales of a quantised
+     * cache (NULL: none): a cache value is code * scale[j] */
+    int q_dtype;
+    const float *k_scale, *v_scale;
 } decode_job;
 
 /* Element index of K/V row (sequence i, K/V head j, position t), or -1 when
@@ -112,18 +149,20 @@ static void decode_row(decode_job *J, int row) {
         }
     }
 
+    double ks = J->k_scale ? (double)J->k_scale[j] : 1.0;
+    double vs = J->v_scale ? (double)J->v_scale[j] : 1.0;
     double *s = (double *)malloc(sizeof(double) * (size_t)A);
     /* score_t = (Q_i . K_j,t) * scale */
     for (int t = 0; t < A; t++) {
         double dot = 0.0;
         size_t kr = (size_t)kv_row(J, i, j, t);
         for (int x = 0; x < d; x++)
-            dot += elem(J->q, qoff + x, J->dtype) * elem(J->k, kr + x, J->dtype);
+            dot += elem(J->q, qoff + x, J->q_dtype) * (ks * elem(J->k, kr + x, J->dtype));
         s[t] = J->scale * dot;
     }
     /* alpha_t = softmax_t(score); subtracting the max leaves it unchanged */
-    double m = s[0];
-    for (int t = 1; t < A; t++)
+    double m = -INFINITY;
+    for (int t = 0; t < A; t++)
         if (s[t] > m) m = s[t];
     double Z = 0.0;
     for (int t = 0; t < A; t++) {
@@ -135,7 +174,7 @@ static void decode_row(decode_job *J, int row) {
     for (int x = 0; x < d; x++) {
         double acc = 0.0;
         for (int t = 0; t < A; t++)
-            acc += s[t] * elem(J->v, (size_t)kv_row(J, i, j, t) + x, J->dtype);
+            acc += s[t] * (vs * elem(J->v, (size_t)kv_row(J, i, j, t) + x, J->dtype));
         o[x] = acc;
     }
     if (J->alpha) {
@@ -184,7 +223,7 @@ int oracle_decode_attn_multi(const void *q, const void *k, const void *v,
     if (b < 1 || T < 1 || h < 1 || g < 1 || S < 1 || d < 1 || h % g != 0)
         return ORACLE_BAD_SHAPE;
     decode_job J = {q, k, v, seq_lens, b, T, h, g, S, d, dtype, (double)scale,
-                    out, alpha, 0, 0, 0, NULL, 0, 0, 0};
+                    out, alpha, 0, 0, 0, NULL, 0, 0, 0, dtype, NULL, NULL};
     return run_decode(&J, nthreads);
 }
 
@@ -207,7 +246,7 @@ int oracle_decode_attn_paged_multi(const void *q, const void *k_pages,
         return ORACLE_BAD_SHAPE;
     decode_job J = {q, k_pages, v_pages, seq_lens, b, T, h, g, page_size * max_pages,
                     d, dtype, (double)scale, out, NULL, 0, 0, 0, block_table,
-                    page_size, max_pages, num_pages};
+                    page_size, max_pages, num_pages, dtype, NULL, NULL};
     return run_decode(&J, nthreads);
 }
 
@@ -340,4 +379,99 @@ void oracle_lse_combine(int n, const double *m, const double *l,
 uint64_t oracle_kv_bytes(int layers, int g, int64_t S, int d, int dtype_bytes) {
     return 2ull * (uint64_t)layers * (uint64_t)g * (uint64_t)S * (uint64_t)d *
            (uint64_t)dtype_bytes;
+}
+
+/* ---- fp8 e4m3 cache with per-K/V-head scales ------------------------------ */
+
+int oracle_decode_attn_fp8(const void *q, int q_dtype, const uint8_t *k,
+                           const uint8_t *v, const float *k_scale,
+                           const float *v_scale, const int32_t *seq_lens, int b,
+                           int T, int h, int g, int S, int d, float scale,
+                           double *out, int nthreads) {
+    if (b < 1 || T < 1 || h < 1 || g < 1 || S < 1 || d < 1 || h % g != 0)
+        return ORACLE_BAD_SHAPE;
+    decode_job J = {q, k, v, seq_lens, b, T, h, g, S, d, ORACLE_FP8_E4M3, (double)scale,
+                    out, NULL, 0, 0, 0, NULL, 0, 0, 0, q_dtype, k_scale, v_scale};
+    return run_decode(&J, nthreads);
+}
+
+int oracle_decode_attn_paged_fp8(const void *q, int q_dtype, const uint8_t *k_pages,
+                                 const uint8_t *v_pages, const float *k_scale,
+                                 const float *v_scale, const int32_t *block_table,
+                                 const int32_t *seq_lens, int b, int T, int h, int g,
+                                 int page_size, int max_pages, int num_pages, int d,
+                                 float scale, double *out, int nthreads) {
+    if (b < 1 || T < 1 || h < 1 || g < 1 || d < 1 || h % g != 0 || page_size < 1 ||
+        max_pages < 1 || num_pages < 1)
+        return ORACLE_BAD_SHAPE;
+    decode_job J = {q, k_pages, v_pages, seq_lens, b, T, h, g, page_size * max_pages, d,
+                    ORACLE_FP8_E4M3, (double)scale, out, NULL, 0, 0, 0, block_table,
+                    page_size, max_pages, num_pages, q_dtype, k_scale, v_scale};
+    return run_decode(&J, nthreads);
+}
+
+/* Code of one new element: its fp32 value divided by the head's scale (one
+ * correctly rounded fp32 division), then rounded to e4m3. */
+static uint8_t quantise(const void *src, size_t idx, int dtype, float scale) {
+    float x = (float)elem(src, idx, dtype); /* exact: the source is f32 or bf16 */
+    return oracle_fp8_e4m3_encode(x / scale);
+}
+
+int oracle_append_kv_fp8(uint8_t *k_cache, uint8_t *v_cache, const void *k_new,
+                         const void *v_new, int new_dtype, const float *k_scale,
+                         const float *v_scale, const int32_t *seq_lens, int b, int T,
+                         int g, int S, int d) {
+    if (b < 1 || T < 1 || g < 1 || S < 1 || d < 1) return ORACLE_BAD_SHAPE;
+    int rc = ORACLE_OK;
+    for (int i = 0; i < b; i++) {
+        int L = seq_lens[i];
+        if (L < T || L > S) {
+            rc |= ORACLE_BAD_LEN;
+            continue;
+        }
+        for (int tau = 0; tau < T; tau++)
+            for (int j = 0; j < g; j++) {
+                size_t dst = (((size_t)i * g + j) * S + (size_t)(L - T + tau)) * d;
+                size_t src = (((size_t)i * T + tau) * g + j) * d;
+                for (int x = 0; x < d; x++) {
+                    k_cache[dst + x] = quantise(k_new, src + x, new_dtype, k_scale[j]);
+                    v_cache[dst + x] = quantise(v_new, src + x, new_dtype, v_scale[j]);
+                }
+            }
+    }
+    return rc;
+}
+
+int oracle_append_kv_paged_fp8(uint8_t *k_pages, uint8_t *v_pages, const void *k_new,
+                               const void *v_new, int new_dtype, const float *k_scale,
+                               const float *v_scale, const int32_t *block_table,
+                               const int32_t *seq_lens, int b, int T, int g, int page_size,
+                               int max_pages, int num_pages, int d) {
+    if (b < 1 || T < 1 || g < 1 || d < 1 || page_size < 1 || max_pages < 1 || num_pages < 1)
+        return ORACLE_BAD_SHAPE;
+    int rc = ORACLE_OK;
+    for (int i = 0; i < b; i++) {
+        int L = seq_lens[i];
+        if (L < T || L > page_size * max_pages) {
+            rc |= ORACLE_BAD_LEN;
+            continue;
+        }
+        for (int tau = 0; tau < T; tau++) {
+            int t = L - T + tau;
+            int page = block_table[(size_t)i * max_pages + t / page_size];
+            if (page < 0 || page >= num_pages) {
+                rc |= ORACLE_BAD_PAGE;
+                continue;
+            }
+            for (int j = 0; j < g; j++) {
+                size_t dst = (((size_t)page * g + j) * page_size + (size_t)(t % page_size)) * d;
+                size_t src = (((size_t)i * T + tau) * g + j) * d;
+                for (int x = 0; x < d; x++) {
+                    k_pages[dst + x] = quantise(k_new, src + x, new_dtype, k_scale[j]);
+                    v_pages[dst + x] = quantise(v_new, src + x, new_dtype, v_scale[j]);
+                }
+            }
+        }
+    }
+    return rc;
 }

@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_FP8_E4M3 = 2 };
 
 /* Return bits. ORACLE_BAD_LEN: some seq_lens[i] outside [1, S] ([T, S] with T
  * query tokens); those rows
@@ -105,6 +105,39 @@ int oracle_append_kv_paged_multi(void *k_pages, void *v_pages, const void *k_new
                                  const int32_t *seq_lens, int b, int T, int g,
                                  int page_size, int max_pages, int num_pages, int d,
                                  int dtype);
+
+/* Low-precision cache ([GQA notes] §十 item 7: a quantised KV cache stacks
+ * with grouping but must be validated on its own): K and V held as fp8 e4m3
+ * codes (OCP E4M3FN: bias 7, 3 mantissa bits, no infinity, largest finite
+ * 448), one scale per K/V head for K and one for V (k_scale, v_scale [g],
+ * fp32); a cache value is code * scale[j]. Decode is the plain definition
+ * (the T-token form above, q of q_dtype [b][T][h][d]) over those values.
+ * Append: each new element x (k_new, v_new [b][T][g][d] of new_dtype) is
+ * stored as encode(x / scale[j]), the division one correctly rounded fp32
+ * operation and the encoding round-to-nearest-even with saturation at
+ * +-448 (a finite value never becomes NaN). */
+double oracle_fp8_e4m3_decode(uint8_t code);
+uint8_t oracle_fp8_e4m3_encode(float x);
+int oracle_decode_attn_fp8(const void *q, int q_dtype, const uint8_t *k,
+                           const uint8_t *v, const float *k_scale,
+                           const float *v_scale, const int32_t *seq_lens, int b,
+                           int T, int h, int g, int S, int d, float scale,
+                           double *out, int nthreads);
+int oracle_decode_attn_paged_fp8(const void *q, int q_dtype, const uint8_t *k_pages,
+                                 const uint8_t *v_pages, const float *k_scale,
+                                 const float *v_scale, const int32_t *block_table,
+                                 const int32_t *seq_lens, int b, int T, int h, int g,
+                                 int page_size, int max_pages, int num_pages, int d,
+                                 float scale, double *out, int nthreads);
+int oracle_append_kv_fp8(uint8_t *k_cache, uint8_t *v_cache, const void *k_new,
+                         const void *v_new, int new_dtype, const float *k_scale,
+                         const float *v_scale, const int32_t *seq_lens, int b, int T,
+                         int g, int S, int d);
+int oracle_append_kv_paged_fp8(uint8_t *k_pages, uint8_t *v_pages, const void *k_new,
+                               const void *v_new, int new_dtype, const float *k_scale,
+                               const float *v_scale, const int32_t *block_table,
+                               const int32_t *seq_lens, int b, int T, int g, int page_size,
+                               int max_pages, int num_pages, int d);
 
 /* Textbook multi-head attention for one sequence, one K/V head per query
  * head (no sharing): q [h][d], K and V [h][L][d], all double.

@@ -511,6 +511,118 @@ def test_paged_multi_matches_contiguous_multi():
 
 
 # ---------------------------------------------------------------------------
+# fp8 e4m3 cache with per-K/V-head scales ([GQA notes] §十 item 7)
+# ---------------------------------------------------------------------------
+
+def _torch_fp8_values(codes: np.ndarray) -> np.ndarray:
+    """Values of e4m3 codes by torch's float8_e4m3fn (a library decoder)."""
+    t = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def test_fp8_decode_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = _torch_fp8_values(codes)
+    got = np.array([oracle.fp8_decode(c) for c in codes])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert oracle.fp8_decode(0x7E) == 448.0 and oracle.fp8_decode(0x01) == 2.0 ** -9
+
+
+def test_fp8_encode_matches_torch_in_range_and_saturates():
+    rng = np.random.default_rng(8)
+    reps = _torch_fp8_values(np.arange(256, dtype=np.uint8))
+    finite = reps[np.isfinite(reps)]
+    mids = (np.sort(np.unique(finite))[1:] + np.sort(np.unique(finite))[:-1]) / 2  # ties
+    x = np.concatenate([finite, mids, rng.standard_normal(3000) * 30,
+                        rng.standard_normal(1000) * 1e-3, [463.9, -463.9, 0.0, -0.0]])
+    x = x.astype(np.float32)
+    x = x[np.abs(x) < 464]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.fp8_encode(v) for v in x], np.uint8)
+    assert np.array_equal(got, ref)
+    # beyond the format: saturate at +-448 (torch's cast gives NaN there); NaN stays NaN
+    for v, code in ((464.0, 0x7E), (1e30, 0x7E), (float("inf"), 0x7E), (-1e5, 0xFE),
+                    (float("-inf"), 0xFE)):
+        assert oracle.fp8_encode(v) == code
+    assert oracle.fp8_encode(float("nan")) & 0x7F == 0x7F
+
+
+def _fp8_case(rng, b, T, h, g, S, d):
+    k = rng.integers(0, 256, (b, g, S, d), dtype=np.uint8)
+    v = rng.integers(0, 256, (b, g, S, d), dtype=np.uint8)
+    for c in (k, v):  # no NaN codes in a cache
+        c[(c & 0x7F) == 0x7F] = 0x7E
+    ks = (rng.uniform(0.005, 0.05, g)).astype(np.float32)
+    vs = (rng.uniform(0.005, 0.05, g)).astype(np.float32)
+    q = bf16_bits(randn(b, T, h, d))
+    return q, k, v, ks, vs
+
+
+@pytest.mark.parametrize("T,h,g", [(1, 8, 2), (1, 4, 4), (3, 8, 1), (1, 12, 3)])
+def test_fp8_decode_matches_sdpa_on_dequantised_cache(T, h, g):
+    """fp8 decode = torch SDPA (float64) on the cache dequantised by torch's
+    e4m3 decoder times the head's scale; causal last-T rows for T > 1."""
+    rng = np.random.default_rng(T * 100 + h * 10 + g)
+    b, S, d = 3, 40, 64
+    q, k, v, ks, vs = _fp8_case(rng, b, T, h, g, S, d)
+    lens = np.array([40, T + 3, 17], np.int32)
+    out, rc = oracle.decode_attn_fp8(q, k, v, ks, vs, lens, 0.125)
+    assert rc == oracle.OK
+    kd = _torch_fp8_values(k) * ks[None, :, None, None].astype(np.float64)
+    vd = _torch_fp8_values(v) * vs[None, :, None, None].astype(np.float64)
+    qd = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).double().numpy()
+    for i in range(b):
+        ref = _causal_sdpa_last_rows(qd[i], kd[i], vd[i], int(lens[i]), 0.125, rng)
+        np.testing.assert_allclose(out[i], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_fp8_paged_matches_contiguous():
+    rng = np.random.default_rng(81)
+    b, T, h, g, S, d, P = 3, 2, 8, 2, 48, 64, 16
+    q, k, v, ks, vs = _fp8_case(rng, b, T, h, g, S, d)
+    lens = np.array([48, 18, 5], np.int32)
+    kp, vp, bt = _paged_from_contiguous(k, v, P, rng)
+    kp[np.isnan(kp.astype(np.float32))] = 0  # (uint8 pages carry no NaN marker)
+    out, rc = oracle.decode_attn_paged_fp8(q, kp, vp, ks, vs, bt, lens, 0.125)
+    assert rc == oracle.OK
+    flat, _ = oracle.decode_attn_fp8(q, k, v, ks, vs, lens, 0.125)
+    assert np.array_equal(out, flat)
+    kn, vn = bf16_bits(randn(b, T, g, d)), bf16_bits(randn(b, T, g, d))
+    assert oracle.append_kv_paged_fp8(kp, vp, kn, vn, ks, vs, bt, lens) == oracle.OK
+    assert oracle.append_kv_fp8(k, v, kn, vn, ks, vs, lens) == oracle.OK
+    for i in range(b):
+        for t in range(int(lens[i])):
+            np.testing.assert_array_equal(kp[bt[i, t // P], :, t % P], k[i, :, t])
+            np.testing.assert_array_equal(vp[bt[i, t // P], :, t % P], v[i, :, t])
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_fp8_append_quantises_with_the_head_scale(T):
+    """Codes of the appended rows = torch's e4m3 cast of (x / scale) in float32
+    (in range), at positions L-T .. L-1; every other byte untouched."""
+    rng = np.random.default_rng(90 + T)
+    b, g, S, d = 3, 2, 12, 64
+    k = rng.integers(0, 126, (b, g, S, d), dtype=np.uint8)
+    v = rng.integers(0, 126, (b, g, S, d), dtype=np.uint8)
+    ks = np.array([0.01, 0.03], np.float32)
+    vs = np.array([0.02, 0.012], np.float32)  # |x / scale| stays below 448
+    kn, vn = randn(b, T, g, d), randn(b, T, g, d)
+    lens = np.array([T, 12, 7], np.int32)
+    k2, v2 = k.copy(), v.copy()
+    assert oracle.append_kv_fp8(k2, v2, kn, vn, ks, vs, lens) == oracle.OK
+    ek, ev = k.copy(), v.copy()
+    cast = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for i in range(b):
+        for tau in range(T):
+            pos = lens[i] - T + tau
+            ek[i, :, pos] = cast((torch.from_numpy(kn[i, tau]) / torch.from_numpy(ks)[:, None]).numpy())
+            ev[i, :, pos] = cast((torch.from_numpy(vn[i, tau]) / torch.from_numpy(vs)[:, None]).numpy())
+    assert np.array_equal(k2, ek) and np.array_equal(v2, ev)
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: each mutant of the oracle's source must fail a pin above
 # ---------------------------------------------------------------------------
 
@@ -522,11 +634,17 @@ MUTANTS = {
     "token order reversed": ("int A = L - J->T + 1 + tau;", "int A = L - tau;"),
     "every token uses the first token's query": ("size_t qoff = (size_t)row * d;", "size_t qoff = ((size_t)i * J->T * J->h + hq) * d;"),
     "appended tokens reversed": ("* S + (size_t)(L - T + tau)) * row;", "* S + (size_t)(L - 1 - tau)) * row;"),
+    "fp8 exponent bias off by one": ("(1.0 + m / 8.0) * ldexp(1.0, e - 7)", "(1.0 + m / 8.0) * ldexp(1.0, e - 8)"),
+    "fp8 subnormal scale wrong": ("(m / 8.0) * ldexp(1.0, -6)", "(m / 8.0) * ldexp(1.0, -7)"),
+    "fp8 ties rounded away from zero": ("int sm = (int)nearbyintf(fr * 16.0f);", "int sm = (int)roundf(fr * 16.0f);"),
+    "key scale ignored": ("double ks = J->k_scale ? (double)J->k_scale[j] : 1.0;", "double ks = 1.0;"),
+    "value scale of the key": ("double vs = J->v_scale ? (double)J->v_scale[j] : 1.0;", "double vs = J->k_scale ? (double)J->k_scale[j] : 1.0;"),
+    "quantised by multiplying": ("return oracle_fp8_e4m3_encode(x / scale);", "return oracle_fp8_e4m3_encode(x * scale);"),
     "no normalisation": ("for (int t = 0; t < A; t++) s[t] /= Z;", ""),
-    "key and value swapped": ("elem(J->v, (size_t)kv_row(J, i, j, t) + x, J->dtype);\n        o[x]", "elem(J->k, (size_t)kv_row(J, i, j, t) + x, J->dtype);\n        o[x]"),
+    "key and value swapped": ("elem(J->v, (size_t)kv_row(J, i, j, t) + x, J->dtype));\n        o[x]", "elem(J->k, (size_t)kv_row(J, i, j, t) + x, J->dtype));\n        o[x]"),
     "page looked up one position late": ("(size_t)i * J->max_pages + t / J->page_size]", "(size_t)i * J->max_pages + (t + 1) / J->page_size]"),
     "row within the page ignored": ("J->page_size + t % J->page_size) * J->d", "J->page_size) * J->d"),
-    "query index transposed": ("elem(J->q, qoff + x, J->dtype)", "elem(J->q, (size_t)x * J->h + hq, J->dtype)"),
+    "query index transposed": ("elem(J->q, qoff + x, J->q_dtype)", "elem(J->q, (size_t)x * J->h + hq, J->q_dtype)"),
 }
 
 
@@ -550,7 +668,9 @@ def test_planted_mistakes_are_caught(tmp_path, name, monkeypatch):
     # reuse the argument declarations of the real library
     for fn in ("oracle_decode_attn", "oracle_mha_per_head", "oracle_decode_attn_paged",
                "oracle_decode_attn_multi", "oracle_decode_attn_paged_multi",
-               "oracle_append_kv_multi", "oracle_append_kv_paged_multi"):
+               "oracle_append_kv_multi", "oracle_append_kv_paged_multi",
+               "oracle_fp8_e4m3_decode", "oracle_fp8_e4m3_encode", "oracle_decode_attn_fp8",
+               "oracle_decode_attn_paged_fp8", "oracle_append_kv_fp8", "oracle_append_kv_paged_fp8"):
         getattr(mutant, fn).argtypes = getattr(real, fn).argtypes
         getattr(mutant, fn).restype = getattr(real, fn).restype
     monkeypatch.setattr(oracle, "_lib", mutant)
@@ -559,7 +679,10 @@ def test_planted_mistakes_are_caught(tmp_path, name, monkeypatch):
                 lambda: test_matches_torch_sdpa(8, 8),
                 lambda: test_paged_matches_gathered_sdpa(16, 8, 2),
                 lambda: test_multi_matches_causal_sdpa(4, 8, 2),
-                lambda: test_append_multi_writes_t_rows_per_head(False)):
+                lambda: test_append_multi_writes_t_rows_per_head(False),
+                test_fp8_decode_matches_torch, test_fp8_encode_matches_torch_in_range_and_saturates,
+                lambda: test_fp8_decode_matches_sdpa_on_dequantised_cache(1, 8, 2),
+                lambda: test_fp8_append_quantises_with_the_head_scale(1)):
         try:
             pin()
         except AssertionError:
