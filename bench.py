@@ -27,8 +27,12 @@ With --tokens T each sequence brings T query tokens per step (a draft of T
 tokens verified at once, causal mask): mqa_append_kv_multi + mqa_decode_attn_multi
 (or their paged forms); q and out are T times larger, the K/V bytes the same.
 
+With --kv-dtype fp8 the cache holds fp8 e4m3 codes with per-K/V-head scales
+(mqa_append_kv_fp8 quantises the new rows, mqa_decode_attn_fp8 reads one byte
+per element): the K/V bytes per position halve; q stays bf16.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--page-size P]
-                       [--tokens T]
+                       [--tokens T] [--kv-dtype bf16|fp8]
 """
 from __future__ import annotations
 
@@ -69,6 +73,8 @@ def parse():
                     help="paged KV cache with pages of this many rows (0: contiguous cache)")
     ap.add_argument("--tokens", type=int, default=1,
                     help="query tokens per sequence per step (causal; 1: plain decode)")
+    ap.add_argument("--kv-dtype", choices=["bf16", "fp8"], default="bf16",
+                    help="cache element type (fp8: e4m3 codes with per-K/V-head scales)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -102,18 +108,24 @@ def main() -> int:
 
     P = args.page_size
     T = args.tokens
-    if (P or T > 1) and args.kernel == "valu":
-        print("paged and multi-token calls run the matrix-core kernels only", file=sys.stderr)
+    F8 = args.kv_dtype == "fp8"
+    if (P or T > 1 or F8) and args.kernel == "valu":
+        print("paged, multi-token and fp8 calls run the matrix-core kernels only", file=sys.stderr)
+        return 2
+    if F8 and w.dtype != torch.bfloat16:
+        print("an fp8 cache takes bf16 queries: pick a bf16 workload", file=sys.stderr)
         return 2
     steps_in = []
     for r in range(reps):
-        if T > 1:
+        if F8:
+            t = W.make_fp8_step(w, dev, T=T, layer=r, page_size=P)
+        elif T > 1:
             t = W.make_multi_step(w, dev, T=T, layer=r, page_size=P)
         elif P:
             t = W.make_paged_step(w, dev, page_size=P, layer=r)
         else:
             t = W.make_step(w, dev, layer=r)
-        if P:
+        if P and "k_cache" in t:
             del t["k_cache"], t["v_cache"]  # the pages hold the cache
         steps_in.append(t)
     cap = steps_in[0]["capacity"] if P else w.S
@@ -132,9 +144,13 @@ def main() -> int:
     else:
         schedule = mqa.decode_schedule(w.b, w.h, w.g, cap, w.d, w.dtype, args.split_chunk, kernel)
     B = w.elem_bytes
-    kv_read = int(sum(2 * w.g * int(L) * w.d * B for L in lens))
+    KB = 1 if F8 else B  # bytes per cached element
+    kv_read = int(sum(2 * w.g * int(L) * w.d * KB for L in lens))
     dec_bytes = kv_read + w.b * T * w.h * w.d * B + w.b * T * w.h * w.d * 4
-    app_bytes = 2 * (2 * w.b * T * w.g * w.d * B)
+    app_bytes = 2 * (w.b * T * w.g * w.d * (B + KB))  # new rows read, codes or rows written
+    if F8:
+        dec_bytes += 2 * w.g * 4  # the scales
+        app_bytes += 2 * w.g * 4
     if P:
         dec_bytes += 4 * int(sum(-(-int(L) // P) for L in lens))
         app_bytes += 4 * w.b * T
@@ -147,7 +163,15 @@ def main() -> int:
     def layer_call(r, ev=None):
         t = steps_in[r]
         kw = dict(out=outs[r], workspace=ws, split_chunk=args.split_chunk, err_flags=err)
-        if P:
+        if F8:
+            sc = (t["k_scale"], t["v_scale"])
+            if P:
+                mqa.append_kv_paged_fp8(t["k_pages"], t["v_pages"], t["k_new"], t["v_new"], *sc,
+                                        t["block_table"], t["seq_lens"], err_flags=err)
+            else:
+                mqa.append_kv_fp8(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], *sc,
+                                  t["seq_lens"], err_flags=err)
+        elif P:
             pages = (t["k_pages"], t["v_pages"])
             append = mqa.append_kv_paged_multi if T > 1 else mqa.append_kv_paged
             append(*pages, t["k_new"], t["v_new"], t["block_table"], t["seq_lens"], err_flags=err)
@@ -156,7 +180,12 @@ def main() -> int:
             append(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], t["seq_lens"], err_flags=err)
         if ev is not None:
             ev[0].record()
-        if P:
+        if F8 and P:
+            mqa.decode_attn_paged_fp8(t["q"], t["k_pages"], t["v_pages"], *sc, t["block_table"],
+                                      t["seq_lens"], **kw)
+        elif F8:
+            mqa.decode_attn_fp8(t["q"], t["k_cache"], t["v_cache"], *sc, t["seq_lens"], **kw)
+        elif P:
             decode = mqa.decode_attn_paged_multi if T > 1 else mqa.decode_attn_paged
             decode(t["q"], *pages, t["block_table"], t["seq_lens"], **kw)
         elif T > 1:
@@ -213,7 +242,7 @@ def main() -> int:
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = dec_bytes / (dec_ms_avg * 1e-3) / 1e9
     traffic = None
-    tag = w.name + (f"-paged{P}" if P else "") + (f"-t{T}" if T > 1 else "")
+    tag = w.name + (f"-paged{P}" if P else "") + (f"-t{T}" if T > 1 else "") + ("-fp8" if F8 else "")
     tf = os.path.join(ROOT, "profiles", f"decode_{tag}_traffic.json")
     if os.path.exists(tf):
         rec = json.load(open(tf))
@@ -241,6 +270,7 @@ def main() -> int:
                    "layers": layers, "schedule": schedule,
                    "kv_layout": f"paged, {P}-row pages" if P else "contiguous",
                    "query_tokens": T,
+                   "kv_dtype": "fp8 e4m3, per-K/V-head scales" if F8 else "bf16",
                    "split_chunk": chunk if schedule != "mfma-balanced" else None,
                    "cache_copies_rotated": reps,
                    "accumulate": "fp32", "out": "fp32"},
@@ -248,7 +278,8 @@ def main() -> int:
         "flops_per_step": flops_per_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("mqa_decode_attn" + ("_paged" if P else "") + ("_multi" if T > 1 else ""))
+            "kernel": ("mqa_decode_attn" + ("_paged" if P else "")
+                       + ("_fp8" if F8 else "_multi" if T > 1 else ""))
                       + " launch, schedule " + schedule,
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
@@ -263,13 +294,13 @@ def main() -> int:
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, steps_in[0], lens, per_layer, layers,
-                                              args.cpu_seconds, P, T)
+                                              args.cpu_seconds, P, T, F8)
 
     print(json.dumps(result), flush=True)
     return 0
 
 
-def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1):
+def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1, F8=False):
     """The oracle (plain double loops) on the host cores, one layer's step."""
     import numpy as np
 
@@ -280,7 +311,22 @@ def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1
     scale = float(np.float32(1.0 / math.sqrt(w.d)))
     lens32 = lens.astype(np.int32)
     q = W.to_oracle(t["q"])
-    if page_size:
+    if F8:
+        ks, vs = t["k_scale"].cpu().numpy(), t["v_scale"].cpu().numpy()
+        if page_size:
+            kp, vp = t["k_pages"].cpu().numpy(), t["v_pages"].cpu().numpy()
+            bt = t["block_table"].cpu().numpy()
+
+            def run(n):
+                oracle.decode_attn_paged_fp8(q[:n].copy(), kp, vp, ks, vs, bt[:n].copy(),
+                                             lens32[:n], scale, nthreads=nthreads)
+        else:
+            kc, vc = t["k_cache"].cpu().numpy(), t["v_cache"].cpu().numpy()
+
+            def run(n):
+                oracle.decode_attn_fp8(q[:n].copy(), kc[:n].copy(), vc[:n].copy(), ks, vs,
+                                       lens32[:n], scale, nthreads=nthreads)
+    elif page_size:
         kp, vp = W.to_oracle(t["k_pages"]), W.to_oracle(t["v_pages"])
         bt = t["block_table"].cpu().numpy()
         paged = oracle.decode_attn_paged_multi if T > 1 else oracle.decode_attn_paged
@@ -305,7 +351,8 @@ def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1
     run(nb)
     dt = time.perf_counter() - t0
     B = w.elem_bytes
-    sample_bytes = int(sum(2 * w.g * int(L) * w.d * B for L in lens32[:nb])) + nb * T * w.h * w.d * (B + 4)
+    KB = 1 if F8 else B
+    sample_bytes = int(sum(2 * w.g * int(L) * w.d * KB for L in lens32[:nb])) + nb * T * w.h * w.d * (B + 4)
     gbs = sample_bytes / dt / 1e9
     return {
         "value": round(gbs, 4),

@@ -264,6 +264,61 @@ mqa_status mqa_decode_attn_paged_multi(const void *q, const void *k_pages,
                                        int split_chunk, int32_t *err_flags,
                                        hipStream_t stream);
 
+/*
+ * Low-precision cache: fp8 e4m3 codes with per-K/V-head scales. [GQA notes]
+ * §十 item 7 (a quantised KV cache stacks with grouping but is validated on
+ * its own); the pages fix no format, so: OCP E4M3FN codes (sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits, no infinity, S.1111.111 NaN, largest
+ * finite 448), one fp32 scale per K/V head for K (k_scale[g]) and one for V
+ * (v_scale[g]), device pointers; a cached value is code * scale[j]. The K/V
+ * bytes per position halve against bf16.
+ *
+ *   k_cache, v_cache : [b][g][S][d] uint8 codes (pages: [num_pages][g][P][d])
+ *   q                : [b][T][h][d] bf16 (T query tokens, T = 1: [b][h][d])
+ *   k_new, v_new     : [b][T][g][d] bf16
+ *   out              : [b][T][h][d] fp32
+ * Append stores e4m3(x / scale[j]) for each new element: one correctly
+ * rounded fp32 division, then the nearest code, ties to the even code,
+ * magnitudes at or above 448 saturated (finite inputs never become NaN).
+ * Decode computes the attention of the T-token section over the dequantised
+ * values (codes are decoded exactly to bf16 for the matrix cores; the K scale
+ * multiplies the scores, the V scale the outputs). Lengths, pages, the
+ * workspace (mqa_decode_multi_workspace_bytes with dt = MQA_BF16) and the
+ * errors are as above; the scale pointers must be 4-byte aligned.
+ */
+mqa_status mqa_append_kv_fp8(void *k_cache, void *v_cache, const void *k_new,
+                             const void *v_new, const float *k_scale,
+                             const float *v_scale, const int32_t *seq_lens,
+                             int b, int T, int g, int S, int d,
+                             int32_t *err_flags, hipStream_t stream);
+
+mqa_status mqa_append_kv_paged_fp8(void *k_pages, void *v_pages,
+                                   const void *k_new, const void *v_new,
+                                   const float *k_scale, const float *v_scale,
+                                   const int32_t *block_table,
+                                   const int32_t *seq_lens, int b, int T, int g,
+                                   int page_size, int max_pages, int num_pages,
+                                   int d, int32_t *err_flags, hipStream_t stream);
+
+mqa_status mqa_decode_attn_fp8(const void *q, const void *k_cache,
+                               const void *v_cache, const float *k_scale,
+                               const float *v_scale, const int32_t *seq_lens,
+                               int b, int T, int h, int g, int S, int d,
+                               float scale, float *out, void *workspace,
+                               size_t workspace_bytes, int split_chunk,
+                               int32_t *err_flags, hipStream_t stream);
+
+mqa_status mqa_decode_attn_paged_fp8(const void *q, const void *k_pages,
+                                     const void *v_pages, const float *k_scale,
+                                     const float *v_scale,
+                                     const int32_t *block_table,
+                                     const int32_t *seq_lens, int b, int T,
+                                     int h, int g, int page_size, int max_pages,
+                                     int num_pages, int d, float scale,
+                                     float *out, void *workspace,
+                                     size_t workspace_bytes, int split_chunk,
+                                     int32_t *err_flags, hipStream_t stream);
+
 /* Static text for a status code (never NULL). */
 const char *mqa_status_string(mqa_status s);
 

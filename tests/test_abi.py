@@ -228,3 +228,42 @@ def test_multi_workspace_and_schedule():
     n4 = mqa.decode_multi_workspace_bytes(8, 4, 32, 1, 1024, 128, mqa.BF16, 256)
     assert n1 == 8 * 32 * 4 * (128 * 4 + 8)  # partials (o, m, l) of 4 partitions per row
     assert n4 == 4 * n1                        # one set per query token
+
+
+def fp8_decode(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, lens=FAKE, b=2, T=1, h=8, g=2, S=64, d=128,
+             scale=0.088, out=FAKE, ws=FAKE, ws_bytes=1 << 30, chunk=0)
+    a.update(kw)
+    return mqa.lib().mqa_decode_attn_fp8(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["lens"], a["b"],
+                                         a["T"], a["h"], a["g"], a["S"], a["d"],
+                                         ctypes.c_float(a["scale"]), a["out"], a["ws"], a["ws_bytes"],
+                                         a["chunk"], None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=None), mqa.ERR_NULL),
+    (dict(vs=None), mqa.ERR_NULL),
+    (dict(T=0), mqa.ERR_SHAPE),
+    (dict(T=65), mqa.ERR_SHAPE),
+    (dict(d=96), mqa.ERR_UNSUPPORTED),
+    (dict(h=6, g=4), mqa.ERR_SHAPE),
+    (dict(k=MISALIGNED), mqa.ERR_ALIGN),
+    (dict(ks=ctypes.c_void_p(0x10002)), mqa.ERR_ALIGN),
+    (dict(ws_bytes=16), mqa.ERR_WORKSPACE),
+])
+def test_fp8_decode_rejects_bad_arguments_before_launch(kw, status):
+    assert fp8_decode(**kw) == status
+
+
+def test_fp8_append_rejects_bad_arguments_before_launch():
+    L = mqa.lib()
+    assert L.mqa_append_kv_fp8(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 2, 1, 2, 64, 128, None,
+                               None) == mqa.ERR_NULL
+    assert L.mqa_append_kv_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 0, 2, 64, 128, None,
+                               None) == mqa.ERR_SHAPE
+    assert L.mqa_append_kv_fp8(FAKE, MISALIGNED, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1, 2, 64, 128,
+                               None, None) == mqa.ERR_ALIGN
+    assert L.mqa_append_kv_paged_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 2, 1, 2, 16, 4,
+                                     8, 128, None, None) == mqa.ERR_NULL
+    assert L.mqa_append_kv_paged_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1, 2, 16, 0,
+                                     8, 128, None, None) == mqa.ERR_SHAPE

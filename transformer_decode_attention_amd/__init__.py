@@ -22,6 +22,9 @@ Entry points (same names as the C ABI, without the ``mqa_`` prefix):
   decode_attn_paged_multi(q, k_pages, v_pages, block_table, seq_lens, ...) -> out
   decode_multi_workspace_bytes(b, T, h, g, S, d, dtype, split_chunk=0)
   decode_multi_schedule(b, T, h, g, S, d, dtype, split_chunk=0)
+  append_kv_fp8 / decode_attn_fp8 / append_kv_paged_fp8 / decode_attn_paged_fp8:
+      the same over a cache of fp8 e4m3 codes (uint8 or float8_e4m3fn tensors)
+      with per-K/V-head scales k_scale, v_scale (float32 [g]); q and new rows bf16
   kv_bytes(layers, g, S, d, dtype_bytes)
   status_string(status)
 
@@ -41,7 +44,8 @@ __all__ = [
     "decode_schedule", "kv_bytes", "status_string", "MQAError", "LIB_PATH", "DEVERR_SEQLEN",
     "DEVERR_PAGE", "append_kv_paged", "decode_attn_paged", "decode_paged_workspace_bytes",
     "append_kv_multi", "decode_attn_multi", "append_kv_paged_multi", "decode_attn_paged_multi",
-    "decode_multi_workspace_bytes", "decode_multi_schedule",
+    "decode_multi_workspace_bytes", "decode_multi_schedule", "append_kv_fp8", "decode_attn_fp8",
+    "append_kv_paged_fp8", "decode_attn_paged_fp8",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa_decode.so")
@@ -59,7 +63,8 @@ EXPORTS = (
     "mqa_kv_bytes", "mqa_append_kv_paged", "mqa_decode_paged_workspace_bytes",
     "mqa_decode_attn_paged", "mqa_append_kv_multi", "mqa_decode_multi_workspace_bytes",
     "mqa_decode_multi_schedule", "mqa_decode_attn_multi", "mqa_append_kv_paged_multi",
-    "mqa_decode_attn_paged_multi",
+    "mqa_decode_attn_paged_multi", "mqa_append_kv_fp8", "mqa_append_kv_paged_fp8",
+    "mqa_decode_attn_fp8", "mqa_decode_attn_paged_fp8",
 )
 SCHEDULES = {0: "valu-partitions", 1: "mfma-partitions", 2: "mfma-balanced"}
 
@@ -119,6 +124,18 @@ def _load() -> ctypes.CDLL:
                                               i32, i32, i32, ctypes.c_float, vp, vp,
                                               ctypes.c_size_t, i32, vp, vp]
     L.mqa_decode_attn_paged_multi.restype = i32
+    L.mqa_append_kv_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    L.mqa_append_kv_fp8.restype = i32
+    L.mqa_append_kv_paged_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                          i32, i32, vp, vp]
+    L.mqa_append_kv_paged_fp8.restype = i32
+    L.mqa_decode_attn_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                      ctypes.c_float, vp, vp, ctypes.c_size_t, i32, vp, vp]
+    L.mqa_decode_attn_fp8.restype = i32
+    L.mqa_decode_attn_paged_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                            i32, i32, i32, ctypes.c_float, vp, vp, ctypes.c_size_t,
+                                            i32, vp, vp]
+    L.mqa_decode_attn_paged_fp8.restype = i32
     return L
 
 
@@ -469,3 +486,107 @@ def decode_attn_paged_multi(q: torch.Tensor, k_pages: torch.Tensor, v_pages: tor
     if st != OK:
         raise MQAError(st, "mqa_decode_attn_paged_multi")
     return out
+
+
+# ---- fp8 e4m3 cache with per-K/V-head scales (q and new rows bf16) ----
+
+_FP8_TYPES = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
+
+
+def _check_fp8(k, v, k_scale, v_scale, g):
+    for n, t in (("k cache", k), ("v cache", v), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _dev(t, n)
+    if k.dtype not in _FP8_TYPES or v.dtype != k.dtype:
+        raise TypeError("an fp8 cache is uint8 or float8_e4m3fn codes")
+    for n, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if sc.dtype != torch.float32 or sc.shape != (g,) or not sc.is_contiguous():
+            raise ValueError(f"{n} must be contiguous float32 [g]")
+
+
+def _rows4(x, name):
+    _dev(x, name)
+    if x.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16")
+    return x if x.dim() == 4 else x.unsqueeze(1)
+
+
+def append_kv_fp8(k_cache, v_cache, k_new, v_new, k_scale, v_scale, seq_lens, err_flags=None):
+    """k_new/v_new bf16 [b, g, d] or [b, T, g, d] -> e4m3(x / scale[j]) at positions L-T .. L-1."""
+    b, g, S, d = k_cache.shape
+    _check_fp8(k_cache, v_cache, k_scale, v_scale, g)
+    kn, vn = _rows4(k_new, "k_new"), _rows4(v_new, "v_new")
+    if kn.shape[0] != b or kn.shape[2:] != (g, d) or vn.shape != kn.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("cache [b, g, S, d] and new rows [b, (T,) g, d] must match")
+    _dev(seq_lens, "seq_lens")
+    st = lib().mqa_append_kv_fp8(_ptr(k_cache), _ptr(v_cache), _ptr(kn), _ptr(vn), _ptr(k_scale),
+                                 _ptr(v_scale), _ptr(seq_lens), b, kn.shape[1], g, S, d,
+                                 _ptr(err_flags), _stream(k_cache.device))
+    if st != OK:
+        raise MQAError(st, "mqa_append_kv_fp8")
+
+
+def append_kv_paged_fp8(k_pages, v_pages, k_new, v_new, k_scale, v_scale, block_table, seq_lens,
+                        err_flags=None):
+    """append_kv_fp8 into pages [num_pages, g, page_size, d] of codes."""
+    num_pages, g, P, d = k_pages.shape
+    _check_fp8(k_pages, v_pages, k_scale, v_scale, g)
+    kn, vn = _rows4(k_new, "k_new"), _rows4(v_new, "v_new")
+    for n, t in (("block_table", block_table), ("seq_lens", seq_lens)):
+        _dev(t, n)
+    b, max_pages = block_table.shape
+    st = lib().mqa_append_kv_paged_fp8(_ptr(k_pages), _ptr(v_pages), _ptr(kn), _ptr(vn),
+                                       _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+                                       _ptr(seq_lens), b, kn.shape[1], g, P, max_pages, num_pages,
+                                       d, _ptr(err_flags), _stream(k_pages.device))
+    if st != OK:
+        raise MQAError(st, "mqa_append_kv_paged_fp8")
+
+
+def decode_attn_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale=None, out=None,
+                    workspace=None, split_chunk: int = 0, err_flags=None):
+    """Decode over an fp8 cache -> out fp32 shaped like q ([b, h, d] or [b, T, h, d])."""
+    b, g, S, d = k_cache.shape
+    _check_fp8(k_cache, v_cache, k_scale, v_scale, g)
+    q4 = _rows4(q, "q")
+    _dev(seq_lens, "seq_lens")
+    T, h = q4.shape[1], q4.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o4 = None if out is None else (out if out.dim() == 4 else out.unsqueeze(1))
+    o4, workspace = _multi_out(q4, o4, workspace,
+                               decode_multi_workspace_bytes(b, T, h, g, S, d, BF16, split_chunk))
+    st = lib().mqa_decode_attn_fp8(_ptr(q4), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                   _ptr(v_scale), _ptr(seq_lens), b, T, h, g, S, d,
+                                   ctypes.c_float(scale), _ptr(o4), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), split_chunk,
+                                   _ptr(err_flags), _stream(q.device))
+    if st != OK:
+        raise MQAError(st, "mqa_decode_attn_fp8")
+    return o4 if q.dim() == 4 else o4[:, 0]
+
+
+def decode_attn_paged_fp8(q, k_pages, v_pages, k_scale, v_scale, block_table, seq_lens, scale=None,
+                          out=None, workspace=None, split_chunk: int = 0, err_flags=None):
+    """decode_attn_fp8 over pages [num_pages, g, page_size, d] of codes."""
+    num_pages, g, P, d = k_pages.shape
+    _check_fp8(k_pages, v_pages, k_scale, v_scale, g)
+    q4 = _rows4(q, "q")
+    for n, t in (("block_table", block_table), ("seq_lens", seq_lens)):
+        _dev(t, n)
+    b, max_pages = block_table.shape
+    T, h = q4.shape[1], q4.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o4 = None if out is None else (out if out.dim() == 4 else out.unsqueeze(1))
+    o4, workspace = _multi_out(q4, o4, workspace,
+                               decode_multi_workspace_bytes(b, T, h, g, P * max_pages, d, BF16,
+                                                            split_chunk))
+    st = lib().mqa_decode_attn_paged_fp8(_ptr(q4), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
+                                         _ptr(v_scale), _ptr(block_table), _ptr(seq_lens), b, T, h,
+                                         g, P, max_pages, num_pages, d, ctypes.c_float(scale),
+                                         _ptr(o4), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), split_chunk,
+                                         _ptr(err_flags), _stream(q.device))
+    if st != OK:
+        raise MQAError(st, "mqa_decode_attn_paged_fp8")
+    return o4 if q.dim() == 4 else o4[:, 0]

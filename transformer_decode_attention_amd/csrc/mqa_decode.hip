@@ -209,6 +209,80 @@ __global__ void append_kv_paged_kernel(uint8_t *__restrict__ kp, uint8_t *__rest
     *(uint4 *)(dp + dst) = *(const uint4 *)(s + src);
 }
 
+// fp8 e4m3 (OCP E4M3FN: bias 7, 3 mantissa bits, no infinity, largest
+// finite 448) code of f: the nearest value, ties to the even code;
+// magnitudes at or above 448 saturate to +-448, so a finite value never
+// becomes NaN; NaN stays NaN.
+__device__ __forceinline__ uint32_t e4m3_code(float f) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, f);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return sign | 0x7fu;   // NaN
+    if (a >= 0x43e00000u) return sign | 0x7eu;  // >= 448, infinity included
+    if (a < 0x3c800000u)                        // below 2^-6: multiples of 2^-9 (code 8 = 2^-6)
+        return sign | (uint32_t)__builtin_rintf(__builtin_bit_cast(float, a) * 512.0f);
+    // normal: exponent re-biased (127 -> 7), 3 of 23 mantissa bits kept,
+    // nearest-even on the 20 dropped (a carry moves to the next exponent)
+    uint32_t code = (((a >> 23) - 120u) << 3) | ((a >> 20) & 7u);
+    const uint32_t rem = a & 0xfffffu;
+    if (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) code += 1;
+    return sign | code;
+}
+
+// Quantised append into an fp8 cache: token tau of the new rows (bf16
+// [b][T][g][d]) goes to position L - T + tau as e4m3(x / scale[j]), one
+// correctly rounded fp32 division per element ([GQA notes] §十 item 7: a
+// quantised KV cache). Contiguous cache [b][g][S][d] (bt NULL) or pages
+// [num_pages][g][P][d] through block table bt (S then the page size P).
+// Thread t converts one 8-element chunk.
+__global__ void append_kv_fp8_kernel(uint8_t *__restrict__ kc, uint8_t *__restrict__ vc,
+                                     const uint16_t *__restrict__ kn,
+                                     const uint16_t *__restrict__ vn,
+                                     const float *__restrict__ k_scale,
+                                     const float *__restrict__ v_scale,
+                                     const int32_t *__restrict__ bt,
+                                     const int32_t *__restrict__ seq_lens, int b, int T, int g,
+                                     int S, int max_pages, int num_pages, int d,
+                                     int32_t *__restrict__ err) {
+    const int cpr = d >> 3;
+    const long long total = 2ll * b * T * g * cpr;
+    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= total) return;
+    const AppendSlot a(t, cpr, b, T, g);
+    const int L = seq_lens[a.i];
+    const int cap = bt ? S * max_pages : S;
+    if (L < T || L > cap) {
+        if (a.first() && err) atomicOr(err, MQA_DEVERR_SEQLEN);
+        return;
+    }
+    const int pos = L - T + a.tau;
+    size_t row;
+    if (bt) {
+        const int page = bt[(size_t)a.i * max_pages + pos / S];
+        if (page < 0 || page >= num_pages) {
+            if (a.c == 0 && a.j == 0 && a.which == 0 && err) atomicOr(err, MQA_DEVERR_PAGE);
+            return;
+        }
+        row = ((size_t)page * g + a.j) * S + pos % S;
+    } else {
+        row = ((size_t)a.i * g + a.j) * S + pos;
+    }
+    const uint16_t *src = (a.which ? vn : kn) + (((size_t)a.i * T + a.tau) * g + a.j) * d + 8 * a.c;
+    const float sc = (a.which ? v_scale : k_scale)[a.j];
+    const u32x4_t in = *(const u32x4_t *)src;  // 8 bf16
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const uint32_t bits = (in[e >> 1] >> (16 * (e & 1))) << 16;  // bf16 -> fp32, exact
+        const uint32_t code = e4m3_code(__fdiv_rn(__builtin_bit_cast(float, bits), sc));
+        if (e < 4)
+            lo |= code << (8 * e);
+        else
+            hi |= code << (8 * (e - 4));
+    }
+    *(uint2 *)((a.which ? vc : kc) + row * d + 8 * a.c) = make_uint2(lo, hi);
+}
+
 // ---------------------------------------------------------------------------
 // split kernel: one wave per query head in the score phase, one lane per row
 // ---------------------------------------------------------------------------
@@ -574,6 +648,18 @@ struct MfmaCfg {
     static_assert(NW * HB * (D + 2) * 4 <= NW * VBUF, "merge scratch must fit");
 };
 
+// Layout of one cache row in memory: bf16 (2 bytes per element) or fp8 e4m3
+// codes (1 byte). Each lane loads K 16 bytes at a time (one MFMA k-step of 8
+// elements in bf16, two in fp8) and V 16 bytes per wave-wide load.
+template <int D, bool F8>
+struct KvFmt {
+    static constexpr int RB = F8 ? D : 2 * D;               // bytes per cache row
+    static constexpr int KLOADS = RB / 64;                  // K loads per lane per 16-row half
+    static constexpr int VCPR = RB / 16;                    // 16-byte chunks per row
+    static constexpr int VRPI = 64 / VCPR;                  // rows per wave-wide V load
+    static constexpr int VLOADS = MfmaCfg<D>::STEP / VRPI;  // V loads per lane per step
+};
+
 // The lane index as a value the compiler must recompute where it is used:
 // addresses derived from it in rarely taken code are then not hoisted out of
 // the hot loop (where they would hold registers for its whole length).
@@ -602,21 +688,50 @@ struct MfmaState {
     }
 };
 
-// Q^T operand of query head `hq`: lane holds Q[hq][32k + 8qd .. +8].
-template <int D>
+// Q^T operand of query head `hq`: for k-step k lane holds Q[hq][d0 .. d0+8],
+// d0 = 32k + 8qd, in the order the K operand's lanes hold K's elements. With
+// an fp8 cache a lane's 16-byte K load holds 16 elements, which feed two
+// k-steps: then d0 = 16qd + 8(k%2) + 64(k/2) (any order of d gives the same
+// dot product, as long as Q and K agree).
+template <int D, bool F8 = false>
 __device__ __forceinline__ void load_q_operand(const uint16_t *__restrict__ q, size_t qrow,
                                                int qd, bf16x8_t (&qop)[MfmaCfg<D>::KSTEPS]) {
 #pragma unroll
-    for (int k = 0; k < MfmaCfg<D>::KSTEPS; k++)
-        qop[k] = *(const bf16x8_t *)(q + qrow * D + 32 * k + 8 * qd);
+    for (int k = 0; k < MfmaCfg<D>::KSTEPS; k++) {
+        const int d0 = F8 ? 16 * qd + 8 * (k & 1) + 64 * (k >> 1) : 32 * k + 8 * qd;
+        qop[k] = *(const bf16x8_t *)(q + qrow * D + d0);
+    }
 }
 
-// K and V of one 32-position step as loaded: K straight into the A operand
-// of the score MFMA, V row-contiguous (16 bytes per lane).
-template <int D>
+// 16 fp8 e4m3 codes (4 dwords, element e in byte e) -> elements 0..7 and
+// 8..15 as bf16. Exact: every e4m3 value is a bf16 value, so the fp32 the
+// conversion instruction returns (it decodes OCP e4m3, measured for all 256
+// codes on the device) has nothing in its low 16 bits.
+__device__ __forceinline__ void fp8x16_to_bf16(const u32x4_t &w, bf16x8_t &lo, bf16x8_t &hi) {
+    uint32_t o[8];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);  // bytes 0, 1
+        const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);   // bytes 2, 3
+        // (elements copied out first: a bit cast of a vector element
+        // expression reads element 0 with this compiler)
+        const float a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
+        o[2 * k] = (__builtin_bit_cast(uint32_t, a1) & 0xffff0000u) |
+                   (__builtin_bit_cast(uint32_t, a0) >> 16);
+        o[2 * k + 1] = (__builtin_bit_cast(uint32_t, b1) & 0xffff0000u) |
+                       (__builtin_bit_cast(uint32_t, b0) >> 16);
+    }
+    lo = __builtin_bit_cast(bf16x8_t, (u32x4_t){o[0], o[1], o[2], o[3]});
+    hi = __builtin_bit_cast(bf16x8_t, (u32x4_t){o[4], o[5], o[6], o[7]});
+}
+
+// K and V of one 32-position step as loaded: K in the lanes of the A operand
+// of the score MFMA (bf16: the operand itself), V row-contiguous (16 bytes
+// per lane).
+template <int D, bool F8 = false>
 struct StepData {
-    bf16x8_t kop[2][MfmaCfg<D>::KSTEPS];
-    u32x4_t vld[MfmaCfg<D>::VLOADS];
+    u32x4_t kraw[2][KvFmt<D, F8>::KLOADS];  // per 16-row half
+    u32x4_t vld[KvFmt<D, F8>::VLOADS];
 };
 
 // Where the K/V rows of one 32-position step come from: for each 16-row half,
@@ -630,14 +745,15 @@ struct StepSrc {
 
 // Contiguous cache [b][g][S][d]: both halves in the head's S rows, the
 // descriptors' extent the sequence length.
-template <int D>
+template <int D, bool F8 = false>
 struct ContigKV {
     static constexpr bool kPaged = false;
+    static constexpr bool kF8 = F8;
     static constexpr int kStage = 1;
     const uint8_t *k, *v;
     int g, S;
     __device__ __forceinline__ StepSrc step(int i, int j, int L, int t0, bool &) const {
-        constexpr uint32_t RB = MfmaCfg<D>::ROW_BYTES;
+        constexpr uint32_t RB = KvFmt<D, F8>::RB;
         const size_t head = ((size_t)i * g + j) * (size_t)S * RB;
         const rsrc_t kr = make_rsrc(k + head, (uint32_t)L * RB);
         const rsrc_t vr = make_rsrc(v + head, (uint32_t)L * RB);
@@ -653,12 +769,14 @@ struct ContigKV {
 // t % P of page block_table[i][t / P] ([MQA blog] §3.3). P is a multiple of
 // 16, so each half of a step lies in one page. A referenced page id outside
 // [0, num_pages) reads nothing and sets `bad`. The kernels stage the page ids
-// of their steps in LDS (up to kStage entries, two per step) before the
-// first step, so that no table lookup sits between a claim and its loads.
-template <int D>
+// of their steps in LDS (up to kStage entries, two per step; further steps
+// look the table up) before the first step, so that no table lookup sits
+// between a claim and its loads.
+template <int D, bool F8 = false>
 struct PagedKV {
     static constexpr bool kPaged = true;
-    static constexpr int kStage = 4096;
+    static constexpr bool kF8 = F8;
+    static constexpr int kStage = F8 ? 1024 : 4096;  // (fp8: eight waves' buffers share the LDS)
     const uint8_t *k, *v;
     const int32_t *bt;
     int g, P, max_pages, num_pages;
@@ -669,7 +787,7 @@ struct PagedKV {
     // the step at t0 of K/V head j, its halves in pages id0 and id1
     __device__ __forceinline__ StepSrc step_ids(int j, int L, int t0, int id0, int id1,
                                                 bool &bad) const {
-        constexpr uint32_t RB = MfmaCfg<D>::ROW_BYTES;
+        constexpr uint32_t RB = KvFmt<D, F8>::RB;
         StepSrc s;
 #pragma unroll
         for (int hf = 0; hf < 2; hf++) {
@@ -717,24 +835,22 @@ __device__ __forceinline__ void stage_page_ids(const KV &kv, int *pg, int n, Whe
 }
 
 // Issue the loads of one step.
-template <int D>
-__device__ __forceinline__ void load_step(const StepSrc &src, int lane, StepData<D> &sd) {
-    using C = MfmaCfg<D>;
+template <int D, bool F8 = false>
+__device__ __forceinline__ void load_step(const StepSrc &src, int lane, StepData<D, F8> &sd) {
+    using F = KvFmt<D, F8>;
     const int r = lane & 15, qd = lane >> 4;
-    const int vl_row = lane / C::CPR, vl_chunk = lane % C::CPR;
-    const uint32_t kl = r * C::ROW_BYTES + 16 * qd;
-    const uint32_t vl = vl_row * C::ROW_BYTES + 16 * vl_chunk;
+    const int vl_row = lane / F::VCPR, vl_chunk = lane % F::VCPR;
+    const uint32_t kl = r * F::RB + 16 * qd;
+    const uint32_t vl = vl_row * F::RB + 16 * vl_chunk;
 #pragma unroll
     for (int pb = 0; pb < 2; pb++)
 #pragma unroll
-        for (int k = 0; k < C::KSTEPS; k++)
-            sd.kop[pb][k] = __builtin_bit_cast(
-                bf16x8_t, buffer_stream16(src.k[pb], src.off[pb] + kl + 64 * k));
+        for (int k = 0; k < F::KLOADS; k++)
+            sd.kraw[pb][k] = buffer_stream16(src.k[pb], src.off[pb] + kl + 64 * k);
 #pragma unroll
-    for (int ii = 0; ii < C::VLOADS; ii++) {
-        constexpr int H = 16 / C::RPI;  // V loads per half
-        sd.vld[ii] = buffer_stream16(src.v[ii / H],
-                                     src.off[ii / H] + vl + (ii % H) * C::RPI * C::ROW_BYTES);
+    for (int ii = 0; ii < F::VLOADS; ii++) {
+        constexpr int H = 16 / F::VRPI;  // V loads per half
+        sd.vld[ii] = buffer_stream16(src.v[ii / H], src.off[ii / H] + vl + (ii % H) * F::VRPI * F::RB);
     }
 }
 
@@ -756,18 +872,29 @@ __device__ __forceinline__ void poison_state(MfmaState<D> (&st)[NHB], int32_t *e
 // t_end); t_lo is the smallest t_row of the wave. A row can then have no
 // position in a step, so exponentials of masked scores are set to 0 (not
 // exp2(-inf - -inf)).
-template <int D, bool MULTI, int NHB>
-__device__ __forceinline__ void compute_step(const StepData<D> &sd, int t0, int t_end, int t_lo,
+template <int D, bool MULTI, int NHB, bool F8 = false>
+__device__ __forceinline__ void compute_step(const StepData<D, F8> &sd, int t0, int t_end, int t_lo,
                                              const int (&t_row)[NHB],
                                              const bf16x8_t (&qop)[NHB][MfmaCfg<D>::KSTEPS],
                                              MfmaState<D> (&st)[NHB], uint8_t *vb, int lane,
                                              float qk_scale_log2) {
     using C = MfmaCfg<D>;
+    using F = KvFmt<D, F8>;
     const int r = lane & 15, qd = lane >> 4;
-    const int vl_row = lane / C::CPR, vl_chunk = lane % C::CPR;
+    const int vl_row = lane / F::VCPR, vl_chunk = lane % F::VCPR;
     const bool tail = t0 + C::STEP > (MULTI ? t_lo : t_end);
-    const auto &kop = sd.kop;
     const auto &vld = sd.vld;
+    // K operands (fp8: decoded to bf16 here; the scales are applied outside)
+    bf16x8_t kop[2][C::KSTEPS];
+#pragma unroll
+    for (int pb = 0; pb < 2; pb++)
+#pragma unroll
+        for (int k = 0; k < F::KLOADS; k++) {
+            if constexpr (F8)
+                fp8x16_to_bf16(sd.kraw[pb][k], kop[pb][2 * k], kop[pb][2 * k + 1]);
+            else
+                kop[pb][k] = __builtin_bit_cast(bf16x8_t, sd.kraw[pb][k]);
+        }
 
     // ---- scores ----
     float s2[NHB][8];
@@ -791,10 +918,18 @@ __device__ __forceinline__ void compute_step(const StepData<D> &sd, int t0, int 
 
     // ---- V into the staging buffer (rows past the end zeroed: they may be NaN) ----
 #pragma unroll
-    for (int ii = 0; ii < C::VLOADS; ii++) {
+    for (int ii = 0; ii < F::VLOADS; ii++) {
+        const int row = ii * F::VRPI + vl_row;
         u32x4_t v = vld[ii];
-        if (tail && t0 + ii * C::RPI + vl_row >= t_end) v = u32x4_t{0u, 0u, 0u, 0u};
-        *(u32x4_t *)(vb + (ii * C::RPI + vl_row) * C::VSTRIDE + 16 * vl_chunk) = v;
+        if (tail && t0 + row >= t_end) v = u32x4_t{0u, 0u, 0u, 0u};
+        if constexpr (F8) {  // 16 codes -> 16 bf16 (32 bytes) of the row
+            bf16x8_t lo, hi;
+            fp8x16_to_bf16(v, lo, hi);
+            *(bf16x8_t *)(vb + row * C::VSTRIDE + 32 * vl_chunk) = lo;
+            *(bf16x8_t *)(vb + row * C::VSTRIDE + 32 * vl_chunk + 16) = hi;
+        } else {
+            *(u32x4_t *)(vb + row * C::VSTRIDE + 16 * vl_chunk) = v;
+        }
     }
 
     // ---- online softmax for head r of each block ----
@@ -890,7 +1025,7 @@ struct QRows {
 // one computes (NBUF register sets in rotation; the loop is unrolled by NBUF
 // so that each set keeps fixed registers). Past the last step a prefetch
 // asks for nothing.
-template <int D, bool MULTI, int NHB, int NBUF, class Src>
+template <int D, bool MULTI, int NHB, int NBUF, bool F8, class Src>
 __device__ __forceinline__ void run_steps(const Src &src, const StepSrc &nothing, int s_begin,
                                           int s_end, int stride, int t_end, int t_lo,
                                           const int (&t_row)[NHB],
@@ -901,13 +1036,13 @@ __device__ __forceinline__ void run_steps(const Src &src, const StepSrc &nothing
     static_assert(NBUF >= 2, "at least one step in flight");
     int stp = s_begin;
     if (stp >= s_end) return;
-    StepData<D> buf[NBUF];
+    StepData<D, F8> buf[NBUF];
     bool bad[NBUF];
 #pragma unroll
     for (int k = 0; k < NBUF - 1; k++) {
         const int sk = stp + k * stride;
         bad[k] = false;
-        load_step<D>(sk < s_end ? src(sk, bad[k]) : nothing, lane, buf[k]);
+        load_step<D, F8>(sk < s_end ? src(sk, bad[k]) : nothing, lane, buf[k]);
     }
     while (true) {
 #pragma unroll
@@ -916,9 +1051,9 @@ __device__ __forceinline__ void run_steps(const Src &src, const StepSrc &nothing
             const int kn = (k + NBUF - 1) % NBUF;
             const int sn = stp + (NBUF - 1) * stride;
             bad[kn] = false;
-            load_step<D>(sn < s_end ? src(sn, bad[kn]) : nothing, lane, buf[kn]);
-            compute_step<D, MULTI, NHB>(buf[k], stp * C::STEP, t_end, t_lo, t_row, qop, st, vb,
-                                        lane, qk_scale_log2);
+            load_step<D, F8>(sn < s_end ? src(sn, bad[kn]) : nothing, lane, buf[kn]);
+            compute_step<D, MULTI, NHB, F8>(buf[k], stp * C::STEP, t_end, t_lo, t_row, qop, st,
+                                            vb, lane, qk_scale_log2);
             if (bad[k]) poison_state<D>(st, err, lane);
             stp += stride;
             if (stp >= s_end) return;
@@ -970,9 +1105,11 @@ template <int D, class KV, bool MULTI, int NHB>
 __global__ void __launch_bounds__(256)
 split_mfma_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__restrict__ seq_lens,
                   const QRows<MULTI> qr, int g, int S, int R, int ngroups, int chunk, int nsplit,
-                  float qk_scale_log2, float *__restrict__ part_o, float2 *__restrict__ part_ml,
-                  int32_t *__restrict__ err) {
+                  float qk_base, const float *__restrict__ k_scale,
+                  const float *__restrict__ v_scale, float *__restrict__ part_o,
+                  float2 *__restrict__ part_ml, int32_t *__restrict__ err) {
     using C = MfmaCfg<D>;
+    constexpr bool F8 = KV::kF8;
     __shared__ __attribute__((aligned(16))) uint8_t vbuf[C::NW][C::VBUF];
     __shared__ int pg[KV::kStage];  // paged: the page ids of the partition's steps
 
@@ -997,7 +1134,7 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
 #pragma unroll
     for (int b = 0; b < NHB; b++) {
         const int rho = min((hg * NHB + b) * C::HB + r, R - 1);
-        load_q_operand<D>(q, qr.row(i, j, rho), qd, qop[b]);
+        load_q_operand<D, F8>(q, qr.row(i, j, rho), qd, qop[b]);
         t_row[b] = min(t_end, L - qr.T + 1 + qr.tok(rho));
     }
     const int t_lo = min(t_end, L - qr.T + 1);  // the earliest of the wave
@@ -1035,8 +1172,11 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
     MfmaState<D> st[NHB];
 #pragma unroll
     for (int b = 0; b < NHB; b++) st[b].reset();
-    run_steps<D, MULTI, NHB, 2>(src, kv.none(), s0 + w, s0 + nsteps, C::NW, t_end, t_lo, t_row,
-                                qop, st, vbuf[w], lane, qk_scale_log2, err);
+    // an fp8 cache: scores scale by the head's K scale, outputs by its V scale
+    const float qk_scale_log2 = F8 ? qk_base * k_scale[j] : qk_base;
+    const float vsc = F8 ? v_scale[j] : 1.f;
+    run_steps<D, MULTI, NHB, 2, F8>(src, kv.none(), s0 + w, s0 + nsteps, C::NW, t_end, t_lo, t_row,
+                                    qop, st, vbuf[w], lane, qk_scale_log2, err);
 
     // merge the waves' states block by block through the staging buffers
     float *mrg = (float *)&vbuf[0][0];
@@ -1053,7 +1193,7 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
             float M, l;
             const float o = merge_waves<D>(mrg, mls, 0, C::NW, hh, x, M, l);
             const size_t hrow = ((size_t)i * g + j) * R + hb * C::HB + hh;
-            part_o[(hrow * nsplit + s) * D + x] = o;
+            part_o[(hrow * nsplit + s) * D + x] = o * vsc;
             if (x == 0) part_ml[hrow * nsplit + s] = make_float2(M, l);
         }
     }
@@ -1188,11 +1328,13 @@ __global__ void __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(1, 8)))
 streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
                     const int32_t *__restrict__ seq_lens, int b, const QRows<MULTI> qr,
-                    int g, int S, int R, int ngroups, float qk_scale_log2,
+                    int g, int S, int R, int ngroups, float qk_base,
+                    const float *__restrict__ k_scale, const float *__restrict__ v_scale,
                     float *__restrict__ out, float *__restrict__ part_o,
                     float2 *__restrict__ part_ml, int4 *__restrict__ cut_desc,
                     int32_t *__restrict__ err) {
     using C = MfmaCfg<D>;
+    constexpr bool F8 = KV::kF8;  // fp8 cache: per-K/V-head scales on scores and outputs
     static_assert(NW == 4 || NW == 8, "waves per work-group (the segment records hold 8 bits)");
     __shared__ __attribute__((aligned(16))) uint8_t vbuf[NW][C::VBUF];
     __shared__ f32x4_t slot_o[NW][NHB][C::NB][64];  // a wave's acc, lane-native order
@@ -1326,7 +1468,8 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
     auto load_q = [&](int i_, int j_, bf16x8_t (&qo)[NHB][C::KSTEPS]) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < NHB; k++)
-            load_q_operand<D>(q, qr.row(i_, j_, min((hb * NHB + k) * C::HB + r, R - 1)), qd, qo[k]);
+            load_q_operand<D, F8>(q, qr.row(i_, j_, min((hb * NHB + k) * C::HB + r, R - 1)), qd,
+                                  qo[k]);
     };
     // where the rows of flat step tt (of unit (i_, j_), first step u0_) are
     auto src_of = [&](int i_, int j_, int L_, int u0_, int tt, bool &bad)
@@ -1354,8 +1497,10 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
     int ci = i_first, cL = 0, cn = 0, cj = 0, cu0 = 0;
     locate(t, ci, cL, cn, cj, cu0);
     bool bad_now = false;  // the current step read an invalid page
-    StepData<D> A, B;
-    load_step<D>(src_of(ci, cj, cL, cu0, t, bad_now), lane, A);
+    StepData<D, F8> A, B;
+    load_step<D, F8>(src_of(ci, cj, cL, cu0, t, bad_now), lane, A);
+    float cqs = F8 ? qk_base * k_scale[cj] : qk_base;  // the unit's score factor
+    float cvs = F8 ? v_scale[cj] : 1.f;                // and output factor
     bf16x8_t qop[NHB][C::KSTEPS];
     load_q(ci, cj, qop);
     MfmaState<D> st[NHB];
@@ -1447,7 +1592,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
                     const size_t prow = ((size_t)wg * 2 + slot) * HBT + hs;
 #pragma unroll
                     for (int nb = 0; nb < C::NB; nb++)
-                        part_o[prow * D + 16 * nb + r] = st[k].acc[nb][v];
+                        part_o[prow * D + 16 * nb + r] = st[k].acc[nb][v] * cvs;
                     if (r == 0) part_ml[prow] = make_float2(Mv[k][v], Lv[k][v]);
                 }
             return;
@@ -1459,7 +1604,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
             for (int v = 0; v < 4; v++) {
                 const int hs = (hb * NHB + k) * C::HB + 4 * qd + v;
                 if (hs >= R) continue;
-                const float inv = 1.f / Lv[k][v];
+                const float inv = cvs / Lv[k][v];
                 const size_t orow = qr.row(ci, cj, hs);
 #pragma unroll
                 for (int nb = 0; nb < C::NB; nb++)
@@ -1469,7 +1614,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
 
     // one step: claim and prefetch the next, compute this one, close the
     // segment if the next claim leaves it
-    auto body = [&](StepData<D> &now, StepData<D> &later) __attribute__((always_inline)) -> bool {
+    auto body = [&](StepData<D, F8> &now, StepData<D, F8> &later) __attribute__((always_inline)) -> bool {
         const int tn = claim();
         const bool more = tn < x1;
         int ni = ci, nL = cL, nn = cn, nj = cj, nu0 = cu0;
@@ -1477,25 +1622,32 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
         const bool next_unit = more && nu0 != cu0;
         bool bad_next = false;
         // nothing left: a step that loads nothing
-        load_step<D>(more ? src_of(ni, nj, nL, nu0, tn, bad_next) : kv.none(), lane, later);
+        load_step<D, F8>(more ? src_of(ni, nj, nL, nu0, tn, bad_next) : kv.none(), lane, later);
         // causal ends of several tokens: this lane's row in each block, the
         // wave's earliest
         int t_row[NHB];
 #pragma unroll
         for (int k = 0; k < NHB; k++) t_row[k] = cL - qr.T + 1 + tau[k];
-        compute_step<D, MULTI, NHB>(now, (t - cu0) * C::STEP, cL, cL - qr.T + 1, t_row, qop, st,
-                                    vbuf[w], lane, qk_scale_log2);
+        compute_step<D, MULTI, NHB, F8>(now, (t - cu0) * C::STEP, cL, cL - qr.T + 1, t_row, qop,
+                                        st, vbuf[w], lane, cqs);
         if (bad_now) poison_state<D>(st, err, lane);
         bad_now = bad_next;
         mine++;
         // the next unit's q, in flight during the segment's close
         if (next_unit) load_q(ni, nj, qop);
+        float nqs = cqs, nvs = cvs;  // the next unit's factors, in flight with its q
+        if (F8 && next_unit) {
+            nqs = qk_base * k_scale[nj];
+            nvs = v_scale[nj];
+        }
         if (!more || next_unit) {
             finish_segment();
 #pragma unroll
             for (int k = 0; k < NHB; k++) st[k].reset();
             mine = 0;
         }
+        cqs = nqs;
+        cvs = nvs;
         if (!more) return false;
         // wave-uniform; said explicitly so that the loop state stays scalar
         t = __builtin_amdgcn_readfirstlane(tn);
@@ -1823,7 +1975,8 @@ void dispatch_rows(int hpw, const void *q, const void *k, const void *v, const i
 // T query tokens per sequence (T > 1: the causal variant of the kernels).
 template <int D, class KV, bool MULTI, int NHB>
 mqa_status run_mfma_rows(const KV &kv, const void *q, const int32_t *seq_lens, int b, int T,
-                         int h, int g, int S, float qs, float *out, void *workspace, int chunk,
+                         int h, int g, int S, float qs, const float *k_scale,
+                         const float *v_scale, float *out, void *workspace, int chunk,
                          int nsplit, bool balanced, int32_t *err_flags, hipStream_t stream) {
     const int Gh = h / g, R = T * Gh;
     const int nhb = (R + 15) / 16;
@@ -1836,9 +1989,14 @@ mqa_status run_mfma_rows(const KV &kv, const void *q, const int32_t *seq_lens, i
         float *po = (float *)workspace;
         float2 *pml = (float2 *)((uint8_t *)workspace + L.ml_off);
         int4 *desc = (int4 *)((uint8_t *)workspace + L.desc_off);
-        hipLaunchKernelGGL((streamk_mfma_kernel<D, kStreamWaves, KV, MULTI, NHB>), dim3(nwg),
-                           dim3(64 * kStreamWaves), 0, stream, (const uint16_t *)q, kv, seq_lens, b,
-                           qr, g, S, R, ngroups, qs, out, po, pml, desc, err_flags);
+        // an fp8 cache costs more per byte (the decode to bf16): eight waves
+        // per compute unit then hide the latencies of one another's steps
+        // (measured faster for fp8, slower for bf16, whose steps are cheaper)
+        constexpr int NWV = (KV::kF8 && NHB == 1) ? 8 : kStreamWaves;
+        hipLaunchKernelGGL((streamk_mfma_kernel<D, NWV, KV, MULTI, NHB>), dim3(nwg),
+                           dim3(64 * NWV), 0, stream, (const uint16_t *)q, kv, seq_lens, b,
+                           qr, g, S, R, ngroups, qs, k_scale, v_scale, out, po, pml, desc,
+                           err_flags);
         // pieces per cut unit: ~2 when there are more units than work-groups,
         // ~nwg/units when each unit spans many ranges
         constexpr int HPB = 256 / (D / 4);  // head slots per block with one piece lane
@@ -1856,7 +2014,7 @@ mqa_status run_mfma_rows(const KV &kv, const void *q, const int32_t *seq_lens, i
         (float2 *)((uint8_t *)workspace + ((rows * D * sizeof(float) + 255) & ~(size_t)255));
     hipLaunchKernelGGL((split_mfma_kernel<D, KV, MULTI, NHB>), dim3(nsplit, g * ngroups, b),
                        dim3(256), 0, stream, (const uint16_t *)q, kv, seq_lens, qr, g, S, R, ngroups,
-                       chunk, nsplit, qs, part_o, part_ml, err_flags);
+                       chunk, nsplit, qs, k_scale, v_scale, part_o, part_ml, err_flags);
     if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
     hipLaunchKernelGGL(combine_kernel<D>, dim3(T * h, b), dim3(256), 0, stream, part_o, part_ml,
                        seq_lens, qc, R, S, chunk, nsplit, out, err_flags);
@@ -1866,20 +2024,24 @@ mqa_status run_mfma_rows(const KV &kv, const void *q, const int32_t *seq_lens, i
 template <int D, class KV>
 mqa_status run_mfma(const KV &kv, const void *q, const int32_t *seq_lens, int b, int T, int h,
                     int g, int S, float qs, float *out, void *workspace, int chunk, int nsplit,
-                    bool balanced, int32_t *err_flags, hipStream_t stream) {
+                    bool balanced, int32_t *err_flags, hipStream_t stream,
+                    const float *k_scale = nullptr, const float *v_scale = nullptr) {
     const bool two = row_blocks(T * (h / g)).per_wave == 2;
     if (T > 1) {
         if (two)
-            return run_mfma_rows<D, KV, true, 2>(kv, q, seq_lens, b, T, h, g, S, qs, out, workspace,
-                                                 chunk, nsplit, balanced, err_flags, stream);
-        return run_mfma_rows<D, KV, true, 1>(kv, q, seq_lens, b, T, h, g, S, qs, out, workspace,
-                                             chunk, nsplit, balanced, err_flags, stream);
+            return run_mfma_rows<D, KV, true, 2>(kv, q, seq_lens, b, T, h, g, S, qs, k_scale,
+                                                 v_scale, out, workspace, chunk, nsplit, balanced,
+                                                 err_flags, stream);
+        return run_mfma_rows<D, KV, true, 1>(kv, q, seq_lens, b, T, h, g, S, qs, k_scale, v_scale,
+                                             out, workspace, chunk, nsplit, balanced, err_flags,
+                                             stream);
     }
     if (two)
-        return run_mfma_rows<D, KV, false, 2>(kv, q, seq_lens, b, 1, h, g, S, qs, out, workspace,
-                                              chunk, nsplit, balanced, err_flags, stream);
-    return run_mfma_rows<D, KV, false, 1>(kv, q, seq_lens, b, 1, h, g, S, qs, out, workspace,
-                                          chunk, nsplit, balanced, err_flags, stream);
+        return run_mfma_rows<D, KV, false, 2>(kv, q, seq_lens, b, 1, h, g, S, qs, k_scale, v_scale,
+                                              out, workspace, chunk, nsplit, balanced, err_flags,
+                                              stream);
+    return run_mfma_rows<D, KV, false, 1>(kv, q, seq_lens, b, 1, h, g, S, qs, k_scale, v_scale, out,
+                                          workspace, chunk, nsplit, balanced, err_flags, stream);
 }
 
 // T-token calls: T in [1, S]; beyond one token only the bf16 matrix-core path
@@ -2163,6 +2325,126 @@ mqa_status mqa_decode_attn_paged(const void *q, const void *k_pages, const void 
     return mqa_decode_attn_paged_multi(q, k_pages, v_pages, block_table, seq_lens, b, 1, h, g,
                                        page_size, max_pages, num_pages, d, dt, scale, out,
                                        workspace, workspace_bytes, split_chunk, err_flags, stream);
+}
+
+// ---- fp8 e4m3 cache with per-K/V-head scales ----
+
+namespace {
+mqa_status launch_append_fp8(void *k, void *v, const void *k_new, const void *v_new,
+                             const float *k_scale, const float *v_scale, const int32_t *bt,
+                             const int32_t *seq_lens, int b, int T, int g, int S, int max_pages,
+                             int num_pages, int d, int32_t *err_flags, hipStream_t stream) {
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_new) || !aligned16(v_new) ||
+        ((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u))
+        return MQA_ERR_ALIGN;
+    const long long total = 2ll * b * T * g * (d / 8);
+    if ((total + 255) / 256 > 0x7fffffffll) return MQA_ERR_SHAPE;
+    hipLaunchKernelGGL(append_kv_fp8_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       stream, (uint8_t *)k, (uint8_t *)v, (const uint16_t *)k_new,
+                       (const uint16_t *)v_new, k_scale, v_scale, bt, seq_lens, b, T, g, S,
+                       max_pages, num_pages, d, err_flags);
+    return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+}
+
+// sizes of an fp8-cache call (q, k_new, v_new are bf16; the cache rows are
+// d bytes, checked here as if bf16, which is stricter)
+mqa_status check_fp8(int b, int T, int h, int g, int S, int d, int split_chunk) {
+    const mqa_status st = check_sizes(b, h, g, S, d, MQA_BF16, split_chunk);
+    if (st != MQA_OK) return st;
+    return check_tokens(T, h, S, MQA_BF16);
+}
+}  // namespace
+
+mqa_status mqa_append_kv_fp8(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                             const float *k_scale, const float *v_scale, const int32_t *seq_lens,
+                             int b, int T, int g, int S, int d, int32_t *err_flags,
+                             hipStream_t stream) {
+    if (!k_cache || !v_cache || !k_new || !v_new || !k_scale || !v_scale || !seq_lens)
+        return MQA_ERR_NULL;
+    const mqa_status st = check_fp8(b, T, g, g, S, d, 0);
+    if (st != MQA_OK) return st;
+    return launch_append_fp8(k_cache, v_cache, k_new, v_new, k_scale, v_scale, nullptr, seq_lens, b,
+                             T, g, S, 1, 1, d, err_flags, stream);
+}
+
+mqa_status mqa_append_kv_paged_fp8(void *k_pages, void *v_pages, const void *k_new,
+                                   const void *v_new, const float *k_scale, const float *v_scale,
+                                   const int32_t *block_table, const int32_t *seq_lens, int b,
+                                   int T, int g, int page_size, int max_pages, int num_pages,
+                                   int d, int32_t *err_flags, hipStream_t stream) {
+    if (!k_pages || !v_pages || !k_new || !v_new || !k_scale || !v_scale || !block_table ||
+        !seq_lens)
+        return MQA_ERR_NULL;
+    if (page_size < 1 || max_pages < 1 || num_pages < 1 ||
+        (long long)page_size * max_pages > (1ll << 30))
+        return MQA_ERR_SHAPE;
+    const mqa_status st = check_fp8(b, T, g, g, page_size * max_pages, d, 0);
+    if (st != MQA_OK) return st;
+    return launch_append_fp8(k_pages, v_pages, k_new, v_new, k_scale, v_scale, block_table,
+                             seq_lens, b, T, g, page_size, max_pages, num_pages, d, err_flags,
+                             stream);
+}
+
+mqa_status mqa_decode_attn_fp8(const void *q, const void *k_cache, const void *v_cache,
+                               const float *k_scale, const float *v_scale,
+                               const int32_t *seq_lens, int b, int T, int h, int g, int S, int d,
+                               float scale, float *out, void *workspace, size_t workspace_bytes,
+                               int split_chunk, int32_t *err_flags, hipStream_t stream) {
+    if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !seq_lens || !out)
+        return MQA_ERR_NULL;
+    mqa_status st = check_fp8(b, T, h, g, S, d, split_chunk);
+    if (st != MQA_OK) return st;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        ((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u))
+        return MQA_ERR_ALIGN;
+    const mqa_dtype dt = MQA_BF16;
+    const int chunk = resolve_chunk(b, h, g, S, dt, split_chunk, T);
+    const int nsplit = (S + chunk - 1) / chunk;
+    if (!workspace || workspace_bytes < workspace_need(b, h, g, S, d, dt, split_chunk, MQA_KERNEL_MFMA, T))
+        return MQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MQA_ERR_ALIGN;
+    const bool bal = use_streamk(b, h, g, S, dt, split_chunk, MQA_KERNEL_MFMA, T);
+    const float qs = scale * kLog2e;
+    const uint8_t *kb = (const uint8_t *)k_cache, *vb = (const uint8_t *)v_cache;
+    if (d == 128)
+        return run_mfma<128>(ContigKV<128, true>{kb, vb, g, S}, q, seq_lens, b, T, h, g, S, qs, out,
+                             workspace, chunk, nsplit, bal, err_flags, stream, k_scale, v_scale);
+    return run_mfma<64>(ContigKV<64, true>{kb, vb, g, S}, q, seq_lens, b, T, h, g, S, qs, out,
+                        workspace, chunk, nsplit, bal, err_flags, stream, k_scale, v_scale);
+}
+
+mqa_status mqa_decode_attn_paged_fp8(const void *q, const void *k_pages, const void *v_pages,
+                                     const float *k_scale, const float *v_scale,
+                                     const int32_t *block_table, const int32_t *seq_lens, int b,
+                                     int T, int h, int g, int page_size, int max_pages,
+                                     int num_pages, int d, float scale, float *out, void *workspace,
+                                     size_t workspace_bytes, int split_chunk, int32_t *err_flags,
+                                     hipStream_t stream) {
+    if (!q || !k_pages || !v_pages || !k_scale || !v_scale || !block_table || !seq_lens || !out)
+        return MQA_ERR_NULL;
+    mqa_status st = check_paged(b, h, g, page_size, max_pages, num_pages, d, MQA_BF16, split_chunk);
+    if (st != MQA_OK) return st;
+    const int S = page_size * max_pages;
+    if ((st = check_tokens(T, h, S, MQA_BF16)) != MQA_OK) return st;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(out) ||
+        ((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u))
+        return MQA_ERR_ALIGN;
+    const mqa_dtype dt = MQA_BF16;
+    const int chunk = resolve_chunk(b, h, g, S, dt, split_chunk, T);
+    const int nsplit = (S + chunk - 1) / chunk;
+    if (!workspace || workspace_bytes < workspace_need(b, h, g, S, d, dt, split_chunk, MQA_KERNEL_MFMA, T))
+        return MQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MQA_ERR_ALIGN;
+    const bool bal = use_streamk(b, h, g, S, dt, split_chunk, MQA_KERNEL_MFMA, T);
+    const float qs = scale * kLog2e;
+    const uint8_t *kb = (const uint8_t *)k_pages, *vb = (const uint8_t *)v_pages;
+    if (d == 128)
+        return run_mfma<128>(PagedKV<128, true>{kb, vb, block_table, g, page_size, max_pages, num_pages},
+                             q, seq_lens, b, T, h, g, S, qs, out, workspace, chunk, nsplit, bal,
+                             err_flags, stream, k_scale, v_scale);
+    return run_mfma<64>(PagedKV<64, true>{kb, vb, block_table, g, page_size, max_pages, num_pages}, q,
+                        seq_lens, b, T, h, g, S, qs, out, workspace, chunk, nsplit, bal, err_flags,
+                        stream, k_scale, v_scale);
 }
 
 }  // extern "C"

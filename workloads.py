@@ -29,6 +29,12 @@ Several query tokens per sequence (make_multi_step): q [b, T, h, d] and
 k_new/v_new [b, T, g, d] drawn like the one-token ones (streams +8, +9, +10),
 lengths raised to at least T.
 
+fp8 caches (make_fp8_step): codes drawn bit by bit on the device, not
+converted from values: sign uniform, exponent field 7 + round(N(0, 1.5))
+clipped to [1, 14] (magnitudes around 1, as quantised N(0, 1) data),
+mantissa uniform (stream +11); per-K/V-head scales U[0.25, 1] for K and for
+V (stream +12, CPU); q and the new rows as above (bf16).
+
 Paged variants (make_paged_step): the same values scattered into pages of
 page_size rows with page ids drawn as a random permutation (CPU generator,
 stream +7) of b * ceil(S / page_size) + extra_pages pages; pages no sequence
@@ -180,4 +186,59 @@ def make_multi_step(w: Workload, device="cpu", T: int = 4, layer: int = 0,
     t["v_new"] = _normal((w.b, T, w.g, w.d), base + 10, w.dtype, device)
     t["seq_lens"] = torch.clamp(t["seq_lens"], min=T)
     t["T"] = T
+    return t
+
+
+def make_fp8_step(w: Workload, device="cpu", T: int = 1, layer: int = 0,
+                  page_size: int = 0) -> dict:
+    """A step over an fp8 e4m3 cache: k_cache/v_cache uint8 codes [b, g, S, d]
+    (or k_pages/v_pages with block_table), k_scale/v_scale float32 [g], q bf16
+    [b, h, d] (T = 1) or [b, T, h, d], k_new/v_new bf16 [b, g, d] or [b, T, g, d],
+    seq_lens (post-append, at least T)."""
+    base = w.seed + 100 * layer
+    gen = torch.Generator(device=device).manual_seed(base + 11)
+    shape = (w.b, w.g, w.S, w.d)
+
+    def codes():
+        kw = dict(generator=gen, device=device)
+        sign = torch.randint(0, 2, shape, dtype=torch.uint8, **kw)
+        expo = (7 + torch.round(torch.randn(shape, **kw) * 1.5)).clamp(1, 14).to(torch.uint8)
+        mant = torch.randint(0, 8, shape, dtype=torch.uint8, **kw)
+        return (sign << 7) | (expo << 3) | mant
+
+    k, v = codes(), codes()
+    sgen = torch.Generator().manual_seed(base + 12)
+    t = {
+        "k_cache": k, "v_cache": v,
+        "k_scale": (0.25 + 0.75 * torch.rand(w.g, generator=sgen)).to(device),
+        "v_scale": (0.25 + 0.75 * torch.rand(w.g, generator=sgen)).to(device),
+        "seq_lens": torch.clamp(seq_lens(w), min=T).to(device),
+    }
+    if T == 1:
+        t["q"] = _normal((w.b, w.h, w.d), base + 1, torch.bfloat16, device)
+        t["k_new"] = _normal((w.b, w.g, w.d), base + 4, torch.bfloat16, device)
+        t["v_new"] = _normal((w.b, w.g, w.d), base + 5, torch.bfloat16, device)
+    else:
+        t["q"] = _normal((w.b, T, w.h, w.d), base + 8, torch.bfloat16, device)
+        t["k_new"] = _normal((w.b, T, w.g, w.d), base + 9, torch.bfloat16, device)
+        t["v_new"] = _normal((w.b, T, w.g, w.d), base + 10, torch.bfloat16, device)
+    t["T"] = T
+    if page_size:
+        P = page_size
+        b, g, S, d = shape
+        maxp = -(-S // P)
+        num = b * maxp + 3
+        pgen = torch.Generator().manual_seed(base + 7)
+        ids = torch.randperm(num, generator=pgen)[: b * maxp].view(b, maxp).to(torch.int32)
+        for name, c in (("k_pages", k), ("v_pages", v)):
+            padded = torch.zeros((b, g, maxp * P, d), dtype=torch.uint8, device=device)
+            padded[:, :, :S] = c
+            per_page = padded.view(b, g, maxp, P, d).permute(0, 2, 1, 3, 4).reshape(b * maxp, g, P, d)
+            dst = torch.full((num, g, P, d), 0x7F, dtype=torch.uint8, device=device)  # NaN codes
+            dst[ids.view(-1).long().to(device)] = per_page
+            t[name] = dst
+        del t["k_cache"], t["v_cache"]
+        t["block_table"] = ids.to(device)
+        t["page_size"] = P
+        t["capacity"] = maxp * P
     return t
