@@ -16,7 +16,9 @@ Sources, cited by page title and section:
   [MQA blog]  nanhubrain.csdn.net MQA article §2.2 (append on the sequence axis),
               §3.3 (paged cache, 16 tokens per page).
   [GQA notes] §十 item 10 (the causal mask stays per query position when several
-              query tokens attend at once), §十 item 7 (a quantised KV cache).
+              query tokens attend at once), §十 item 7 (a quantised KV cache), §十 item 6
+              (position encoding applied per head).
+  [MQA concept] 玩家對比 (GQA with a sliding window).
 """
 from __future__ import annotations
 
@@ -103,6 +105,18 @@ def lib() -> ctypes.CDLL:
         L.oracle_append_kv_paged_fp8.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32,
                                                  i32, i32, i32, i32]
         L.oracle_append_kv_paged_fp8.restype = i32
+        L.oracle_decode_attn_ex.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, vp,
+                                            i32, i32, i32, i32, i32, i32, i32, ctypes.c_float, vp,
+                                            i32]
+        L.oracle_decode_attn_ex.restype = i32
+        L.oracle_rope_table.argtypes = [ctypes.c_double, i32, i32, vp]
+        L.oracle_rope_table.restype = None
+        L.oracle_rope_rows.argtypes = [vp, vp, vp, i32, i32]
+        L.oracle_rope_rows.restype = None
+        L.oracle_rope_q.argtypes = [vp, vp, vp, i32, i32, i32, i32]
+        L.oracle_rope_q.restype = i32
+        L.oracle_append_kv_rope.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32]
+        L.oracle_append_kv_rope.restype = i32
         L.oracle_kv_bytes.argtypes = [i32, i32, ctypes.c_int64, i32, i32]
         L.oracle_kv_bytes.restype = ctypes.c_uint64
         _lib = L
@@ -350,6 +364,76 @@ def append_kv_paged_fp8(k_pages: np.ndarray, v_pages: np.ndarray, k_new: np.ndar
                                             _ptr(_c(vn)), _dtype_code(kn), _ptr(_f32(k_scale)),
                                             _ptr(_f32(v_scale)), _ptr(bt), _ptr(sl), b, T, g, P,
                                             bt.shape[1], num_pages, d)
+
+
+# ---- every option at once; rotary position embedding ----
+
+def decode_attn_ex(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens: np.ndarray,
+                   scale: float, window: int = 0, k_scale=None, v_scale=None,
+                   block_table=None, nthreads: int = 1):
+    """Decode with every option: q [b, h, d] or [b, T, h, d]; k, v contiguous
+    [b, g, S, d] or pages [num_pages, g, P, d] (with block_table [b, max_pages]);
+    float32, bf16 bits (uint16) or fp8 codes (uint8, with k_scale, v_scale [g]);
+    window > 0: a query at position p sees only t in (p - window, p].
+    Returns (out shaped like q, status)."""
+    q4 = q if q.ndim == 4 else q[:, None]
+    b, T, h, d = q4.shape
+    if k.dtype == np.uint8:
+        kvd = FP8_E4M3
+        ks, vs = _f32(k_scale), _f32(v_scale)
+    else:
+        kvd = _dtype_code(k)
+        ks = vs = None
+    g = k.shape[1]
+    if block_table is not None:
+        bt = _c(block_table.astype(np.int32))
+        P, maxp, num, S = k.shape[2], bt.shape[1], k.shape[0], 0
+    else:
+        bt, P, maxp, num, S = None, 0, 0, 0, k.shape[2]
+    out = np.empty((b, T, h, d), np.float64)
+    sl = _c(seq_lens.astype(np.int32))
+    rc = lib().oracle_decode_attn_ex(_ptr(_c(q4)), _dtype_code(q4), _ptr(_c(k)), _ptr(_c(v)), kvd,
+                                     _ptr(ks), _ptr(vs), _ptr(bt), P, maxp, num, _ptr(sl), b, T,
+                                     h, g, S, d, int(window), ctypes.c_float(scale), _ptr(out),
+                                     int(nthreads))
+    return (out if q.ndim == 4 else out[:, 0]), rc
+
+
+def rope_table(base: float, n_pos: int, d: int) -> np.ndarray:
+    """cos_sin [n_pos, d/2, 2] float32 of the rotary angles p * base^(-2i/d)."""
+    t = np.empty((n_pos, d // 2, 2), np.float32)
+    lib().oracle_rope_table(float(base), int(n_pos), int(d), _ptr(t))
+    return t
+
+
+def rope_rows(x: np.ndarray, pos: np.ndarray, cos_sin: np.ndarray) -> np.ndarray:
+    """A rotated copy of bf16 rows x [..., d] (uint16 bits) at positions pos [n rows]."""
+    y = _c(x.copy()).reshape(-1, x.shape[-1])
+    lib().oracle_rope_rows(_ptr(y), _ptr(_c(pos.astype(np.int32))), _ptr(_c(cos_sin)),
+                           y.shape[0], y.shape[1])
+    return y.reshape(x.shape)
+
+
+def rope_q(q: np.ndarray, cos_sin: np.ndarray, seq_lens: np.ndarray):
+    """A rotated copy of q [b, h, d] or [b, T, h, d] (bf16 bits), token tau at
+    position L - T + tau. Returns (q', status)."""
+    q4 = _c((q if q.ndim == 4 else q[:, None]).copy())
+    b, T, h, d = q4.shape
+    rc = lib().oracle_rope_q(_ptr(q4), _ptr(_c(cos_sin)), _ptr(_c(seq_lens.astype(np.int32))),
+                             b, T, h, d)
+    return (q4 if q.ndim == 4 else q4[:, 0]), rc
+
+
+def append_kv_rope(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray,
+                   v_new: np.ndarray, cos_sin: np.ndarray, seq_lens: np.ndarray) -> int:
+    """In place (bf16 bits): keys rotated at their positions, values as they are."""
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    kn = k_new if k_new.ndim == 4 else k_new[:, None]
+    vn = v_new if v_new.ndim == 4 else v_new[:, None]
+    b, g, S, d = k_cache.shape
+    return lib().oracle_append_kv_rope(_ptr(k_cache), _ptr(v_cache), _ptr(_c(kn)), _ptr(_c(vn)),
+                                       _ptr(_c(cos_sin)), _ptr(_c(seq_lens.astype(np.int32))),
+                                       b, kn.shape[1], g, S, d)
 
 
 def mha_per_head(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:

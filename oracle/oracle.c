@@ -112,6 +112,7 @@ typedef struct {
      * cache (NULL: none): a cache value is code * scale[j] */
     int q_dtype;
     const float *k_scale, *v_scale;
+    int window; /* > 0: a query at position p sees only t > p - window */
 } decode_job;
 
 /* Element index of K/V row (sequence i, K/V head j, position t), or -1 when
@@ -140,8 +141,11 @@ static void decode_row(decode_job *J, int row) {
      * positions up to its own, t <= L-T+tau (the causal mask is applied per
      * query position, shared K/V or not: [GQA notes] §十 item 10). */
     int A = L - J->T + 1 + tau;
+    /* a sliding window of W positions keeps t in [A - W, A) (the window
+     * start replaces 0; the GQA + SWA models of [MQA concept] 玩家對比) */
+    int a0 = (J->window > 0 && A > J->window) ? A - J->window : 0;
     size_t qoff = (size_t)row * d;
-    for (int t = 0; t < A; t++) {
+    for (int t = a0; t < A; t++) {
         if (kv_row(J, i, j, t) < 0) { /* a position on an invalid page */
             for (int x = 0; x < d; x++) o[x] = NAN;
             J->flags |= ORACLE_BAD_PAGE;
@@ -153,7 +157,7 @@ static void decode_row(decode_job *J, int row) {
     double vs = J->v_scale ? (double)J->v_scale[j] : 1.0;
     double *s = (double *)malloc(sizeof(double) * (size_t)A);
     /* score_t = (Q_i . K_j,t) * scale */
-    for (int t = 0; t < A; t++) {
+    for (int t = a0; t < A; t++) {
         double dot = 0.0;
         size_t kr = (size_t)kv_row(J, i, j, t);
         for (int x = 0; x < d; x++)
@@ -162,24 +166,24 @@ static void decode_row(decode_job *J, int row) {
     }
     /* alpha_t = softmax_t(score); subtracting the max leaves it unchanged */
     double m = -INFINITY;
-    for (int t = 0; t < A; t++)
+    for (int t = a0; t < A; t++)
         if (s[t] > m) m = s[t];
     double Z = 0.0;
-    for (int t = 0; t < A; t++) {
+    for (int t = a0; t < A; t++) {
         s[t] = exp(s[t] - m);
         Z += s[t];
     }
-    for (int t = 0; t < A; t++) s[t] /= Z;
+    for (int t = a0; t < A; t++) s[t] /= Z;
     /* O_i = sum_t alpha_t V_j,t */
     for (int x = 0; x < d; x++) {
         double acc = 0.0;
-        for (int t = 0; t < A; t++)
+        for (int t = a0; t < A; t++)
             acc += s[t] * (vs * elem(J->v, (size_t)kv_row(J, i, j, t) + x, J->dtype));
         o[x] = acc;
     }
     if (J->alpha) {
         double *a = J->alpha + (size_t)row * S;
-        for (int t = 0; t < S; t++) a[t] = t < A ? s[t] : 0.0;
+        for (int t = 0; t < S; t++) a[t] = (t >= a0 && t < A) ? s[t] : 0.0;
     }
     free(s);
 }
@@ -223,7 +227,7 @@ int oracle_decode_attn_multi(const void *q, const void *k, const void *v,
     if (b < 1 || T < 1 || h < 1 || g < 1 || S < 1 || d < 1 || h % g != 0)
         return ORACLE_BAD_SHAPE;
     decode_job J = {q, k, v, seq_lens, b, T, h, g, S, d, dtype, (double)scale,
-                    out, alpha, 0, 0, 0, NULL, 0, 0, 0, dtype, NULL, NULL};
+                    out, alpha, 0, 0, 0, NULL, 0, 0, 0, dtype, NULL, NULL, 0};
     return run_decode(&J, nthreads);
 }
 
@@ -246,7 +250,7 @@ int oracle_decode_attn_paged_multi(const void *q, const void *k_pages,
         return ORACLE_BAD_SHAPE;
     decode_job J = {q, k_pages, v_pages, seq_lens, b, T, h, g, page_size * max_pages,
                     d, dtype, (double)scale, out, NULL, 0, 0, 0, block_table,
-                    page_size, max_pages, num_pages, dtype, NULL, NULL};
+                    page_size, max_pages, num_pages, dtype, NULL, NULL, 0};
     return run_decode(&J, nthreads);
 }
 
@@ -391,7 +395,7 @@ int oracle_decode_attn_fp8(const void *q, int q_dtype, const uint8_t *k,
     if (b < 1 || T < 1 || h < 1 || g < 1 || S < 1 || d < 1 || h % g != 0)
         return ORACLE_BAD_SHAPE;
     decode_job J = {q, k, v, seq_lens, b, T, h, g, S, d, ORACLE_FP8_E4M3, (double)scale,
-                    out, NULL, 0, 0, 0, NULL, 0, 0, 0, q_dtype, k_scale, v_scale};
+                    out, NULL, 0, 0, 0, NULL, 0, 0, 0, q_dtype, k_scale, v_scale, 0};
     return run_decode(&J, nthreads);
 }
 
@@ -406,7 +410,7 @@ int oracle_decode_attn_paged_fp8(const void *q, int q_dtype, const uint8_t *k_pa
         return ORACLE_BAD_SHAPE;
     decode_job J = {q, k_pages, v_pages, seq_lens, b, T, h, g, page_size * max_pages, d,
                     ORACLE_FP8_E4M3, (double)scale, out, NULL, 0, 0, 0, block_table,
-                    page_size, max_pages, num_pages, q_dtype, k_scale, v_scale};
+                    page_size, max_pages, num_pages, q_dtype, k_scale, v_scale, 0};
     return run_decode(&J, nthreads);
 }
 
@@ -472,6 +476,113 @@ int oracle_append_kv_paged_fp8(uint8_t *k_pages, uint8_t *v_pages, const void *k
                 }
             }
         }
+    }
+    return rc;
+}
+
+/* ---- every option at once: layout, cache element type, tokens, window ---- */
+
+int oracle_decode_attn_ex(const void *q, int q_dtype, const void *k, const void *v,
+                          int kv_dtype, const float *k_scale, const float *v_scale,
+                          const int32_t *block_table, int page_size, int max_pages,
+                          int num_pages, const int32_t *seq_lens, int b, int T, int h, int g,
+                          int S, int d, int window, float scale, double *out, int nthreads) {
+    if (b < 1 || T < 1 || h < 1 || g < 1 || d < 1 || h % g != 0 || window < 0)
+        return ORACLE_BAD_SHAPE;
+    if (block_table) {
+        if (page_size < 1 || max_pages < 1 || num_pages < 1) return ORACLE_BAD_SHAPE;
+        S = page_size * max_pages;
+    } else if (S < 1) {
+        return ORACLE_BAD_SHAPE;
+    }
+    decode_job J = {q, k, v, seq_lens, b, T, h, g, S, d, kv_dtype, (double)scale, out, NULL,
+                    0, 0, 0, block_table, page_size, max_pages, num_pages, q_dtype,
+                    k_scale, v_scale, window};
+    return run_decode(&J, nthreads);
+}
+
+/* ---- rotary position embedding (RoPE) -------------------------------------- */
+
+/* cos_sin[p][i] = (cos(p * th_i), sin(p * th_i)) rounded to fp32, th_i =
+ * base^(-2i/d), i < d/2: the rotation angles of position p (computed in
+ * double). */
+void oracle_rope_table(double base, int n_pos, int d, float *cos_sin) {
+    for (int p = 0; p < n_pos; p++)
+        for (int i = 0; i < d / 2; i++) {
+            double th = pow(base, -2.0 * i / d);
+            cos_sin[((size_t)p * (d / 2) + i) * 2 + 0] = (float)cos(p * th);
+            cos_sin[((size_t)p * (d / 2) + i) * 2 + 1] = (float)sin(p * th);
+        }
+}
+
+/* Nearest bf16 of a float (ties to even; NaN kept). */
+static uint16_t bf16_round(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7fffu + lsb) >> 16);
+}
+
+/* Rotate one bf16 row of d elements at position pos: element i and element
+ * i + d/2 form a pair (the halves convention), turned by the angle of pair
+ * i: a' = a c - b s, b' = b c + a s, each product and the sum rounded to fp32
+ * in that order (no fused multiply-add), the results rounded to bf16. */
+static void rope_row(uint16_t *row, int pos, const float *cos_sin, int d) {
+    int hd = d / 2;
+    for (int i = 0; i < hd; i++) {
+        float a = (float)elem(row, (size_t)i, ORACLE_BF16);
+        float b = (float)elem(row, (size_t)(i + hd), ORACLE_BF16);
+        float c = cos_sin[((size_t)pos * hd + i) * 2 + 0];
+        float s = cos_sin[((size_t)pos * hd + i) * 2 + 1];
+        float ac = a * c, bs = b * s, bc = b * c, as = a * s;
+        float ra = ac - bs, rb = bc + as;
+        row[i] = bf16_round(ra);
+        row[i + hd] = bf16_round(rb);
+    }
+}
+
+/* In place: rows x [n][d] (bf16 bits) rotated at positions pos[n]. */
+void oracle_rope_rows(uint16_t *x, const int32_t *pos, const float *cos_sin, int n, int d) {
+    for (int r = 0; r < n; r++) rope_row(x + (size_t)r * d, pos[r], cos_sin, d);
+}
+
+/* q [b][T][h][d] (bf16) rotated in place: token tau of sequence i at
+ * position L_i - T + tau. Sequences with a bad length are left alone. */
+int oracle_rope_q(uint16_t *q, const float *cos_sin, const int32_t *seq_lens, int b, int T,
+                  int h, int d) {
+    int rc = ORACLE_OK;
+    for (int i = 0; i < b; i++) {
+        int L = seq_lens[i];
+        if (L < T) {
+            rc |= ORACLE_BAD_LEN;
+            continue;
+        }
+        for (int tau = 0; tau < T; tau++)
+            for (int hq = 0; hq < h; hq++)
+                rope_row(q + (((size_t)i * T + tau) * h + hq) * d, L - T + tau, cos_sin, d);
+    }
+    return rc;
+}
+
+/* Append with RoPE on K ([GQA notes] §十 item 6: the rotation is applied
+ * per head, to each K/V head's key as to each query head's query): token
+ * tau's key row, rotated at its position L - T + tau, and its value row, as
+ * is, go to that position (bf16 cache [b][g][S][d]; k_new, v_new
+ * [b][T][g][d]). */
+int oracle_append_kv_rope(uint16_t *k_cache, uint16_t *v_cache, const uint16_t *k_new,
+                          const uint16_t *v_new, const float *cos_sin,
+                          const int32_t *seq_lens, int b, int T, int g, int S, int d) {
+    int rc = oracle_append_kv_multi(k_cache, v_cache, k_new, v_new, seq_lens, b, T, g, S, d,
+                                    ORACLE_BF16);
+    if (rc == ORACLE_BAD_SHAPE) return rc;
+    for (int i = 0; i < b; i++) {
+        int L = seq_lens[i];
+        if (L < T || L > S) continue;
+        for (int tau = 0; tau < T; tau++)
+            for (int j = 0; j < g; j++)
+                rope_row(k_cache + (((size_t)i * g + j) * S + (size_t)(L - T + tau)) * d,
+                         L - T + tau, cos_sin, d);
     }
     return rc;
 }

@@ -139,6 +139,35 @@ int oracle_append_kv_paged_fp8(uint8_t *k_pages, uint8_t *v_pages, const void *k
                                const int32_t *seq_lens, int b, int T, int g, int page_size,
                                int max_pages, int num_pages, int d);
 
+/* Every option of the decode at once: q (q_dtype) [b][T][h][d]; K/V
+ * contiguous [b][g][S][d] (block_table NULL) or pages [num_pages][g][P][d]
+ * through block_table [b][max_pages] (S is then P * max_pages); kv_dtype
+ * f32, bf16 or fp8 e4m3 (with k_scale, v_scale [g]; NULL otherwise); a
+ * sliding window: window > 0 keeps, for a query at position p, only the
+ * positions t in (p - window, p] (the window start replaces 0: [MQA
+ * concept] 玩家對比 lists GQA with a sliding window); 0 keeps all t <= p. */
+int oracle_decode_attn_ex(const void *q, int q_dtype, const void *k, const void *v,
+                          int kv_dtype, const float *k_scale, const float *v_scale,
+                          const int32_t *block_table, int page_size, int max_pages,
+                          int num_pages, const int32_t *seq_lens, int b, int T, int h, int g,
+                          int S, int d, int window, float scale, double *out, int nthreads);
+
+/* Rotary position embedding on bf16 rows ([GQA notes] §十 item 6: position
+ * information is applied per head, to queries and to each K/V head's keys
+ * alike; the pages give no formula, so the common rotary form): pairs
+ * (x_i, x_{i+d/2}), i < d/2, are turned by the angle p * base^(-2i/d) of
+ * position p. oracle_rope_table writes cos_sin [n_pos][d/2][2] fp32 (cos,
+ * sin) from the angles in double. The rotation of a pair is a' = a c - b s,
+ * b' = b c + a s in fp32 (each product rounded, then the sum, no fused
+ * multiply-add), rounded to bf16 (nearest, ties to even). */
+void oracle_rope_table(double base, int n_pos, int d, float *cos_sin);
+void oracle_rope_rows(uint16_t *x, const int32_t *pos, const float *cos_sin, int n, int d);
+int oracle_rope_q(uint16_t *q, const float *cos_sin, const int32_t *seq_lens, int b, int T,
+                  int h, int d);
+int oracle_append_kv_rope(uint16_t *k_cache, uint16_t *v_cache, const uint16_t *k_new,
+                          const uint16_t *v_new, const float *cos_sin,
+                          const int32_t *seq_lens, int b, int T, int g, int S, int d);
+
 /* Textbook multi-head attention for one sequence, one K/V head per query
  * head (no sharing): q [h][d], K and V [h][L][d], all double.
  * [GQA notes] §二: O_i = softmax(Q_i K_i^T / sqrt(d_h)) V_i. */

@@ -623,13 +623,149 @@ def test_fp8_append_quantises_with_the_head_scale(T):
 
 
 # ---------------------------------------------------------------------------
+# sliding window ([MQA concept] 玩家對比: GQA + SWA) and rotary positions
+# ---------------------------------------------------------------------------
+
+def _sdpa_rows(q_rows, k, v, scale):
+    """torch SDPA (float64) of query rows [h, d] over k, v [g, n, d]."""
+    h, d = q_rows.shape
+    g, n, _ = k.shape
+    o = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.ascontiguousarray(q_rows)).view(1, h, 1, d),
+        torch.from_numpy(np.ascontiguousarray(k)).view(1, g, n, d),
+        torch.from_numpy(np.ascontiguousarray(v)).view(1, g, n, d), scale=scale,
+        enable_gqa=(g != h))
+    return o.view(h, d).numpy()
+
+
+@pytest.mark.parametrize("T,W", [(1, 5), (1, 32), (3, 7), (2, 1)])
+def test_window_matches_sdpa_on_the_window(T, W):
+    """Each token sees only its last W positions: torch SDPA over that slice."""
+    b, h, g, S, d = 3, 8, 2, 40, 64
+    q, k, v = randn(b, T, h, d), randn(b, g, S, d), randn(b, g, S, d)
+    lens = np.array([40, T + 2, 23], np.int32)
+    out, rc = oracle.decode_attn_ex(q, k, v, lens, 0.125, window=W)
+    assert rc == oracle.OK
+    for i in range(b):
+        for tau in range(T):
+            A = int(lens[i]) - T + 1 + tau
+            a0 = max(0, A - W)
+            ref = _sdpa_rows(q[i, tau].astype(np.float64), k[i, :, a0:A].astype(np.float64),
+                             v[i, :, a0:A].astype(np.float64), 0.125)
+            np.testing.assert_allclose(out[i, tau], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_window_special_cases():
+    b, h, g, S, d = 2, 4, 1, 20, 64
+    q, k, v = randn(b, h, d), randn(b, g, S, d), randn(b, g, S, d)
+    lens = np.array([20, 9], np.int32)
+    full, _, _ = oracle.decode_attn(q, k, v, lens, 0.125)
+    wide, _ = oracle.decode_attn_ex(q, k, v, lens, 0.125, window=20)
+    assert np.array_equal(full, wide)  # a window at least the length changes nothing
+    one, _ = oracle.decode_attn_ex(q, k, v, lens, 0.125, window=1)
+    for i in range(b):  # a window of one position returns that position's value row
+        np.testing.assert_allclose(one[i], np.broadcast_to(v[i, 0, lens[i] - 1], (h, d)), rtol=1e-12)
+    # fp8 and paged forms of the general call agree with the dedicated ones
+    rng = np.random.default_rng(5)
+    qb, kc, vc, ks, vs = _fp8_case(rng, b, 1, h, g, S, d)
+    f8, _ = oracle.decode_attn_fp8(qb, kc, vc, ks, vs, lens, 0.125)
+    ex, _ = oracle.decode_attn_ex(qb, kc, vc, lens, 0.125, k_scale=ks, v_scale=vs)
+    assert np.array_equal(f8, ex)
+    kp, vp, bt = _paged_from_contiguous(k, v, 16, rng)
+    pg, _ = oracle.decode_attn_paged(q, kp, vp, bt, lens, 0.125)
+    ex2, _ = oracle.decode_attn_ex(q, kp, vp, lens, 0.125, block_table=bt)
+    assert np.array_equal(pg, ex2)
+
+
+def _bf16_val(bits_arr):
+    return torch.from_numpy(np.ascontiguousarray(bits_arr).view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def test_rope_table_closed_forms():
+    d, base = 64, 10000.0
+    t = oracle.rope_table(base, 50, d)
+    p = np.arange(50)
+    np.testing.assert_array_equal(t[:, 0, 0], np.cos(p).astype(np.float32))  # pair 0: angle p
+    np.testing.assert_array_equal(t[:, 0, 1], np.sin(p).astype(np.float32))
+    th = base ** (-2.0 * np.arange(d // 2) / d)
+    np.testing.assert_array_equal(t[1, :, 0], np.cos(th).astype(np.float32))
+    np.testing.assert_array_equal(t[7, :, 1], np.sin(7 * th).astype(np.float32))
+    assert (t[0, :, 0] == 1).all() and (t[0, :, 1] == 0).all()
+
+
+def test_rope_rotation_properties():
+    """Position 0 is the identity; each pair (i, i + d/2) keeps its length;
+    rotated dot products depend only on the distance of the positions."""
+    d = 64
+    t = oracle.rope_table(10000.0, 200, d)
+    x = bf16_bits(randn(6, d))
+    assert np.array_equal(oracle.rope_rows(x, np.zeros(6, np.int32), t), x)
+    # a unit vector in element i turns towards element i + d/2: (cos, sin) of the pair's angle
+    for i in (0, 5, d // 2 - 1):
+        e = np.zeros((1, d), np.float32)
+        e[0, i] = 1.0
+        r = _bf16_val(oracle.rope_rows(bf16_bits(e), np.array([37], np.int32), t))[0]
+        expect = np.zeros(d)
+        expect[i], expect[i + d // 2] = t[37, i, 0], t[37, i, 1]
+        np.testing.assert_allclose(r, expect, rtol=2 ** -8, atol=1e-30)
+    pos = np.array([0, 3, 17, 64, 150, 199], np.int32)
+    y = _bf16_val(oracle.rope_rows(x, pos, t))
+    xv = _bf16_val(x)
+    n0 = xv[:, :d // 2] ** 2 + xv[:, d // 2:] ** 2
+    n1 = y[:, :d // 2] ** 2 + y[:, d // 2:] ** 2
+    np.testing.assert_allclose(n1, n0, rtol=2e-2, atol=1e-3)  # bf16 rounding of the results
+    # the pair convention: (i, i + d/2) -- adjacent pairs (2i, 2i+1) would not keep these norms
+    qrow, krow = bf16_bits(randn(1, d)), bf16_bits(randn(1, d))
+    dots = []
+    for p1, p2 in ((10, 4), (56, 50), (199, 193), (106, 100)):  # distance 6 each time
+        a = _bf16_val(oracle.rope_rows(qrow, np.array([p1], np.int32), t))[0]
+        b_ = _bf16_val(oracle.rope_rows(krow, np.array([p2], np.int32), t))[0]
+        dots.append(a @ b_)
+    far = _bf16_val(oracle.rope_rows(krow, np.array([180], np.int32), t))[0] @ \
+        _bf16_val(oracle.rope_rows(qrow, np.array([10], np.int32), t))[0]
+    assert np.ptp(dots) < 0.05 * np.abs(dots).max() + 0.05
+    assert abs(far - dots[0]) > 0.05  # another distance, another product
+
+
+def test_rope_append_and_q():
+    rng = np.random.default_rng(12)
+    b, T, g, S, d, h = 3, 2, 2, 16, 64, 4
+    t = oracle.rope_table(10000.0, S, d)
+    kc, vc = bf16_bits(randn(b, g, S, d)), bf16_bits(randn(b, g, S, d))
+    kn, vn = bf16_bits(randn(b, T, g, d)), bf16_bits(randn(b, T, g, d))
+    lens = np.array([2, 16, 9], np.int32)
+    k2, v2 = kc.copy(), vc.copy()
+    assert oracle.append_kv_rope(k2, v2, kn, vn, t, lens) == oracle.OK
+    ek, ev = kc.copy(), vc.copy()
+    for i in range(b):
+        for tau in range(T):
+            pos = lens[i] - T + tau
+            ek[i, :, pos] = oracle.rope_rows(kn[i, tau], np.full(g, pos, np.int32), t)
+            ev[i, :, pos] = vn[i, tau]
+    assert np.array_equal(k2, ek) and np.array_equal(v2, ev)
+    q = bf16_bits(randn(b, T, h, d))
+    qr, rc = oracle.rope_q(q, t, lens)
+    assert rc == oracle.OK
+    for i in range(b):
+        for tau in range(T):
+            pos = np.full(h, lens[i] - T + tau, np.int32)
+            assert np.array_equal(qr[i, tau], oracle.rope_rows(q[i, tau], pos, t))
+    del rng
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: each mutant of the oracle's source must fail a pin above
 # ---------------------------------------------------------------------------
 
 MUTANTS = {
     "group map i % g": ("int j = hq / G;", "int j = hq % J->g;"),
     "scale dropped": ("s[t] = J->scale * dot;", "s[t] = dot;"),
-    "attended length off by one": ("for (int t = 0; t < A; t++) {\n        double dot", "for (int t = 0; t < A - 1; t++) {\n        double dot"),
+    "attended length off by one": ("for (int t = a0; t < A; t++) {\n        double dot", "for (int t = a0; t < A - 1; t++) {\n        double dot"),
+    "window one position short": ("? A - J->window : 0;", "? A - J->window + 1 : 0;"),
+    "window ignored": ("int a0 = (J->window > 0 && A > J->window)", "int a0 = (0 && A > J->window)"),
+    "rope pairs adjacent": ("float b = (float)elem(row, (size_t)(i + hd), ORACLE_BF16);", "float b = (float)elem(row, (size_t)(i ^ 1), ORACLE_BF16);"),
+    "rope sine sign flipped": ("float ra = ac - bs, rb = bc + as;", "float ra = ac + bs, rb = bc - as;"),
+    "rope angle exponent over d/2": ("double th = pow(base, -2.0 * i / d);", "double th = pow(base, -1.0 * i / d);"),
     "causal mask dropped": ("int A = L - J->T + 1 + tau;", "int A = L;"),
     "token order reversed": ("int A = L - J->T + 1 + tau;", "int A = L - tau;"),
     "every token uses the first token's query": ("size_t qoff = (size_t)row * d;", "size_t qoff = ((size_t)i * J->T * J->h + hq) * d;"),
@@ -640,7 +776,7 @@ MUTANTS = {
     "key scale ignored": ("double ks = J->k_scale ? (double)J->k_scale[j] : 1.0;", "double ks = 1.0;"),
     "value scale of the key": ("double vs = J->v_scale ? (double)J->v_scale[j] : 1.0;", "double vs = J->k_scale ? (double)J->k_scale[j] : 1.0;"),
     "quantised by multiplying": ("return oracle_fp8_e4m3_encode(x / scale);", "return oracle_fp8_e4m3_encode(x * scale);"),
-    "no normalisation": ("for (int t = 0; t < A; t++) s[t] /= Z;", ""),
+    "no normalisation": ("for (int t = a0; t < A; t++) s[t] /= Z;", ""),
     "key and value swapped": ("elem(J->v, (size_t)kv_row(J, i, j, t) + x, J->dtype));\n        o[x]", "elem(J->k, (size_t)kv_row(J, i, j, t) + x, J->dtype));\n        o[x]"),
     "page looked up one position late": ("(size_t)i * J->max_pages + t / J->page_size]", "(size_t)i * J->max_pages + (t + 1) / J->page_size]"),
     "row within the page ignored": ("J->page_size + t % J->page_size) * J->d", "J->page_size) * J->d"),
@@ -670,7 +806,9 @@ def test_planted_mistakes_are_caught(tmp_path, name, monkeypatch):
                "oracle_decode_attn_multi", "oracle_decode_attn_paged_multi",
                "oracle_append_kv_multi", "oracle_append_kv_paged_multi",
                "oracle_fp8_e4m3_decode", "oracle_fp8_e4m3_encode", "oracle_decode_attn_fp8",
-               "oracle_decode_attn_paged_fp8", "oracle_append_kv_fp8", "oracle_append_kv_paged_fp8"):
+               "oracle_decode_attn_paged_fp8", "oracle_append_kv_fp8", "oracle_append_kv_paged_fp8",
+               "oracle_decode_attn_ex", "oracle_rope_table", "oracle_rope_rows", "oracle_rope_q",
+               "oracle_append_kv_rope"):
         getattr(mutant, fn).argtypes = getattr(real, fn).argtypes
         getattr(mutant, fn).restype = getattr(real, fn).restype
     monkeypatch.setattr(oracle, "_lib", mutant)
@@ -682,7 +820,9 @@ def test_planted_mistakes_are_caught(tmp_path, name, monkeypatch):
                 lambda: test_append_multi_writes_t_rows_per_head(False),
                 test_fp8_decode_matches_torch, test_fp8_encode_matches_torch_in_range_and_saturates,
                 lambda: test_fp8_decode_matches_sdpa_on_dequantised_cache(1, 8, 2),
-                lambda: test_fp8_append_quantises_with_the_head_scale(1)):
+                lambda: test_fp8_append_quantises_with_the_head_scale(1),
+                lambda: test_window_matches_sdpa_on_the_window(3, 7), test_window_special_cases,
+                test_rope_table_closed_forms, test_rope_rotation_properties):
         try:
             pin()
         except AssertionError:
