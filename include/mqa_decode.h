@@ -57,7 +57,9 @@ typedef enum {
     MQA_ERR_HIP = 6          /* the HIP runtime reported a launch error */
 } mqa_status;
 
-typedef enum { MQA_F32 = 0, MQA_BF16 = 1 } mqa_dtype;
+/* Element types. MQA_FP8_E4M3 is a cache type only (mqa_decode_attn_ex,
+ * the _fp8 calls); q and new rows are then bf16. */
+typedef enum { MQA_F32 = 0, MQA_BF16 = 1, MQA_FP8_E4M3 = 2 } mqa_dtype;
 
 /* Which partition kernel computes the attention (see mqa_decode_attn_kernel). */
 typedef enum {
@@ -67,9 +69,11 @@ typedef enum {
 } mqa_kernel;
 
 /* Bits ORed into *err_flags by the kernels: some seq_lens[i] outside [1, S];
- * some position of a paged call on a page id outside [0, num_pages). */
+ * some position of a paged call on a page id outside [0, num_pages); some
+ * position of a rotary call past the rows of its cos/sin table. */
 #define MQA_DEVERR_SEQLEN 1
 #define MQA_DEVERR_PAGE 2
+#define MQA_DEVERR_ROPE 4
 
 /*
  * Append this step's K/V rows to the cache, bit-exactly.
@@ -318,6 +322,61 @@ mqa_status mqa_decode_attn_paged_fp8(const void *q, const void *k_pages,
                                      float *out, void *workspace,
                                      size_t workspace_bytes, int split_chunk,
                                      int32_t *err_flags, hipStream_t stream);
+
+/*
+ * One call with every option: layout (contiguous or paged), cache element
+ * type (bf16, fp8 with scales, or f32), T query tokens, and a sliding window
+ * ([MQA concept] 玩家對比 lists GQA with a sliding window: a query at position
+ * p then sees only the positions t in (p - window, p]; the window start
+ * replaces 0). The entry points above are this call with some fields fixed.
+ * Fields not used by the chosen layout or type are ignored. f32 caches take
+ * the one-token contiguous path only (T = 1, no window, no pages).
+ */
+typedef struct {
+    const void *q;                  /* [b][T][h][d]: bf16 (f32 with an f32 cache) */
+    const void *k, *v;              /* [b][g][S][d] or pages [num_pages][g][page_size][d] */
+    const int32_t *block_table;     /* [b][max_pages] int32; NULL: contiguous cache */
+    const int32_t *seq_lens;        /* [b], post-append lengths */
+    const float *k_scale, *v_scale; /* [g] fp32, fp8 cache only */
+    float *out;                     /* [b][T][h][d] fp32 */
+    void *workspace;                /* mqa_decode_ex_workspace_bytes() bytes, 16-byte aligned */
+    size_t workspace_bytes;
+    int32_t *err_flags;             /* device int32 or NULL */
+    int b, T, h, g, d;
+    int S;                          /* contiguous capacity */
+    int page_size, max_pages, num_pages;
+    int kv_dtype;                   /* mqa_dtype of the cache */
+    int window;                     /* > 0: sliding window of that many positions; 0: none */
+    int split_chunk;                /* 0: automatic */
+    float scale;                    /* softmax scale, normally 1/sqrt(d) */
+} mqa_decode_desc;
+
+size_t mqa_decode_ex_workspace_bytes(const mqa_decode_desc *desc);
+mqa_status mqa_decode_attn_ex(const mqa_decode_desc *desc, hipStream_t stream);
+
+/*
+ * Rotary position embedding on bf16 rows. [GQA notes] §十 item 6: position
+ * information is applied per head, to every query head and to each K/V
+ * head's keys (shared or not); the pages give no formula, so the common
+ * rotary form: pairs (x_i, x_{i+d/2}), i < d/2, are turned by the angle of
+ * their position, a' = a c - b s, b' = b c + a s with (c, s) =
+ * cos_sin[pos][i] (a caller-built fp32 table [n_pos][d/2][2], e.g. from
+ * angles pos * base^(-2i/d)); each product and sum is rounded to fp32 in
+ * that order (no fused multiply-add) and the results to bf16 (nearest,
+ * ties to even). A position at or past n_pos is skipped and flagged
+ * MQA_DEVERR_ROPE.
+ *
+ * mqa_rope_q rotates q [b][T][h][d] in place, token tau of sequence i at
+ * position seq_lens[i] - T + tau. mqa_append_kv_rope is mqa_append_kv_multi
+ * with each key row rotated at its position before it is stored (values as
+ * they are); bf16 contiguous cache.
+ */
+mqa_status mqa_rope_q(void *q, const float *cos_sin, int n_pos, const int32_t *seq_lens, int b,
+                      int T, int h, int d, int32_t *err_flags, hipStream_t stream);
+mqa_status mqa_append_kv_rope(void *k_cache, void *v_cache, const void *k_new,
+                              const void *v_new, const float *cos_sin, int n_pos,
+                              const int32_t *seq_lens, int b, int T, int g, int S, int d,
+                              int32_t *err_flags, hipStream_t stream);
 
 /* Static text for a status code (never NULL). */
 const char *mqa_status_string(mqa_status s);

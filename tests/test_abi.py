@@ -9,6 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -267,3 +268,74 @@ def test_fp8_append_rejects_bad_arguments_before_launch():
                                      8, 128, None, None) == mqa.ERR_NULL
     assert L.mqa_append_kv_paged_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1, 2, 16, 0,
                                      8, 128, None, None) == mqa.ERR_SHAPE
+
+
+def test_decode_desc_layout_matches_the_header(tmp_path):
+    """The ctypes mirror of mqa_decode_desc has the C struct's offsets and size
+    (a small C program built with the host compiler prints them)."""
+    src = tmp_path / "layout.c"
+    fields = [f[0] for f in mqa.DecodeDesc._fields_]
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"mqa_decode.h\"\n"
+                   "int main(void) {\n"
+                   + "".join(f'  printf("%zu\\n", offsetof(mqa_decode_desc, {f}));\n' for f in fields)
+                   + '  printf("%zu\\n", sizeof(mqa_decode_desc));\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    r = subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", inc, "-I", "/opt/rocm/include",
+                        "-o", str(exe), str(src)], capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("host compiler cannot include the HIP runtime header: " + r.stderr[:200])
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = [getattr(mqa.DecodeDesc, f).offset for f in fields] + [ctypes.sizeof(mqa.DecodeDesc)]
+    assert got == want
+
+
+def ex_desc(**kw):
+    d = mqa.DecodeDesc()
+    d.q = d.k = d.v = d.seq_lens = d.out = d.workspace = 0x10000
+    d.b, d.T, d.h, d.g, d.d, d.S = 2, 1, 8, 2, 128, 64
+    d.kv_dtype, d.window, d.split_chunk, d.scale = mqa.BF16, 0, 0, 0.088
+    d.workspace_bytes = 1 << 30
+    for k_, v_ in kw.items():
+        setattr(d, k_, v_)
+    return d
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), mqa.ERR_NULL),
+    (dict(window=-1), mqa.ERR_SHAPE),
+    (dict(kv_dtype=7), mqa.ERR_UNSUPPORTED),
+    (dict(kv_dtype=mqa.F32, T=2), mqa.ERR_UNSUPPORTED),
+    (dict(kv_dtype=mqa.F32, window=4), mqa.ERR_UNSUPPORTED),
+    (dict(kv_dtype=mqa.FP8_E4M3), mqa.ERR_NULL),              # no scales
+    (dict(block_table=0x10000, page_size=24, max_pages=4, num_pages=8), mqa.ERR_SHAPE),
+    (dict(T=65), mqa.ERR_SHAPE),
+    (dict(workspace_bytes=16), mqa.ERR_WORKSPACE),
+    (dict(out=0x10008), mqa.ERR_ALIGN),
+])
+def test_decode_ex_rejects_bad_arguments_before_launch(kw, status):
+    d = ex_desc(**kw)
+    assert mqa.lib().mqa_decode_attn_ex(ctypes.byref(d), None) == status
+
+
+def test_decode_ex_workspace_matches_the_dedicated_calls():
+    L = mqa.lib()
+    d = ex_desc(b=64, h=64, g=8, S=4096)
+    assert L.mqa_decode_ex_workspace_bytes(ctypes.byref(d)) == \
+        mqa.decode_workspace_bytes(64, 64, 8, 4096, 128, mqa.BF16)
+    d = ex_desc(b=64, h=64, g=8, S=4096, T=4, window=100)
+    assert L.mqa_decode_ex_workspace_bytes(ctypes.byref(d)) == \
+        mqa.decode_multi_workspace_bytes(64, 4, 64, 8, 4096, 128, mqa.BF16)
+
+
+def test_rope_calls_reject_bad_arguments_before_launch():
+    L = mqa.lib()
+    assert L.mqa_rope_q(FAKE, None, 16, FAKE, 2, 1, 8, 128, None, None) == mqa.ERR_NULL
+    assert L.mqa_rope_q(FAKE, FAKE, 0, FAKE, 2, 1, 8, 128, None, None) == mqa.ERR_SHAPE
+    assert L.mqa_rope_q(FAKE, FAKE, 16, FAKE, 2, 1, 8, 96, None, None) == mqa.ERR_UNSUPPORTED
+    assert L.mqa_rope_q(MISALIGNED, FAKE, 16, FAKE, 2, 1, 8, 128, None, None) == mqa.ERR_ALIGN
+    assert L.mqa_append_kv_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, 2, 0, 2, 64, 128, None,
+                                None) == mqa.ERR_SHAPE
+    assert L.mqa_append_kv_rope(FAKE, FAKE, FAKE, FAKE, None, 16, FAKE, 2, 1, 2, 64, 128, None,
+                                None) == mqa.ERR_NULL

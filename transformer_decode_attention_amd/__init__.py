@@ -25,6 +25,10 @@ Entry points (same names as the C ABI, without the ``mqa_`` prefix):
   append_kv_fp8 / decode_attn_fp8 / append_kv_paged_fp8 / decode_attn_paged_fp8:
       the same over a cache of fp8 e4m3 codes (uint8 or float8_e4m3fn tensors)
       with per-K/V-head scales k_scale, v_scale (float32 [g]); q and new rows bf16
+  decode_attn_ex(q, k, v, seq_lens, block_table=None, k_scale=None, v_scale=None, window=0, ...)
+      every option at once (layout, cache type, tokens, sliding window)
+  rope_q(q, cos_sin, seq_lens) / append_kv_rope(k_cache, v_cache, k_new, v_new, cos_sin, seq_lens)
+      rotary position embedding of the queries / of the keys on append
   kv_bytes(layers, g, S, d, dtype_bytes)
   status_string(status)
 
@@ -45,15 +49,17 @@ __all__ = [
     "DEVERR_PAGE", "append_kv_paged", "decode_attn_paged", "decode_paged_workspace_bytes",
     "append_kv_multi", "decode_attn_multi", "append_kv_paged_multi", "decode_attn_paged_multi",
     "decode_multi_workspace_bytes", "decode_multi_schedule", "append_kv_fp8", "decode_attn_fp8",
-    "append_kv_paged_fp8", "decode_attn_paged_fp8",
+    "append_kv_paged_fp8", "decode_attn_paged_fp8", "decode_attn_ex", "rope_q", "append_kv_rope",
+    "DEVERR_ROPE", "FP8_E4M3",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa_decode.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 DEVERR_SEQLEN = 1
 DEVERR_PAGE = 2
+DEVERR_ROPE = 4
 
 KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
 
@@ -64,8 +70,23 @@ EXPORTS = (
     "mqa_decode_attn_paged", "mqa_append_kv_multi", "mqa_decode_multi_workspace_bytes",
     "mqa_decode_multi_schedule", "mqa_decode_attn_multi", "mqa_append_kv_paged_multi",
     "mqa_decode_attn_paged_multi", "mqa_append_kv_fp8", "mqa_append_kv_paged_fp8",
-    "mqa_decode_attn_fp8", "mqa_decode_attn_paged_fp8",
+    "mqa_decode_attn_fp8", "mqa_decode_attn_paged_fp8", "mqa_decode_ex_workspace_bytes",
+    "mqa_decode_attn_ex", "mqa_rope_q", "mqa_append_kv_rope",
 )
+
+
+class DecodeDesc(ctypes.Structure):
+    """mqa_decode_desc of include/mqa_decode.h, field for field."""
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("err_flags", ctypes.c_void_p),
+                ("b", ctypes.c_int), ("T", ctypes.c_int), ("h", ctypes.c_int), ("g", ctypes.c_int),
+                ("d", ctypes.c_int), ("S", ctypes.c_int), ("page_size", ctypes.c_int),
+                ("max_pages", ctypes.c_int), ("num_pages", ctypes.c_int),
+                ("kv_dtype", ctypes.c_int), ("window", ctypes.c_int),
+                ("split_chunk", ctypes.c_int), ("scale", ctypes.c_float)]
 SCHEDULES = {0: "valu-partitions", 1: "mfma-partitions", 2: "mfma-balanced"}
 
 
@@ -136,6 +157,14 @@ def _load() -> ctypes.CDLL:
                                             i32, i32, i32, ctypes.c_float, vp, vp, ctypes.c_size_t,
                                             i32, vp, vp]
     L.mqa_decode_attn_paged_fp8.restype = i32
+    L.mqa_decode_ex_workspace_bytes.argtypes = [ctypes.POINTER(DecodeDesc)]
+    L.mqa_decode_ex_workspace_bytes.restype = ctypes.c_size_t
+    L.mqa_decode_attn_ex.argtypes = [ctypes.POINTER(DecodeDesc), vp]
+    L.mqa_decode_attn_ex.restype = i32
+    L.mqa_rope_q.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, vp, vp]
+    L.mqa_rope_q.restype = i32
+    L.mqa_append_kv_rope.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, vp, vp]
+    L.mqa_append_kv_rope.restype = i32
     return L
 
 
@@ -590,3 +619,92 @@ def decode_attn_paged_fp8(q, k_pages, v_pages, k_scale, v_scale, block_table, se
     if st != OK:
         raise MQAError(st, "mqa_decode_attn_paged_fp8")
     return o4 if q.dim() == 4 else o4[:, 0]
+
+
+# ---- every option at once; rotary position embedding ----
+
+def decode_attn_ex(q, k, v, seq_lens, block_table=None, k_scale=None, v_scale=None, window=0,
+                   scale=None, out=None, workspace=None, split_chunk: int = 0, err_flags=None):
+    """Decode with every option (mqa_decode_attn_ex): q [b, h, d] or [b, T, h, d];
+    k, v contiguous [b, g, S, d] or pages [num_pages, g, P, d] with block_table
+    [b, max_pages]; a bf16, f32 or fp8 (uint8 / float8_e4m3fn codes with k_scale,
+    v_scale [g]) cache; window > 0: sliding window. Returns out shaped like q."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("seq_lens", seq_lens)):
+        _dev(t, n)
+    q4 = q if q.dim() == 4 else q.unsqueeze(1)
+    b, T, h, d = q4.shape
+    g = k.shape[1]
+    if k.dtype in _FP8_TYPES:
+        kvd = FP8_E4M3
+        _check_fp8(k, v, k_scale, v_scale, g)
+    else:
+        kvd = _dtype_code(k.dtype)
+    desc = DecodeDesc()
+    desc.q, desc.k, desc.v, desc.seq_lens = _ptr(q4), _ptr(k), _ptr(v), _ptr(seq_lens)
+    desc.b, desc.T, desc.h, desc.g, desc.d = b, T, h, g, d
+    if block_table is not None:
+        _dev(block_table, "block_table")
+        desc.block_table = _ptr(block_table)
+        desc.page_size, desc.max_pages, desc.num_pages = k.shape[2], block_table.shape[1], k.shape[0]
+    else:
+        desc.S = k.shape[2]
+    if kvd == FP8_E4M3:
+        desc.k_scale, desc.v_scale = _ptr(k_scale), _ptr(v_scale)
+    desc.kv_dtype, desc.window, desc.split_chunk = kvd, int(window), int(split_chunk)
+    desc.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o4 = None if out is None else (out if out.dim() == 4 else out.unsqueeze(1))
+    if o4 is None:
+        o4 = torch.empty((b, T, h, d), dtype=torch.float32, device=q.device)
+    _dev(o4, "out")
+    desc.out = _ptr(o4)
+    if workspace is None:
+        n = int(lib().mqa_decode_ex_workspace_bytes(ctypes.byref(desc)))
+        if n == 0:
+            raise ValueError("invalid arguments")
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    desc.workspace = _ptr(workspace)
+    desc.workspace_bytes = workspace.numel() * workspace.element_size()
+    desc.err_flags = _ptr(err_flags)
+    st = lib().mqa_decode_attn_ex(ctypes.byref(desc), _stream(q.device))
+    if st != OK:
+        raise MQAError(st, "mqa_decode_attn_ex")
+    return o4 if q.dim() == 4 else o4[:, 0]
+
+
+def _cos_sin(cs, d):
+    _dev(cs, "cos_sin")
+    if cs.dtype != torch.float32 or cs.dim() != 3 or cs.shape[1:] != (d // 2, 2):
+        raise ValueError("cos_sin must be float32 [n_pos, d/2, 2]")
+    return cs.shape[0]
+
+
+def rope_q(q, cos_sin, seq_lens, err_flags=None):
+    """Rotate q ([b, h, d] or [b, T, h, d], bf16) in place at positions L - T + tau."""
+    q4 = _rows4(q, "q")
+    _dev(seq_lens, "seq_lens")
+    b, T, h, d = q4.shape
+    n_pos = _cos_sin(cos_sin, d)
+    st = lib().mqa_rope_q(_ptr(q4), _ptr(cos_sin), n_pos, _ptr(seq_lens), b, T, h, d,
+                          _ptr(err_flags), _stream(q.device))
+    if st != OK:
+        raise MQAError(st, "mqa_rope_q")
+    return q
+
+
+def append_kv_rope(k_cache, v_cache, k_new, v_new, cos_sin, seq_lens, err_flags=None):
+    """append_kv_multi with the keys rotated at their positions (bf16 cache)."""
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
+        _dev(t, n)
+    kn, vn = _rows4(k_new, "k_new"), _rows4(v_new, "v_new")
+    b, g, S, d = k_cache.shape
+    if k_cache.dtype != torch.bfloat16 or v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise TypeError("the rotated append takes a bf16 cache")
+    if kn.shape[0] != b or kn.shape[2:] != (g, d) or vn.shape != kn.shape:
+        raise ValueError("new rows must be [b, (T,) g, d]")
+    n_pos = _cos_sin(cos_sin, d)
+    st = lib().mqa_append_kv_rope(_ptr(k_cache), _ptr(v_cache), _ptr(kn), _ptr(vn), _ptr(cos_sin),
+                                  n_pos, _ptr(seq_lens), b, kn.shape[1], g, S, d, _ptr(err_flags),
+                                  _stream(k_cache.device))
+    if st != OK:
+        raise MQAError(st, "mqa_append_kv_rope")

@@ -284,6 +284,107 @@ __global__ void append_kv_fp8_kernel(uint8_t *__restrict__ kc, uint8_t *__restri
 }
 
 // ---------------------------------------------------------------------------
+// rotary position embedding on bf16 rows
+// ---------------------------------------------------------------------------
+
+// Nearest bf16 of a float, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Rotate 8 pairs of a bf16 row in place: elements i0 .. i0+7 (a) and their
+// partners i0 + d/2 .. (b), turned by the angles of position pos: a' = a c -
+// b s, b' = b c + a s, each product and sum rounded to fp32 in that order
+// (no fused multiply-add), then to bf16 ([GQA notes] §十 item 6: position
+// information applied per head, to queries and keys alike; cos_sin [n][d/2][2]).
+__device__ __forceinline__ void rope8(const u32x4_t &a_in, const u32x4_t &b_in, const float *cs,
+                                      u32x4_t &a_out, u32x4_t &b_out) {
+#pragma clang fp contract(off)  // each product rounded on its own, as specified
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+        uint32_t ra = 0, rb = 0;
+#pragma unroll
+        for (int hlf = 0; hlf < 2; hlf++) {
+            const int e = 2 * w + hlf;
+            const float a = __builtin_bit_cast(float, (a_in[w] >> (16 * hlf)) << 16);
+            const float b = __builtin_bit_cast(float, (b_in[w] >> (16 * hlf)) << 16);
+            const float c = cs[2 * e], sn = cs[2 * e + 1];
+            const float ac = a * c, bs = b * sn, bc = b * c, as = a * sn;
+            const float na = ac - bs, nb = bc + as;
+            ra |= bf16_rne(na) << (16 * hlf);
+            rb |= bf16_rne(nb) << (16 * hlf);
+        }
+        a_out[w] = ra;
+        b_out[w] = rb;
+    }
+}
+
+// q [b][T][h][d] rotated in place, token tau of sequence i at position
+// L_i - T + tau. Thread t takes 8 pairs of one row.
+__global__ void rope_q_kernel(uint16_t *__restrict__ q, const float *__restrict__ cos_sin, int n_pos,
+                              const int32_t *__restrict__ seq_lens, int b, int T, int h, int d,
+                              int32_t *__restrict__ err) {
+    const int groups = d >> 4;  // 8-pair groups per row
+    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (long long)b * T * h * groups) return;
+    const int c = (int)(t % groups);
+    const long long row = t / groups;  // (i, tau, hq)
+    const int tau = (int)(row / h % T), i = (int)(row / h / T);
+    const int pos = seq_lens[i] - T + tau;
+    if (pos < 0 || pos >= n_pos) {
+        if (c == 0 && row % h == 0 && err) atomicOr(err, pos < 0 ? MQA_DEVERR_SEQLEN : MQA_DEVERR_ROPE);
+        return;
+    }
+    uint16_t *x = q + row * d + 8 * c;
+    const float *cs = cos_sin + ((size_t)pos * (d >> 1) + 8 * c) * 2;
+    u32x4_t a = *(const u32x4_t *)x, bb = *(const u32x4_t *)(x + (d >> 1));
+    u32x4_t na, nb;
+    rope8(a, bb, cs, na, nb);
+    *(u32x4_t *)x = na;
+    *(u32x4_t *)(x + (d >> 1)) = nb;
+}
+
+// The T-token append with the keys rotated at their positions (values as
+// they are): bf16 cache [b][g][S][d], new rows [b][T][g][d]. Thread t takes
+// 8 pairs of one (sequence, token, K/V head).
+__global__ void append_kv_rope_kernel(uint16_t *__restrict__ kc, uint16_t *__restrict__ vc,
+                                      const uint16_t *__restrict__ kn,
+                                      const uint16_t *__restrict__ vn,
+                                      const float *__restrict__ cos_sin, int n_pos,
+                                      const int32_t *__restrict__ seq_lens, int b, int T, int g,
+                                      int S, int d, int32_t *__restrict__ err) {
+    const int groups = d >> 4;
+    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (long long)b * T * g * groups) return;
+    const int c = (int)(t % groups);
+    const long long r = t / groups;  // ((i * T + tau) * g + j)
+    const int j = (int)(r % g), tau = (int)(r / g % T), i = (int)(r / g / T);
+    const bool first = c == 0 && j == 0 && tau == 0;
+    const int L = seq_lens[i];
+    if (L < T || L > S) {
+        if (first && err) atomicOr(err, MQA_DEVERR_SEQLEN);
+        return;
+    }
+    const int pos = L - T + tau;
+    if (pos >= n_pos) {
+        if (c == 0 && j == 0 && err) atomicOr(err, MQA_DEVERR_ROPE);
+        return;
+    }
+    const size_t src = (size_t)r * d + 8 * c;
+    const size_t dst = (((size_t)i * g + j) * S + pos) * d + 8 * c;
+    const int hd = d >> 1;
+    u32x4_t na, nb;
+    rope8(*(const u32x4_t *)(kn + src), *(const u32x4_t *)(kn + src + hd),
+          cos_sin + ((size_t)pos * hd + 8 * c) * 2, na, nb);
+    *(u32x4_t *)(kc + dst) = na;
+    *(u32x4_t *)(kc + dst + hd) = nb;
+    *(u32x4_t *)(vc + dst) = *(const u32x4_t *)(vn + src);
+    *(u32x4_t *)(vc + dst + hd) = *(const u32x4_t *)(vn + src + hd);
+}
+
+// ---------------------------------------------------------------------------
 // split kernel: one wave per query head in the score phase, one lane per row
 // ---------------------------------------------------------------------------
 
@@ -871,10 +972,12 @@ __device__ __forceinline__ void poison_state(MfmaState<D> (&st)[NHB], int32_t *e
 // also stops at its own t_row[b] (its token's causal end, per lane, <=
 // t_end); t_lo is the smallest t_row of the wave. A row can then have no
 // position in a step, so exponentials of masked scores are set to 0 (not
-// exp2(-inf - -inf)).
+// exp2(-inf - -inf)). With a sliding window row r also starts at t_rs[hb]
+// (per lane); t_hs is the latest start of the wave (0: no window).
 template <int D, bool MULTI, int NHB, bool F8 = false>
 __device__ __forceinline__ void compute_step(const StepData<D, F8> &sd, int t0, int t_end, int t_lo,
-                                             const int (&t_row)[NHB],
+                                             const int (&t_row)[NHB], int t_hs,
+                                             const int (&t_rs)[NHB],
                                              const bf16x8_t (&qop)[NHB][MfmaCfg<D>::KSTEPS],
                                              MfmaState<D> (&st)[NHB], uint8_t *vb, int lane,
                                              float qk_scale_log2) {
@@ -883,6 +986,7 @@ __device__ __forceinline__ void compute_step(const StepData<D, F8> &sd, int t0, 
     const int r = lane & 15, qd = lane >> 4;
     const int vl_row = lane / F::VCPR, vl_chunk = lane % F::VCPR;
     const bool tail = t0 + C::STEP > (MULTI ? t_lo : t_end);
+    const bool head = MULTI && t0 < t_hs;  // wave-uniform
     const auto &vld = sd.vld;
     // K operands (fp8: decoded to bf16 here; the scales are applied outside)
     bf16x8_t kop[2][C::KSTEPS];
@@ -912,7 +1016,9 @@ __device__ __forceinline__ void compute_step(const StepData<D, F8> &sd, int t0, 
 #pragma unroll
         for (int e = 0; e < 8; e++) {
             s2[hb][e] = sc[e >> 2][e & 3] * qk_scale_log2;
-            if (tail && t0 + kslot(qd, e) >= (MULTI ? t_row[hb] : t_end)) s2[hb][e] = -INFINITY;
+            const int pos = t0 + kslot(qd, e);
+            if ((tail && pos >= (MULTI ? t_row[hb] : t_end)) || (head && pos < t_rs[hb]))
+                s2[hb][e] = -INFINITY;
         }
     }
 
@@ -1008,10 +1114,32 @@ __device__ __forceinline__ void compute_step(const StepData<D, F8> &sd, int t0, 
 // positions t <= L - T + tau: the causal mask stays per query position when
 // K/V heads are shared ([GQA notes] §十 item 10). Otherwise R = Gh and every
 // row sees t < L.
+// A sliding window of W positions (W > 0; only with MULTI) keeps, for the
+// query at position p, the positions t in (p - W, p]: the window start
+// replaces 0 ([MQA concept] 玩家對比: GQA with a sliding window). The first
+// 32-position step any row of a length-L sequence sees:
+__device__ __forceinline__ int window_first_step(int L, int T, int W) {
+    return W > 0 ? max(0, L - T + 1 - W) / 32 : 0;
+}
+
 template <bool MULTI>
 struct QRows {
     int T, Gh, h;
+    int W;  // sliding window (0: none)
     __device__ __forceinline__ int tok(int rho) const { return MULTI ? rho / Gh : 0; }
+    __device__ __forceinline__ int first_step(int L) const {
+        if constexpr (MULTI)
+            return window_first_step(L, T, W);
+        else
+            return 0;
+    }
+    // first position row rho of a length-L sequence sees
+    __device__ __forceinline__ int row_start(int L, int rho) const {
+        if constexpr (MULTI)
+            return W > 0 ? max(0, L - T + 1 + rho / Gh - W) : 0;
+        else
+            return 0;
+    }
     __device__ __forceinline__ size_t row(int i, int j, int rho) const {
         if constexpr (MULTI)
             return ((size_t)i * T + rho / Gh) * h + (size_t)j * Gh + rho % Gh;
@@ -1028,7 +1156,8 @@ struct QRows {
 template <int D, bool MULTI, int NHB, int NBUF, bool F8, class Src>
 __device__ __forceinline__ void run_steps(const Src &src, const StepSrc &nothing, int s_begin,
                                           int s_end, int stride, int t_end, int t_lo,
-                                          const int (&t_row)[NHB],
+                                          const int (&t_row)[NHB], int t_hs,
+                                          const int (&t_rs)[NHB],
                                           const bf16x8_t (&qop)[NHB][MfmaCfg<D>::KSTEPS],
                                           MfmaState<D> (&st)[NHB], uint8_t *vb, int lane,
                                           float qk_scale_log2, int32_t *err) {
@@ -1052,8 +1181,8 @@ __device__ __forceinline__ void run_steps(const Src &src, const StepSrc &nothing
             const int sn = stp + (NBUF - 1) * stride;
             bad[kn] = false;
             load_step<D, F8>(sn < s_end ? src(sn, bad[kn]) : nothing, lane, buf[kn]);
-            compute_step<D, MULTI, NHB, F8>(buf[k], stp * C::STEP, t_end, t_lo, t_row, qop, st,
-                                            vb, lane, qk_scale_log2);
+            compute_step<D, MULTI, NHB, F8>(buf[k], stp * C::STEP, t_end, t_lo, t_row, t_hs, t_rs,
+                                            qop, st, vb, lane, qk_scale_log2);
             if (bad[k]) poison_state<D>(st, err, lane);
             stp += stride;
             if (stp >= s_end) return;
@@ -1122,7 +1251,11 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
     const int t_begin = s * chunk;
     if (t_begin >= L) return;
     const int t_end = min(t_begin + chunk, L);
-    const int nsteps = (t_end - t_begin + C::STEP - 1) / C::STEP;
+    // steps of this partition any row sees, numbered from the sequence start
+    // (a window can leave a partition with none: the combine skips it)
+    const int s0 = max(t_begin / C::STEP, qr.first_step(L));
+    const int nsteps = (t_end + C::STEP - 1) / C::STEP - s0;
+    if (nsteps <= 0) return;
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1130,22 +1263,22 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
 
     // padded rows reuse the last real one and are never written out
     bf16x8_t qop[NHB][C::KSTEPS];
-    int t_row[NHB];  // causal ends (several tokens): this lane's row in each block
+    int t_row[NHB], t_rs[NHB];  // causal ends and window starts: this lane's row in each block
 #pragma unroll
     for (int b = 0; b < NHB; b++) {
         const int rho = min((hg * NHB + b) * C::HB + r, R - 1);
         load_q_operand<D, F8>(q, qr.row(i, j, rho), qd, qop[b]);
         t_row[b] = min(t_end, L - qr.T + 1 + qr.tok(rho));
+        t_rs[b] = qr.row_start(L, rho);
     }
-    const int t_lo = min(t_end, L - qr.T + 1);  // the earliest of the wave
+    const int t_lo = min(t_end, L - qr.T + 1);  // the earliest end of the wave
+    const int t_hs = qr.row_start(L, R - 1);     // and the latest start
 
-    // steps of this partition, numbered from the sequence start
-    const int s0 = t_begin / C::STEP;
     const int ne = KV::kPaged ? min(2 * nsteps, KV::kStage) : 0;
     if constexpr (KV::kPaged) {
         stage_page_ids<256>(kv, pg, ne, [&](int e, int &i_, int &row, int &L_) {
             i_ = i;
-            row = t_begin + 16 * e;
+            row = s0 * C::STEP + 16 * e;
             L_ = L;
         });
         __syncthreads();
@@ -1176,7 +1309,7 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
     const float qk_scale_log2 = F8 ? qk_base * k_scale[j] : qk_base;
     const float vsc = F8 ? v_scale[j] : 1.f;
     run_steps<D, MULTI, NHB, 2, F8>(src, kv.none(), s0 + w, s0 + nsteps, C::NW, t_end, t_lo, t_row,
-                                    qop, st, vbuf[w], lane, qk_scale_log2, err);
+                                    t_hs, t_rs, qop, st, vbuf[w], lane, qk_scale_log2, err);
 
     // merge the waves' states block by block through the staging buffers
     float *mrg = (float *)&vbuf[0][0];
@@ -1227,8 +1360,8 @@ constexpr int kRing = 16;              // segment records per head block
 
 // steps of sequence i (0 for an invalid length: below the T tokens of the
 // step, or past the capacity)
-__device__ __forceinline__ int seq_steps(int L, int S, int T) {
-    return (L < T || L > S) ? 0 : (L + 31) / 32;
+__device__ __forceinline__ int seq_steps(int L, int S, int T, int W) {
+    return (L < T || L > S) ? 0 : (L + 31) / 32 - window_first_step(L, T, W);
 }
 
 // Exclusive prefixes over sequences, whole work-group (NT threads): steps
@@ -1238,7 +1371,7 @@ __device__ __forceinline__ int seq_steps(int L, int S, int T) {
 // host keeps the step total below 2^31.
 template <int NT>
 __device__ __forceinline__ void unit_prefix(const int32_t *__restrict__ seq_lens, int b, int S,
-                                            int T, int units_per_seq, int *pre, int *vpre,
+                                            int T, int W, int units_per_seq, int *pre, int *vpre,
                                             int *lens, int2 *wtot) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int per = (b + NT - 1) / NT;
@@ -1247,7 +1380,7 @@ __device__ __forceinline__ void unit_prefix(const int32_t *__restrict__ seq_lens
     for (int a = a0; a < a1; a++) {
         const int L = seq_lens[a];
         lens[a] = L;  // kept in LDS for the rest of the kernel
-        const int n = seq_steps(L, S, T);
+        const int n = seq_steps(L, S, T, W);
         run += n;
         vrun += n > 0;
     }
@@ -1269,7 +1402,7 @@ __device__ __forceinline__ void unit_prefix(const int32_t *__restrict__ seq_lens
     }
     acc *= units_per_seq;
     for (int a = a0; a < a1; a++) {
-        const int n = seq_steps(lens[a], S, T);
+        const int n = seq_steps(lens[a], S, T, W);
         pre[a] = acc;
         vpre[a] = vacc;
         acc += n * units_per_seq;
@@ -1352,7 +1485,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
 
     if (threadIdx.x < NW) slot_busy[threadIdx.x] = 0;
     if (threadIdx.x < 4) cursor[threadIdx.x] = 0;
-    unit_prefix<64 * NW>(seq_lens, b, S, qr.T, g, pre, vpre, lens, wtot);  // its barriers publish the above
+    unit_prefix<64 * NW>(seq_lens, b, S, qr.T, qr.W, g, pre, vpre, lens, wtot);  // its barriers publish the above
     // everything that steers the loops below is wave-uniform: keep it scalar
     const int T = __builtin_amdgcn_readfirstlane(pre[b]);
     const int wg = blockIdx.x;
@@ -1390,7 +1523,8 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
             }
             i_ = lo;
             L_ = lens[lo];
-            row = (tt - pre[lo]) % seq_steps(L_, S, qr.T) * C::STEP + 16 * (e & 1);
+            row = ((tt - pre[lo]) % seq_steps(L_, S, qr.T, qr.W) + qr.first_step(L_)) * C::STEP +
+                  16 * (e & 1);
         });
 
     // The range's last segment [xl, x1) is claimed first, then [x0, xl): a
@@ -1414,8 +1548,8 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
     const int i_last = __builtin_amdgcn_readfirstlane(last_seq);
     const int ord0 = __builtin_amdgcn_readfirstlane(vpre[i_first]) * g +
                      (x0 - __builtin_amdgcn_readfirstlane(pre[i_first])) /
-                         seq_steps(__builtin_amdgcn_readfirstlane(lens[i_first]), S, qr.T);
-    const int n_last = seq_steps(__builtin_amdgcn_readfirstlane(lens[i_last]), S, qr.T);
+                         seq_steps(__builtin_amdgcn_readfirstlane(lens[i_first]), S, qr.T, qr.W);
+    const int n_last = seq_steps(__builtin_amdgcn_readfirstlane(lens[i_last]), S, qr.T, qr.W);
     const int p_last = __builtin_amdgcn_readfirstlane(pre[i_last]);
     const int u0_last = p_last + (x1 - 1 - p_last) / n_last * n_last;  // the last unit's first step
     const int xl = max(x0, u0_last);
@@ -1460,7 +1594,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
         if (tt < u0_) i_ = i_first;
         while (__builtin_amdgcn_readfirstlane(pre[i_ + 1]) <= tt) i_++;
         L_ = __builtin_amdgcn_readfirstlane(lens[i_]);
-        n_ = seq_steps(L_, S, qr.T);
+        n_ = seq_steps(L_, S, qr.T, qr.W);
         const int p = __builtin_amdgcn_readfirstlane(pre[i_]);
         j_ = (tt - p) / n_;
         u0_ = p + j_ * n_;
@@ -1474,7 +1608,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
     // where the rows of flat step tt (of unit (i_, j_), first step u0_) are
     auto src_of = [&](int i_, int j_, int L_, int u0_, int tt, bool &bad)
                       __attribute__((always_inline)) {
-        const int t0 = (tt - u0_) * C::STEP;
+        const int t0 = (tt - u0_ + qr.first_step(L_)) * C::STEP;
         if constexpr (KV::kPaged) {
             const int e = 2 * (tt - x0);
             int id0, id1;
@@ -1625,11 +1759,17 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
         load_step<D, F8>(more ? src_of(ni, nj, nL, nu0, tn, bad_next) : kv.none(), lane, later);
         // causal ends of several tokens: this lane's row in each block, the
         // wave's earliest
-        int t_row[NHB];
+        // (and the window starts)
+        int t_row[NHB], t_rs[NHB];
 #pragma unroll
-        for (int k = 0; k < NHB; k++) t_row[k] = cL - qr.T + 1 + tau[k];
-        compute_step<D, MULTI, NHB, F8>(now, (t - cu0) * C::STEP, cL, cL - qr.T + 1, t_row, qop,
-                                        st, vbuf[w], lane, cqs);
+        for (int k = 0; k < NHB; k++) {
+            t_row[k] = cL - qr.T + 1 + tau[k];
+            t_rs[k] = qr.W > 0 ? max(0, t_row[k] - qr.W) : 0;
+        }
+        const int t_hs = qr.W > 0 ? max(0, cL - qr.W) : 0;
+        compute_step<D, MULTI, NHB, F8>(now, (t - cu0 + qr.first_step(cL)) * C::STEP, cL,
+                                        cL - qr.T + 1, t_row, t_hs, t_rs, qop, st, vbuf[w], lane,
+                                        cqs);
         if (bad_now) poison_state<D>(st, err, lane);
         bad_now = bad_next;
         mine++;
@@ -1765,11 +1905,13 @@ combine_kernel(const float *__restrict__ part_o, const float2 *__restrict__ part
         return;
     }
     const int n = (L + chunk - 1) / chunk;
+    // partitions wholly before a window hold no partial
+    const int n0 = window_first_step(L, qr.T, qr.W) * 32 / chunk;
     const float2 *ml = part_ml + row * nsplit;
     const float *po = part_o + row * nsplit * D + 4 * c4;
     float M = -INFINITY, den = 0.f;
     f32x4_t num = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int p0 = pl; p0 < n; p0 += BATCH * PL) {
+    for (int p0 = n0 + pl; p0 < n; p0 += BATCH * PL) {
         float2 e[BATCH];
         f32x4_t o[BATCH];
 #pragma unroll
@@ -1977,12 +2119,13 @@ template <int D, class KV, bool MULTI, int NHB>
 mqa_status run_mfma_rows(const KV &kv, const void *q, const int32_t *seq_lens, int b, int T,
                          int h, int g, int S, float qs, const float *k_scale,
                          const float *v_scale, float *out, void *workspace, int chunk,
-                         int nsplit, bool balanced, int32_t *err_flags, hipStream_t stream) {
+                         int nsplit, bool balanced, int32_t *err_flags, hipStream_t stream,
+                         int W) {
     const int Gh = h / g, R = T * Gh;
     const int nhb = (R + 15) / 16;
     const int ngroups = (nhb + NHB - 1) / NHB;
-    const QRows<MULTI> qr{T, Gh, h};
-    const QRows<true> qc{T, Gh, h};
+    const QRows<MULTI> qr{T, Gh, h, W};
+    const QRows<true> qc{T, Gh, h, W};
     if (balanced) {
         const int nwg = streamk_wgs(b, g, S);
         const StreamkLayout L = streamk_layout(h, g, D, T);
@@ -2021,27 +2164,29 @@ mqa_status run_mfma_rows(const KV &kv, const void *q, const int32_t *seq_lens, i
     return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
 }
 
+// (several tokens or a sliding window: the MULTI kernels, with per-row
+// ends and starts)
 template <int D, class KV>
 mqa_status run_mfma(const KV &kv, const void *q, const int32_t *seq_lens, int b, int T, int h,
                     int g, int S, float qs, float *out, void *workspace, int chunk, int nsplit,
                     bool balanced, int32_t *err_flags, hipStream_t stream,
-                    const float *k_scale = nullptr, const float *v_scale = nullptr) {
+                    const float *k_scale = nullptr, const float *v_scale = nullptr, int W = 0) {
     const bool two = row_blocks(T * (h / g)).per_wave == 2;
-    if (T > 1) {
+    if (T > 1 || W > 0) {
         if (two)
             return run_mfma_rows<D, KV, true, 2>(kv, q, seq_lens, b, T, h, g, S, qs, k_scale,
                                                  v_scale, out, workspace, chunk, nsplit, balanced,
-                                                 err_flags, stream);
+                                                 err_flags, stream, W);
         return run_mfma_rows<D, KV, true, 1>(kv, q, seq_lens, b, T, h, g, S, qs, k_scale, v_scale,
                                              out, workspace, chunk, nsplit, balanced, err_flags,
-                                             stream);
+                                             stream, W);
     }
     if (two)
         return run_mfma_rows<D, KV, false, 2>(kv, q, seq_lens, b, 1, h, g, S, qs, k_scale, v_scale,
                                               out, workspace, chunk, nsplit, balanced, err_flags,
-                                              stream);
+                                              stream, 0);
     return run_mfma_rows<D, KV, false, 1>(kv, q, seq_lens, b, 1, h, g, S, qs, k_scale, v_scale, out,
-                                          workspace, chunk, nsplit, balanced, err_flags, stream);
+                                          workspace, chunk, nsplit, balanced, err_flags, stream, 0);
 }
 
 // T-token calls: T in [1, S]; beyond one token only the bf16 matrix-core path
@@ -2166,7 +2311,7 @@ mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache, const void
         else dispatch_rows<float, 64>(hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream);
     }
     if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
-    const QRows<true> qc{1, h / g, h};
+    const QRows<true> qc{1, h / g, h, 0};
     if (d == 128)
         hipLaunchKernelGGL(combine_kernel<128>, dim3(h, b), dim3(256), 0, stream, part_o, part_ml,
                            seq_lens, qc, h / g, S, chunk, nsplit, out, err_flags);
@@ -2445,6 +2590,123 @@ mqa_status mqa_decode_attn_paged_fp8(const void *q, const void *k_pages, const v
     return run_mfma<64>(PagedKV<64, true>{kb, vb, block_table, g, page_size, max_pages, num_pages}, q,
                         seq_lens, b, T, h, g, S, qs, out, workspace, chunk, nsplit, bal, err_flags,
                         stream, k_scale, v_scale);
+}
+
+// ---- every option at once; rotary position embedding ----
+
+extern "C++" {
+namespace {
+// Validate a descriptor; on success S is the capacity (paged: P * max_pages).
+mqa_status check_desc(const mqa_decode_desc *ds, int &S) {
+    if (!ds) return MQA_ERR_NULL;
+    if (!ds->q || !ds->k || !ds->v || !ds->seq_lens || !ds->out) return MQA_ERR_NULL;
+    if (ds->window < 0 || ds->T < 1) return MQA_ERR_SHAPE;
+    const bool paged = ds->block_table != nullptr;
+    const int kd = ds->kv_dtype;
+    if (kd != MQA_F32 && kd != MQA_BF16 && kd != MQA_FP8_E4M3) return MQA_ERR_UNSUPPORTED;
+    if (kd == MQA_F32 && (paged || ds->T != 1 || ds->window != 0)) return MQA_ERR_UNSUPPORTED;
+    if (kd == MQA_FP8_E4M3 && (!ds->k_scale || !ds->v_scale)) return MQA_ERR_NULL;
+    mqa_status st;
+    if (paged) {
+        st = check_paged(ds->b, ds->h, ds->g, ds->page_size, ds->max_pages, ds->num_pages, ds->d,
+                         MQA_BF16, ds->split_chunk);
+        S = ds->page_size * ds->max_pages;
+    } else {
+        st = check_sizes(ds->b, ds->h, ds->g, ds->S, ds->d, kd == MQA_F32 ? MQA_F32 : MQA_BF16,
+                         ds->split_chunk);
+        S = ds->S;
+    }
+    if (st != MQA_OK) return st;
+    if (kd != MQA_F32 && (st = check_tokens(ds->T, ds->h, S, MQA_BF16)) != MQA_OK) return st;
+    if (!aligned16(ds->q) || !aligned16(ds->k) || !aligned16(ds->v) || !aligned16(ds->out))
+        return MQA_ERR_ALIGN;
+    if (kd == MQA_FP8_E4M3 && (((uintptr_t)ds->k_scale & 3u) || ((uintptr_t)ds->v_scale & 3u)))
+        return MQA_ERR_ALIGN;
+    return MQA_OK;
+}
+
+template <int D, bool F8>
+mqa_status run_desc(const mqa_decode_desc *ds, int S, int chunk, int nsplit, bool bal, float qs,
+                    hipStream_t stream) {
+    const uint8_t *kb = (const uint8_t *)ds->k, *vb = (const uint8_t *)ds->v;
+    if (ds->block_table)
+        return run_mfma<D>(PagedKV<D, F8>{kb, vb, ds->block_table, ds->g, ds->page_size,
+                                          ds->max_pages, ds->num_pages},
+                           ds->q, ds->seq_lens, ds->b, ds->T, ds->h, ds->g, S, qs, ds->out,
+                           ds->workspace, chunk, nsplit, bal, ds->err_flags, stream, ds->k_scale,
+                           ds->v_scale, ds->window);
+    return run_mfma<D>(ContigKV<D, F8>{kb, vb, ds->g, S}, ds->q, ds->seq_lens, ds->b, ds->T, ds->h,
+                       ds->g, S, qs, ds->out, ds->workspace, chunk, nsplit, bal, ds->err_flags,
+                       stream, ds->k_scale, ds->v_scale, ds->window);
+}
+}  // namespace
+}  // extern "C++"
+
+size_t mqa_decode_ex_workspace_bytes(const mqa_decode_desc *ds) {
+    int S = 0;
+    if (check_desc(ds, S) != MQA_OK) return 0;
+    if (ds->kv_dtype == MQA_F32)
+        return workspace_need(ds->b, ds->h, ds->g, S, ds->d, MQA_F32, ds->split_chunk,
+                              MQA_KERNEL_AUTO);
+    return workspace_need(ds->b, ds->h, ds->g, S, ds->d, MQA_BF16, ds->split_chunk,
+                          MQA_KERNEL_MFMA, ds->T);
+}
+
+mqa_status mqa_decode_attn_ex(const mqa_decode_desc *ds, hipStream_t stream) {
+    int S = 0;
+    const mqa_status st = check_desc(ds, S);
+    if (st != MQA_OK) return st;
+    if (ds->kv_dtype == MQA_F32)
+        return mqa_decode_attn(ds->q, ds->k, ds->v, ds->seq_lens, ds->b, ds->h, ds->g, S, ds->d,
+                               MQA_F32, ds->scale, ds->out, ds->workspace, ds->workspace_bytes,
+                               ds->split_chunk, ds->err_flags, stream);
+    const mqa_dtype dt = MQA_BF16;
+    const int chunk = resolve_chunk(ds->b, ds->h, ds->g, S, dt, ds->split_chunk, ds->T);
+    const int nsplit = (S + chunk - 1) / chunk;
+    if (!ds->workspace || ds->workspace_bytes < workspace_need(ds->b, ds->h, ds->g, S, ds->d, dt,
+                                                               ds->split_chunk, MQA_KERNEL_MFMA, ds->T))
+        return MQA_ERR_WORKSPACE;
+    if (!aligned16(ds->workspace)) return MQA_ERR_ALIGN;
+    const bool bal = use_streamk(ds->b, ds->h, ds->g, S, dt, ds->split_chunk, MQA_KERNEL_MFMA, ds->T);
+    const float qs = ds->scale * kLog2e;
+    const bool f8 = ds->kv_dtype == MQA_FP8_E4M3;
+    if (ds->d == 128)
+        return f8 ? run_desc<128, true>(ds, S, chunk, nsplit, bal, qs, stream)
+                  : run_desc<128, false>(ds, S, chunk, nsplit, bal, qs, stream);
+    return f8 ? run_desc<64, true>(ds, S, chunk, nsplit, bal, qs, stream)
+              : run_desc<64, false>(ds, S, chunk, nsplit, bal, qs, stream);
+}
+
+mqa_status mqa_rope_q(void *q, const float *cos_sin, int n_pos, const int32_t *seq_lens, int b,
+                      int T, int h, int d, int32_t *err_flags, hipStream_t stream) {
+    if (!q || !cos_sin || !seq_lens) return MQA_ERR_NULL;
+    if (b < 1 || T < 1 || h < 1 || n_pos < 1) return MQA_ERR_SHAPE;
+    if (d != 64 && d != 128) return MQA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(cos_sin)) return MQA_ERR_ALIGN;
+    const long long total = (long long)b * T * h * (d / 16);
+    if ((total + 255) / 256 > 0x7fffffffll) return MQA_ERR_SHAPE;
+    hipLaunchKernelGGL(rope_q_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                       (uint16_t *)q, cos_sin, n_pos, seq_lens, b, T, h, d, err_flags);
+    return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+}
+
+mqa_status mqa_append_kv_rope(void *k_cache, void *v_cache, const void *k_new,
+                              const void *v_new, const float *cos_sin, int n_pos,
+                              const int32_t *seq_lens, int b, int T, int g, int S, int d,
+                              int32_t *err_flags, hipStream_t stream) {
+    if (!k_cache || !v_cache || !k_new || !v_new || !cos_sin || !seq_lens) return MQA_ERR_NULL;
+    mqa_status st = check_sizes(b, g, g, S, d, MQA_BF16, 0);
+    if (st != MQA_OK) return st;
+    if (T < 1 || T > S || n_pos < 1) return MQA_ERR_SHAPE;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new) ||
+        !aligned16(cos_sin))
+        return MQA_ERR_ALIGN;
+    const long long total = (long long)b * T * g * (d / 16);
+    if ((total + 255) / 256 > 0x7fffffffll) return MQA_ERR_SHAPE;
+    hipLaunchKernelGGL(append_kv_rope_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       stream, (uint16_t *)k_cache, (uint16_t *)v_cache, (const uint16_t *)k_new,
+                       (const uint16_t *)v_new, cos_sin, n_pos, seq_lens, b, T, g, S, d, err_flags);
+    return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
 }
 
 }  // extern "C"
