@@ -31,8 +31,17 @@ With --kv-dtype fp8 the cache holds fp8 e4m3 codes with per-K/V-head scales
 (mqa_append_kv_fp8 quantises the new rows, mqa_decode_attn_fp8 reads one byte
 per element): the K/V bytes per position halve; q stays bf16.
 
+With --window W the decode is mqa_decode_attn_ex with a sliding window of W
+positions: a query at position p reads only (p - W, p], so the K/V bytes count
+the L - max(0, L - T + 1 - W) positions the step's tokens see.
+
+With --rope the append is mqa_rope_q + mqa_append_kv_rope (query and new key
+rows rotated at their positions from a cos/sin table built once by the caller,
+contiguous bf16 cache); the rotation adds q read and written
+(2*b*T*h*d*B) and the table rows read (2*b*T*(d/2)*8) to the step's bytes.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--page-size P]
-                       [--tokens T] [--kv-dtype bf16|fp8]
+                       [--tokens T] [--kv-dtype bf16|fp8] [--window W] [--rope]
 """
 from __future__ import annotations
 
@@ -75,6 +84,10 @@ def parse():
                     help="query tokens per sequence per step (causal; 1: plain decode)")
     ap.add_argument("--kv-dtype", choices=["bf16", "fp8"], default="bf16",
                     help="cache element type (fp8: e4m3 codes with per-K/V-head scales)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window of this many positions (mqa_decode_attn_ex); 0: none")
+    ap.add_argument("--rope", action="store_true",
+                    help="rotate q and the new keys at their positions before the append")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -115,6 +128,17 @@ def main() -> int:
     if F8 and w.dtype != torch.bfloat16:
         print("an fp8 cache takes bf16 queries: pick a bf16 workload", file=sys.stderr)
         return 2
+    WIN = args.window
+    ROPE = args.rope
+    if WIN < 0:
+        print("--window takes a positive size (0: none)", file=sys.stderr)
+        return 2
+    if (WIN or ROPE) and args.kernel == "valu":
+        print("the window and rotation calls run the matrix-core kernels only", file=sys.stderr)
+        return 2
+    if ROPE and (P or F8 or w.dtype != torch.bfloat16):
+        print("--rope rotates rows of a contiguous bf16 cache", file=sys.stderr)
+        return 2
     steps_in = []
     for r in range(reps):
         if F8:
@@ -129,9 +153,23 @@ def main() -> int:
             del t["k_cache"], t["v_cache"]  # the pages hold the cache
         steps_in.append(t)
     cap = steps_in[0]["capacity"] if P else w.S
-    ws = torch.empty(mqa.decode_multi_workspace_bytes(w.b, T, w.h, w.g, cap, w.d, w.dtype,
-                                                      args.split_chunk),
-                     dtype=torch.uint8, device=dev)
+    t0 = steps_in[0]
+    if WIN:
+        kk, vv = ("k_pages", "v_pages") if P else ("k_cache", "v_cache")
+        nws = mqa.decode_ex_workspace_bytes(t0["q"], t0[kk], t0[vv], t0["seq_lens"],
+                                            block_table=t0.get("block_table") if P else None,
+                                            k_scale=t0.get("k_scale"), v_scale=t0.get("v_scale"),
+                                            window=WIN, split_chunk=args.split_chunk)
+    else:
+        nws = mqa.decode_multi_workspace_bytes(w.b, T, w.h, w.g, cap, w.d, w.dtype,
+                                               args.split_chunk)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    cos_sin = None
+    if ROPE:
+        # the caller's table: angle pos * 10000^(-2i/d), fp32, [S][d/2][2]
+        inv = np.power(10000.0, -2.0 * np.arange(w.d // 2, dtype=np.float64) / w.d)
+        ang = np.arange(w.S, dtype=np.float64)[:, None] * inv[None, :]
+        cos_sin = torch.from_numpy(np.stack([np.cos(ang), np.sin(ang)], -1).astype(np.float32)).to(dev)
     lens = steps_in[0]["seq_lens"].cpu().numpy().astype(np.int64)
     chunk = mqa.decode_resolve_chunk(w.b, w.h, w.g, cap, w.d, w.dtype, args.split_chunk)
     oshape = (w.b, T, w.h, w.d) if T > 1 else (w.b, w.h, w.d)
@@ -145,20 +183,27 @@ def main() -> int:
         schedule = mqa.decode_schedule(w.b, w.h, w.g, cap, w.d, w.dtype, args.split_chunk, kernel)
     B = w.elem_bytes
     KB = 1 if F8 else B  # bytes per cached element
-    kv_read = int(sum(2 * w.g * int(L) * w.d * KB for L in lens))
+    # positions the step's tokens see: all L, or the window's (L - T + 1 - W, L)
+    seen = [int(L) - (max(0, int(L) - T + 1 - WIN) if WIN else 0) for L in lens]
+    kv_read = int(sum(2 * w.g * n * w.d * KB for n in seen))
     dec_bytes = kv_read + w.b * T * w.h * w.d * B + w.b * T * w.h * w.d * 4
     app_bytes = 2 * (w.b * T * w.g * w.d * (B + KB))  # new rows read, codes or rows written
     if F8:
         dec_bytes += 2 * w.g * 4  # the scales
         app_bytes += 2 * w.g * 4
     if P:
-        dec_bytes += 4 * int(sum(-(-int(L) // P) for L in lens))
+        first = [(max(0, int(L) - T + 1 - WIN) // P if WIN else 0) for L in lens]
+        dec_bytes += 4 * int(sum(-(-int(L) // P) - f for L, f in zip(lens, first)))
         app_bytes += 4 * w.b * T
+    if ROPE:
+        app_bytes += 2 * w.b * T * w.h * w.d * B + 2 * w.b * T * (w.d // 2) * 8
     per_layer = dec_bytes + app_bytes
     step_bytes = per_layer * layers
-    # token tau of a sequence of length L attends L - T + 1 + tau positions
-    flops_per_step = 4 * w.h * w.d * layers * int(sum(T * (int(L) - T + 1) + T * (T - 1) // 2
-                                                      for L in lens))
+    # token tau of a sequence of length L attends L - T + 1 + tau positions (at most W)
+    def attended(L):
+        n = [L - T + 1 + tau for tau in range(T)]
+        return sum(min(x, WIN) if WIN else x for x in n)
+    flops_per_step = 4 * w.h * w.d * layers * int(sum(attended(int(L)) for L in lens))
 
     def layer_call(r, ev=None):
         t = steps_in[r]
@@ -175,12 +220,21 @@ def main() -> int:
             pages = (t["k_pages"], t["v_pages"])
             append = mqa.append_kv_paged_multi if T > 1 else mqa.append_kv_paged
             append(*pages, t["k_new"], t["v_new"], t["block_table"], t["seq_lens"], err_flags=err)
+        elif ROPE:
+            mqa.rope_q(t["q"], cos_sin, t["seq_lens"], err_flags=err)
+            mqa.append_kv_rope(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], cos_sin,
+                               t["seq_lens"], err_flags=err)
         else:
             append = mqa.append_kv_multi if T > 1 else mqa.append_kv
             append(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], t["seq_lens"], err_flags=err)
         if ev is not None:
             ev[0].record()
-        if F8 and P:
+        if WIN:
+            kk, vv = ("k_pages", "v_pages") if P else ("k_cache", "v_cache")
+            mqa.decode_attn_ex(t["q"], t[kk], t[vv], t["seq_lens"],
+                               block_table=t.get("block_table") if P else None,
+                               k_scale=t.get("k_scale"), v_scale=t.get("v_scale"), window=WIN, **kw)
+        elif F8 and P:
             mqa.decode_attn_paged_fp8(t["q"], t["k_pages"], t["v_pages"], *sc, t["block_table"],
                                       t["seq_lens"], **kw)
         elif F8:
@@ -242,7 +296,8 @@ def main() -> int:
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = dec_bytes / (dec_ms_avg * 1e-3) / 1e9
     traffic = None
-    tag = w.name + (f"-paged{P}" if P else "") + (f"-t{T}" if T > 1 else "") + ("-fp8" if F8 else "")
+    tag = (w.name + (f"-paged{P}" if P else "") + (f"-t{T}" if T > 1 else "") + ("-fp8" if F8 else "")
+           + (f"-w{WIN}" if WIN else "") + ("-rope" if ROPE else ""))
     tf = os.path.join(ROOT, "profiles", f"decode_{tag}_traffic.json")
     if os.path.exists(tf):
         rec = json.load(open(tf))
@@ -271,6 +326,7 @@ def main() -> int:
                    "kv_layout": f"paged, {P}-row pages" if P else "contiguous",
                    "query_tokens": T,
                    "kv_dtype": "fp8 e4m3, per-K/V-head scales" if F8 else "bf16",
+                   "window": WIN or None, "rope_on_append": ROPE,
                    "split_chunk": chunk if schedule != "mfma-balanced" else None,
                    "cache_copies_rotated": reps,
                    "accumulate": "fp32", "out": "fp32"},
@@ -278,8 +334,9 @@ def main() -> int:
         "flops_per_step": flops_per_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("mqa_decode_attn" + ("_paged" if P else "")
-                       + ("_fp8" if F8 else "_multi" if T > 1 else ""))
+            "kernel": ("mqa_decode_attn_ex (window)" if WIN else
+                       ("mqa_decode_attn" + ("_paged" if P else "")
+                        + ("_fp8" if F8 else "_multi" if T > 1 else "")))
                       + " launch, schedule " + schedule,
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
@@ -294,13 +351,14 @@ def main() -> int:
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, steps_in[0], lens, per_layer, layers,
-                                              args.cpu_seconds, P, T, F8)
+                                              args.cpu_seconds, P, T, F8, WIN)
 
     print(json.dumps(result), flush=True)
     return 0
 
 
-def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1, F8=False):
+def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1, F8=False,
+                 window=0):
     """The oracle (plain double loops) on the host cores, one layer's step."""
     import numpy as np
 
@@ -311,7 +369,21 @@ def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1
     scale = float(np.float32(1.0 / math.sqrt(w.d)))
     lens32 = lens.astype(np.int32)
     q = W.to_oracle(t["q"])
-    if F8:
+    if window:
+        kk, vv = ("k_pages", "v_pages") if page_size else ("k_cache", "v_cache")
+        conv = (lambda x: x.cpu().numpy()) if F8 else W.to_oracle
+        kx, vx = conv(t[kk]), conv(t[vv])
+        ks = t["k_scale"].cpu().numpy() if F8 else None
+        vs = t["v_scale"].cpu().numpy() if F8 else None
+        bt = t["block_table"].cpu().numpy() if page_size else None
+
+        def run(n):
+            kn, vn = (kx, vx) if page_size else (kx[:n].copy(), vx[:n].copy())
+            oracle.decode_attn_ex(q[:n].copy(), kn, vn, lens32[:n], scale, window=window,
+                                  k_scale=ks, v_scale=vs,
+                                  block_table=None if bt is None else bt[:n].copy(),
+                                  nthreads=nthreads)
+    elif F8:
         ks, vs = t["k_scale"].cpu().numpy(), t["v_scale"].cpu().numpy()
         if page_size:
             kp, vp = t["k_pages"].cpu().numpy(), t["v_pages"].cpu().numpy()
@@ -341,18 +413,19 @@ def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1
             flat(q[:n].copy(), kc[:n].copy(), vc[:n].copy(), lens32[:n], scale, nthreads=nthreads)
     # bounded sample: the first sequences of the batch, sized to the budget
     # from a one-sequence probe
+    seen = np.array([int(L) - (max(0, int(L) - T + 1 - window) if window else 0) for L in lens32])
     t0 = time.perf_counter()
     run(1)
-    one = max(time.perf_counter() - t0, 1e-4) / max(int(lens32[0]), 1)  # s per position
+    one = max(time.perf_counter() - t0, 1e-4) / max(int(seen[0]), 1)  # s per position seen
     nb = 1
-    while nb < w.b and one * int(lens32[:nb + 1].sum()) * 1.0 <= budget_s:
+    while nb < w.b and one * int(seen[:nb + 1].sum()) * 1.0 <= budget_s:
         nb += 1
     t0 = time.perf_counter()
     run(nb)
     dt = time.perf_counter() - t0
     B = w.elem_bytes
     KB = 1 if F8 else B
-    sample_bytes = int(sum(2 * w.g * int(L) * w.d * KB for L in lens32[:nb])) + nb * T * w.h * w.d * (B + 4)
+    sample_bytes = int(sum(2 * w.g * int(n) * w.d * KB for n in seen[:nb])) + nb * T * w.h * w.d * (B + 4)
     gbs = sample_bytes / dt / 1e9
     return {
         "value": round(gbs, 4),
@@ -360,7 +433,7 @@ def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1
         "cores": nthreads,
         "kind": "oracle",
         "sample": f"decode attention of the first {nb} of {w.b} sequences of one layer "
-                  f"({int(lens32[:nb].sum())} positions), {dt:.2f} s wall",
+                  f"({int(seen[:nb].sum())} positions seen), {dt:.2f} s wall",
         "est_ms_per_step": round(1e3 * (per_layer_bytes * layers) / (gbs * 1e9), 3),
     }
 

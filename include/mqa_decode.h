@@ -351,6 +351,14 @@ typedef struct {
     float scale;                    /* softmax scale, normally 1/sqrt(d) */
 } mqa_decode_desc;
 
+/*
+ * Workspace bytes mqa_decode_attn_ex needs for this descriptor; 0 when the
+ * shape fields are invalid. Reads only the sizes, kv_dtype, window,
+ * split_chunk and whether block_table is NULL: the data pointers may be
+ * unset. mqa_decode_attn_ex checks the pointers (NULL: MQA_ERR_NULL; q, k,
+ * v, out 16-byte aligned, scales 4-byte aligned: else MQA_ERR_ALIGN) and
+ * that workspace_bytes is at least this figure (else MQA_ERR_WORKSPACE).
+ */
 size_t mqa_decode_ex_workspace_bytes(const mqa_decode_desc *desc);
 mqa_status mqa_decode_attn_ex(const mqa_decode_desc *desc, hipStream_t stream);
 

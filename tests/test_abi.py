@@ -329,6 +329,21 @@ def test_decode_ex_workspace_matches_the_dedicated_calls():
         mqa.decode_multi_workspace_bytes(64, 4, 64, 8, 4096, 128, mqa.BF16)
 
 
+def test_decode_ex_workspace_query_reads_sizes_only():
+    """The size query takes a descriptor whose data pointers are unset, and
+    still rejects bad shapes (0 bytes)."""
+    L = mqa.lib()
+    full = ex_desc(b=64, h=64, g=8, S=4096, T=2, window=512)
+    bare = ex_desc(b=64, h=64, g=8, S=4096, T=2, window=512, q=None, k=None, v=None,
+                   seq_lens=None, out=None, workspace=None, kv_dtype=mqa.FP8_E4M3)
+    n = L.mqa_decode_ex_workspace_bytes(ctypes.byref(full))
+    assert n > 0 and L.mqa_decode_ex_workspace_bytes(ctypes.byref(bare)) == n
+    assert L.mqa_decode_ex_workspace_bytes(ctypes.byref(ex_desc(q=None, window=-1))) == 0
+    assert L.mqa_decode_ex_workspace_bytes(ctypes.byref(ex_desc(out=None, T=65))) == 0
+    # the decode itself still checks the pointers
+    assert L.mqa_decode_attn_ex(ctypes.byref(bare), None) == mqa.ERR_NULL
+
+
 def test_rope_calls_reject_bad_arguments_before_launch():
     L = mqa.lib()
     assert L.mqa_rope_q(FAKE, None, 16, FAKE, 2, 1, 8, 128, None, None) == mqa.ERR_NULL

@@ -49,7 +49,8 @@ __all__ = [
     "DEVERR_PAGE", "append_kv_paged", "decode_attn_paged", "decode_paged_workspace_bytes",
     "append_kv_multi", "decode_attn_multi", "append_kv_paged_multi", "decode_attn_paged_multi",
     "decode_multi_workspace_bytes", "decode_multi_schedule", "append_kv_fp8", "decode_attn_fp8",
-    "append_kv_paged_fp8", "decode_attn_paged_fp8", "decode_attn_ex", "rope_q", "append_kv_rope",
+    "append_kv_paged_fp8", "decode_attn_paged_fp8", "decode_attn_ex", "decode_ex_workspace_bytes",
+    "rope_q", "append_kv_rope",
     "DEVERR_ROPE", "FP8_E4M3",
 ]
 
@@ -623,15 +624,9 @@ def decode_attn_paged_fp8(q, k_pages, v_pages, k_scale, v_scale, block_table, se
 
 # ---- every option at once; rotary position embedding ----
 
-def decode_attn_ex(q, k, v, seq_lens, block_table=None, k_scale=None, v_scale=None, window=0,
-                   scale=None, out=None, workspace=None, split_chunk: int = 0, err_flags=None):
-    """Decode with every option (mqa_decode_attn_ex): q [b, h, d] or [b, T, h, d];
-    k, v contiguous [b, g, S, d] or pages [num_pages, g, P, d] with block_table
-    [b, max_pages]; a bf16, f32 or fp8 (uint8 / float8_e4m3fn codes with k_scale,
-    v_scale [g]) cache; window > 0: sliding window. Returns out shaped like q."""
-    for n, t in (("q", q), ("k", k), ("v", v), ("seq_lens", seq_lens)):
+def _ex_desc(q4, k, v, seq_lens, block_table, k_scale, v_scale, window, scale, split_chunk):
+    for n, t in (("q", q4), ("k", k), ("v", v), ("seq_lens", seq_lens)):
         _dev(t, n)
-    q4 = q if q.dim() == 4 else q.unsqueeze(1)
     b, T, h, d = q4.shape
     g = k.shape[1]
     if k.dtype in _FP8_TYPES:
@@ -652,6 +647,30 @@ def decode_attn_ex(q, k, v, seq_lens, block_table=None, k_scale=None, v_scale=No
         desc.k_scale, desc.v_scale = _ptr(k_scale), _ptr(v_scale)
     desc.kv_dtype, desc.window, desc.split_chunk = kvd, int(window), int(split_chunk)
     desc.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    return desc
+
+
+def decode_ex_workspace_bytes(q, k, v, seq_lens, block_table=None, k_scale=None, v_scale=None,
+                              window=0, split_chunk: int = 0) -> int:
+    """Workspace bytes decode_attn_ex needs for these operands
+    (mqa_decode_ex_workspace_bytes; raises on invalid arguments)."""
+    q4 = q if q.dim() == 4 else q.unsqueeze(1)
+    desc = _ex_desc(q4, k, v, seq_lens, block_table, k_scale, v_scale, window, None, split_chunk)
+    n = int(lib().mqa_decode_ex_workspace_bytes(ctypes.byref(desc)))
+    if n == 0:
+        raise ValueError("invalid arguments")
+    return n
+
+
+def decode_attn_ex(q, k, v, seq_lens, block_table=None, k_scale=None, v_scale=None, window=0,
+                   scale=None, out=None, workspace=None, split_chunk: int = 0, err_flags=None):
+    """Decode with every option (mqa_decode_attn_ex): q [b, h, d] or [b, T, h, d];
+    k, v contiguous [b, g, S, d] or pages [num_pages, g, P, d] with block_table
+    [b, max_pages]; a bf16, f32 or fp8 (uint8 / float8_e4m3fn codes with k_scale,
+    v_scale [g]) cache; window > 0: sliding window. Returns out shaped like q."""
+    q4 = q if q.dim() == 4 else q.unsqueeze(1)
+    b, T, h, d = q4.shape
+    desc = _ex_desc(q4, k, v, seq_lens, block_table, k_scale, v_scale, window, scale, split_chunk)
     o4 = None if out is None else (out if out.dim() == 4 else out.unsqueeze(1))
     if o4 is None:
         o4 = torch.empty((b, T, h, d), dtype=torch.float32, device=q.device)

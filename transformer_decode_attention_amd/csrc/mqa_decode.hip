@@ -2597,15 +2597,18 @@ mqa_status mqa_decode_attn_paged_fp8(const void *q, const void *k_pages, const v
 extern "C++" {
 namespace {
 // Validate a descriptor; on success S is the capacity (paged: P * max_pages).
-mqa_status check_desc(const mqa_decode_desc *ds, int &S) {
+// sizes_only: the workspace query, which reads the shape fields and the
+// presence of block_table but no data pointer
+mqa_status check_desc(const mqa_decode_desc *ds, int &S, bool sizes_only = false) {
     if (!ds) return MQA_ERR_NULL;
-    if (!ds->q || !ds->k || !ds->v || !ds->seq_lens || !ds->out) return MQA_ERR_NULL;
+    if (!sizes_only && (!ds->q || !ds->k || !ds->v || !ds->seq_lens || !ds->out))
+        return MQA_ERR_NULL;
     if (ds->window < 0 || ds->T < 1) return MQA_ERR_SHAPE;
     const bool paged = ds->block_table != nullptr;
     const int kd = ds->kv_dtype;
     if (kd != MQA_F32 && kd != MQA_BF16 && kd != MQA_FP8_E4M3) return MQA_ERR_UNSUPPORTED;
     if (kd == MQA_F32 && (paged || ds->T != 1 || ds->window != 0)) return MQA_ERR_UNSUPPORTED;
-    if (kd == MQA_FP8_E4M3 && (!ds->k_scale || !ds->v_scale)) return MQA_ERR_NULL;
+    if (!sizes_only && kd == MQA_FP8_E4M3 && (!ds->k_scale || !ds->v_scale)) return MQA_ERR_NULL;
     mqa_status st;
     if (paged) {
         st = check_paged(ds->b, ds->h, ds->g, ds->page_size, ds->max_pages, ds->num_pages, ds->d,
@@ -2618,6 +2621,7 @@ mqa_status check_desc(const mqa_decode_desc *ds, int &S) {
     }
     if (st != MQA_OK) return st;
     if (kd != MQA_F32 && (st = check_tokens(ds->T, ds->h, S, MQA_BF16)) != MQA_OK) return st;
+    if (sizes_only) return MQA_OK;
     if (!aligned16(ds->q) || !aligned16(ds->k) || !aligned16(ds->v) || !aligned16(ds->out))
         return MQA_ERR_ALIGN;
     if (kd == MQA_FP8_E4M3 && (((uintptr_t)ds->k_scale & 3u) || ((uintptr_t)ds->v_scale & 3u)))
@@ -2644,7 +2648,7 @@ mqa_status run_desc(const mqa_decode_desc *ds, int S, int chunk, int nsplit, boo
 
 size_t mqa_decode_ex_workspace_bytes(const mqa_decode_desc *ds) {
     int S = 0;
-    if (check_desc(ds, S) != MQA_OK) return 0;
+    if (check_desc(ds, S, true) != MQA_OK) return 0;
     if (ds->kv_dtype == MQA_F32)
         return workspace_need(ds->b, ds->h, ds->g, S, ds->d, MQA_F32, ds->split_chunk,
                               MQA_KERNEL_AUTO);
