@@ -10,7 +10,9 @@ Prints one JSON line:
   value        achieved HBM GB/s of the step (algorithmic bytes / step time)
   ms_per_step  step time (µs/step = 1000 * ms_per_step, also in "us_per_step")
   roofline     for the dominant kernel launch (mqa_decode_attn), timed with
-               HIP events on the stream the kernels run on
+               HIP events on the stream the kernels run on (a second pass over
+               the same steps, each behind a spin kernel so that the events
+               time the kernels and not Python's issue of the calls)
   cpu_baseline the CPU oracle, timed on the host's cores on a bounded sample
 
 Algorithmic bytes per decode launch and layer: the K and V rows attended
@@ -273,11 +275,18 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
-    # timed region again, with HIP events around every decode launch (same stream)
+    # timed region again, with HIP events around every decode launch (same
+    # stream). A spin kernel queued ahead of each step keeps the GPU busy while
+    # Python issues the step's calls, so each event pair brackets the decode
+    # kernels alone and not the host's issue time (which small launches would
+    # otherwise show).
+    spin = spin_cycles(torch, 40e-3 * max(1, layers))
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(layers)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for k in range(args.steps):
+        if spin:
+            torch.cuda._sleep(spin)
         step(k, ev[k])
     torch.cuda.synchronize()
     dec_ms = [a.elapsed_time(b) for evk in ev for (a, b) in evk]
@@ -355,6 +364,22 @@ def main() -> int:
 
     print(json.dumps(result), flush=True)
     return 0
+
+
+def spin_cycles(torch, ms: float) -> int:
+    """Argument of torch.cuda._sleep that keeps the GPU busy for about `ms`
+    milliseconds (calibrated with events; 0 where the call is unavailable)."""
+    if not hasattr(torch.cuda, "_sleep"):
+        return 0
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 1 << 20
+    torch.cuda._sleep(n)  # first launch
+    a.record()
+    torch.cuda._sleep(n)
+    b.record()
+    torch.cuda.synchronize()
+    per_ms = n / max(a.elapsed_time(b), 1e-3)
+    return int(min(per_ms * ms, 1 << 40))
 
 
 def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1, F8=False,
