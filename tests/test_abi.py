@@ -324,9 +324,17 @@ def test_decode_ex_workspace_matches_the_dedicated_calls():
     d = ex_desc(b=64, h=64, g=8, S=4096)
     assert L.mqa_decode_ex_workspace_bytes(ctypes.byref(d)) == \
         mqa.decode_workspace_bytes(64, 64, 8, 4096, 128, mqa.BF16)
-    d = ex_desc(b=64, h=64, g=8, S=4096, T=4, window=100)
+    d = ex_desc(b=64, h=64, g=8, S=4096, T=4)
     assert L.mqa_decode_ex_workspace_bytes(ctypes.byref(d)) == \
         mqa.decode_multi_workspace_bytes(64, 4, 64, 8, 4096, 128, mqa.BF16)
+    # a window: partitions cover at most W + T + 30 positions (from the
+    # window's first 32-position step to the end), and no more than S
+    d = ex_desc(b=4, h=32, g=1, S=32768, T=4, window=100)
+    assert L.mqa_decode_ex_workspace_bytes(ctypes.byref(d)) == \
+        mqa.decode_multi_workspace_bytes(4, 4, 32, 1, 134, 128, mqa.BF16)
+    d = ex_desc(b=4, h=32, g=1, S=120, T=4, window=100)
+    assert L.mqa_decode_ex_workspace_bytes(ctypes.byref(d)) == \
+        mqa.decode_multi_workspace_bytes(4, 4, 32, 1, 120, 128, mqa.BF16)
 
 
 def test_decode_ex_workspace_query_reads_sizes_only():

@@ -83,9 +83,17 @@ def test_window_several_tokens(window, T):
 
 @pytest.mark.parametrize("chunk", [0, 64])
 def test_window_partitions(chunk):
-    """Few units (fixed partitions): partitions wholly before the window hold
-    nothing and the combine skips them."""
+    """Few units (fixed partitions): the partitions are counted from the
+    window's first step, so they cover only what the window leaves."""
     run_window(wl("win-part", 4, 32, 1, 128, 3000, 1500, 3000, 920 + chunk), 300,
+               split_chunk=chunk)
+
+
+@pytest.mark.parametrize("window,T,chunk", [(77, 4, 0), (77, 4, 64), (1000, 2, 0), (5, 1, 0)])
+def test_window_partitions_long_context(window, T, chunk):
+    """MQA at long context, a window far shorter than the sequences (which
+    start anywhere relative to the 32-position steps), several tokens."""
+    run_window(wl("win-part-long", 3, 32, 1, 128, 9000, 1, 9000, 925 + window + T), window, T=T,
                split_chunk=chunk)
 
 

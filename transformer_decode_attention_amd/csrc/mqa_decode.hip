@@ -1248,14 +1248,13 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
     const int i = blockIdx.z;
     const int L = seq_lens[i];
     if (L < qr.T || L > S) return;  // reported by the combine
-    const int t_begin = s * chunk;
+    // partitions are counted from the first step any row sees (position 0
+    // without a window), so a window leaves none of them empty
+    const int t_begin = qr.first_step(L) * C::STEP + s * chunk;
     if (t_begin >= L) return;
     const int t_end = min(t_begin + chunk, L);
-    // steps of this partition any row sees, numbered from the sequence start
-    // (a window can leave a partition with none: the combine skips it)
-    const int s0 = max(t_begin / C::STEP, qr.first_step(L));
+    const int s0 = t_begin / C::STEP;  // steps numbered from the sequence start
     const int nsteps = (t_end + C::STEP - 1) / C::STEP - s0;
-    if (nsteps <= 0) return;
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1904,14 +1903,13 @@ combine_kernel(const float *__restrict__ part_o, const float2 *__restrict__ part
         if (k == 0 && threadIdx.x == 0 && err) atomicOr(err, MQA_DEVERR_SEQLEN);
         return;
     }
-    const int n = (L + chunk - 1) / chunk;
-    // partitions wholly before a window hold no partial
-    const int n0 = window_first_step(L, qr.T, qr.W) * 32 / chunk;
+    // partitions start at the window's first step (0 without a window)
+    const int n = (L - window_first_step(L, qr.T, qr.W) * 32 + chunk - 1) / chunk;
     const float2 *ml = part_ml + row * nsplit;
     const float *po = part_o + row * nsplit * D + 4 * c4;
     float M = -INFINITY, den = 0.f;
     f32x4_t num = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int p0 = n0 + pl; p0 < n; p0 += BATCH * PL) {
+    for (int p0 = pl; p0 < n; p0 += BATCH * PL) {
         float2 e[BATCH];
         f32x4_t o[BATCH];
 #pragma unroll
@@ -2009,6 +2007,14 @@ RowBlocks row_blocks(int R) {
     rb.per_wave = rb.blocks > 1 ? 2 : 1;
     rb.groups = (rb.blocks + rb.per_wave - 1) / rb.per_wave;
     return rb;
+}
+
+// Positions a call's partitions cover at most: the capacity, or with a
+// sliding window of W positions and T tokens the span from the window's
+// first 32-position step to the end (L - 32*floor((L-T+1-W)/32) <= W+T+30).
+int window_span(int S, int T, int W) {
+    const long long span = (long long)W + T + 30;
+    return W > 0 && span < S ? (int)span : S;
 }
 
 // (T query tokens: T*h/g query rows per (sequence, K/V head).)
@@ -2127,7 +2133,7 @@ mqa_status run_mfma_rows(const KV &kv, const void *q, const int32_t *seq_lens, i
     const QRows<MULTI> qr{T, Gh, h, W};
     const QRows<true> qc{T, Gh, h, W};
     if (balanced) {
-        const int nwg = streamk_wgs(b, g, S);
+        const int nwg = streamk_wgs(b, g, window_span(S, T, W));
         const StreamkLayout L = streamk_layout(h, g, D, T);
         float *po = (float *)workspace;
         float2 *pml = (float2 *)((uint8_t *)workspace + L.ml_off);
@@ -2652,8 +2658,8 @@ size_t mqa_decode_ex_workspace_bytes(const mqa_decode_desc *ds) {
     if (ds->kv_dtype == MQA_F32)
         return workspace_need(ds->b, ds->h, ds->g, S, ds->d, MQA_F32, ds->split_chunk,
                               MQA_KERNEL_AUTO);
-    return workspace_need(ds->b, ds->h, ds->g, S, ds->d, MQA_BF16, ds->split_chunk,
-                          MQA_KERNEL_MFMA, ds->T);
+    return workspace_need(ds->b, ds->h, ds->g, window_span(S, ds->T, ds->window), ds->d, MQA_BF16,
+                          ds->split_chunk, MQA_KERNEL_MFMA, ds->T);
 }
 
 mqa_status mqa_decode_attn_ex(const mqa_decode_desc *ds, hipStream_t stream) {
@@ -2665,13 +2671,14 @@ mqa_status mqa_decode_attn_ex(const mqa_decode_desc *ds, hipStream_t stream) {
                                MQA_F32, ds->scale, ds->out, ds->workspace, ds->workspace_bytes,
                                ds->split_chunk, ds->err_flags, stream);
     const mqa_dtype dt = MQA_BF16;
-    const int chunk = resolve_chunk(ds->b, ds->h, ds->g, S, dt, ds->split_chunk, ds->T);
-    const int nsplit = (S + chunk - 1) / chunk;
-    if (!ds->workspace || ds->workspace_bytes < workspace_need(ds->b, ds->h, ds->g, S, ds->d, dt,
+    const int Sw = window_span(S, ds->T, ds->window);  // what the partitions cover
+    const int chunk = resolve_chunk(ds->b, ds->h, ds->g, Sw, dt, ds->split_chunk, ds->T);
+    const int nsplit = (Sw + chunk - 1) / chunk;
+    if (!ds->workspace || ds->workspace_bytes < workspace_need(ds->b, ds->h, ds->g, Sw, ds->d, dt,
                                                                ds->split_chunk, MQA_KERNEL_MFMA, ds->T))
         return MQA_ERR_WORKSPACE;
     if (!aligned16(ds->workspace)) return MQA_ERR_ALIGN;
-    const bool bal = use_streamk(ds->b, ds->h, ds->g, S, dt, ds->split_chunk, MQA_KERNEL_MFMA, ds->T);
+    const bool bal = use_streamk(ds->b, ds->h, ds->g, Sw, dt, ds->split_chunk, MQA_KERNEL_MFMA, ds->T);
     const float qs = ds->scale * kLog2e;
     const bool f8 = ds->kv_dtype == MQA_FP8_E4M3;
     if (ds->d == 128)
