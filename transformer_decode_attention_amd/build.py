@@ -29,6 +29,11 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
     # No packed-FP32 instructions anywhere in the device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-core accumulators in ordinary vector registers. The kernels'
+    # online-softmax rescale multiplies the accumulators on the vector ALUs;
+    # with accumulators in AGPRs the compiler copied all of them to VGPRs and
+    # back on every 32-position step (~130 extra instructions per step).
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -964,8 +964,44 @@ __device__ __forceinline__ void poison_state(MfmaState<D> (&st)[NHB], int32_t *e
     if (err && lane == 0) atomicOr(err, MQA_DEVERR_PAGE);
 }
 
+// V rows of the step at t0 into the wave's staging buffer vb (rows at or
+// past t_end zeroed: they may hold anything, NaN included). Done before the
+// next step's loads are issued, so that this step's V registers are free for
+// them (the wave then holds one step of V in registers, not two).
+template <int D, bool F8>
+__device__ __forceinline__ void stage_v_rows(const StepData<D, F8> &sd, int t0, int t_end,
+                                             uint8_t *vb, int lane) {
+    using C = MfmaCfg<D>;
+    using F = KvFmt<D, F8>;
+    const int vl_row = lane / F::VCPR, vl_chunk = lane % F::VCPR;
+    const bool tail = t0 + C::STEP > t_end;  // wave-uniform
+#pragma unroll
+    for (int ii = 0; ii < F::VLOADS; ii++) {
+        const int row = ii * F::VRPI + vl_row;
+        u32x4_t v = sd.vld[ii];
+        if (tail && t0 + row >= t_end) v = u32x4_t{0u, 0u, 0u, 0u};
+        if constexpr (F8) {  // 16 codes -> 16 bf16 (32 bytes) of the row
+            bf16x8_t lo, hi;
+            fp8x16_to_bf16(v, lo, hi);
+            *(bf16x8_t *)(vb + row * C::VSTRIDE + 32 * vl_chunk) = lo;
+            *(bf16x8_t *)(vb + row * C::VSTRIDE + 32 * vl_chunk + 16) = hi;
+        } else {
+            *(u32x4_t *)(vb + row * C::VSTRIDE + 16 * vl_chunk) = v;
+        }
+    }
+}
+template <int D, bool F8>
+__device__ __forceinline__ void stage_v(const StepData<D, F8> &sd, int t0, int t_end, uint8_t *vb,
+                                        int lane) {
+    if (t0 + MfmaCfg<D>::STEP > t_end)  // wave-uniform: a real branch
+        stage_v_rows<D, F8>(sd, t0, t_end, vb, lane);
+    else
+        stage_v_rows<D, F8>(sd, t0, 0x7fffffff, vb, lane);
+}
+
 // One 32-position step [t0, t0+32) of one wave from loaded data, rows >=
-// t_end masked; vb is the wave's staging buffer. The wave computes NHB blocks
+// t_end masked; vb is the wave's staging buffer, which already holds the
+// step's V rows (stage_v). The wave computes NHB blocks
 // of 16 query rows against the same K and V registers (block b: its q
 // operand qop[b] and state st[b]), so the K/V bytes are loaded once for all
 // of them. MULTI (several query tokens per sequence): query row r of block b
@@ -974,20 +1010,20 @@ __device__ __forceinline__ void poison_state(MfmaState<D> (&st)[NHB], int32_t *e
 // position in a step, so exponentials of masked scores are set to 0 (not
 // exp2(-inf - -inf)). With a sliding window row r also starts at t_rs[hb]
 // (per lane); t_hs is the latest start of the wave (0: no window).
-template <int D, bool MULTI, int NHB, bool F8 = false>
-__device__ __forceinline__ void compute_step(const StepData<D, F8> &sd, int t0, int t_end, int t_lo,
-                                             const int (&t_row)[NHB], int t_hs,
-                                             const int (&t_rs)[NHB],
-                                             const bf16x8_t (&qop)[NHB][MfmaCfg<D>::KSTEPS],
-                                             MfmaState<D> (&st)[NHB], uint8_t *vb, int lane,
-                                             float qk_scale_log2) {
+// MASKED: the step may hold masked positions (a tail past the earliest end,
+// or a head before the latest start); the other steps skip every mask test.
+template <int D, bool MULTI, int NHB, bool F8, bool MASKED>
+__device__ __forceinline__ void compute_step_v(const StepData<D, F8> &sd, int t0, int t_end, int t_lo,
+                                               const int (&t_row)[NHB], int t_hs,
+                                               const int (&t_rs)[NHB],
+                                               const bf16x8_t (&qop)[NHB][MfmaCfg<D>::KSTEPS],
+                                               MfmaState<D> (&st)[NHB], uint8_t *vb, int lane,
+                                               float qk_scale_log2) {
     using C = MfmaCfg<D>;
     using F = KvFmt<D, F8>;
     const int r = lane & 15, qd = lane >> 4;
-    const int vl_row = lane / F::VCPR, vl_chunk = lane % F::VCPR;
-    const bool tail = t0 + C::STEP > (MULTI ? t_lo : t_end);
-    const bool head = MULTI && t0 < t_hs;  // wave-uniform
-    const auto &vld = sd.vld;
+    const bool tail = MASKED && t0 + C::STEP > (MULTI ? t_lo : t_end);
+    const bool head = MASKED && MULTI && t0 < t_hs;  // wave-uniform
     // K operands (fp8: decoded to bf16 here; the scales are applied outside)
     bf16x8_t kop[2][C::KSTEPS];
 #pragma unroll
@@ -1019,22 +1055,6 @@ __device__ __forceinline__ void compute_step(const StepData<D, F8> &sd, int t0, 
             const int pos = t0 + kslot(qd, e);
             if ((tail && pos >= (MULTI ? t_row[hb] : t_end)) || (head && pos < t_rs[hb]))
                 s2[hb][e] = -INFINITY;
-        }
-    }
-
-    // ---- V into the staging buffer (rows past the end zeroed: they may be NaN) ----
-#pragma unroll
-    for (int ii = 0; ii < F::VLOADS; ii++) {
-        const int row = ii * F::VRPI + vl_row;
-        u32x4_t v = vld[ii];
-        if (tail && t0 + row >= t_end) v = u32x4_t{0u, 0u, 0u, 0u};
-        if constexpr (F8) {  // 16 codes -> 16 bf16 (32 bytes) of the row
-            bf16x8_t lo, hi;
-            fp8x16_to_bf16(v, lo, hi);
-            *(bf16x8_t *)(vb + row * C::VSTRIDE + 32 * vl_chunk) = lo;
-            *(bf16x8_t *)(vb + row * C::VSTRIDE + 32 * vl_chunk + 16) = hi;
-        } else {
-            *(u32x4_t *)(vb + row * C::VSTRIDE + 16 * vl_chunk) = v;
         }
     }
 
@@ -1108,6 +1128,23 @@ __device__ __forceinline__ void compute_step(const StepData<D, F8> &sd, int t0, 
     }
 }
 
+template <int D, bool MULTI, int NHB, bool F8 = false>
+__device__ __forceinline__ void compute_step(const StepData<D, F8> &sd, int t0, int t_end, int t_lo,
+                                             const int (&t_row)[NHB], int t_hs,
+                                             const int (&t_rs)[NHB],
+                                             const bf16x8_t (&qop)[NHB][MfmaCfg<D>::KSTEPS],
+                                             MfmaState<D> (&st)[NHB], uint8_t *vb, int lane,
+                                             float qk_scale_log2) {
+    // wave-uniform: a real branch between the two forms
+    const bool masked = t0 + MfmaCfg<D>::STEP > (MULTI ? t_lo : t_end) || (MULTI && t0 < t_hs);
+    if (masked)
+        compute_step_v<D, MULTI, NHB, F8, true>(sd, t0, t_end, t_lo, t_row, t_hs, t_rs, qop, st, vb,
+                                                lane, qk_scale_log2);
+    else
+        compute_step_v<D, MULTI, NHB, F8, false>(sd, t0, t_end, t_lo, t_row, t_hs, t_rs, qop, st,
+                                                 vb, lane, qk_scale_log2);
+}
+
 // Query rows of a unit (sequence i, K/V head j). With T query tokens per
 // sequence (MULTI) a unit has R = T * Gh rows, row rho = tau * Gh + head,
 // q and out are [b][T][h][d], and token tau (position L - T + tau) sees the
@@ -1179,6 +1216,7 @@ __device__ __forceinline__ void run_steps(const Src &src, const StepSrc &nothing
             // the step NBUF-1 ahead, into the set computed last
             const int kn = (k + NBUF - 1) % NBUF;
             const int sn = stp + (NBUF - 1) * stride;
+            stage_v<D, F8>(buf[k], stp * C::STEP, t_end, vb, lane);
             bad[kn] = false;
             load_step<D, F8>(sn < s_end ? src(sn, bad[kn]) : nothing, lane, buf[kn]);
             compute_step<D, MULTI, NHB, F8>(buf[k], stp * C::STEP, t_end, t_lo, t_row, t_hs, t_rs,
@@ -1748,6 +1786,8 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
     // one step: claim and prefetch the next, compute this one, close the
     // segment if the next claim leaves it
     auto body = [&](StepData<D, F8> &now, StepData<D, F8> &later) __attribute__((always_inline)) -> bool {
+        const int t0_now = (t - cu0 + qr.first_step(cL)) * C::STEP;
+        stage_v<D, F8>(now, t0_now, cL, vbuf[w], lane);
         const int tn = claim();
         const bool more = tn < x1;
         int ni = ci, nL = cL, nn = cn, nj = cj, nu0 = cu0;
@@ -1766,9 +1806,8 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
             t_rs[k] = qr.W > 0 ? max(0, t_row[k] - qr.W) : 0;
         }
         const int t_hs = qr.W > 0 ? max(0, cL - qr.W) : 0;
-        compute_step<D, MULTI, NHB, F8>(now, (t - cu0 + qr.first_step(cL)) * C::STEP, cL,
-                                        cL - qr.T + 1, t_row, t_hs, t_rs, qop, st, vbuf[w], lane,
-                                        cqs);
+        compute_step<D, MULTI, NHB, F8>(now, t0_now, cL, cL - qr.T + 1, t_row, t_hs, t_rs, qop, st,
+                                        vbuf[w], lane, cqs);
         if (bad_now) poison_state<D>(st, err, lane);
         bad_now = bad_next;
         mine++;
