@@ -328,6 +328,24 @@ def test_few_units_many_heads(h, g, d):
     _check_lens(w, [3000, 1, 1777])
 
 
+def test_largest_head_slab():
+    """The largest cache the kernels take: one K/V head of 2^23 - 32 bf16 rows
+    of d = 128 (just under 2 GiB, the limit of their 32-bit offsets), every
+    position attended, the new row appended at the last one."""
+    S = (1 << 23) - 32
+    w = W.Workload("max-slab", b=1, h=8, g=1, d=128, S=S, dtype=torch.bfloat16, seed=27, L=S)
+    print(check_case(w), flush=True)
+
+
+def test_balanced_schedule_at_its_sequence_limit():
+    """1024 sequences (the most the balanced schedule takes) with ragged lengths."""
+    gen = torch.Generator().manual_seed(10)
+    lens = torch.randint(1, 161, (1024,), generator=gen).tolist()
+    w = W.Workload("b1024", b=1024, h=16, g=2, d=128, S=160, dtype=torch.bfloat16, seed=26)
+    assert mqa.decode_schedule(w.b, w.h, w.g, w.S, w.d, w.dtype) == "mfma-balanced"
+    _check_lens(w, lens)
+
+
 def test_large_batch_uses_fixed_partitions():
     """More sequences than the balanced schedule takes: the fixed partitions serve it."""
     gen = torch.Generator().manual_seed(9)
