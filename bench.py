@@ -14,6 +14,12 @@ Prints one JSON line:
                the same steps, each behind a spin kernel so that the events
                time the kernels and not Python's issue of the calls)
   cpu_baseline the CPU oracle, timed on the host's cores on a bounded sample
+               (and on one thread, for scale)
+  graph        the same steps captured once in a HIP graph and replayed: the
+               step time without Python's issue of the calls (context; the
+               small configurations are bound by that issue time when eager)
+  hbm_copy_gbs a plain 1 GiB device-to-device copy (read + write bytes / time):
+               what a simple streaming kernel attains on this part (context)
 
 Algorithmic bytes per decode launch and layer: the K and V rows attended
 (sum_i 2*g*L_i*d*B) + q (b*h*d*B) + out (b*h*d*4). The append adds
@@ -90,6 +96,8 @@ def parse():
                     help="sliding window of this many positions (mqa_decode_attn_ex); 0: none")
     ap.add_argument("--rope", action="store_true",
                     help="rotate q and the new keys at their positions before the append")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replay timing")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -293,6 +301,10 @@ def main() -> int:
     dec_ms_avg = float(np.mean(dec_ms))
     assert int(err.item()) == 0, "device reported an error"
 
+    graph = None if args.no_graph else graph_timing(torch, step, layers, reps, args.steps)
+    assert int(err.item()) == 0, "device reported an error in the graph replays"
+    hbm_copy = copy_gbs(torch, dev)
+
     if args.copy_probe:
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -356,6 +368,8 @@ def main() -> int:
             "us_per_launch": round(dec_ms_avg * 1e3, 3),
         },
         "cpu_baseline": None,
+        "graph": graph,
+        "hbm_copy_gbs": hbm_copy,
     }
 
     if not args.no_cpu_baseline:
@@ -364,6 +378,66 @@ def main() -> int:
 
     print(json.dumps(result), flush=True)
     return 0
+
+
+def graph_timing(torch, step, layers, reps, steps):
+    """Capture a whole number of steps (one per cache copy, or one step of
+    every layer) in a HIP graph and time its replays; None if capture fails."""
+    per = 1 if layers > 1 else reps
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for k in range(per):
+                step(k)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(per):
+                step(k)
+        g.replay()
+        torch.cuda.synchronize()
+        n = max(1, steps // per)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / (n * per)
+        return {"ms_per_step": round(ms, 6), "us_per_step": round(ms * 1e3, 3),
+                "steps": n * per, "steps_per_graph": per}
+    except RuntimeError as e:  # report, do not fail the bench line
+        return {"error": str(e)[:200]}
+
+
+def copy_gbs(torch, dev) -> float:
+    """Read + write bytes per second of a 1 GiB device copy (best of 5)."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = float("inf")
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b))
+    del src, dst
+    return round(2 * n / (best * 1e-3) / 1e9, 1)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def spin_cycles(torch, ms: float) -> int:
@@ -391,6 +465,7 @@ def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1
     import workloads as W
 
     nthreads = max(1, min(16, os.cpu_count() or 1))
+    threads = [nthreads]  # the thread count run() uses (changed for the one-thread pass)
     scale = float(np.float32(1.0 / math.sqrt(w.d)))
     lens32 = lens.astype(np.int32)
     q = W.to_oracle(t["q"])
@@ -407,7 +482,7 @@ def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1
             oracle.decode_attn_ex(q[:n].copy(), kn, vn, lens32[:n], scale, window=window,
                                   k_scale=ks, v_scale=vs,
                                   block_table=None if bt is None else bt[:n].copy(),
-                                  nthreads=nthreads)
+                                  nthreads=threads[0])
     elif F8:
         ks, vs = t["k_scale"].cpu().numpy(), t["v_scale"].cpu().numpy()
         if page_size:
@@ -416,26 +491,26 @@ def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1
 
             def run(n):
                 oracle.decode_attn_paged_fp8(q[:n].copy(), kp, vp, ks, vs, bt[:n].copy(),
-                                             lens32[:n], scale, nthreads=nthreads)
+                                             lens32[:n], scale, nthreads=threads[0])
         else:
             kc, vc = t["k_cache"].cpu().numpy(), t["v_cache"].cpu().numpy()
 
             def run(n):
                 oracle.decode_attn_fp8(q[:n].copy(), kc[:n].copy(), vc[:n].copy(), ks, vs,
-                                       lens32[:n], scale, nthreads=nthreads)
+                                       lens32[:n], scale, nthreads=threads[0])
     elif page_size:
         kp, vp = W.to_oracle(t["k_pages"]), W.to_oracle(t["v_pages"])
         bt = t["block_table"].cpu().numpy()
         paged = oracle.decode_attn_paged_multi if T > 1 else oracle.decode_attn_paged
 
         def run(n):
-            paged(q[:n].copy(), kp, vp, bt[:n].copy(), lens32[:n], scale, nthreads=nthreads)
+            paged(q[:n].copy(), kp, vp, bt[:n].copy(), lens32[:n], scale, nthreads=threads[0])
     else:
         kc, vc = W.to_oracle(t["k_cache"]), W.to_oracle(t["v_cache"])
         flat = oracle.decode_attn_multi if T > 1 else oracle.decode_attn
 
         def run(n):
-            flat(q[:n].copy(), kc[:n].copy(), vc[:n].copy(), lens32[:n], scale, nthreads=nthreads)
+            flat(q[:n].copy(), kc[:n].copy(), vc[:n].copy(), lens32[:n], scale, nthreads=threads[0])
     # bounded sample: the first sequences of the batch, sized to the budget
     # from a one-sequence probe
     seen = np.array([int(L) - (max(0, int(L) - T + 1 - window) if window else 0) for L in lens32])
@@ -459,6 +534,12 @@ def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1
     KB = 1 if F8 else B
     sample_bytes = int(sum(2 * w.g * int(n) * w.d * KB for n in seen[:nb])) + nb * T * w.h * w.d * (B + 4)
     gbs = sample_bytes / dt / 1e9
+    # one thread, on the first sequence alone (bounded the same way)
+    threads[0] = 1
+    t0 = time.perf_counter()
+    run(1)
+    dt1 = time.perf_counter() - t0
+    one_bytes = 2 * w.g * int(seen[0]) * w.d * KB + T * w.h * w.d * (B + 4)
     return {
         "value": round(gbs, 4),
         "unit": "GB/s",
@@ -468,6 +549,8 @@ def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1
                   f"({int(seen[:nb].sum())} positions seen), {dt:.2f} s wall per pass"
                   + (f", mean of {reps} passes" if reps > 1 else ""),
         "est_ms_per_step": round(1e3 * (per_layer_bytes * layers) / (gbs * 1e9), 3),
+        "one_thread_gbs": round(one_bytes / dt1 / 1e9, 4),
+        "cpu": cpu_model(),
     }
 
 
