@@ -69,7 +69,12 @@ SRC = os.path.join(ROOT, "transformer_decode_attention_amd", "csrc", "mqa_decode
 
 
 def source_sha() -> str:
-    return hashlib.sha256(open(SRC, "rb").read()).hexdigest()[:16]
+    """Hash of what the library is built from: the kernel source and the
+    compiler flags (a traffic record taken on another build is not reported)."""
+    from transformer_decode_attention_amd import build
+    h = hashlib.sha256(open(SRC, "rb").read())
+    h.update(" ".join(build.FLAGS).encode())
+    return h.hexdigest()[:16]
 
 
 def parse():
