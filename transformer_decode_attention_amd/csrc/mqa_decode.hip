@@ -1369,6 +1369,151 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
     }
 }
 
+// Fixed partitions for units of more than 16 query rows: one work-group of
+// eight waves per (partition, K/V head, pair of 16-row blocks, sequence).
+// Waves w and w+4 form a pair that takes the partition's steps w%4, w%4 + 4,
+// ... for blocks 2hg and 2hg+1. The pair's loader (w < 4) loads each step
+// once and writes its K (in the score MFMA's operand order, 16 bytes per
+// lane) and its V rows (the staging layout of the transpose reads) into one
+// of the pair's two LDS buffers; after a work-group barrier both waves read
+// the step from there and compute their own block. Each wave then needs one
+// block's registers, so every SIMD holds two waves (a loader and a reader)
+// whose latencies overlap, and the K/V bytes still leave HBM once.
+template <int D, class KV, bool MULTI>
+__global__ void __launch_bounds__(512)
+split_pair_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__restrict__ seq_lens,
+                  const QRows<MULTI> qr, int g, int S, int R, int ngroups, int chunk, int nsplit,
+                  float qk_base, const float *__restrict__ k_scale,
+                  const float *__restrict__ v_scale, float *__restrict__ part_o,
+                  float2 *__restrict__ part_ml, int32_t *__restrict__ err) {
+    using C = MfmaCfg<D>;
+    using F = KvFmt<D, KV::kF8>;
+    constexpr bool F8 = KV::kF8;
+    constexpr int KBYTES = 2 * F::KLOADS * 64 * 16;  // one step's K, operand order
+    constexpr int BUF = KBYTES + C::VBUF + 16;        // + V rows + the step's bad-page flag
+    static_assert(8 * C::HB * (D + 2) * 4 <= 4 * 2 * BUF, "merge scratch must fit");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4][2][BUF];
+    __shared__ int pg[KV::kStage];  // paged: the page ids of the partition's steps
+
+    const int s = blockIdx.x;
+    const int j = blockIdx.y / ngroups;
+    const int hg = blockIdx.y % ngroups;  // blocks 2hg, 2hg+1
+    const int i = blockIdx.z;
+    const int L = seq_lens[i];
+    if (L < qr.T || L > S) return;  // reported by the combine
+    const int t_begin = qr.first_step(L) * C::STEP + s * chunk;
+    if (t_begin >= L) return;
+    const int t_end = min(t_begin + chunk, L);
+    const int s0 = t_begin / C::STEP;
+    const int nsteps = (t_end + C::STEP - 1) / C::STEP - s0;
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, qd = lane >> 4;
+    const int pair = w % 4;
+    const bool loader = w < 4;
+    const int hb = hg * 2 + w / 4;  // this wave's block
+    const bool rows = hb * C::HB < R;
+
+    bf16x8_t qop[1][C::KSTEPS];
+    int t_row[1], t_rs[1];
+    {
+        const int rho = min(hb * C::HB + r, R - 1);  // padded rows reuse the last real one
+        load_q_operand<D, F8>(q, qr.row(i, j, rho), qd, qop[0]);
+        t_row[0] = min(t_end, L - qr.T + 1 + qr.tok(rho));
+        t_rs[0] = qr.row_start(L, rho);
+    }
+    const int t_lo = min(t_end, L - qr.T + 1);
+    const int t_hs = qr.row_start(L, R - 1);
+
+    const int ne = KV::kPaged ? min(2 * nsteps, KV::kStage) : 0;
+    if constexpr (KV::kPaged) {
+        stage_page_ids<512>(kv, pg, ne, [&](int e, int &i_, int &row, int &L_) {
+            i_ = i;
+            row = s0 * C::STEP + 16 * e;
+            L_ = L;
+        });
+        __syncthreads();
+    }
+    auto src = [&](int stp, bool &bad) __attribute__((always_inline)) {
+        const int t0 = stp * C::STEP;
+        if constexpr (KV::kPaged) {
+            const int e = 2 * (stp - s0);
+            int id0, id1;
+            if (e < ne) {
+                id0 = pg[e];
+                id1 = pg[e + 1];
+            } else {
+                id0 = kv.page_id(i, t0, L);
+                id1 = kv.page_id(i, t0 + 16, L);
+            }
+            return kv.step_ids(j, L, t0, __builtin_amdgcn_readfirstlane(id0),
+                               __builtin_amdgcn_readfirstlane(id1), bad);
+        } else {
+            return kv.step(i, j, L, t0, bad);
+        }
+    };
+
+    MfmaState<D> st[1];
+    st[0].reset();
+    const float qk_scale_log2 = F8 ? qk_base * k_scale[j] : qk_base;
+    const float vsc = F8 ? v_scale[j] : 1.f;
+    // every wave runs the same number of iterations (one barrier each)
+    const int niter = (nsteps + 3) / 4;
+    StepData<D, F8> nxt;  // the loader's step in flight
+    bool bad_nxt = false;
+    if (loader) load_step<D, F8>(pair < nsteps ? src(s0 + pair, bad_nxt) : kv.none(), lane, nxt);
+    for (int it = 0; it < niter; it++) {
+        const int stp = s0 + pair + 4 * it;
+        const bool have = stp < s0 + nsteps;  // wave-uniform
+        uint8_t *buf = lds[pair][it & 1];
+        if (loader) {
+            if (have) {
+#pragma unroll
+                for (int pb = 0; pb < 2; pb++)
+#pragma unroll
+                    for (int k = 0; k < F::KLOADS; k++)
+                        *(u32x4_t *)(buf + ((pb * F::KLOADS + k) * 64 + lane) * 16) = nxt.kraw[pb][k];
+                stage_v<D, F8>(nxt, stp * C::STEP, t_end, buf + KBYTES, lane);
+                if (lane == 0) *(int *)(buf + KBYTES + C::VBUF) = bad_nxt ? 1 : 0;
+            }
+            const int sn = stp + 4;
+            bad_nxt = false;
+            load_step<D, F8>(sn < s0 + nsteps ? src(sn, bad_nxt) : kv.none(), lane, nxt);
+        }
+        __syncthreads();  // the pair's buffer holds step stp
+        if (have && rows) {
+            StepData<D, F8> cur;
+#pragma unroll
+            for (int pb = 0; pb < 2; pb++)
+#pragma unroll
+                for (int k = 0; k < F::KLOADS; k++)
+                    cur.kraw[pb][k] = *(const u32x4_t *)(buf + ((pb * F::KLOADS + k) * 64 + lane) * 16);
+            compute_step<D, MULTI, 1, F8>(cur, stp * C::STEP, t_end, t_lo, t_row, t_hs, t_rs, qop, st,
+                                          buf + KBYTES, lane, qk_scale_log2);
+            if (*(const int *)(buf + KBYTES + C::VBUF)) poison_state<D>(st, err, lane);
+        }
+    }
+
+    // merge the four waves of each block through LDS (slots 0..3: block 2hg,
+    // slots 4..7: block 2hg+1)
+    float *mrg = (float *)&lds[0][0][0];
+    float *mls = mrg + 8 * C::HB * D;
+    __syncthreads();  // every wave is done with the buffers
+    publish_state<D>(st[0], mrg, mls, w, lane);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 2 * C::HB * D; idx += 512) {
+        const int bb = idx / (C::HB * D), hh = idx / D % C::HB, x = idx % D;
+        const int hbo = hg * 2 + bb;
+        if (hbo * C::HB + hh >= R) continue;
+        float M, l;
+        const float o = merge_waves<D>(mrg, mls, 4 * bb, 4, hh, x, M, l);
+        const size_t hrow = ((size_t)i * g + j) * R + hbo * C::HB + hh;
+        part_o[(hrow * nsplit + s) * D + x] = o * vsc;
+        if (x == 0) part_ml[hrow * nsplit + s] = make_float2(M, l);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // balanced ("stream-K") schedule for the bf16 kernel
 // ---------------------------------------------------------------------------
@@ -2200,9 +2345,21 @@ mqa_status run_mfma_rows(const KV &kv, const void *q, const int32_t *seq_lens, i
     float *part_o = (float *)workspace;
     float2 *part_ml =
         (float2 *)((uint8_t *)workspace + ((rows * D * sizeof(float) + 255) & ~(size_t)255));
-    hipLaunchKernelGGL((split_mfma_kernel<D, KV, MULTI, NHB>), dim3(nsplit, g * ngroups, b),
-                       dim3(256), 0, stream, (const uint16_t *)q, kv, seq_lens, qr, g, S, R, ngroups,
-                       chunk, nsplit, qs, k_scale, v_scale, part_o, part_ml, err_flags);
+    // more than two blocks of rows (several tokens of many heads): work-groups
+    // of eight waves sharing each step through LDS, one block per wave
+    // (measured: MQA 32K with four tokens 71 -> 55 us); up to two blocks, one
+    // wave computes both (its partitions hold few steps per wave, where the
+    // pair kernel's per-step barrier costs more than its second wave gains)
+    if (nhb > 2) {
+        const int ng2 = (nhb + 1) / 2;
+        hipLaunchKernelGGL((split_pair_kernel<D, KV, MULTI>), dim3(nsplit, g * ng2, b), dim3(512), 0,
+                           stream, (const uint16_t *)q, kv, seq_lens, qr, g, S, R, ng2, chunk, nsplit,
+                           qs, k_scale, v_scale, part_o, part_ml, err_flags);
+    } else {
+        hipLaunchKernelGGL((split_mfma_kernel<D, KV, MULTI, NHB>), dim3(nsplit, g * ngroups, b),
+                           dim3(256), 0, stream, (const uint16_t *)q, kv, seq_lens, qr, g, S, R,
+                           ngroups, chunk, nsplit, qs, k_scale, v_scale, part_o, part_ml, err_flags);
+    }
     if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
     hipLaunchKernelGGL(combine_kernel<D>, dim3(T * h, b), dim3(256), 0, stream, part_o, part_ml,
                        seq_lens, qc, R, S, chunk, nsplit, out, err_flags);
