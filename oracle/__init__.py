@@ -31,6 +31,7 @@ import numpy as np
 F32 = 0
 BF16 = 1
 FP8_E4M3 = 2
+INT8 = 3
 OK = 0
 BAD_LEN = 1
 BAD_SHAPE = 2
@@ -105,6 +106,15 @@ def lib() -> ctypes.CDLL:
         L.oracle_append_kv_paged_fp8.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32,
                                                  i32, i32, i32, i32]
         L.oracle_append_kv_paged_fp8.restype = i32
+        L.oracle_int8_decode.argtypes = [ctypes.c_int8]
+        L.oracle_int8_decode.restype = ctypes.c_double
+        L.oracle_int8_encode.argtypes = [ctypes.c_float]
+        L.oracle_int8_encode.restype = ctypes.c_int8
+        L.oracle_append_kv_int8.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32]
+        L.oracle_append_kv_int8.restype = i32
+        L.oracle_append_kv_paged_int8.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, i32,
+                                                  i32, i32, i32, i32, i32]
+        L.oracle_append_kv_paged_int8.restype = i32
         L.oracle_decode_attn_ex.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, vp,
                                             i32, i32, i32, i32, i32, i32, i32, ctypes.c_float, vp,
                                             i32]
@@ -366,6 +376,52 @@ def append_kv_paged_fp8(k_pages: np.ndarray, v_pages: np.ndarray, k_new: np.ndar
                                             bt.shape[1], num_pages, d)
 
 
+# ---- int8 cache with per-K/V-head scales (the pages' INT8 K/V) ----
+
+def int8_decode(code: int) -> float:
+    """Value of one int8 code before the head's scale (two's complement)."""
+    return float(lib().oracle_int8_decode(int(code)))
+
+
+def int8_encode(x: float) -> int:
+    """int8 code of a float32 value: nearest, ties to even, saturating at +-127, NaN -> 0."""
+    return int(lib().oracle_int8_encode(float(np.float32(x))))
+
+
+def append_kv_int8(k_codes: np.ndarray, v_codes: np.ndarray, k_new: np.ndarray,
+                   v_new: np.ndarray, k_scale: np.ndarray, v_scale: np.ndarray,
+                   seq_lens: np.ndarray) -> int:
+    """append_kv_fp8 with int8 codes ([b, g, S, d] int8)."""
+    assert k_codes.dtype == np.int8 and v_codes.dtype == np.int8
+    assert k_codes.flags.c_contiguous and v_codes.flags.c_contiguous
+    kn = k_new if k_new.ndim == 4 else k_new[:, None]
+    vn = v_new if v_new.ndim == 4 else v_new[:, None]
+    b, g, S, d = k_codes.shape
+    T = kn.shape[1]
+    sl = _c(seq_lens.astype(np.int32))
+    return lib().oracle_append_kv_int8(_ptr(k_codes), _ptr(v_codes), _ptr(_c(kn)), _ptr(_c(vn)),
+                                       _dtype_code(kn), _ptr(_f32(k_scale)), _ptr(_f32(v_scale)),
+                                       _ptr(sl), b, T, g, S, d)
+
+
+def append_kv_paged_int8(k_pages: np.ndarray, v_pages: np.ndarray, k_new: np.ndarray,
+                         v_new: np.ndarray, k_scale: np.ndarray, v_scale: np.ndarray,
+                         block_table: np.ndarray, seq_lens: np.ndarray) -> int:
+    """append_kv_int8 into a paged cache [num_pages, g, page_size, d] of int8 codes."""
+    assert k_pages.dtype == np.int8 and v_pages.dtype == np.int8
+    assert k_pages.flags.c_contiguous and v_pages.flags.c_contiguous
+    kn = k_new if k_new.ndim == 4 else k_new[:, None]
+    vn = v_new if v_new.ndim == 4 else v_new[:, None]
+    num_pages, g, P, d = k_pages.shape
+    b, T = kn.shape[:2]
+    bt = _c(block_table.astype(np.int32))
+    sl = _c(seq_lens.astype(np.int32))
+    return lib().oracle_append_kv_paged_int8(_ptr(k_pages), _ptr(v_pages), _ptr(_c(kn)),
+                                             _ptr(_c(vn)), _dtype_code(kn), _ptr(_f32(k_scale)),
+                                             _ptr(_f32(v_scale)), _ptr(bt), _ptr(sl), b, T, g, P,
+                                             bt.shape[1], num_pages, d)
+
+
 # ---- every option at once; rotary position embedding ----
 
 def decode_attn_ex(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens: np.ndarray,
@@ -373,13 +429,14 @@ def decode_attn_ex(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens: np.nda
                    block_table=None, nthreads: int = 1):
     """Decode with every option: q [b, h, d] or [b, T, h, d]; k, v contiguous
     [b, g, S, d] or pages [num_pages, g, P, d] (with block_table [b, max_pages]);
-    float32, bf16 bits (uint16) or fp8 codes (uint8, with k_scale, v_scale [g]);
+    float32, bf16 bits (uint16), fp8 codes (uint8) or int8 codes (int8), the codes
+    with k_scale, v_scale [g];
     window > 0: a query at position p sees only t in (p - window, p].
     Returns (out shaped like q, status)."""
     q4 = q if q.ndim == 4 else q[:, None]
     b, T, h, d = q4.shape
-    if k.dtype == np.uint8:
-        kvd = FP8_E4M3
+    if k.dtype in (np.uint8, np.int8):
+        kvd = FP8_E4M3 if k.dtype == np.uint8 else INT8
         ks, vs = _f32(k_scale), _f32(v_scale)
     else:
         kvd = _dtype_code(k)

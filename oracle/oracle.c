@@ -42,9 +42,24 @@ uint8_t oracle_fp8_e4m3_encode(float f) {
     return sign | (uint8_t)((E << 3) | (sm - 8));
 }
 
+/* int8 codes, two's complement: the code itself is the value before the
+ * head's scale. Encoding: nearest integer, ties to even (the default
+ * rounding mode), saturating at +-127 (-128 is never produced, so the codes
+ * are symmetric about 0); NaN becomes 0. */
+double oracle_int8_decode(int8_t c) { return (double)c; }
+
+int8_t oracle_int8_encode(float f) {
+    if (isnan(f)) return 0;
+    float r = nearbyintf(f);
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    return (int8_t)r;
+}
+
 /* Read element idx of a buffer of the given type, widened exactly to double. */
 static double elem(const void *base, size_t idx, int dtype) {
     if (dtype == ORACLE_FP8_E4M3) return oracle_fp8_e4m3_decode(((const uint8_t *)base)[idx]);
+    if (dtype == ORACLE_INT8) return oracle_int8_decode(((const int8_t *)base)[idx]);
     if (dtype == ORACLE_F32) {
         float f;
         memcpy(&f, (const char *)base + 4 * idx, 4);
@@ -59,7 +74,7 @@ static double elem(const void *base, size_t idx, int dtype) {
 }
 
 static size_t elem_bytes(int dtype) {
-    return dtype == ORACLE_F32 ? 4u : dtype == ORACLE_FP8_E4M3 ? 1u : 2u;
+    return dtype == ORACLE_F32 ? 4u : (dtype == ORACLE_FP8_E4M3 || dtype == ORACLE_INT8) ? 1u : 2u;
 }
 
 int oracle_append_kv_multi(void *k_cache, void *v_cache, const void *k_new,
@@ -414,17 +429,20 @@ int oracle_decode_attn_paged_fp8(const void *q, int q_dtype, const uint8_t *k_pa
     return run_decode(&J, nthreads);
 }
 
-/* Code of one new element: its fp32 value divided by the head's scale (one
- * correctly rounded fp32 division), then rounded to e4m3. */
-static uint8_t quantise(const void *src, size_t idx, int dtype, float scale) {
+/* Code (of type `code`: fp8 e4m3 or int8) of one new element: its fp32
+ * value divided by the head's scale (one correctly rounded fp32 division),
+ * then encoded. */
+static uint8_t quantise(const void *src, size_t idx, int dtype, float scale, int code) {
     float x = (float)elem(src, idx, dtype); /* exact: the source is f32 or bf16 */
-    return oracle_fp8_e4m3_encode(x / scale);
+    float y = x / scale;
+    if (code == ORACLE_INT8) return (uint8_t)oracle_int8_encode(y);
+    return oracle_fp8_e4m3_encode(y);
 }
 
-int oracle_append_kv_fp8(uint8_t *k_cache, uint8_t *v_cache, const void *k_new,
-                         const void *v_new, int new_dtype, const float *k_scale,
-                         const float *v_scale, const int32_t *seq_lens, int b, int T,
-                         int g, int S, int d) {
+static int append_codes(uint8_t *k_cache, uint8_t *v_cache, const void *k_new,
+                        const void *v_new, int new_dtype, const float *k_scale,
+                        const float *v_scale, const int32_t *seq_lens, int b, int T, int g,
+                        int S, int d, int code) {
     if (b < 1 || T < 1 || g < 1 || S < 1 || d < 1) return ORACLE_BAD_SHAPE;
     int rc = ORACLE_OK;
     for (int i = 0; i < b; i++) {
@@ -438,19 +456,19 @@ int oracle_append_kv_fp8(uint8_t *k_cache, uint8_t *v_cache, const void *k_new,
                 size_t dst = (((size_t)i * g + j) * S + (size_t)(L - T + tau)) * d;
                 size_t src = (((size_t)i * T + tau) * g + j) * d;
                 for (int x = 0; x < d; x++) {
-                    k_cache[dst + x] = quantise(k_new, src + x, new_dtype, k_scale[j]);
-                    v_cache[dst + x] = quantise(v_new, src + x, new_dtype, v_scale[j]);
+                    k_cache[dst + x] = quantise(k_new, src + x, new_dtype, k_scale[j], code);
+                    v_cache[dst + x] = quantise(v_new, src + x, new_dtype, v_scale[j], code);
                 }
             }
     }
     return rc;
 }
 
-int oracle_append_kv_paged_fp8(uint8_t *k_pages, uint8_t *v_pages, const void *k_new,
-                               const void *v_new, int new_dtype, const float *k_scale,
-                               const float *v_scale, const int32_t *block_table,
-                               const int32_t *seq_lens, int b, int T, int g, int page_size,
-                               int max_pages, int num_pages, int d) {
+static int append_codes_paged(uint8_t *k_pages, uint8_t *v_pages, const void *k_new,
+                              const void *v_new, int new_dtype, const float *k_scale,
+                              const float *v_scale, const int32_t *block_table,
+                              const int32_t *seq_lens, int b, int T, int g, int page_size,
+                              int max_pages, int num_pages, int d, int code) {
     if (b < 1 || T < 1 || g < 1 || d < 1 || page_size < 1 || max_pages < 1 || num_pages < 1)
         return ORACLE_BAD_SHAPE;
     int rc = ORACLE_OK;
@@ -471,13 +489,49 @@ int oracle_append_kv_paged_fp8(uint8_t *k_pages, uint8_t *v_pages, const void *k
                 size_t dst = (((size_t)page * g + j) * page_size + (size_t)(t % page_size)) * d;
                 size_t src = (((size_t)i * T + tau) * g + j) * d;
                 for (int x = 0; x < d; x++) {
-                    k_pages[dst + x] = quantise(k_new, src + x, new_dtype, k_scale[j]);
-                    v_pages[dst + x] = quantise(v_new, src + x, new_dtype, v_scale[j]);
+                    k_pages[dst + x] = quantise(k_new, src + x, new_dtype, k_scale[j], code);
+                    v_pages[dst + x] = quantise(v_new, src + x, new_dtype, v_scale[j], code);
                 }
             }
         }
     }
     return rc;
+}
+
+int oracle_append_kv_fp8(uint8_t *k_cache, uint8_t *v_cache, const void *k_new,
+                         const void *v_new, int new_dtype, const float *k_scale,
+                         const float *v_scale, const int32_t *seq_lens, int b, int T,
+                         int g, int S, int d) {
+    return append_codes(k_cache, v_cache, k_new, v_new, new_dtype, k_scale, v_scale, seq_lens,
+                        b, T, g, S, d, ORACLE_FP8_E4M3);
+}
+
+int oracle_append_kv_paged_fp8(uint8_t *k_pages, uint8_t *v_pages, const void *k_new,
+                               const void *v_new, int new_dtype, const float *k_scale,
+                               const float *v_scale, const int32_t *block_table,
+                               const int32_t *seq_lens, int b, int T, int g, int page_size,
+                               int max_pages, int num_pages, int d) {
+    return append_codes_paged(k_pages, v_pages, k_new, v_new, new_dtype, k_scale, v_scale,
+                              block_table, seq_lens, b, T, g, page_size, max_pages, num_pages, d,
+                              ORACLE_FP8_E4M3);
+}
+
+int oracle_append_kv_int8(int8_t *k_cache, int8_t *v_cache, const void *k_new,
+                          const void *v_new, int new_dtype, const float *k_scale,
+                          const float *v_scale, const int32_t *seq_lens, int b, int T,
+                          int g, int S, int d) {
+    return append_codes((uint8_t *)k_cache, (uint8_t *)v_cache, k_new, v_new, new_dtype,
+                        k_scale, v_scale, seq_lens, b, T, g, S, d, ORACLE_INT8);
+}
+
+int oracle_append_kv_paged_int8(int8_t *k_pages, int8_t *v_pages, const void *k_new,
+                                const void *v_new, int new_dtype, const float *k_scale,
+                                const float *v_scale, const int32_t *block_table,
+                                const int32_t *seq_lens, int b, int T, int g, int page_size,
+                                int max_pages, int num_pages, int d) {
+    return append_codes_paged((uint8_t *)k_pages, (uint8_t *)v_pages, k_new, v_new, new_dtype,
+                              k_scale, v_scale, block_table, seq_lens, b, T, g, page_size,
+                              max_pages, num_pages, d, ORACLE_INT8);
 }
 
 /* ---- every option at once: layout, cache element type, tokens, window ---- */

@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_FP8_E4M3 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_FP8_E4M3 = 2, ORACLE_INT8 = 3 };
 
 /* Return bits. ORACLE_BAD_LEN: some seq_lens[i] outside [1, S] ([T, S] with T
  * query tokens); those rows
@@ -139,10 +139,31 @@ int oracle_append_kv_paged_fp8(uint8_t *k_pages, uint8_t *v_pages, const void *k
                                const int32_t *seq_lens, int b, int T, int g, int page_size,
                                int max_pages, int num_pages, int d);
 
+/* int8 cache (the other low-precision format the pages name: [MQA concept]'s
+ * risk list and [MQA blog] §4.3 problem 3 speak of INT8/INT4 K/V). Codes are
+ * two's-complement int8 with the same per-K/V-head scales as the fp8 cache
+ * (value = code * scale[j]); decode is the plain definition over those
+ * values (oracle_decode_attn_ex with kv_dtype ORACLE_INT8). Append stores
+ * encode(x / scale[j]): one correctly rounded fp32 division, then the
+ * nearest integer, ties to even, saturated at +-127 (never -128: the codes
+ * are symmetric about 0); NaN becomes 0. */
+double oracle_int8_decode(int8_t code);
+int8_t oracle_int8_encode(float x);
+int oracle_append_kv_int8(int8_t *k_cache, int8_t *v_cache, const void *k_new,
+                          const void *v_new, int new_dtype, const float *k_scale,
+                          const float *v_scale, const int32_t *seq_lens, int b, int T,
+                          int g, int S, int d);
+int oracle_append_kv_paged_int8(int8_t *k_pages, int8_t *v_pages, const void *k_new,
+                                const void *v_new, int new_dtype, const float *k_scale,
+                                const float *v_scale, const int32_t *block_table,
+                                const int32_t *seq_lens, int b, int T, int g, int page_size,
+                                int max_pages, int num_pages, int d);
+
 /* Every option of the decode at once: q (q_dtype) [b][T][h][d]; K/V
  * contiguous [b][g][S][d] (block_table NULL) or pages [num_pages][g][P][d]
  * through block_table [b][max_pages] (S is then P * max_pages); kv_dtype
- * f32, bf16 or fp8 e4m3 (with k_scale, v_scale [g]; NULL otherwise); a
+ * f32, bf16, fp8 e4m3 or int8 (codes with k_scale, v_scale [g]; NULL
+ * otherwise); a
  * sliding window: window > 0 keeps, for a query at position p, only the
  * positions t in (p - window, p] (the window start replaces 0: [MQA
  * concept] 玩家對比 lists GQA with a sliding window); 0 keeps all t <= p. */

@@ -623,6 +623,101 @@ def test_fp8_append_quantises_with_the_head_scale(T):
 
 
 # ---------------------------------------------------------------------------
+# int8 cache with per-K/V-head scales (the pages' INT8 K/V)
+# ---------------------------------------------------------------------------
+
+def test_int8_decode_is_twos_complement():
+    """All 256 codes against torch's int8 reading of the same bytes."""
+    codes = np.arange(256, dtype=np.uint8).view(np.int8)
+    ref = torch.from_numpy(codes.copy()).double().numpy()
+    got = np.array([oracle.int8_decode(int(c)) for c in codes])
+    assert np.array_equal(got, ref)
+    assert oracle.int8_decode(-1) == -1.0 and oracle.int8_decode(-128) == -128.0
+
+
+def test_int8_encode_matches_torch_round_and_saturates():
+    """Nearest integer with ties to even (torch.round), clamped to +-127; the
+    ties k + 0.5 and the saturation edges explicitly; NaN to 0."""
+    rng = np.random.default_rng(13)
+    xs = np.concatenate([rng.uniform(-140, 140, 4000), np.arange(-130, 131) + 0.5,
+                         [126.49, 126.5, 127.5, 128.0, -127.5, -128.0, -1e30, 1e30, 0.0, -0.0]])
+    xs = xs.astype(np.float32)
+    ref = torch.round(torch.from_numpy(xs)).clamp(-127, 127).to(torch.int8).numpy()
+    got = np.array([oracle.int8_encode(x) for x in xs], np.int8)
+    assert np.array_equal(got, ref)
+    assert oracle.int8_encode(float("nan")) == 0
+    assert oracle.int8_encode(-128.0) == -127  # -128 is never produced
+
+
+def _int8_case(rng, b, T, h, g, S, d):
+    k = rng.integers(-127, 128, (b, g, S, d), dtype=np.int8)
+    v = rng.integers(-127, 128, (b, g, S, d), dtype=np.int8)
+    ks = (rng.uniform(0.005, 0.03, g)).astype(np.float32)
+    vs = (rng.uniform(0.005, 0.03, g)).astype(np.float32)
+    q = bf16_bits(randn(b, T, h, d))
+    return q, k, v, ks, vs
+
+
+@pytest.mark.parametrize("T,h,g,W", [(1, 8, 2, 0), (3, 8, 1, 0), (1, 12, 3, 0), (2, 8, 2, 9)])
+def test_int8_decode_matches_sdpa_on_dequantised_cache(T, h, g, W):
+    """int8 decode (through the general call) = torch SDPA (float64) on the
+    codes times the head's scale; causal last-T rows; a window where given."""
+    rng = np.random.default_rng(T * 100 + h * 10 + g + W)
+    b, S, d = 3, 40, 64
+    q, k, v, ks, vs = _int8_case(rng, b, T, h, g, S, d)
+    lens = np.array([40, T + 3, 17], np.int32)
+    out, rc = oracle.decode_attn_ex(q, k, v, lens, 0.125, window=W, k_scale=ks, v_scale=vs)
+    assert rc == oracle.OK
+    kd = torch.from_numpy(k).double().numpy() * ks[None, :, None, None].astype(np.float64)
+    vd = torch.from_numpy(v).double().numpy() * vs[None, :, None, None].astype(np.float64)
+    qd = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).double().numpy()
+    for i in range(b):
+        if W == 0:
+            ref = _causal_sdpa_last_rows(qd[i], kd[i], vd[i], int(lens[i]), 0.125, rng)
+            np.testing.assert_allclose(out[i], ref, rtol=1e-10, atol=1e-12)
+        else:
+            for tau in range(T):
+                A = int(lens[i]) - T + 1 + tau
+                a0 = max(0, A - W)
+                ref = _sdpa_rows(qd[i, tau], kd[i, :, a0:A], vd[i, :, a0:A], 0.125)
+                np.testing.assert_allclose(out[i, tau], ref, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_int8_append_quantises_with_the_head_scale(T):
+    """Codes of the appended rows = torch.round(x / scale) clamped to +-127
+    (the division in float32), at positions L-T .. L-1, contiguous and paged;
+    every other byte untouched. Large values saturate."""
+    rng = np.random.default_rng(95 + T)
+    b, g, S, d, P = 3, 2, 32, 64, 16
+    k = rng.integers(-127, 128, (b, g, S, d), dtype=np.int8)
+    v = rng.integers(-127, 128, (b, g, S, d), dtype=np.int8)
+    ks = np.array([0.01, 0.03], np.float32)
+    vs = np.array([0.02, 0.012], np.float32)
+    kn, vn = randn(b, T, g, d, scale=1.5), randn(b, T, g, d, scale=1.5)  # some beyond 127 * scale
+    lens = np.array([T, 32, 7], np.int32)
+    kp, vp, bt = _paged_from_contiguous(k.astype(np.float32), v.astype(np.float32), P, rng)
+    kp = np.nan_to_num(kp).astype(np.int8)
+    vp = np.nan_to_num(vp).astype(np.int8)
+    k2, v2 = k.copy(), v.copy()
+    assert oracle.append_kv_int8(k2, v2, kn, vn, ks, vs, lens) == oracle.OK
+    assert oracle.append_kv_paged_int8(kp, vp, kn, vn, ks, vs, bt, lens) == oracle.OK
+    ek, ev = k.copy(), v.copy()
+    q8 = lambda x, sc: torch.round(torch.from_numpy(x) / torch.from_numpy(sc)[:, None]).clamp(-127, 127).to(torch.int8).numpy()
+    for i in range(b):
+        for tau in range(T):
+            pos = lens[i] - T + tau
+            ek[i, :, pos] = q8(kn[i, tau], ks)
+            ev[i, :, pos] = q8(vn[i, tau], vs)
+    assert np.array_equal(k2, ek) and np.array_equal(v2, ev)
+    assert (np.abs(ek.astype(np.int32)) == 127).any()  # the saturation was exercised
+    for i in range(b):
+        for t in range(int(lens[i])):
+            np.testing.assert_array_equal(kp[bt[i, t // P], :, t % P], k2[i, :, t])
+            np.testing.assert_array_equal(vp[bt[i, t // P], :, t % P], v2[i, :, t])
+
+
+# ---------------------------------------------------------------------------
 # sliding window ([MQA concept] 玩家對比: GQA + SWA) and rotary positions
 # ---------------------------------------------------------------------------
 
@@ -775,7 +870,10 @@ MUTANTS = {
     "fp8 ties rounded away from zero": ("int sm = (int)nearbyintf(fr * 16.0f);", "int sm = (int)roundf(fr * 16.0f);"),
     "key scale ignored": ("double ks = J->k_scale ? (double)J->k_scale[j] : 1.0;", "double ks = 1.0;"),
     "value scale of the key": ("double vs = J->v_scale ? (double)J->v_scale[j] : 1.0;", "double vs = J->k_scale ? (double)J->k_scale[j] : 1.0;"),
-    "quantised by multiplying": ("return oracle_fp8_e4m3_encode(x / scale);", "return oracle_fp8_e4m3_encode(x * scale);"),
+    "quantised by multiplying": ("float y = x / scale;", "float y = x * scale;"),
+    "int8 ties rounded away from zero": ("float r = nearbyintf(f);", "float r = roundf(f);"),
+    "int8 saturates one step too far": ("if (r > 127.0f) r = 127.0f;", "if (r > 128.0f) r = 128.0f;"),
+    "int8 codes read as unsigned": ("return oracle_int8_decode(((const int8_t *)base)[idx]);", "return oracle_int8_decode((int8_t)((const uint8_t *)base)[idx] & 0x7F);"),
     "no normalisation": ("for (int t = a0; t < A; t++) s[t] /= Z;", ""),
     "key and value swapped": ("elem(J->v, (size_t)kv_row(J, i, j, t) + x, J->dtype));\n        o[x]", "elem(J->k, (size_t)kv_row(J, i, j, t) + x, J->dtype));\n        o[x]"),
     "page looked up one position late": ("(size_t)i * J->max_pages + t / J->page_size]", "(size_t)i * J->max_pages + (t + 1) / J->page_size]"),
@@ -808,7 +906,8 @@ def test_planted_mistakes_are_caught(tmp_path, name, monkeypatch):
                "oracle_fp8_e4m3_decode", "oracle_fp8_e4m3_encode", "oracle_decode_attn_fp8",
                "oracle_decode_attn_paged_fp8", "oracle_append_kv_fp8", "oracle_append_kv_paged_fp8",
                "oracle_decode_attn_ex", "oracle_rope_table", "oracle_rope_rows", "oracle_rope_q",
-               "oracle_append_kv_rope"):
+               "oracle_append_kv_rope", "oracle_int8_decode", "oracle_int8_encode",
+               "oracle_append_kv_int8", "oracle_append_kv_paged_int8"):
         getattr(mutant, fn).argtypes = getattr(real, fn).argtypes
         getattr(mutant, fn).restype = getattr(real, fn).restype
     monkeypatch.setattr(oracle, "_lib", mutant)
@@ -822,7 +921,11 @@ def test_planted_mistakes_are_caught(tmp_path, name, monkeypatch):
                 lambda: test_fp8_decode_matches_sdpa_on_dequantised_cache(1, 8, 2),
                 lambda: test_fp8_append_quantises_with_the_head_scale(1),
                 lambda: test_window_matches_sdpa_on_the_window(3, 7), test_window_special_cases,
-                test_rope_table_closed_forms, test_rope_rotation_properties):
+                test_rope_table_closed_forms, test_rope_rotation_properties,
+                test_int8_decode_is_twos_complement,
+                test_int8_encode_matches_torch_round_and_saturates,
+                lambda: test_int8_decode_matches_sdpa_on_dequantised_cache(1, 8, 2, 0),
+                lambda: test_int8_append_quantises_with_the_head_scale(1)):
         try:
             pin()
         except AssertionError:
