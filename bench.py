@@ -37,7 +37,9 @@ tokens verified at once, causal mask): mqa_append_kv_multi + mqa_decode_attn_mul
 
 With --kv-dtype fp8 the cache holds fp8 e4m3 codes with per-K/V-head scales
 (mqa_append_kv_fp8 quantises the new rows, mqa_decode_attn_fp8 reads one byte
-per element): the K/V bytes per position halve; q stays bf16.
+per element): the K/V bytes per position halve; q stays bf16. --kv-dtype int8
+does the same with int8 codes (mqa_append_kv_int8, decode through
+mqa_decode_attn_ex).
 
 With --window W the decode is mqa_decode_attn_ex with a sliding window of W
 positions: a query at position p reads only (p - W, p], so the K/V bytes count
@@ -49,7 +51,7 @@ contiguous bf16 cache); the rotation adds q read and written
 (2*b*T*h*d*B) and the table rows read (2*b*T*(d/2)*8) to the step's bytes.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--page-size P]
-                       [--tokens T] [--kv-dtype bf16|fp8] [--window W] [--rope]
+                       [--tokens T] [--kv-dtype bf16|fp8|int8] [--window W] [--rope]
 """
 from __future__ import annotations
 
@@ -95,7 +97,7 @@ def parse():
                     help="paged KV cache with pages of this many rows (0: contiguous cache)")
     ap.add_argument("--tokens", type=int, default=1,
                     help="query tokens per sequence per step (causal; 1: plain decode)")
-    ap.add_argument("--kv-dtype", choices=["bf16", "fp8"], default="bf16",
+    ap.add_argument("--kv-dtype", choices=["bf16", "fp8", "int8"], default="bf16",
                     help="cache element type (fp8: e4m3 codes with per-K/V-head scales)")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window of this many positions (mqa_decode_attn_ex); 0: none")
@@ -136,7 +138,8 @@ def main() -> int:
 
     P = args.page_size
     T = args.tokens
-    F8 = args.kv_dtype == "fp8"
+    F8 = args.kv_dtype in ("fp8", "int8")  # one-byte codes with per-K/V-head scales
+    I8 = args.kv_dtype == "int8"
     if (P or T > 1 or F8) and args.kernel == "valu":
         print("paged, multi-token and fp8 calls run the matrix-core kernels only", file=sys.stderr)
         return 2
@@ -157,7 +160,7 @@ def main() -> int:
     steps_in = []
     for r in range(reps):
         if F8:
-            t = W.make_fp8_step(w, dev, T=T, layer=r, page_size=P)
+            t = W.make_fp8_step(w, dev, T=T, layer=r, page_size=P, int8=I8)
         elif T > 1:
             t = W.make_multi_step(w, dev, T=T, layer=r, page_size=P)
         elif P:
@@ -169,7 +172,7 @@ def main() -> int:
         steps_in.append(t)
     cap = steps_in[0]["capacity"] if P else w.S
     t0 = steps_in[0]
-    if WIN:
+    if WIN or I8:
         kk, vv = ("k_pages", "v_pages") if P else ("k_cache", "v_cache")
         nws = mqa.decode_ex_workspace_bytes(t0["q"], t0[kk], t0[vv], t0["seq_lens"],
                                             block_table=t0.get("block_table") if P else None,
@@ -226,11 +229,13 @@ def main() -> int:
         if F8:
             sc = (t["k_scale"], t["v_scale"])
             if P:
-                mqa.append_kv_paged_fp8(t["k_pages"], t["v_pages"], t["k_new"], t["v_new"], *sc,
-                                        t["block_table"], t["seq_lens"], err_flags=err)
+                append = mqa.append_kv_paged_int8 if I8 else mqa.append_kv_paged_fp8
+                append(t["k_pages"], t["v_pages"], t["k_new"], t["v_new"], *sc, t["block_table"],
+                       t["seq_lens"], err_flags=err)
             else:
-                mqa.append_kv_fp8(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], *sc,
-                                  t["seq_lens"], err_flags=err)
+                append = mqa.append_kv_int8 if I8 else mqa.append_kv_fp8
+                append(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], *sc, t["seq_lens"],
+                       err_flags=err)
         elif P:
             pages = (t["k_pages"], t["v_pages"])
             append = mqa.append_kv_paged_multi if T > 1 else mqa.append_kv_paged
@@ -244,7 +249,7 @@ def main() -> int:
             append(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], t["seq_lens"], err_flags=err)
         if ev is not None:
             ev[0].record()
-        if WIN:
+        if WIN or I8:
             kk, vv = ("k_pages", "v_pages") if P else ("k_cache", "v_cache")
             mqa.decode_attn_ex(t["q"], t[kk], t[vv], t["seq_lens"],
                                block_table=t.get("block_table") if P else None,
@@ -322,7 +327,8 @@ def main() -> int:
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = dec_bytes / (dec_ms_avg * 1e-3) / 1e9
     traffic = None
-    tag = (w.name + (f"-paged{P}" if P else "") + (f"-t{T}" if T > 1 else "") + ("-fp8" if F8 else "")
+    tag = (w.name + (f"-paged{P}" if P else "") + (f"-t{T}" if T > 1 else "")
+           + (("-int8" if I8 else "-fp8") if F8 else "")
            + (f"-w{WIN}" if WIN else "") + ("-rope" if ROPE else ""))
     tf = os.path.join(ROOT, "profiles", f"decode_{tag}_traffic.json")
     if os.path.exists(tf):
@@ -351,7 +357,7 @@ def main() -> int:
                    "layers": layers, "schedule": schedule,
                    "kv_layout": f"paged, {P}-row pages" if P else "contiguous",
                    "query_tokens": T,
-                   "kv_dtype": "fp8 e4m3, per-K/V-head scales" if F8 else "bf16",
+                   "kv_dtype": ("int8" if I8 else "fp8 e4m3") + ", per-K/V-head scales" if F8 else "bf16",
                    "window": WIN or None, "rope_on_append": ROPE,
                    "split_chunk": chunk if schedule != "mfma-balanced" else None,
                    "cache_copies_rotated": reps,
@@ -360,7 +366,8 @@ def main() -> int:
         "flops_per_step": flops_per_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("mqa_decode_attn_ex (window)" if WIN else
+            "kernel": ("mqa_decode_attn_ex" + (" (window)" if WIN else "") + (" (int8)" if I8 else "")
+                       if WIN or I8 else
                        ("mqa_decode_attn" + ("_paged" if P else "")
                         + ("_fp8" if F8 else "_multi" if T > 1 else "")))
                       + " launch, schedule " + schedule,
@@ -379,7 +386,7 @@ def main() -> int:
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, steps_in[0], lens, per_layer, layers,
-                                              args.cpu_seconds, P, T, F8, WIN)
+                                              args.cpu_seconds, P, T, F8, WIN, I8)
 
     print(json.dumps(result), flush=True)
     return 0
@@ -462,7 +469,7 @@ def spin_cycles(torch, ms: float) -> int:
 
 
 def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1, F8=False,
-                 window=0):
+                 window=0, I8=False):
     """The oracle (plain double loops) on the host cores, one layer's step."""
     import numpy as np
 
@@ -474,7 +481,7 @@ def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1
     scale = float(np.float32(1.0 / math.sqrt(w.d)))
     lens32 = lens.astype(np.int32)
     q = W.to_oracle(t["q"])
-    if window:
+    if window or I8:  # the general call (an int8 cache is read through it)
         kk, vv = ("k_pages", "v_pages") if page_size else ("k_cache", "v_cache")
         conv = (lambda x: x.cpu().numpy()) if F8 else W.to_oracle
         kx, vx = conv(t[kk]), conv(t[vv])

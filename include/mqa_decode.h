@@ -57,9 +57,10 @@ typedef enum {
     MQA_ERR_HIP = 6          /* the HIP runtime reported a launch error */
 } mqa_status;
 
-/* Element types. MQA_FP8_E4M3 is a cache type only (mqa_decode_attn_ex,
- * the _fp8 calls); q and new rows are then bf16. */
-typedef enum { MQA_F32 = 0, MQA_BF16 = 1, MQA_FP8_E4M3 = 2 } mqa_dtype;
+/* Element types. MQA_FP8_E4M3 and MQA_INT8 are cache types only
+ * (mqa_decode_attn_ex, the _fp8 and _int8 calls); q and new rows are then
+ * bf16. */
+typedef enum { MQA_F32 = 0, MQA_BF16 = 1, MQA_FP8_E4M3 = 2, MQA_INT8 = 3 } mqa_dtype;
 
 /* Which partition kernel computes the attention (see mqa_decode_attn_kernel). */
 typedef enum {
@@ -324,8 +325,36 @@ mqa_status mqa_decode_attn_paged_fp8(const void *q, const void *k_pages,
                                      int32_t *err_flags, hipStream_t stream);
 
 /*
+ * int8 cache: the same layout, scales and calls' semantics as the fp8 cache
+ * above, with two's-complement int8 codes ([MQA concept]'s risk list and
+ * [MQA blog] §4.3 problem 3 speak of INT8 K/V; the pages fix no format):
+ * a cached value is code * scale[j]. Append stores the nearest integer to
+ * x / scale[j] (one correctly rounded fp32 division), ties to even,
+ * saturated at +-127 (-128 is never written); NaN becomes 0. Decode goes
+ * through mqa_decode_attn_ex with kv_dtype = MQA_INT8 (codes decoded
+ * exactly to bf16; the K scale on the scores, the V scale on the outputs).
+ *
+ *   k_cache, v_cache : [b][g][S][d] int8 codes (pages: [num_pages][g][P][d])
+ *   k_new, v_new     : [b][T][g][d] bf16
+ */
+mqa_status mqa_append_kv_int8(void *k_cache, void *v_cache, const void *k_new,
+                              const void *v_new, const float *k_scale,
+                              const float *v_scale, const int32_t *seq_lens,
+                              int b, int T, int g, int S, int d,
+                              int32_t *err_flags, hipStream_t stream);
+
+mqa_status mqa_append_kv_paged_int8(void *k_pages, void *v_pages,
+                                    const void *k_new, const void *v_new,
+                                    const float *k_scale, const float *v_scale,
+                                    const int32_t *block_table,
+                                    const int32_t *seq_lens, int b, int T,
+                                    int g, int page_size, int max_pages,
+                                    int num_pages, int d, int32_t *err_flags,
+                                    hipStream_t stream);
+
+/*
  * One call with every option: layout (contiguous or paged), cache element
- * type (bf16, fp8 with scales, or f32), T query tokens, and a sliding window
+ * type (bf16, fp8 or int8 codes with scales, or f32), T query tokens, and a sliding window
  * ([MQA concept] 玩家對比 lists GQA with a sliding window: a query at position
  * p then sees only the positions t in (p - window, p]; the window start
  * replaces 0). The entry points above are this call with some fields fixed.
@@ -337,7 +366,7 @@ typedef struct {
     const void *k, *v;              /* [b][g][S][d] or pages [num_pages][g][page_size][d] */
     const int32_t *block_table;     /* [b][max_pages] int32; NULL: contiguous cache */
     const int32_t *seq_lens;        /* [b], post-append lengths */
-    const float *k_scale, *v_scale; /* [g] fp32, fp8 cache only */
+    const float *k_scale, *v_scale; /* [g] fp32, fp8 and int8 caches only */
     float *out;                     /* [b][T][h][d] fp32 */
     void *workspace;                /* mqa_decode_ex_workspace_bytes() bytes, 16-byte aligned */
     size_t workspace_bytes;

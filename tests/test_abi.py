@@ -352,6 +352,23 @@ def test_decode_ex_workspace_query_reads_sizes_only():
     assert L.mqa_decode_attn_ex(ctypes.byref(bare), None) == mqa.ERR_NULL
 
 
+def test_int8_calls_reject_bad_arguments_before_launch():
+    """The int8 cache through the general call needs its scales; the int8
+    appends check like the fp8 ones."""
+    L = mqa.lib()
+    assert L.mqa_decode_attn_ex(ctypes.byref(ex_desc(kv_dtype=mqa.INT8)), None) == mqa.ERR_NULL
+    d = ex_desc(kv_dtype=mqa.INT8, k_scale=0x10002, v_scale=0x10000)
+    assert L.mqa_decode_attn_ex(ctypes.byref(d), None) == mqa.ERR_ALIGN
+    assert L.mqa_decode_ex_workspace_bytes(ctypes.byref(ex_desc(kv_dtype=mqa.INT8))) == \
+        L.mqa_decode_ex_workspace_bytes(ctypes.byref(ex_desc(kv_dtype=mqa.FP8_E4M3)))
+    assert L.mqa_append_kv_int8(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 2, 1, 2, 64, 128, None,
+                                None) == mqa.ERR_NULL
+    assert L.mqa_append_kv_int8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 0, 2, 64, 128, None,
+                                None) == mqa.ERR_SHAPE
+    assert L.mqa_append_kv_paged_int8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1, 2, 16,
+                                      4, 0, 128, None, None) == mqa.ERR_SHAPE
+
+
 def test_rope_calls_reject_bad_arguments_before_launch():
     L = mqa.lib()
     assert L.mqa_rope_q(FAKE, None, 16, FAKE, 2, 1, 8, 128, None, None) == mqa.ERR_NULL

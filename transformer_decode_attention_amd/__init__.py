@@ -50,14 +50,14 @@ __all__ = [
     "append_kv_multi", "decode_attn_multi", "append_kv_paged_multi", "decode_attn_paged_multi",
     "decode_multi_workspace_bytes", "decode_multi_schedule", "append_kv_fp8", "decode_attn_fp8",
     "append_kv_paged_fp8", "decode_attn_paged_fp8", "decode_attn_ex", "decode_ex_workspace_bytes",
-    "rope_q", "append_kv_rope",
-    "DEVERR_ROPE", "FP8_E4M3",
+    "rope_q", "append_kv_rope", "append_kv_int8", "append_kv_paged_int8",
+    "DEVERR_ROPE", "FP8_E4M3", "INT8",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa_decode.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)
-F32, BF16, FP8_E4M3 = 0, 1, 2
+F32, BF16, FP8_E4M3, INT8 = 0, 1, 2, 3
 DEVERR_SEQLEN = 1
 DEVERR_PAGE = 2
 DEVERR_ROPE = 4
@@ -72,7 +72,8 @@ EXPORTS = (
     "mqa_decode_multi_schedule", "mqa_decode_attn_multi", "mqa_append_kv_paged_multi",
     "mqa_decode_attn_paged_multi", "mqa_append_kv_fp8", "mqa_append_kv_paged_fp8",
     "mqa_decode_attn_fp8", "mqa_decode_attn_paged_fp8", "mqa_decode_ex_workspace_bytes",
-    "mqa_decode_attn_ex", "mqa_rope_q", "mqa_append_kv_rope",
+    "mqa_decode_attn_ex", "mqa_rope_q", "mqa_append_kv_rope", "mqa_append_kv_int8",
+    "mqa_append_kv_paged_int8",
 )
 
 
@@ -151,6 +152,10 @@ def _load() -> ctypes.CDLL:
     L.mqa_append_kv_paged_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                           i32, i32, vp, vp]
     L.mqa_append_kv_paged_fp8.restype = i32
+    L.mqa_append_kv_int8.argtypes = L.mqa_append_kv_fp8.argtypes
+    L.mqa_append_kv_int8.restype = i32
+    L.mqa_append_kv_paged_int8.argtypes = L.mqa_append_kv_paged_fp8.argtypes
+    L.mqa_append_kv_paged_int8.restype = i32
     L.mqa_decode_attn_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                       ctypes.c_float, vp, vp, ctypes.c_size_t, i32, vp, vp]
     L.mqa_decode_attn_fp8.restype = i32
@@ -523,10 +528,13 @@ def decode_attn_paged_multi(q: torch.Tensor, k_pages: torch.Tensor, v_pages: tor
 _FP8_TYPES = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
 
 
-def _check_fp8(k, v, k_scale, v_scale, g):
+def _check_fp8(k, v, k_scale, v_scale, g, int8: bool = False):
     for n, t in (("k cache", k), ("v cache", v), ("k_scale", k_scale), ("v_scale", v_scale)):
         _dev(t, n)
-    if k.dtype not in _FP8_TYPES or v.dtype != k.dtype:
+    if int8:
+        if k.dtype != torch.int8 or v.dtype != k.dtype:
+            raise TypeError("an int8 cache is int8 codes")
+    elif k.dtype not in _FP8_TYPES or v.dtype != k.dtype:
         raise TypeError("an fp8 cache is uint8 or float8_e4m3fn codes")
     for n, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
         if sc.dtype != torch.float32 or sc.shape != (g,) or not sc.is_contiguous():
@@ -540,36 +548,61 @@ def _rows4(x, name):
     return x if x.dim() == 4 else x.unsqueeze(1)
 
 
-def append_kv_fp8(k_cache, v_cache, k_new, v_new, k_scale, v_scale, seq_lens, err_flags=None):
-    """k_new/v_new bf16 [b, g, d] or [b, T, g, d] -> e4m3(x / scale[j]) at positions L-T .. L-1."""
+def _append_codes(fn, int8, k_cache, v_cache, k_new, v_new, k_scale, v_scale, seq_lens,
+                  err_flags):
     b, g, S, d = k_cache.shape
-    _check_fp8(k_cache, v_cache, k_scale, v_scale, g)
+    _check_fp8(k_cache, v_cache, k_scale, v_scale, g, int8)
     kn, vn = _rows4(k_new, "k_new"), _rows4(v_new, "v_new")
     if kn.shape[0] != b or kn.shape[2:] != (g, d) or vn.shape != kn.shape or v_cache.shape != k_cache.shape:
         raise ValueError("cache [b, g, S, d] and new rows [b, (T,) g, d] must match")
     _dev(seq_lens, "seq_lens")
-    st = lib().mqa_append_kv_fp8(_ptr(k_cache), _ptr(v_cache), _ptr(kn), _ptr(vn), _ptr(k_scale),
-                                 _ptr(v_scale), _ptr(seq_lens), b, kn.shape[1], g, S, d,
-                                 _ptr(err_flags), _stream(k_cache.device))
+    st = getattr(lib(), fn)(_ptr(k_cache), _ptr(v_cache), _ptr(kn), _ptr(vn), _ptr(k_scale),
+                            _ptr(v_scale), _ptr(seq_lens), b, kn.shape[1], g, S, d,
+                            _ptr(err_flags), _stream(k_cache.device))
     if st != OK:
-        raise MQAError(st, "mqa_append_kv_fp8")
+        raise MQAError(st, fn)
+
+
+def _append_codes_paged(fn, int8, k_pages, v_pages, k_new, v_new, k_scale, v_scale, block_table,
+                        seq_lens, err_flags):
+    num_pages, g, P, d = k_pages.shape
+    _check_fp8(k_pages, v_pages, k_scale, v_scale, g, int8)
+    kn, vn = _rows4(k_new, "k_new"), _rows4(v_new, "v_new")
+    for n, t in (("block_table", block_table), ("seq_lens", seq_lens)):
+        _dev(t, n)
+    b, max_pages = block_table.shape
+    st = getattr(lib(), fn)(_ptr(k_pages), _ptr(v_pages), _ptr(kn), _ptr(vn), _ptr(k_scale),
+                            _ptr(v_scale), _ptr(block_table), _ptr(seq_lens), b, kn.shape[1], g,
+                            P, max_pages, num_pages, d, _ptr(err_flags), _stream(k_pages.device))
+    if st != OK:
+        raise MQAError(st, fn)
+
+
+def append_kv_fp8(k_cache, v_cache, k_new, v_new, k_scale, v_scale, seq_lens, err_flags=None):
+    """k_new/v_new bf16 [b, g, d] or [b, T, g, d] -> e4m3(x / scale[j]) at positions L-T .. L-1."""
+    _append_codes("mqa_append_kv_fp8", False, k_cache, v_cache, k_new, v_new, k_scale, v_scale,
+                  seq_lens, err_flags)
 
 
 def append_kv_paged_fp8(k_pages, v_pages, k_new, v_new, k_scale, v_scale, block_table, seq_lens,
                         err_flags=None):
     """append_kv_fp8 into pages [num_pages, g, page_size, d] of codes."""
-    num_pages, g, P, d = k_pages.shape
-    _check_fp8(k_pages, v_pages, k_scale, v_scale, g)
-    kn, vn = _rows4(k_new, "k_new"), _rows4(v_new, "v_new")
-    for n, t in (("block_table", block_table), ("seq_lens", seq_lens)):
-        _dev(t, n)
-    b, max_pages = block_table.shape
-    st = lib().mqa_append_kv_paged_fp8(_ptr(k_pages), _ptr(v_pages), _ptr(kn), _ptr(vn),
-                                       _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
-                                       _ptr(seq_lens), b, kn.shape[1], g, P, max_pages, num_pages,
-                                       d, _ptr(err_flags), _stream(k_pages.device))
-    if st != OK:
-        raise MQAError(st, "mqa_append_kv_paged_fp8")
+    _append_codes_paged("mqa_append_kv_paged_fp8", False, k_pages, v_pages, k_new, v_new, k_scale,
+                        v_scale, block_table, seq_lens, err_flags)
+
+
+def append_kv_int8(k_cache, v_cache, k_new, v_new, k_scale, v_scale, seq_lens, err_flags=None):
+    """k_new/v_new bf16 -> int8 codes round-half-even(x / scale[j]) clamped to +-127
+    at positions L-T .. L-1 of an int8 cache [b, g, S, d]."""
+    _append_codes("mqa_append_kv_int8", True, k_cache, v_cache, k_new, v_new, k_scale, v_scale,
+                  seq_lens, err_flags)
+
+
+def append_kv_paged_int8(k_pages, v_pages, k_new, v_new, k_scale, v_scale, block_table, seq_lens,
+                         err_flags=None):
+    """append_kv_int8 into pages [num_pages, g, page_size, d] of int8 codes."""
+    _append_codes_paged("mqa_append_kv_paged_int8", True, k_pages, v_pages, k_new, v_new, k_scale,
+                        v_scale, block_table, seq_lens, err_flags)
 
 
 def decode_attn_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale=None, out=None,
@@ -632,6 +665,9 @@ def _ex_desc(q4, k, v, seq_lens, block_table, k_scale, v_scale, window, scale, s
     if k.dtype in _FP8_TYPES:
         kvd = FP8_E4M3
         _check_fp8(k, v, k_scale, v_scale, g)
+    elif k.dtype == torch.int8:
+        kvd = INT8
+        _check_fp8(k, v, k_scale, v_scale, g, int8=True)
     else:
         kvd = _dtype_code(k.dtype)
     desc = DecodeDesc()
@@ -643,7 +679,7 @@ def _ex_desc(q4, k, v, seq_lens, block_table, k_scale, v_scale, window, scale, s
         desc.page_size, desc.max_pages, desc.num_pages = k.shape[2], block_table.shape[1], k.shape[0]
     else:
         desc.S = k.shape[2]
-    if kvd == FP8_E4M3:
+    if kvd in (FP8_E4M3, INT8):
         desc.k_scale, desc.v_scale = _ptr(k_scale), _ptr(v_scale)
     desc.kv_dtype, desc.window, desc.split_chunk = kvd, int(window), int(split_chunk)
     desc.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -666,8 +702,9 @@ def decode_attn_ex(q, k, v, seq_lens, block_table=None, k_scale=None, v_scale=No
                    scale=None, out=None, workspace=None, split_chunk: int = 0, err_flags=None):
     """Decode with every option (mqa_decode_attn_ex): q [b, h, d] or [b, T, h, d];
     k, v contiguous [b, g, S, d] or pages [num_pages, g, P, d] with block_table
-    [b, max_pages]; a bf16, f32 or fp8 (uint8 / float8_e4m3fn codes with k_scale,
-    v_scale [g]) cache; window > 0: sliding window. Returns out shaped like q."""
+    [b, max_pages]; a bf16, f32, fp8 (uint8 / float8_e4m3fn codes) or int8 (int8
+    codes) cache, the codes with k_scale, v_scale [g]; window > 0: sliding window.
+    Returns out shaped like q."""
     q4 = q if q.dim() == 4 else q.unsqueeze(1)
     b, T, h, d = q4.shape
     desc = _ex_desc(q4, k, v, seq_lens, block_table, k_scale, v_scale, window, scale, split_chunk)

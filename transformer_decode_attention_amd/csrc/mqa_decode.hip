@@ -229,13 +229,22 @@ __device__ __forceinline__ uint32_t e4m3_code(float f) {
     return sign | code;
 }
 
-// Quantised append into an fp8 cache: token tau of the new rows (bf16
-// [b][T][g][d]) goes to position L - T + tau as e4m3(x / scale[j]), one
+// int8 code (two's complement, in the low byte) of f: the nearest integer,
+// ties to even, saturated at +-127 (-128 is never produced); NaN becomes 0.
+__device__ __forceinline__ uint32_t int8_code(float f) {
+    if (f != f) return 0u;
+    const float r = fminf(fmaxf(__builtin_rintf(f), -127.f), 127.f);
+    return (uint32_t)(int)r & 0xffu;
+}
+
+// Quantised append into a one-byte cache: token tau of the new rows (bf16
+// [b][T][g][d]) goes to position L - T + tau as code(x / scale[j]), one
 // correctly rounded fp32 division per element ([GQA notes] §十 item 7: a
-// quantised KV cache). Contiguous cache [b][g][S][d] (bt NULL) or pages
-// [num_pages][g][P][d] through block table bt (S then the page size P).
-// Thread t converts one 8-element chunk.
-__global__ void append_kv_fp8_kernel(uint8_t *__restrict__ kc, uint8_t *__restrict__ vc,
+// quantised KV cache); the code is e4m3 or, with I8, int8. Contiguous cache
+// [b][g][S][d] (bt NULL) or pages [num_pages][g][P][d] through block table
+// bt (S then the page size P). Thread t converts one 8-element chunk.
+template <bool I8>
+__global__ void append_kv_codes_kernel(uint8_t *__restrict__ kc, uint8_t *__restrict__ vc,
                                      const uint16_t *__restrict__ kn,
                                      const uint16_t *__restrict__ vn,
                                      const float *__restrict__ k_scale,
@@ -274,7 +283,8 @@ __global__ void append_kv_fp8_kernel(uint8_t *__restrict__ kc, uint8_t *__restri
 #pragma unroll
     for (int e = 0; e < 8; e++) {
         const uint32_t bits = (in[e >> 1] >> (16 * (e & 1))) << 16;  // bf16 -> fp32, exact
-        const uint32_t code = e4m3_code(__fdiv_rn(__builtin_bit_cast(float, bits), sc));
+        const float y = __fdiv_rn(__builtin_bit_cast(float, bits), sc);
+        const uint32_t code = I8 ? int8_code(y) : e4m3_code(y);
         if (e < 4)
             lo |= code << (8 * e);
         else
@@ -826,6 +836,35 @@ __device__ __forceinline__ void fp8x16_to_bf16(const u32x4_t &w, bf16x8_t &lo, b
     hi = __builtin_bit_cast(bf16x8_t, (u32x4_t){o[4], o[5], o[6], o[7]});
 }
 
+// 16 int8 codes (two's complement, element e in byte e) -> elements 0..7
+// and 8..15 as bf16. Exact: a code's magnitude is at most 128, which needs
+// at most 8 significant bits, so its fp32 value has nothing in the low 16
+// bits.
+__device__ __forceinline__ void int8x16_to_bf16(const u32x4_t &w, bf16x8_t &lo, bf16x8_t &hi) {
+    uint32_t o[8];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const uint32_t wk = w[k];  // (a scalar copy: see fp8x16_to_bf16)
+#pragma unroll
+        for (int p = 0; p < 2; p++) {
+            const float f0 = (float)(int8_t)(wk >> (16 * p)), f1 = (float)(int8_t)(wk >> (16 * p + 8));
+            o[2 * k + p] = (__builtin_bit_cast(uint32_t, f1) & 0xffff0000u) |
+                           (__builtin_bit_cast(uint32_t, f0) >> 16);
+        }
+    }
+    lo = __builtin_bit_cast(bf16x8_t, (u32x4_t){o[0], o[1], o[2], o[3]});
+    hi = __builtin_bit_cast(bf16x8_t, (u32x4_t){o[4], o[5], o[6], o[7]});
+}
+
+// 16 one-byte codes of a cache of fp8 (I8 false) or int8 codes -> bf16.
+template <bool I8>
+__device__ __forceinline__ void codes16_to_bf16(const u32x4_t &w, bf16x8_t &lo, bf16x8_t &hi) {
+    if constexpr (I8)
+        int8x16_to_bf16(w, lo, hi);
+    else
+        fp8x16_to_bf16(w, lo, hi);
+}
+
 // K and V of one 32-position step as loaded: K in the lanes of the A operand
 // of the score MFMA (bf16: the operand itself), V row-contiguous (16 bytes
 // per lane).
@@ -846,10 +885,12 @@ struct StepSrc {
 
 // Contiguous cache [b][g][S][d]: both halves in the head's S rows, the
 // descriptors' extent the sequence length.
-template <int D, bool F8 = false>
+template <int D, bool F8 = false, bool I8 = false>
 struct ContigKV {
     static constexpr bool kPaged = false;
-    static constexpr bool kF8 = F8;
+    static constexpr bool kF8 = F8;  // one byte per element (fp8 or int8 codes)
+    static constexpr bool kI8 = I8;  // the codes are int8
+    static_assert(F8 || !I8, "int8 codes are one byte");
     static constexpr int kStage = 1;
     const uint8_t *k, *v;
     int g, S;
@@ -873,10 +914,12 @@ struct ContigKV {
 // of their steps in LDS (up to kStage entries, two per step; further steps
 // look the table up) before the first step, so that no table lookup sits
 // between a claim and its loads.
-template <int D, bool F8 = false>
+template <int D, bool F8 = false, bool I8 = false>
 struct PagedKV {
     static constexpr bool kPaged = true;
-    static constexpr bool kF8 = F8;
+    static constexpr bool kF8 = F8;  // one byte per element (fp8 or int8 codes)
+    static constexpr bool kI8 = I8;  // the codes are int8
+    static_assert(F8 || !I8, "int8 codes are one byte");
     static constexpr int kStage = F8 ? 1024 : 4096;  // (fp8: eight waves' buffers share the LDS)
     const uint8_t *k, *v;
     const int32_t *bt;
@@ -968,7 +1011,7 @@ __device__ __forceinline__ void poison_state(MfmaState<D> (&st)[NHB], int32_t *e
 // past t_end zeroed: they may hold anything, NaN included). Done before the
 // next step's loads are issued, so that this step's V registers are free for
 // them (the wave then holds one step of V in registers, not two).
-template <int D, bool F8>
+template <int D, bool F8, bool I8>
 __device__ __forceinline__ void stage_v_rows(const StepData<D, F8> &sd, int t0, int t_end,
                                              uint8_t *vb, int lane) {
     using C = MfmaCfg<D>;
@@ -982,7 +1025,7 @@ __device__ __forceinline__ void stage_v_rows(const StepData<D, F8> &sd, int t0, 
         if (tail && t0 + row >= t_end) v = u32x4_t{0u, 0u, 0u, 0u};
         if constexpr (F8) {  // 16 codes -> 16 bf16 (32 bytes) of the row
             bf16x8_t lo, hi;
-            fp8x16_to_bf16(v, lo, hi);
+            codes16_to_bf16<I8>(v, lo, hi);
             *(bf16x8_t *)(vb + row * C::VSTRIDE + 32 * vl_chunk) = lo;
             *(bf16x8_t *)(vb + row * C::VSTRIDE + 32 * vl_chunk + 16) = hi;
         } else {
@@ -990,13 +1033,13 @@ __device__ __forceinline__ void stage_v_rows(const StepData<D, F8> &sd, int t0, 
         }
     }
 }
-template <int D, bool F8>
+template <int D, bool F8, bool I8 = false>
 __device__ __forceinline__ void stage_v(const StepData<D, F8> &sd, int t0, int t_end, uint8_t *vb,
                                         int lane) {
     if (t0 + MfmaCfg<D>::STEP > t_end)  // wave-uniform: a real branch
-        stage_v_rows<D, F8>(sd, t0, t_end, vb, lane);
+        stage_v_rows<D, F8, I8>(sd, t0, t_end, vb, lane);
     else
-        stage_v_rows<D, F8>(sd, t0, 0x7fffffff, vb, lane);
+        stage_v_rows<D, F8, I8>(sd, t0, 0x7fffffff, vb, lane);
 }
 
 // One 32-position step [t0, t0+32) of one wave from loaded data, rows >=
@@ -1012,7 +1055,7 @@ __device__ __forceinline__ void stage_v(const StepData<D, F8> &sd, int t0, int t
 // (per lane); t_hs is the latest start of the wave (0: no window).
 // MASKED: the step may hold masked positions (a tail past the earliest end,
 // or a head before the latest start); the other steps skip every mask test.
-template <int D, bool MULTI, int NHB, bool F8, bool MASKED>
+template <int D, bool MULTI, int NHB, bool F8, bool MASKED, bool I8>
 __device__ __forceinline__ void compute_step_v(const StepData<D, F8> &sd, int t0, int t_end, int t_lo,
                                                const int (&t_row)[NHB], int t_hs,
                                                const int (&t_rs)[NHB],
@@ -1031,7 +1074,7 @@ __device__ __forceinline__ void compute_step_v(const StepData<D, F8> &sd, int t0
 #pragma unroll
         for (int k = 0; k < F::KLOADS; k++) {
             if constexpr (F8)
-                fp8x16_to_bf16(sd.kraw[pb][k], kop[pb][2 * k], kop[pb][2 * k + 1]);
+                codes16_to_bf16<I8>(sd.kraw[pb][k], kop[pb][2 * k], kop[pb][2 * k + 1]);
             else
                 kop[pb][k] = __builtin_bit_cast(bf16x8_t, sd.kraw[pb][k]);
         }
@@ -1128,7 +1171,7 @@ __device__ __forceinline__ void compute_step_v(const StepData<D, F8> &sd, int t0
     }
 }
 
-template <int D, bool MULTI, int NHB, bool F8 = false>
+template <int D, bool MULTI, int NHB, bool F8 = false, bool I8 = false>
 __device__ __forceinline__ void compute_step(const StepData<D, F8> &sd, int t0, int t_end, int t_lo,
                                              const int (&t_row)[NHB], int t_hs,
                                              const int (&t_rs)[NHB],
@@ -1138,11 +1181,11 @@ __device__ __forceinline__ void compute_step(const StepData<D, F8> &sd, int t0, 
     // wave-uniform: a real branch between the two forms
     const bool masked = t0 + MfmaCfg<D>::STEP > (MULTI ? t_lo : t_end) || (MULTI && t0 < t_hs);
     if (masked)
-        compute_step_v<D, MULTI, NHB, F8, true>(sd, t0, t_end, t_lo, t_row, t_hs, t_rs, qop, st, vb,
-                                                lane, qk_scale_log2);
+        compute_step_v<D, MULTI, NHB, F8, true, I8>(sd, t0, t_end, t_lo, t_row, t_hs, t_rs, qop, st,
+                                                    vb, lane, qk_scale_log2);
     else
-        compute_step_v<D, MULTI, NHB, F8, false>(sd, t0, t_end, t_lo, t_row, t_hs, t_rs, qop, st,
-                                                 vb, lane, qk_scale_log2);
+        compute_step_v<D, MULTI, NHB, F8, false, I8>(sd, t0, t_end, t_lo, t_row, t_hs, t_rs, qop, st,
+                                                     vb, lane, qk_scale_log2);
 }
 
 // Query rows of a unit (sequence i, K/V head j). With T query tokens per
@@ -1190,7 +1233,7 @@ struct QRows {
 // one computes (NBUF register sets in rotation; the loop is unrolled by NBUF
 // so that each set keeps fixed registers). Past the last step a prefetch
 // asks for nothing.
-template <int D, bool MULTI, int NHB, int NBUF, bool F8, class Src>
+template <int D, bool MULTI, int NHB, int NBUF, bool F8, bool I8, class Src>
 __device__ __forceinline__ void run_steps(const Src &src, const StepSrc &nothing, int s_begin,
                                           int s_end, int stride, int t_end, int t_lo,
                                           const int (&t_row)[NHB], int t_hs,
@@ -1216,11 +1259,11 @@ __device__ __forceinline__ void run_steps(const Src &src, const StepSrc &nothing
             // the step NBUF-1 ahead, into the set computed last
             const int kn = (k + NBUF - 1) % NBUF;
             const int sn = stp + (NBUF - 1) * stride;
-            stage_v<D, F8>(buf[k], stp * C::STEP, t_end, vb, lane);
+            stage_v<D, F8, I8>(buf[k], stp * C::STEP, t_end, vb, lane);
             bad[kn] = false;
             load_step<D, F8>(sn < s_end ? src(sn, bad[kn]) : nothing, lane, buf[kn]);
-            compute_step<D, MULTI, NHB, F8>(buf[k], stp * C::STEP, t_end, t_lo, t_row, t_hs, t_rs,
-                                            qop, st, vb, lane, qk_scale_log2);
+            compute_step<D, MULTI, NHB, F8, I8>(buf[k], stp * C::STEP, t_end, t_lo, t_row, t_hs,
+                                                t_rs, qop, st, vb, lane, qk_scale_log2);
             if (bad[k]) poison_state<D>(st, err, lane);
             stp += stride;
             if (stp >= s_end) return;
@@ -1345,8 +1388,9 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
     // an fp8 cache: scores scale by the head's K scale, outputs by its V scale
     const float qk_scale_log2 = F8 ? qk_base * k_scale[j] : qk_base;
     const float vsc = F8 ? v_scale[j] : 1.f;
-    run_steps<D, MULTI, NHB, 2, F8>(src, kv.none(), s0 + w, s0 + nsteps, C::NW, t_end, t_lo, t_row,
-                                    t_hs, t_rs, qop, st, vbuf[w], lane, qk_scale_log2, err);
+    run_steps<D, MULTI, NHB, 2, F8, KV::kI8>(src, kv.none(), s0 + w, s0 + nsteps, C::NW, t_end,
+                                             t_lo, t_row, t_hs, t_rs, qop, st, vbuf[w], lane,
+                                             qk_scale_log2, err);
 
     // merge the waves' states block by block through the staging buffers
     float *mrg = (float *)&vbuf[0][0];
@@ -1474,7 +1518,7 @@ split_pair_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
 #pragma unroll
                     for (int k = 0; k < F::KLOADS; k++)
                         *(u32x4_t *)(buf + ((pb * F::KLOADS + k) * 64 + lane) * 16) = nxt.kraw[pb][k];
-                stage_v<D, F8>(nxt, stp * C::STEP, t_end, buf + KBYTES, lane);
+                stage_v<D, F8, KV::kI8>(nxt, stp * C::STEP, t_end, buf + KBYTES, lane);
                 if (lane == 0) *(int *)(buf + KBYTES + C::VBUF) = bad_nxt ? 1 : 0;
             }
             const int sn = stp + 4;
@@ -1489,8 +1533,9 @@ split_pair_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
 #pragma unroll
                 for (int k = 0; k < F::KLOADS; k++)
                     cur.kraw[pb][k] = *(const u32x4_t *)(buf + ((pb * F::KLOADS + k) * 64 + lane) * 16);
-            compute_step<D, MULTI, 1, F8>(cur, stp * C::STEP, t_end, t_lo, t_row, t_hs, t_rs, qop, st,
-                                          buf + KBYTES, lane, qk_scale_log2);
+            compute_step<D, MULTI, 1, F8, KV::kI8>(cur, stp * C::STEP, t_end, t_lo, t_row, t_hs,
+                                                   t_rs, qop, st, buf + KBYTES, lane,
+                                                   qk_scale_log2);
             if (*(const int *)(buf + KBYTES + C::VBUF)) poison_state<D>(st, err, lane);
         }
     }
@@ -1932,7 +1977,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
     // segment if the next claim leaves it
     auto body = [&](StepData<D, F8> &now, StepData<D, F8> &later) __attribute__((always_inline)) -> bool {
         const int t0_now = (t - cu0 + qr.first_step(cL)) * C::STEP;
-        stage_v<D, F8>(now, t0_now, cL, vbuf[w], lane);
+        stage_v<D, F8, KV::kI8>(now, t0_now, cL, vbuf[w], lane);
         const int tn = claim();
         const bool more = tn < x1;
         int ni = ci, nL = cL, nn = cn, nj = cj, nu0 = cu0;
@@ -1951,8 +1996,8 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
             t_rs[k] = qr.W > 0 ? max(0, t_row[k] - qr.W) : 0;
         }
         const int t_hs = qr.W > 0 ? max(0, cL - qr.W) : 0;
-        compute_step<D, MULTI, NHB, F8>(now, t0_now, cL, cL - qr.T + 1, t_row, t_hs, t_rs, qop, st,
-                                        vbuf[w], lane, cqs);
+        compute_step<D, MULTI, NHB, F8, KV::kI8>(now, t0_now, cL, cL - qr.T + 1, t_row, t_hs, t_rs,
+                                                 qop, st, vbuf[w], lane, cqs);
         if (bad_now) poison_state<D>(st, err, lane);
         bad_now = bad_next;
         mine++;
@@ -2674,19 +2719,21 @@ mqa_status mqa_decode_attn_paged(const void *q, const void *k_pages, const void 
                                        workspace, workspace_bytes, split_chunk, err_flags, stream);
 }
 
-// ---- fp8 e4m3 cache with per-K/V-head scales ----
+// ---- fp8 e4m3 and int8 caches with per-K/V-head scales ----
 
+extern "C++" {
 namespace {
-mqa_status launch_append_fp8(void *k, void *v, const void *k_new, const void *v_new,
-                             const float *k_scale, const float *v_scale, const int32_t *bt,
-                             const int32_t *seq_lens, int b, int T, int g, int S, int max_pages,
-                             int num_pages, int d, int32_t *err_flags, hipStream_t stream) {
+template <bool I8>
+mqa_status launch_append_codes(void *k, void *v, const void *k_new, const void *v_new,
+                               const float *k_scale, const float *v_scale, const int32_t *bt,
+                               const int32_t *seq_lens, int b, int T, int g, int S, int max_pages,
+                               int num_pages, int d, int32_t *err_flags, hipStream_t stream) {
     if (!aligned16(k) || !aligned16(v) || !aligned16(k_new) || !aligned16(v_new) ||
         ((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u))
         return MQA_ERR_ALIGN;
     const long long total = 2ll * b * T * g * (d / 8);
     if ((total + 255) / 256 > 0x7fffffffll) return MQA_ERR_SHAPE;
-    hipLaunchKernelGGL(append_kv_fp8_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+    hipLaunchKernelGGL(append_kv_codes_kernel<I8>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
                        stream, (uint8_t *)k, (uint8_t *)v, (const uint16_t *)k_new,
                        (const uint16_t *)v_new, k_scale, v_scale, bt, seq_lens, b, T, g, S,
                        max_pages, num_pages, d, err_flags);
@@ -2701,6 +2748,7 @@ mqa_status check_fp8(int b, int T, int h, int g, int S, int d, int split_chunk) 
     return check_tokens(T, h, S, MQA_BF16);
 }
 }  // namespace
+}  // extern "C++"
 
 mqa_status mqa_append_kv_fp8(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
                              const float *k_scale, const float *v_scale, const int32_t *seq_lens,
@@ -2710,8 +2758,8 @@ mqa_status mqa_append_kv_fp8(void *k_cache, void *v_cache, const void *k_new, co
         return MQA_ERR_NULL;
     const mqa_status st = check_fp8(b, T, g, g, S, d, 0);
     if (st != MQA_OK) return st;
-    return launch_append_fp8(k_cache, v_cache, k_new, v_new, k_scale, v_scale, nullptr, seq_lens, b,
-                             T, g, S, 1, 1, d, err_flags, stream);
+    return launch_append_codes<false>(k_cache, v_cache, k_new, v_new, k_scale, v_scale, nullptr,
+                                      seq_lens, b, T, g, S, 1, 1, d, err_flags, stream);
 }
 
 mqa_status mqa_append_kv_paged_fp8(void *k_pages, void *v_pages, const void *k_new,
@@ -2727,9 +2775,39 @@ mqa_status mqa_append_kv_paged_fp8(void *k_pages, void *v_pages, const void *k_n
         return MQA_ERR_SHAPE;
     const mqa_status st = check_fp8(b, T, g, g, page_size * max_pages, d, 0);
     if (st != MQA_OK) return st;
-    return launch_append_fp8(k_pages, v_pages, k_new, v_new, k_scale, v_scale, block_table,
-                             seq_lens, b, T, g, page_size, max_pages, num_pages, d, err_flags,
-                             stream);
+    return launch_append_codes<false>(k_pages, v_pages, k_new, v_new, k_scale, v_scale,
+                                      block_table, seq_lens, b, T, g, page_size, max_pages,
+                                      num_pages, d, err_flags, stream);
+}
+
+mqa_status mqa_append_kv_int8(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                              const float *k_scale, const float *v_scale, const int32_t *seq_lens,
+                              int b, int T, int g, int S, int d, int32_t *err_flags,
+                              hipStream_t stream) {
+    if (!k_cache || !v_cache || !k_new || !v_new || !k_scale || !v_scale || !seq_lens)
+        return MQA_ERR_NULL;
+    const mqa_status st = check_fp8(b, T, g, g, S, d, 0);
+    if (st != MQA_OK) return st;
+    return launch_append_codes<true>(k_cache, v_cache, k_new, v_new, k_scale, v_scale, nullptr,
+                                     seq_lens, b, T, g, S, 1, 1, d, err_flags, stream);
+}
+
+mqa_status mqa_append_kv_paged_int8(void *k_pages, void *v_pages, const void *k_new,
+                                    const void *v_new, const float *k_scale, const float *v_scale,
+                                    const int32_t *block_table, const int32_t *seq_lens, int b,
+                                    int T, int g, int page_size, int max_pages, int num_pages,
+                                    int d, int32_t *err_flags, hipStream_t stream) {
+    if (!k_pages || !v_pages || !k_new || !v_new || !k_scale || !v_scale || !block_table ||
+        !seq_lens)
+        return MQA_ERR_NULL;
+    if (page_size < 1 || max_pages < 1 || num_pages < 1 ||
+        (long long)page_size * max_pages > (1ll << 30))
+        return MQA_ERR_SHAPE;
+    const mqa_status st = check_fp8(b, T, g, g, page_size * max_pages, d, 0);
+    if (st != MQA_OK) return st;
+    return launch_append_codes<true>(k_pages, v_pages, k_new, v_new, k_scale, v_scale,
+                                     block_table, seq_lens, b, T, g, page_size, max_pages,
+                                     num_pages, d, err_flags, stream);
 }
 
 mqa_status mqa_decode_attn_fp8(const void *q, const void *k_cache, const void *v_cache,
@@ -2808,9 +2886,10 @@ mqa_status check_desc(const mqa_decode_desc *ds, int &S, bool sizes_only = false
     if (ds->window < 0 || ds->T < 1) return MQA_ERR_SHAPE;
     const bool paged = ds->block_table != nullptr;
     const int kd = ds->kv_dtype;
-    if (kd != MQA_F32 && kd != MQA_BF16 && kd != MQA_FP8_E4M3) return MQA_ERR_UNSUPPORTED;
+    const bool codes = kd == MQA_FP8_E4M3 || kd == MQA_INT8;  // one-byte codes with scales
+    if (kd != MQA_F32 && kd != MQA_BF16 && !codes) return MQA_ERR_UNSUPPORTED;
     if (kd == MQA_F32 && (paged || ds->T != 1 || ds->window != 0)) return MQA_ERR_UNSUPPORTED;
-    if (!sizes_only && kd == MQA_FP8_E4M3 && (!ds->k_scale || !ds->v_scale)) return MQA_ERR_NULL;
+    if (!sizes_only && codes && (!ds->k_scale || !ds->v_scale)) return MQA_ERR_NULL;
     mqa_status st;
     if (paged) {
         st = check_paged(ds->b, ds->h, ds->g, ds->page_size, ds->max_pages, ds->num_pages, ds->d,
@@ -2826,22 +2905,22 @@ mqa_status check_desc(const mqa_decode_desc *ds, int &S, bool sizes_only = false
     if (sizes_only) return MQA_OK;
     if (!aligned16(ds->q) || !aligned16(ds->k) || !aligned16(ds->v) || !aligned16(ds->out))
         return MQA_ERR_ALIGN;
-    if (kd == MQA_FP8_E4M3 && (((uintptr_t)ds->k_scale & 3u) || ((uintptr_t)ds->v_scale & 3u)))
+    if (codes && (((uintptr_t)ds->k_scale & 3u) || ((uintptr_t)ds->v_scale & 3u)))
         return MQA_ERR_ALIGN;
     return MQA_OK;
 }
 
-template <int D, bool F8>
+template <int D, bool F8, bool I8 = false>
 mqa_status run_desc(const mqa_decode_desc *ds, int S, int chunk, int nsplit, bool bal, float qs,
                     hipStream_t stream) {
     const uint8_t *kb = (const uint8_t *)ds->k, *vb = (const uint8_t *)ds->v;
     if (ds->block_table)
-        return run_mfma<D>(PagedKV<D, F8>{kb, vb, ds->block_table, ds->g, ds->page_size,
-                                          ds->max_pages, ds->num_pages},
+        return run_mfma<D>(PagedKV<D, F8, I8>{kb, vb, ds->block_table, ds->g, ds->page_size,
+                                              ds->max_pages, ds->num_pages},
                            ds->q, ds->seq_lens, ds->b, ds->T, ds->h, ds->g, S, qs, ds->out,
                            ds->workspace, chunk, nsplit, bal, ds->err_flags, stream, ds->k_scale,
                            ds->v_scale, ds->window);
-    return run_mfma<D>(ContigKV<D, F8>{kb, vb, ds->g, S}, ds->q, ds->seq_lens, ds->b, ds->T, ds->h,
+    return run_mfma<D>(ContigKV<D, F8, I8>{kb, vb, ds->g, S}, ds->q, ds->seq_lens, ds->b, ds->T, ds->h,
                        ds->g, S, qs, ds->out, ds->workspace, chunk, nsplit, bal, ds->err_flags,
                        stream, ds->k_scale, ds->v_scale, ds->window);
 }
@@ -2876,12 +2955,14 @@ mqa_status mqa_decode_attn_ex(const mqa_decode_desc *ds, hipStream_t stream) {
     if (!aligned16(ds->workspace)) return MQA_ERR_ALIGN;
     const bool bal = use_streamk(ds->b, ds->h, ds->g, Sw, dt, ds->split_chunk, MQA_KERNEL_MFMA, ds->T);
     const float qs = ds->scale * kLog2e;
-    const bool f8 = ds->kv_dtype == MQA_FP8_E4M3;
+    const int kd = ds->kv_dtype;
     if (ds->d == 128)
-        return f8 ? run_desc<128, true>(ds, S, chunk, nsplit, bal, qs, stream)
-                  : run_desc<128, false>(ds, S, chunk, nsplit, bal, qs, stream);
-    return f8 ? run_desc<64, true>(ds, S, chunk, nsplit, bal, qs, stream)
-              : run_desc<64, false>(ds, S, chunk, nsplit, bal, qs, stream);
+        return kd == MQA_INT8       ? run_desc<128, true, true>(ds, S, chunk, nsplit, bal, qs, stream)
+               : kd == MQA_FP8_E4M3 ? run_desc<128, true>(ds, S, chunk, nsplit, bal, qs, stream)
+                                    : run_desc<128, false>(ds, S, chunk, nsplit, bal, qs, stream);
+    return kd == MQA_INT8       ? run_desc<64, true, true>(ds, S, chunk, nsplit, bal, qs, stream)
+           : kd == MQA_FP8_E4M3 ? run_desc<64, true>(ds, S, chunk, nsplit, bal, qs, stream)
+                                : run_desc<64, false>(ds, S, chunk, nsplit, bal, qs, stream);
 }
 
 mqa_status mqa_rope_q(void *q, const float *cos_sin, int n_pos, const int32_t *seq_lens, int b,

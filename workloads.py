@@ -189,29 +189,39 @@ def make_multi_step(w: Workload, device="cpu", T: int = 4, layer: int = 0,
     return t
 
 
+def make_int8_step(w: Workload, device="cpu", T: int = 1, layer: int = 0,
+                   page_size: int = 0) -> dict:
+    """make_fp8_step over an int8 cache (codes N(0, 32) rounded, clamped to
+    +-127; scales U[1/48, 1/24] per K/V head)."""
+    return make_fp8_step(w, device, T, layer, page_size, int8=True)
+
+
 def make_fp8_step(w: Workload, device="cpu", T: int = 1, layer: int = 0,
-                  page_size: int = 0) -> dict:
+                  page_size: int = 0, int8: bool = False) -> dict:
     """A step over an fp8 e4m3 cache: k_cache/v_cache uint8 codes [b, g, S, d]
     (or k_pages/v_pages with block_table), k_scale/v_scale float32 [g], q bf16
     [b, h, d] (T = 1) or [b, T, h, d], k_new/v_new bf16 [b, g, d] or [b, T, g, d],
-    seq_lens (post-append, at least T)."""
+    seq_lens (post-append, at least T). With int8 the codes are int8."""
     base = w.seed + 100 * layer
-    gen = torch.Generator(device=device).manual_seed(base + 11)
+    gen = torch.Generator(device=device).manual_seed(base + (13 if int8 else 11))
     shape = (w.b, w.g, w.S, w.d)
 
     def codes():
         kw = dict(generator=gen, device=device)
+        if int8:  # N(0, 32) rounded and clamped to +-127: N(0,1)-like values at scale ~1/32
+            return torch.round(torch.randn(shape, **kw) * 32).clamp(-127, 127).to(torch.int8)
         sign = torch.randint(0, 2, shape, dtype=torch.uint8, **kw)
         expo = (7 + torch.round(torch.randn(shape, **kw) * 1.5)).clamp(1, 14).to(torch.uint8)
         mant = torch.randint(0, 8, shape, dtype=torch.uint8, **kw)
         return (sign << 7) | (expo << 3) | mant
 
     k, v = codes(), codes()
-    sgen = torch.Generator().manual_seed(base + 12)
+    sgen = torch.Generator().manual_seed(base + (14 if int8 else 12))
+    lo, span = (1 / 48, 1 / 48) if int8 else (0.25, 0.75)
     t = {
         "k_cache": k, "v_cache": v,
-        "k_scale": (0.25 + 0.75 * torch.rand(w.g, generator=sgen)).to(device),
-        "v_scale": (0.25 + 0.75 * torch.rand(w.g, generator=sgen)).to(device),
+        "k_scale": (lo + span * torch.rand(w.g, generator=sgen)).to(device),
+        "v_scale": (lo + span * torch.rand(w.g, generator=sgen)).to(device),
         "seq_lens": torch.clamp(seq_lens(w), min=T).to(device),
     }
     if T == 1:
@@ -231,10 +241,11 @@ def make_fp8_step(w: Workload, device="cpu", T: int = 1, layer: int = 0,
         pgen = torch.Generator().manual_seed(base + 7)
         ids = torch.randperm(num, generator=pgen)[: b * maxp].view(b, maxp).to(torch.int32)
         for name, c in (("k_pages", k), ("v_pages", v)):
-            padded = torch.zeros((b, g, maxp * P, d), dtype=torch.uint8, device=device)
+            padded = torch.zeros((b, g, maxp * P, d), dtype=c.dtype, device=device)
             padded[:, :, :S] = c
             per_page = padded.view(b, g, maxp, P, d).permute(0, 2, 1, 3, 4).reshape(b * maxp, g, P, d)
-            dst = torch.full((num, g, P, d), 0x7F, dtype=torch.uint8, device=device)  # NaN codes
+            # unused pages: NaN codes (fp8), the largest code (int8)
+            dst = torch.full((num, g, P, d), 127 if int8 else 0x7F, dtype=c.dtype, device=device)
             dst[ids.view(-1).long().to(device)] = per_page
             t[name] = dst
         del t["k_cache"], t["v_cache"]
