@@ -93,6 +93,10 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 __device__ __forceinline__ u32x4_t buffer_stream16(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
 }
+// 16 bytes through a descriptor, cached (read again soon by another wave)
+__device__ __forceinline__ u32x4_t buffer_cached16(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 
 // 16-byte global -> LDS copy. The LDS destination of lane l is
 // lds_block + 16*l (lds_block is wave-uniform and goes through m0, which is
@@ -978,9 +982,13 @@ __device__ __forceinline__ void stage_page_ids(const KV &kv, int *pg, int n, Whe
     }
 }
 
-// Issue the loads of one step.
-template <int D, bool F8 = false>
+// Issue the loads of one step: streamed (non-temporal), or with SHARED
+// cached, for steps that another group of waves reads again right after.
+template <int D, bool F8 = false, bool SHARED = false>
 __device__ __forceinline__ void load_step(const StepSrc &src, int lane, StepData<D, F8> &sd) {
+    auto ld = [](rsrc_t r, uint32_t off) __attribute__((always_inline)) {
+        return SHARED ? buffer_cached16(r, off) : buffer_stream16(r, off);
+    };
     using F = KvFmt<D, F8>;
     const int r = lane & 15, qd = lane >> 4;
     const int vl_row = lane / F::VCPR, vl_chunk = lane % F::VCPR;
@@ -990,11 +998,11 @@ __device__ __forceinline__ void load_step(const StepSrc &src, int lane, StepData
     for (int pb = 0; pb < 2; pb++)
 #pragma unroll
         for (int k = 0; k < F::KLOADS; k++)
-            sd.kraw[pb][k] = buffer_stream16(src.k[pb], src.off[pb] + kl + 64 * k);
+            sd.kraw[pb][k] = ld(src.k[pb], src.off[pb] + kl + 64 * k);
 #pragma unroll
     for (int ii = 0; ii < F::VLOADS; ii++) {
         constexpr int H = 16 / F::VRPI;  // V loads per half
-        sd.vld[ii] = buffer_stream16(src.v[ii / H], src.off[ii / H] + vl + (ii % H) * F::VRPI * F::RB);
+        sd.vld[ii] = ld(src.v[ii / H], src.off[ii / H] + vl + (ii % H) * F::VRPI * F::RB);
     }
 }
 
@@ -1683,7 +1691,7 @@ __device__ __forceinline__ void lds_flag_wait(int *f, int v) {
 // each is on a segment that ends earlier in the range, so they cannot form a
 // cycle. Which wave computes which step depends on timing, so the rounding
 // of the sums can differ between calls.
-template <int D, int NW, class KV, bool MULTI, int NHB>
+template <int D, int NW, class KV, bool MULTI, int NHB, bool SHARED = false>
 __global__ void __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(1, 8)))
 streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
@@ -1859,7 +1867,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
     locate(t, ci, cL, cn, cj, cu0);
     bool bad_now = false;  // the current step read an invalid page
     StepData<D, F8> A, B;
-    load_step<D, F8>(src_of(ci, cj, cL, cu0, t, bad_now), lane, A);
+    load_step<D, F8, SHARED>(src_of(ci, cj, cL, cu0, t, bad_now), lane, A);
     float cqs = F8 ? qk_base * k_scale[cj] : qk_base;  // the unit's score factor
     float cvs = F8 ? v_scale[cj] : 1.f;                // and output factor
     bf16x8_t qop[NHB][C::KSTEPS];
@@ -1985,7 +1993,8 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
         const bool next_unit = more && nu0 != cu0;
         bool bad_next = false;
         // nothing left: a step that loads nothing
-        load_step<D, F8>(more ? src_of(ni, nj, nL, nu0, tn, bad_next) : kv.none(), lane, later);
+        load_step<D, F8, SHARED>(more ? src_of(ni, nj, nL, nu0, tn, bad_next) : kv.none(), lane,
+                                 later);
         // causal ends of several tokens: this lane's row in each block, the
         // wave's earliest
         // (and the window starts)
@@ -2371,10 +2380,20 @@ mqa_status run_mfma_rows(const KV &kv, const void *q, const int32_t *seq_lens, i
         // per compute unit then hide the latencies of one another's steps
         // (measured faster for fp8, slower for bf16, whose steps are cheaper)
         constexpr int NWV = (KV::kF8 && NHB == 1) ? 8 : kStreamWaves;
-        hipLaunchKernelGGL((streamk_mfma_kernel<D, NWV, KV, MULTI, NHB>), dim3(nwg),
-                           dim3(64 * NWV), 0, stream, (const uint16_t *)q, kv, seq_lens, b,
-                           qr, g, S, R, ngroups, qs, k_scale, v_scale, out, po, pml, desc,
-                           err_flags);
+        // several head groups read each step one after another: cached loads,
+        // so that the later groups find it in L2 (streamed, about half of
+        // their reads went to HBM again: 956 MB fetched per call for 643 MB
+        // with eight tokens on gqa-70b)
+        if (ngroups > 1)
+            hipLaunchKernelGGL((streamk_mfma_kernel<D, NWV, KV, MULTI, NHB, true>), dim3(nwg),
+                               dim3(64 * NWV), 0, stream, (const uint16_t *)q, kv, seq_lens, b,
+                               qr, g, S, R, ngroups, qs, k_scale, v_scale, out, po, pml, desc,
+                               err_flags);
+        else
+            hipLaunchKernelGGL((streamk_mfma_kernel<D, NWV, KV, MULTI, NHB>), dim3(nwg),
+                               dim3(64 * NWV), 0, stream, (const uint16_t *)q, kv, seq_lens, b,
+                               qr, g, S, R, ngroups, qs, k_scale, v_scale, out, po, pml, desc,
+                               err_flags);
         // pieces per cut unit: ~2 when there are more units than work-groups,
         // ~nwg/units when each unit spans many ranges
         constexpr int HPB = 256 / (D / 4);  // head slots per block with one piece lane
