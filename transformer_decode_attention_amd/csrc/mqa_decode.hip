@@ -819,41 +819,38 @@ __device__ __forceinline__ void load_q_operand(const uint16_t *__restrict__ q, s
 }
 
 // 16 fp8 e4m3 codes (4 dwords, element e in byte e) -> elements 0..7 and
-// 8..15 as bf16. Exact: every e4m3 value is a bf16 value, so the fp32 the
-// conversion instruction returns (it decodes OCP e4m3, measured for all 256
-// codes on the device) has nothing in its low 16 bits.
+// 8..15 as bf16, two codes per instruction (v_cvt_scalef32_pk_bf16_fp8 with
+// scale 1: the low half of the result is byte 0 (word select: byte 2), the
+// high half byte 1 (byte 3); exact, since every e4m3 value is a bf16 value —
+// measured on the device for all 256 codes against the fp32 conversion).
 __device__ __forceinline__ void fp8x16_to_bf16(const u32x4_t &w, bf16x8_t &lo, bf16x8_t &hi) {
     uint32_t o[8];
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-        const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);  // bytes 0, 1
-        const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);   // bytes 2, 3
-        // (elements copied out first: a bit cast of a vector element
-        // expression reads element 0 with this compiler)
-        const float a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
-        o[2 * k] = (__builtin_bit_cast(uint32_t, a1) & 0xffff0000u) |
-                   (__builtin_bit_cast(uint32_t, a0) >> 16);
-        o[2 * k + 1] = (__builtin_bit_cast(uint32_t, b1) & 0xffff0000u) |
-                       (__builtin_bit_cast(uint32_t, b0) >> 16);
+        // (a scalar copy first: a bit cast of a vector element expression
+        // reads element 0 with this compiler)
+        const uint32_t wk = w[k];
+        o[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wk, 1.0f, false));
+        o[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wk, 1.0f, true));
     }
     lo = __builtin_bit_cast(bf16x8_t, (u32x4_t){o[0], o[1], o[2], o[3]});
     hi = __builtin_bit_cast(bf16x8_t, (u32x4_t){o[4], o[5], o[6], o[7]});
 }
 
 // 16 int8 codes (two's complement, element e in byte e) -> elements 0..7
-// and 8..15 as bf16. Exact: a code's magnitude is at most 128, which needs
-// at most 8 significant bits, so its fp32 value has nothing in the low 16
-// bits.
+// and 8..15 as bf16: each byte sign-extended to fp32 (one conversion with a
+// byte select), pairs packed to bf16. Exact: a code's magnitude is at most
+// 128, which needs at most 8 significant bits.
 __device__ __forceinline__ void int8x16_to_bf16(const u32x4_t &w, bf16x8_t &lo, bf16x8_t &hi) {
     uint32_t o[8];
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-        const uint32_t wk = w[k];  // (a scalar copy: see fp8x16_to_bf16)
+        const uint32_t wk = w[k];  // (a scalar copy, as in fp8x16_to_bf16)
 #pragma unroll
         for (int p = 0; p < 2; p++) {
             const float f0 = (float)(int8_t)(wk >> (16 * p)), f1 = (float)(int8_t)(wk >> (16 * p + 8));
-            o[2 * k + p] = (__builtin_bit_cast(uint32_t, f1) & 0xffff0000u) |
-                           (__builtin_bit_cast(uint32_t, f0) >> 16);
+            const bf16x2_t v = {(__bf16)f0, (__bf16)f1};
+            o[2 * k + p] = __builtin_bit_cast(uint32_t, v);
         }
     }
     lo = __builtin_bit_cast(bf16x8_t, (u32x4_t){o[0], o[1], o[2], o[3]});
