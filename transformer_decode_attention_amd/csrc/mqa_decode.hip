@@ -2434,7 +2434,11 @@ mqa_status run_mfma(const KV &kv, const void *q, const int32_t *seq_lens, int b,
                     int g, int S, float qs, float *out, void *workspace, int chunk, int nsplit,
                     bool balanced, int32_t *err_flags, hipStream_t stream,
                     const float *k_scale = nullptr, const float *v_scale = nullptr, int W = 0) {
-    const bool two = row_blocks(T * (h / g)).per_wave == 2;
+    const RowBlocks rb = row_blocks(T * (h / g));
+    // one-byte codes, balanced schedule, two blocks: one block per wave in
+    // eight waves (two head groups reading each step, the second from L2)
+    // rather than both blocks in each of four waves
+    const bool two = rb.per_wave == 2 && !(KV::kF8 && balanced && rb.blocks == 2);
     if (T > 1 || W > 0) {
         if (two)
             return run_mfma_rows<D, KV, true, 2>(kv, q, seq_lens, b, T, h, g, S, qs, k_scale,
