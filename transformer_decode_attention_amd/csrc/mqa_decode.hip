@@ -805,7 +805,7 @@ struct MfmaState {
 
 // Q^T operand of query head `hq`: for k-step k lane holds Q[hq][d0 .. d0+8],
 // d0 = 32k + 8qd, in the order the K operand's lanes hold K's elements. With
-// an fp8 cache a lane's 16-byte K load holds 16 elements, which feed two
+// a one-byte cache (fp8 or int8 codes) a lane's 16-byte K load holds 16 elements, which feed two
 // k-steps: then d0 = 16qd + 8(k%2) + 64(k/2) (any order of d gives the same
 // dot product, as long as Q and K agree).
 template <int D, bool F8 = false>
@@ -1390,7 +1390,7 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
     MfmaState<D> st[NHB];
 #pragma unroll
     for (int b = 0; b < NHB; b++) st[b].reset();
-    // an fp8 cache: scores scale by the head's K scale, outputs by its V scale
+    // a code cache (fp8, int8): scores scale by the head's K scale, outputs by its V scale
     const float qk_scale_log2 = F8 ? qk_base * k_scale[j] : qk_base;
     const float vsc = F8 ? v_scale[j] : 1.f;
     run_steps<D, MULTI, NHB, 2, F8, KV::kI8>(src, kv.none(), s0 + w, s0 + nsteps, C::NW, t_end,
@@ -1699,7 +1699,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
                     float2 *__restrict__ part_ml, int4 *__restrict__ cut_desc,
                     int32_t *__restrict__ err) {
     using C = MfmaCfg<D>;
-    constexpr bool F8 = KV::kF8;  // fp8 cache: per-K/V-head scales on scores and outputs
+    constexpr bool F8 = KV::kF8;  // fp8 or int8 codes: per-K/V-head scales on scores and outputs
     static_assert(NW == 4 || NW == 8, "waves per work-group (the segment records hold 8 bits)");
     __shared__ __attribute__((aligned(16))) uint8_t vbuf[NW][C::VBUF];
     __shared__ f32x4_t slot_o[NW][NHB][C::NB][64];  // a wave's acc, lane-native order
@@ -2373,7 +2373,7 @@ mqa_status run_mfma_rows(const KV &kv, const void *q, const int32_t *seq_lens, i
         float *po = (float *)workspace;
         float2 *pml = (float2 *)((uint8_t *)workspace + L.ml_off);
         int4 *desc = (int4 *)((uint8_t *)workspace + L.desc_off);
-        // an fp8 cache costs more per byte (the decode to bf16): eight waves
+        // a code cache (fp8, int8) costs more per byte (the decode to bf16): eight waves
         // per compute unit then hide the latencies of one another's steps
         // (measured faster for fp8, slower for bf16, whose steps are cheaper)
         constexpr int NWV = (KV::kF8 && NHB == 1) ? 8 : kStreamWaves;
