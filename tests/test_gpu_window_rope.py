@@ -113,10 +113,12 @@ def test_decode_ex_without_options_equals_the_plain_call():
     assert torch.equal(a, b)  # the same kernels, fixed partitions: bitwise
 
 
-def test_rope_q_and_append_bit_exact():
-    b, T, h, g, S, d = 16, 3, 16, 4, 256, 128
+@pytest.mark.parametrize("b,T,h,g,S,d", [(16, 3, 16, 4, 256, 128), (8, 1, 8, 8, 200, 64),
+                                         (4, 5, 32, 1, 300, 64)])
+def test_rope_q_and_append_bit_exact(b, T, h, g, S, d):
+    print(f"[rope] b={b} T={T} h={h} g={g} S={S} d={d}", flush=True)
     cs = oracle.rope_table(10000.0, S, d)
-    w = wl("rope", b, h, g, d, S, 5, S, 950)
+    w = wl("rope", b, h, g, d, S, T, S, 950 + d + T)
     t = W.make_multi_step(w, DEV, T=T)
     lens = t["seq_lens"].cpu().numpy()
     q0 = W.to_oracle(t["q"])
