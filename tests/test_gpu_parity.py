@@ -296,6 +296,44 @@ def _check_lens(w: W.Workload, lens, split_chunk=0, kernel=mqa.KERNEL_AUTO):
     return compare(out, ref, w.name)
 
 
+@pytest.mark.parametrize("chunk", [0, 256])
+def test_lengths_at_step_and_partition_edges(chunk):
+    """Lengths at the edges of the 32-position steps (31, 32, 33), of a
+    partition of C positions (C-1, C, C+1) and of the capacity (S-1, S), with
+    1: fixed partitions (C = 256) and the balanced schedule (C = 0)."""
+    S = 1000
+    edges = [1, 2, 31, 32, 33, 63, 64, 65, 255, 256, 257, 511, 512, 513, S - 1, S]
+    b = 256  # enough (sequence, K/V head) units for the balanced schedule
+    lens = [edges[i % len(edges)] for i in range(b)]
+    w = W.Workload("edges", b=b, h=16, g=2, d=128, S=S, dtype=torch.bfloat16, seed=28)
+    if chunk == 0:
+        assert mqa.decode_schedule(w.b, w.h, w.g, w.S, w.d, w.dtype) == "mfma-balanced"
+    print(_check_lens(w, lens, split_chunk=chunk), flush=True)
+
+
+def test_paged_lengths_at_page_edges():
+    """Paged cache (16-row pages): lengths at page and step edges."""
+    S, P = 200, 16
+    edges = [1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 199, 200]
+    b = 128
+    w = W.Workload("page-edges", b=b, h=16, g=2, d=128, S=S, dtype=torch.bfloat16, seed=29)
+    t = W.make_paged_step(w, DEV, page_size=P)
+    t["seq_lens"] = torch.tensor([edges[i % len(edges)] for i in range(b)], dtype=torch.int32,
+                                 device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = mqa.decode_attn_paged(t["q"], t["k_pages"], t["v_pages"], t["block_table"],
+                                t["seq_lens"], err_flags=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    d = w.d
+    ref, rc = oracle.decode_attn_paged(W.to_oracle(t["q"]), W.to_oracle(t["k_pages"]),
+                                       W.to_oracle(t["v_pages"]), t["block_table"].cpu().numpy(),
+                                       t["seq_lens"].cpu().numpy(),
+                                       float(np.float32(1.0 / math.sqrt(d))), nthreads=NTHREADS)
+    assert rc == oracle.OK
+    compare(out, ref, "page edges")
+
+
 def test_many_short_sequences():
     """Units far smaller than a work-group's range (many units per range)."""
     gen = torch.Generator().manual_seed(8)
