@@ -1,6 +1,6 @@
 """Parity over seeded random combinations of every option.
 
-Forty cases drawn from a fixed seed: head dimension, K/V heads and group
+Forty cases (MQA_COMBO_CASES) drawn from a fixed seed (MQA_COMBO_SEED): head dimension, K/V heads and group
 size, query tokens, cache type (bf16, fp8 or int8 codes), layout (contiguous
 or pages of 16 or 32 rows), sliding window, automatic or fixed partitions,
 batch and ragged lengths. Each runs the matching append and the general
@@ -88,7 +88,11 @@ def host(x, kv):
     return W.to_oracle(x) if kv == "bf16" else x.cpu().numpy()
 
 
-@pytest.mark.parametrize("case", draw_cases(), ids=lambda c: f"case{c[0]}")
+CASES = draw_cases(int(os.environ.get("MQA_COMBO_CASES", "40")),
+                   int(os.environ.get("MQA_COMBO_SEED", "2024")))
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"case{c[0]}")
 def test_random_combination(case):
     k, d, g, G, T, kv, P, S, b, window, chunk = case
     h = g * G
