@@ -1,9 +1,9 @@
 """Parity over seeded random combinations of every option.
 
-Forty cases (MQA_COMBO_CASES) drawn from a fixed seed (MQA_COMBO_SEED): head dimension, K/V heads and group
-size, query tokens, cache type (bf16, fp8 or int8 codes), layout (contiguous
-or pages of 16 or 32 rows), sliding window, automatic or fixed partitions,
-batch and ragged lengths. Each runs the matching append and the general
+Forty cases (MQA_COMBO_CASES) drawn from a fixed seed (MQA_COMBO_SEED):
+head dimension, K/V heads and group size, query tokens, cache type (bf16,
+fp8 or int8 codes), layout (contiguous or pages of 16 or 32 rows), sliding
+window, automatic or fixed partitions, batch and ragged lengths. Each runs the matching append and the general
 decode call (mqa_decode_attn_ex) on the GPU and compares against the oracle
 on the bytes read back: the append bit-exact, the attention within |gpu -
 ref| <= 2e-3 and |gpu - ref| / max(|ref|, rms(ref row)) <= 2e-3.
