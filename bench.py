@@ -20,6 +20,9 @@ Prints one JSON line:
                small configurations are bound by that issue time when eager)
   hbm_copy_gbs a plain 1 GiB device-to-device copy (read + write bytes / time):
                what a simple streaming kernel attains on this part (context)
+  launch_us    time per launch of a chain of 200 empty kernels on the stream,
+               issued eagerly from Python and replayed from a HIP graph (the
+               floors under any one-kernel call; context)
 
 Algorithmic bytes per decode launch and layer: the K and V rows attended
 (sum_i 2*g*L_i*d*B) + q (b*h*d*B) + out (b*h*d*4). The append adds
@@ -314,6 +317,7 @@ def main() -> int:
     graph = None if args.no_graph else graph_timing(torch, step, layers, reps, args.steps)
     assert int(err.item()) == 0, "device reported an error in the graph replays"
     hbm_copy = copy_gbs(torch, dev)
+    launch_us = empty_launch_us(torch)
 
     if args.copy_probe:
         n = 1 << 30
@@ -382,6 +386,7 @@ def main() -> int:
         "cpu_baseline": None,
         "graph": graph,
         "hbm_copy_gbs": hbm_copy,
+        "launch_us": launch_us,
     }
 
     if not args.no_cpu_baseline:
@@ -440,6 +445,43 @@ def copy_gbs(torch, dev) -> float:
         best = min(best, a.elapsed_time(b))
     del src, dst
     return round(2 * n / (best * 1e-3) / 1e9, 1)
+
+
+def empty_launch_us(torch, n: int = 200):
+    """µs per launch of n back-to-back empty kernels (torch.cuda._sleep(0)),
+    issued eagerly and replayed from a graph; None where unavailable."""
+    if not hasattr(torch.cuda, "_sleep"):
+        return None
+
+    def chain():
+        for _ in range(n):
+            torch.cuda._sleep(0)
+
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        return round(a.elapsed_time(b) * 1e3 / n, 3)
+
+    chain()
+    res = {"eager": timed(chain)}
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            chain()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            chain()
+        g.replay()
+        res["graph"] = timed(g.replay)
+    except RuntimeError:
+        res["graph"] = None
+    return res
 
 
 def cpu_model() -> str:
