@@ -129,6 +129,14 @@ def test_multi_paged(T, P):
     run_and_check(w, T, page_size=P)
 
 
+@pytest.mark.parametrize("T,h,g,S,b", [(32, 32, 8, 300, 8), (64, 16, 1, 500, 2), (48, 64, 64, 200, 4)])
+def test_prompt_chunks(T, h, g, S, b):
+    """Long prompt chunks (T = 32 .. 64 tokens: 128 to 3072 query rows per
+    unit), causal within the chunk, lengths from T to the capacity."""
+    w = wl("chunk", b, h, g, 128, S, T, S, 780 + T)
+    run_and_check(w, T)
+
+
 def test_multi_one_token_is_the_plain_decode():
     w = wl("multi-one", 64, 64, 8, 128, 1024, 1, 1024, 750)
     t = W.make_step(w, DEV)
