@@ -2115,23 +2115,36 @@ streamk_combine_kernel(const float *__restrict__ part_o, const float2 *__restric
 
 // Block (k, i): partial row i*T*h + k (k = j*R + rho: K/V head j, query row
 // rho of the unit), written to out row qr.row(i, j, rho). Threads are (piece
-// lane, four columns); piece lane pl merges partitions pl, pl+PL, ... (four
+// lane, four columns); piece lane pl merges partitions pl, pl+PL, ... (BATCH
 // loads in flight at a time) and the lanes are merged in order through LDS,
-// so the result is the same every call.
-template <int D>
+// so the result is the same every call. The first batch is loaded before the
+// sequence length arrives (partitions below nsplit lie in the workspace
+// whatever the length) and masked once the sequence's partition count is
+// known, which saves one dependent round trip to memory.
+template <int D, int BATCH>
 __global__ void __launch_bounds__(256)
 combine_kernel(const float *__restrict__ part_o, const float2 *__restrict__ part_ml,
                const int32_t *__restrict__ seq_lens, const QRows<true> qr, int R, int S, int chunk,
                int nsplit, float *__restrict__ out, int32_t *__restrict__ err) {
     constexpr int C4 = D / 4;           // float4 columns per row
     constexpr int PL = 256 / C4;        // piece lanes
-    constexpr int BATCH = 4;
     __shared__ f32x4_t s_num[PL][C4];
     __shared__ float2 s_md[PL][C4];
     const int k = blockIdx.x, i = blockIdx.y;
     const int pl = threadIdx.x / C4, c4 = threadIdx.x % C4;
     const size_t row = (size_t)i * qr.T * qr.h + k;
     const size_t orow = qr.row(i, k / R, k % R);
+    const float2 *ml = part_ml + row * nsplit;
+    const float *po = part_o + row * nsplit * D + 4 * c4;
+    float2 e[BATCH];
+    f32x4_t o[BATCH];
+#pragma unroll
+    for (int kk = 0; kk < BATCH; kk++) {
+        const int p = pl + kk * PL;
+        const bool ok = p < nsplit;
+        e[kk] = ok ? ml[p] : make_float2(-INFINITY, 0.f);
+        o[kk] = ok ? *(const f32x4_t *)(po + (size_t)p * D) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
     const int L = seq_lens[i];
     if (L < qr.T || L > S) {  // uniform over the block
         if (pl == 0) *(f32x4_t *)(out + orow * D + 4 * c4) = f32x4_t{1.f, 1.f, 1.f, 1.f} * __builtin_nanf("");
@@ -2140,19 +2153,24 @@ combine_kernel(const float *__restrict__ part_o, const float2 *__restrict__ part
     }
     // partitions start at the window's first step (0 without a window)
     const int n = (L - window_first_step(L, qr.T, qr.W) * 32 + chunk - 1) / chunk;
-    const float2 *ml = part_ml + row * nsplit;
-    const float *po = part_o + row * nsplit * D + 4 * c4;
     float M = -INFINITY, den = 0.f;
     f32x4_t num = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int p0 = pl; p0 < n; p0 += BATCH * PL) {
-        float2 e[BATCH];
-        f32x4_t o[BATCH];
+        if (p0 != pl) {
 #pragma unroll
-        for (int kk = 0; kk < BATCH; kk++) {
-            const int p = p0 + kk * PL;
-            const bool ok = p < n;
-            e[kk] = ok ? ml[p] : make_float2(-INFINITY, 0.f);
-            o[kk] = ok ? *(const f32x4_t *)(po + (size_t)p * D) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int kk = 0; kk < BATCH; kk++) {
+                const int p = p0 + kk * PL;
+                const bool ok = p < n;
+                e[kk] = ok ? ml[p] : make_float2(-INFINITY, 0.f);
+                o[kk] = ok ? *(const f32x4_t *)(po + (size_t)p * D) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        } else {  // the first batch: drop partitions past the sequence's last
+#pragma unroll
+            for (int kk = 0; kk < BATCH; kk++)
+                if (p0 + kk * PL >= n) {
+                    e[kk] = make_float2(-INFINITY, 0.f);
+                    o[kk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
         }
         float Mb = M;
 #pragma unroll
@@ -2187,6 +2205,22 @@ combine_kernel(const float *__restrict__ part_o, const float2 *__restrict__ part
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+
+// The log-sum-exp combine over nsplit partitions per row: eight loads in
+// flight per piece lane when a lane has more than four partitions to merge
+// (one round trip instead of two), four otherwise.
+template <int D>
+void launch_combine(dim3 grid, hipStream_t stream, const float *part_o, const float2 *part_ml,
+                    const int32_t *seq_lens, const QRows<true> &qc, int R, int S, int chunk,
+                    int nsplit, float *out, int32_t *err_flags) {
+    constexpr int PL = 256 / (D / 4);
+    if ((nsplit + PL - 1) / PL > 4)
+        hipLaunchKernelGGL((combine_kernel<D, 8>), grid, dim3(256), 0, stream, part_o, part_ml,
+                           seq_lens, qc, R, S, chunk, nsplit, out, err_flags);
+    else
+        hipLaunchKernelGGL((combine_kernel<D, 4>), grid, dim3(256), 0, stream, part_o, part_ml,
+                           seq_lens, qc, R, S, chunk, nsplit, out, err_flags);
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 // Compute units of the current device (256 on MI355X; also the answer when
@@ -2422,8 +2456,8 @@ mqa_status run_mfma_rows(const KV &kv, const void *q, const int32_t *seq_lens, i
                            ngroups, chunk, nsplit, qs, k_scale, v_scale, part_o, part_ml, err_flags);
     }
     if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
-    hipLaunchKernelGGL(combine_kernel<D>, dim3(T * h, b), dim3(256), 0, stream, part_o, part_ml,
-                       seq_lens, qc, R, S, chunk, nsplit, out, err_flags);
+    launch_combine<D>(dim3(T * h, b), stream, part_o, part_ml, seq_lens, qc, R, S, chunk, nsplit,
+                      out, err_flags);
     return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
 }
 
@@ -2580,11 +2614,11 @@ mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache, const void
     if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
     const QRows<true> qc{1, h / g, h, 0};
     if (d == 128)
-        hipLaunchKernelGGL(combine_kernel<128>, dim3(h, b), dim3(256), 0, stream, part_o, part_ml,
-                           seq_lens, qc, h / g, S, chunk, nsplit, out, err_flags);
+        launch_combine<128>(dim3(h, b), stream, part_o, part_ml, seq_lens, qc, h / g, S, chunk,
+                            nsplit, out, err_flags);
     else
-        hipLaunchKernelGGL(combine_kernel<64>, dim3(h, b), dim3(256), 0, stream, part_o, part_ml,
-                           seq_lens, qc, h / g, S, chunk, nsplit, out, err_flags);
+        launch_combine<64>(dim3(h, b), stream, part_o, part_ml, seq_lens, qc, h / g, S, chunk,
+                           nsplit, out, err_flags);
     return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
 }
 
