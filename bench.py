@@ -117,7 +117,7 @@ def main() -> int:
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build runs on a single MI355X and has no "
+        print("bench.py measures one GPU only: the library runs on a single MI355X and has no "
               "multi-GPU path; run with --gpus 1", file=sys.stderr)
         return 2
 
