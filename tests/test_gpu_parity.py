@@ -91,7 +91,7 @@ def test_workload_full_size(name):
 
 
 @pytest.mark.parametrize("name", ["sweep-g1", "sweep-g8", "sweep-g32"])
-@pytest.mark.parametrize("layer", [0, 31])
+@pytest.mark.parametrize("layer", [0, 17, 31])
 def test_sweep_layers(name, layer):
     print(check_case(W.WORKLOADS[name], layer=layer), flush=True)
 
