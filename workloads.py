@@ -14,6 +14,8 @@ section):
              (ybb.press GQA/MQA notes §一 and §七: LLaMA-2-70B-like h=64, g=8,
              4K context, 64 concurrent sequences)
   gqa-70b-full  the same with every L = 4096
+  gqa-70b-tp8   one GPU's share of gqa-70b when the heads are split 8 ways
+             (b=64, h=8, g=1, the same lengths): one K/V head and its 8 query heads
   mqa-32k    b=4, h=32, g=1, d=128, L=32768, bf16 (same notes §一: context of 32K)
   sweep-g{1,8,32}  32 layers of b=16, h=32, d=128, L=8192, bf16, g in {1, 8, 32}
              (compassingai "多查詢注意力", 技術原理: d_model=4096, h=32, seq 8192, 32 layers)
@@ -80,6 +82,8 @@ WORKLOADS = {
                         seed=3000, L=None, L_lo=1024, L_hi=4096),
     "gqa-70b-full": Workload("gqa-70b-full", b=64, h=64, g=8, d=128, S=4096,
                              dtype=torch.bfloat16, seed=3000, L=4096),
+    "gqa-70b-tp8": Workload("gqa-70b-tp8", b=64, h=8, g=1, d=128, S=4096, dtype=torch.bfloat16,
+                            seed=3000, L=None, L_lo=1024, L_hi=4096),
     "mqa-32k": Workload("mqa-32k", b=4, h=32, g=1, d=128, S=32768, dtype=torch.bfloat16,
                         seed=4000, L=32768),
     "sweep-g1": Workload("sweep-g1", b=16, h=32, g=1, d=128, S=8192, dtype=torch.bfloat16,
