@@ -1276,41 +1276,78 @@ __device__ __forceinline__ void run_steps(const Src &src, const StepSrc &nothing
     }
 }
 
-// Publish one wave's state into the merge scratch (mrg [NW][HB][D], mls [NW][HB][2]).
+// Merge of the running states of the waves that share one 16-row block of a
+// partition, in two halves around a work-group barrier. First every wave
+// stores its state in lane order: acc in so[slot][nb][lane] (16 bytes per lane
+// and column block) and (reference max, sum) of head r in sml[slot][r].
 template <int D>
-__device__ __forceinline__ void publish_state(const MfmaState<D> &st, float *mrg, float *mls, int w,
+__device__ __forceinline__ void publish_lanes(const MfmaState<D> &st, f32x4_t *so, float2 *sml, int slot,
                                               int lane) {
     using C = MfmaCfg<D>;
     const int r = lane & 15, qd = lane >> 4;
     const float l_head = st.l_lane + __shfl_xor(st.l_lane, 16);
     const float l_tot = l_head + __shfl_xor(l_head, 32);
 #pragma unroll
-    for (int nb = 0; nb < C::NB; nb++)
-#pragma unroll
-        for (int v = 0; v < 4; v++) mrg[(w * C::HB + 4 * qd + v) * D + 16 * nb + r] = st.acc[nb][v];
-    if (qd == 0) {
-        mls[(w * C::HB + r) * 2 + 0] = st.m_ref;
-        mls[(w * C::HB + r) * 2 + 1] = l_tot;
-    }
+    for (int nb = 0; nb < C::NB; nb++) so[(slot * C::NB + nb) * 64 + lane] = st.acc[nb];
+    if (qd == 0) sml[slot * C::HB + r] = make_float2(st.m_ref, l_tot);
 }
 
-// Merge waves [w0, w0+nw) of the scratch for head hh, column x:
-// returns the unnormalised O, and (M, l) of the merged state.
-template <int D>
-__device__ __forceinline__ float merge_waves(const float *mrg, const float *mls, int w0, int nw,
-                                             int hh, int x, float &M, float &l) {
+// Then wave `part` of the block's `nparts` merges column blocks nb = part,
+// part + nparts, ... of the NSRC published states: lane (r, qd) holds rows
+// 4qd .. 4qd+3 of the block in column 16nb + r of every source, rescaled to
+// the largest reference max (a source that saw no position, max -inf, weighs
+// 0). Row rho0 + 4qd + v (< R; rows past R pad the block and are dropped) of
+// the partition goes to part_o[((row0 + rho) * nsplit + s) * D + col] times
+// vsc, its (max, sum) to part_ml[(row0 + rho) * nsplit + s] (part 0), where
+// row0 is the unit's first partial row: the layout combine_kernel reads.
+template <int D, int NSRC>
+__device__ __forceinline__ void merge_lanes(const f32x4_t *so, const float2 *sml, int part, int nparts,
+                                            int lane, float vsc, int rho0, int R, size_t row0, int nsplit,
+                                            int s, float *__restrict__ part_o,
+                                            float2 *__restrict__ part_ml) {
     using C = MfmaCfg<D>;
-    M = -INFINITY;
-    for (int ww = w0; ww < w0 + nw; ww++) M = fmaxf(M, mls[(ww * C::HB + hh) * 2]);
-    float o = 0.f;
-    l = 0.f;
-    for (int ww = w0; ww < w0 + nw; ww++) {
-        const float mw = mls[(ww * C::HB + hh) * 2];
-        const float sc = mw == -INFINITY ? 0.f : fast_exp2(mw - M);  // idle waves weigh 0
-        o = fmaf(sc, mrg[(ww * C::HB + hh) * D + x], o);
-        l = fmaf(sc, mls[(ww * C::HB + hh) * 2 + 1], l);
+    const int r = lane & 15, qd = lane >> 4;
+    float Ms[NSRC][4], Ls[NSRC][4], Mx[4];
+#pragma unroll
+    for (int v = 0; v < 4; v++) Mx[v] = -INFINITY;
+#pragma unroll
+    for (int src = 0; src < NSRC; src++) {
+        const f32x4_t a = *(const f32x4_t *)&sml[src * C::HB + 4 * qd];
+        const f32x4_t c = *(const f32x4_t *)&sml[src * C::HB + 4 * qd + 2];
+        Ms[src][0] = a[0], Ls[src][0] = a[1], Ms[src][1] = a[2], Ls[src][1] = a[3];
+        Ms[src][2] = c[0], Ls[src][2] = c[1], Ms[src][3] = c[2], Ls[src][3] = c[3];
+#pragma unroll
+        for (int v = 0; v < 4; v++) Mx[v] = fmaxf(Mx[v], Ms[src][v]);
     }
-    return o;
+    float wt[NSRC][4], Lt[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int src = 0; src < NSRC; src++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            wt[src][v] = Ms[src][v] == -INFINITY ? 0.f : fast_exp2(Ms[src][v] - Mx[v]);
+            Lt[v] = fmaf(wt[src][v], Ls[src][v], Lt[v]);
+        }
+    for (int nb = part; nb < C::NB; nb += nparts) {
+        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int src = 0; src < NSRC; src++) {
+            const f32x4_t a = so[(src * C::NB + nb) * 64 + lane];
+#pragma unroll
+            for (int v = 0; v < 4; v++) o[v] = fmaf(wt[src][v], a[v], o[v]);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const int rho = rho0 + 4 * qd + v;
+            if (rho < R) part_o[((row0 + rho) * nsplit + s) * D + 16 * nb + r] = o[v] * vsc;
+        }
+    }
+    if (part == 0 && r == 0) {
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const int rho = rho0 + 4 * qd + v;
+            if (rho < R) part_ml[(row0 + rho) * nsplit + s] = make_float2(Mx[v], Lt[v]);
+        }
+    }
 }
 
 // Fixed partitions: one work-group per (partition of split_chunk positions,
@@ -1397,24 +1434,19 @@ split_mfma_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
                                              t_lo, t_row, t_hs, t_rs, qop, st, vbuf[w], lane,
                                              qk_scale_log2, err);
 
-    // merge the waves' states block by block through the staging buffers
-    float *mrg = (float *)&vbuf[0][0];
-    float *mls = mrg + C::NW * C::HB * D;
+    // merge the waves' states block by block through the staging buffers;
+    // wave w writes column blocks w, w + NW, ...
+    f32x4_t *so = (f32x4_t *)&vbuf[0][0];
+    float2 *sml = (float2 *)(so + C::NW * C::NB * 64);
+    static_assert(C::NW * C::NB * 64 * 16 + C::NW * C::HB * 8 <= C::NW * C::VBUF, "merge scratch must fit");
+    const size_t row0 = ((size_t)i * g + j) * R;  // the unit's first partial row
 #pragma unroll
     for (int b = 0; b < NHB; b++) {
         const int hb = hg * NHB + b;
         __syncthreads();  // every wave is done with the buffers
-        publish_state<D>(st[b], mrg, mls, w, lane);
+        publish_lanes<D>(st[b], so, sml, w, lane);
         __syncthreads();
-        for (int idx = threadIdx.x; idx < C::HB * D; idx += 64 * C::NW) {
-            const int hh = idx / D, x = idx % D;
-            if (hb * C::HB + hh >= R) continue;
-            float M, l;
-            const float o = merge_waves<D>(mrg, mls, 0, C::NW, hh, x, M, l);
-            const size_t hrow = ((size_t)i * g + j) * R + hb * C::HB + hh;
-            part_o[(hrow * nsplit + s) * D + x] = o * vsc;
-            if (x == 0) part_ml[hrow * nsplit + s] = make_float2(M, l);
-        }
+        merge_lanes<D, C::NW>(so, sml, w, C::NW, lane, vsc, hb * C::HB, R, row0, nsplit, s, part_o, part_ml);
     }
 }
 
@@ -1546,22 +1578,17 @@ split_pair_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
     }
 
     // merge the four waves of each block through LDS (slots 0..3: block 2hg,
-    // slots 4..7: block 2hg+1)
-    float *mrg = (float *)&lds[0][0][0];
-    float *mls = mrg + 8 * C::HB * D;
+    // slots 4..7: block 2hg+1); wave w writes column blocks w % 4, w % 4 + 4, ...
+    // of its block
+    f32x4_t *so = (f32x4_t *)&lds[0][0][0];
+    float2 *sml = (float2 *)(so + 8 * C::NB * 64);
+    static_assert(8 * C::NB * 64 * 16 + 8 * C::HB * 8 <= 4 * 2 * BUF, "merge scratch must fit");
     __syncthreads();  // every wave is done with the buffers
-    publish_state<D>(st[0], mrg, mls, w, lane);
+    publish_lanes<D>(st[0], so, sml, w, lane);
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 2 * C::HB * D; idx += 512) {
-        const int bb = idx / (C::HB * D), hh = idx / D % C::HB, x = idx % D;
-        const int hbo = hg * 2 + bb;
-        if (hbo * C::HB + hh >= R) continue;
-        float M, l;
-        const float o = merge_waves<D>(mrg, mls, 4 * bb, 4, hh, x, M, l);
-        const size_t hrow = ((size_t)i * g + j) * R + hbo * C::HB + hh;
-        part_o[(hrow * nsplit + s) * D + x] = o * vsc;
-        if (x == 0) part_ml[hrow * nsplit + s] = make_float2(M, l);
-    }
+    if (!rows) return;  // a padding block past the unit's rows
+    merge_lanes<D, 4>(so + (w / 4) * 4 * C::NB * 64, sml + (w / 4) * 4 * C::HB, w % 4, 4, lane, vsc,
+                      hb * C::HB, R, ((size_t)i * g + j) * R, nsplit, s, part_o, part_ml);
 }
 
 // ---------------------------------------------------------------------------
