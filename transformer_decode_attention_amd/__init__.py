@@ -239,6 +239,26 @@ def _dev(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _err(err_flags: torch.Tensor | None, like: torch.Tensor) -> ctypes.c_void_p | None:
+    """Pointer to the device error word, checked before any launch: None, or a
+    contiguous int32 device tensor of at least one element on the same device
+    as the call's tensors (the kernels OR flag bits into its first element, so
+    a host pointer or a narrower word there would fault the device)."""
+    if err_flags is None:
+        return None
+    if not isinstance(err_flags, torch.Tensor):
+        raise ValueError("err_flags must be a torch.Tensor or None")
+    if not err_flags.is_cuda:
+        raise ValueError("err_flags must be a device tensor")
+    if err_flags.device != like.device:
+        raise ValueError(f"err_flags is on {err_flags.device}, the call's tensors on {like.device}")
+    if err_flags.dtype != torch.int32:
+        raise ValueError("err_flags must be int32")
+    if err_flags.numel() < 1 or not err_flags.is_contiguous():
+        raise ValueError("err_flags must be a contiguous int32 tensor of at least one element")
+    return ctypes.c_void_p(err_flags.data_ptr())
+
+
 def _stream(device: torch.device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
@@ -261,7 +281,7 @@ def append_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
         raise ValueError("seq_lens must be int32 [b]")
     st = lib().mqa_append_kv(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
                             _ptr(seq_lens), b, g, S, d, _dtype_code(k_cache.dtype),
-                            _ptr(err_flags), _stream(k_cache.device))
+                            _err(err_flags, k_cache), _stream(k_cache.device))
     if st != OK:
         raise MQAError(st, "mqa_append_kv")
 
@@ -301,7 +321,7 @@ def decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     _dev(workspace, "workspace")
     args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), b, h, g, S, d, code,
             ctypes.c_float(scale), _ptr(out), _ptr(workspace),
-            workspace.numel() * workspace.element_size(), split_chunk, _ptr(err_flags))
+            workspace.numel() * workspace.element_size(), split_chunk, _err(err_flags, q))
     if kernel == KERNEL_AUTO:
         st = lib().mqa_decode_attn(*args, _stream(q.device))
         where = "mqa_decode_attn"
@@ -342,7 +362,7 @@ def append_kv_paged(k_pages: torch.Tensor, v_pages: torch.Tensor, k_new: torch.T
         raise TypeError("pages and new rows must share one dtype")
     st = lib().mqa_append_kv_paged(_ptr(k_pages), _ptr(v_pages), _ptr(k_new), _ptr(v_new),
                                    _ptr(block_table), _ptr(seq_lens), b, g, P, max_pages,
-                                   num_pages, d, _dtype_code(k_pages.dtype), _ptr(err_flags),
+                                   num_pages, d, _dtype_code(k_pages.dtype), _err(err_flags, k_pages),
                                    _stream(k_pages.device))
     if st != OK:
         raise MQAError(st, "mqa_append_kv_paged")
@@ -385,7 +405,7 @@ def decode_attn_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Ten
                                      _ptr(seq_lens), b, h, g, P, max_pages, num_pages, d, code,
                                      ctypes.c_float(scale), _ptr(out), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), split_chunk,
-                                     _ptr(err_flags), _stream(q.device))
+                                     _err(err_flags, q), _stream(q.device))
     if st != OK:
         raise MQAError(st, "mqa_decode_attn_paged")
     return out
@@ -424,7 +444,7 @@ def append_kv_multi(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.T
         raise TypeError("caches and new rows must share one dtype")
     st = lib().mqa_append_kv_multi(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
                                    _ptr(seq_lens), b, k_new.shape[1], g, S, d,
-                                   _dtype_code(k_cache.dtype), _ptr(err_flags),
+                                   _dtype_code(k_cache.dtype), _err(err_flags, k_cache),
                                    _stream(k_cache.device))
     if st != OK:
         raise MQAError(st, "mqa_append_kv_multi")
@@ -468,7 +488,7 @@ def decode_attn_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     st = lib().mqa_decode_attn_multi(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), b, T,
                                      h, g, S, d, code, ctypes.c_float(scale), _ptr(out),
                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                     split_chunk, _ptr(err_flags), _stream(q.device))
+                                     split_chunk, _err(err_flags, q), _stream(q.device))
     if st != OK:
         raise MQAError(st, "mqa_decode_attn_multi")
     return out
@@ -489,7 +509,7 @@ def append_kv_paged_multi(k_pages: torch.Tensor, v_pages: torch.Tensor, k_new: t
     st = lib().mqa_append_kv_paged_multi(_ptr(k_pages), _ptr(v_pages), _ptr(k_new), _ptr(v_new),
                                          _ptr(block_table), _ptr(seq_lens), b, k_new.shape[1], g,
                                          P, max_pages, num_pages, d, _dtype_code(k_pages.dtype),
-                                         _ptr(err_flags), _stream(k_pages.device))
+                                         _err(err_flags, k_pages), _stream(k_pages.device))
     if st != OK:
         raise MQAError(st, "mqa_append_kv_paged_multi")
 
@@ -517,7 +537,7 @@ def decode_attn_paged_multi(q: torch.Tensor, k_pages: torch.Tensor, v_pages: tor
                                            _ptr(seq_lens), b, T, h, g, P, max_pages, num_pages, d,
                                            code, ctypes.c_float(scale), _ptr(out), _ptr(workspace),
                                            workspace.numel() * workspace.element_size(),
-                                           split_chunk, _ptr(err_flags), _stream(q.device))
+                                           split_chunk, _err(err_flags, q), _stream(q.device))
     if st != OK:
         raise MQAError(st, "mqa_decode_attn_paged_multi")
     return out
@@ -558,7 +578,7 @@ def _append_codes(fn, int8, k_cache, v_cache, k_new, v_new, k_scale, v_scale, se
     _dev(seq_lens, "seq_lens")
     st = getattr(lib(), fn)(_ptr(k_cache), _ptr(v_cache), _ptr(kn), _ptr(vn), _ptr(k_scale),
                             _ptr(v_scale), _ptr(seq_lens), b, kn.shape[1], g, S, d,
-                            _ptr(err_flags), _stream(k_cache.device))
+                            _err(err_flags, k_cache), _stream(k_cache.device))
     if st != OK:
         raise MQAError(st, fn)
 
@@ -573,7 +593,7 @@ def _append_codes_paged(fn, int8, k_pages, v_pages, k_new, v_new, k_scale, v_sca
     b, max_pages = block_table.shape
     st = getattr(lib(), fn)(_ptr(k_pages), _ptr(v_pages), _ptr(kn), _ptr(vn), _ptr(k_scale),
                             _ptr(v_scale), _ptr(block_table), _ptr(seq_lens), b, kn.shape[1], g,
-                            P, max_pages, num_pages, d, _ptr(err_flags), _stream(k_pages.device))
+                            P, max_pages, num_pages, d, _err(err_flags, k_pages), _stream(k_pages.device))
     if st != OK:
         raise MQAError(st, fn)
 
@@ -622,7 +642,7 @@ def decode_attn_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale=None,
                                    _ptr(v_scale), _ptr(seq_lens), b, T, h, g, S, d,
                                    ctypes.c_float(scale), _ptr(o4), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), split_chunk,
-                                   _ptr(err_flags), _stream(q.device))
+                                   _err(err_flags, q), _stream(q.device))
     if st != OK:
         raise MQAError(st, "mqa_decode_attn_fp8")
     return o4 if q.dim() == 4 else o4[:, 0]
@@ -649,7 +669,7 @@ def decode_attn_paged_fp8(q, k_pages, v_pages, k_scale, v_scale, block_table, se
                                          g, P, max_pages, num_pages, d, ctypes.c_float(scale),
                                          _ptr(o4), _ptr(workspace),
                                          workspace.numel() * workspace.element_size(), split_chunk,
-                                         _ptr(err_flags), _stream(q.device))
+                                         _err(err_flags, q), _stream(q.device))
     if st != OK:
         raise MQAError(st, "mqa_decode_attn_paged_fp8")
     return o4 if q.dim() == 4 else o4[:, 0]
@@ -721,7 +741,7 @@ def decode_attn_ex(q, k, v, seq_lens, block_table=None, k_scale=None, v_scale=No
     _dev(workspace, "workspace")
     desc.workspace = _ptr(workspace)
     desc.workspace_bytes = workspace.numel() * workspace.element_size()
-    desc.err_flags = _ptr(err_flags)
+    desc.err_flags = _err(err_flags, q)
     st = lib().mqa_decode_attn_ex(ctypes.byref(desc), _stream(q.device))
     if st != OK:
         raise MQAError(st, "mqa_decode_attn_ex")
@@ -742,7 +762,7 @@ def rope_q(q, cos_sin, seq_lens, err_flags=None):
     b, T, h, d = q4.shape
     n_pos = _cos_sin(cos_sin, d)
     st = lib().mqa_rope_q(_ptr(q4), _ptr(cos_sin), n_pos, _ptr(seq_lens), b, T, h, d,
-                          _ptr(err_flags), _stream(q.device))
+                          _err(err_flags, q), _stream(q.device))
     if st != OK:
         raise MQAError(st, "mqa_rope_q")
     return q
@@ -760,7 +780,7 @@ def append_kv_rope(k_cache, v_cache, k_new, v_new, cos_sin, seq_lens, err_flags=
         raise ValueError("new rows must be [b, (T,) g, d]")
     n_pos = _cos_sin(cos_sin, d)
     st = lib().mqa_append_kv_rope(_ptr(k_cache), _ptr(v_cache), _ptr(kn), _ptr(vn), _ptr(cos_sin),
-                                  n_pos, _ptr(seq_lens), b, kn.shape[1], g, S, d, _ptr(err_flags),
+                                  n_pos, _ptr(seq_lens), b, kn.shape[1], g, S, d, _err(err_flags, k_cache),
                                   _stream(k_cache.device))
     if st != OK:
         raise MQAError(st, "mqa_append_kv_rope")
