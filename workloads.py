@@ -196,7 +196,7 @@ def make_multi_step(w: Workload, device="cpu", T: int = 4, layer: int = 0,
 def make_int8_step(w: Workload, device="cpu", T: int = 1, layer: int = 0,
                    page_size: int = 0) -> dict:
     """make_fp8_step over an int8 cache (codes N(0, 32) rounded, clamped to
-    +-127; scales U[1/48, 1/24] per K/V head)."""
+    -128 .. 127; scales U[1/48, 1/24] per K/V head)."""
     return make_fp8_step(w, device, T, layer, page_size, int8=True)
 
 
@@ -212,11 +212,15 @@ def make_fp8_step(w: Workload, device="cpu", T: int = 1, layer: int = 0,
 
     def codes():
         kw = dict(generator=gen, device=device)
-        if int8:  # N(0, 32) rounded and clamped to +-127: N(0,1)-like values at scale ~1/32
-            return torch.round(torch.randn(shape, **kw) * 32).clamp(-127, 127).to(torch.int8)
+        if int8:  # N(0, 32) rounded and clamped to the code range: N(0,1)-like values at scale ~1/32
+            return torch.round(torch.randn(shape, **kw) * 32).clamp(-128, 127).to(torch.int8)
         sign = torch.randint(0, 2, shape, dtype=torch.uint8, **kw)
-        expo = (7 + torch.round(torch.randn(shape, **kw) * 1.5)).clamp(1, 14).to(torch.uint8)
+        # exponent field 7 + N(0, 1.5) over the whole range 0 .. 15 (0: subnormals,
+        # 15: the 256 .. 448 binade), mantissa uniform; the NaN pattern (15, 7)
+        # becomes (15, 6), the largest finite code
+        expo = (7 + torch.round(torch.randn(shape, **kw) * 1.5)).clamp(0, 15).to(torch.uint8)
         mant = torch.randint(0, 8, shape, dtype=torch.uint8, **kw)
+        mant = torch.where((expo == 15) & (mant == 7), torch.full_like(mant, 6), mant)
         return (sign << 7) | (expo << 3) | mant
 
     k, v = codes(), codes()
