@@ -75,6 +75,10 @@ typedef enum {
 #define MQA_DEVERR_SEQLEN 1
 #define MQA_DEVERR_PAGE 2
 #define MQA_DEVERR_ROPE 4
+/* A wait between the waves of one work-group of the balanced schedule ran
+ * past its bound (a failure of the claim protocol, which a CPU model of it in
+ * the tests rules out): that work-group's rows are NaN, nothing hangs. */
+#define MQA_DEVERR_STALL 8
 
 /*
  * Append this step's K/V rows to the cache, bit-exactly.

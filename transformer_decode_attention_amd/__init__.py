@@ -51,7 +51,7 @@ __all__ = [
     "decode_multi_workspace_bytes", "decode_multi_schedule", "append_kv_fp8", "decode_attn_fp8",
     "append_kv_paged_fp8", "decode_attn_paged_fp8", "decode_attn_ex", "decode_ex_workspace_bytes",
     "rope_q", "append_kv_rope", "append_kv_int8", "append_kv_paged_int8",
-    "DEVERR_ROPE", "FP8_E4M3", "INT8",
+    "DEVERR_ROPE", "DEVERR_STALL", "FP8_E4M3", "INT8",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa_decode.so")
@@ -61,6 +61,7 @@ F32, BF16, FP8_E4M3, INT8 = 0, 1, 2, 3
 DEVERR_SEQLEN = 1
 DEVERR_PAGE = 2
 DEVERR_ROPE = 4
+DEVERR_STALL = 8
 
 KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
 

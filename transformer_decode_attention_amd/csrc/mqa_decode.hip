@@ -1690,11 +1690,27 @@ __device__ __forceinline__ void lds_drain() { asm volatile("s_waitcnt lgkmcnt(0)
 __device__ __forceinline__ void lds_flag_set(int *f, int v) {
     __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-// (the loops test a wave-uniform copy of the flag, so that they exit uniformly)
-__device__ __forceinline__ void lds_flag_wait(int *f, int v) {
+// Wait until *f == v, at most kSpinCap polls (~2^22 * 64 cycles, tens of ms:
+// the waits of the claim protocol last at most a few steps of another wave).
+// A wait that runs out marks the work-group broken (*broken = 1, stored before
+// anything this wave writes to LDS afterwards) and ORs MQA_DEVERR_STALL into
+// *err; the caller then goes on, and every row the work-group writes from
+// then on is NaN, so that a protocol failure can neither hang the GPU nor
+// pass unnoticed. (The loops test a wave-uniform copy of the flag, so that
+// they exit uniformly.)
+constexpr int kSpinCap = 1 << 22;
+__device__ __forceinline__ void lds_flag_wait(int *f, int v, int *broken, int32_t *err) {
+    int n = 0;
     while (__builtin_amdgcn_readfirstlane(
-               __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != v)
+               __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != v) {
+        if (++n == kSpinCap) {
+            lds_flag_set(broken, 1);
+            lds_drain();
+            if (err && (threadIdx.x & 63) == 0) atomicOr(err, MQA_DEVERR_STALL);
+            break;
+        }
         __builtin_amdgcn_s_sleep(1);
+    }
     asm volatile("" ::: "memory");
 }
 
@@ -1736,6 +1752,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
     __shared__ uint32_t rec_val[4][kRing];     // (steps done << 8) | waves (bit per wave of the block)
     __shared__ int cursor[4];                  // steps of the range claimed so far, per head group
     __shared__ int first_seq, last_seq;        // sequences holding the range's first and last steps
+    __shared__ int broken;                     // 1 once a wait between waves ran out (lds_flag_wait)
     __shared__ int pre[kStreamMaxSeq + 1];     // steps before sequence i
     __shared__ int vpre[kStreamMaxSeq + 1];    // valid sequences before sequence i
     __shared__ int lens[kStreamMaxSeq];        // seq_lens
@@ -1743,6 +1760,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
     __shared__ int pg[KV::kStage];             // paged: the page ids of the range's steps
 
     if (threadIdx.x < NW) slot_busy[threadIdx.x] = 0;
+    if (threadIdx.x == 0) broken = 0;
     if (threadIdx.x < 4) cursor[threadIdx.x] = 0;
     unit_prefix<64 * NW>(seq_lens, b, S, qr.T, qr.W, g, pre, vpre, lens, wtot);  // its barriers publish the above
     // everything that steers the loops below is wave-uniform: keep it scalar
@@ -1921,10 +1939,10 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
             }
         }
         if (mine == seg_e - seg_s) {  // the whole segment was this wave's: pass the record on
-            lds_flag_wait(&rec_tag[hb][e], sn);
+            lds_flag_wait(&rec_tag[hb][e], sn, &broken, err);
             if (lane == 0) lds_flag_set(&rec_tag[hb][e], sn + kRing);
         } else {  // other waves have steps of this segment
-            lds_flag_wait(&slot_busy[w], 0);
+            lds_flag_wait(&slot_busy[w], 0, &broken, err);
 #pragma unroll
             for (int k = 0; k < NHB; k++) {
 #pragma unroll
@@ -1933,7 +1951,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
             }
             if (lane == 0) slot_busy[w] = 1;
             lds_drain();
-            lds_flag_wait(&rec_tag[hb][e], sn);  // an earlier segment may still hold the record
+            lds_flag_wait(&rec_tag[hb][e], sn, &broken, err);  // an earlier segment may still hold the record
             const uint32_t add = ((uint32_t)mine << 8) | (1u << wb);
             uint32_t old = 0;
             if (lane == 0) old = atomicAdd(&rec_val[hb][e], add);
@@ -1972,6 +1990,9 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
                 lds_flag_set(&rec_tag[hb][e], sn + kRing);
             }
         }
+        // once a wait of this work-group ran out, its rows are NaN (lds_flag_wait)
+        const bool brk = __builtin_amdgcn_readfirstlane(
+                             __hip_atomic_load(&broken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != 0;
         if (seg_s != cu0 || seg_e != cu0 + cn) {
             // a piece of a cut unit: slot 0 for the range's first segment, 1
             // for its last; streamk_combine_kernel merges the pieces
@@ -1986,7 +2007,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
 #pragma unroll
                     for (int nb = 0; nb < C::NB; nb++)
                         part_o[prow * D + 16 * nb + r] = st[k].acc[nb][v] * cvs;
-                    if (r == 0) part_ml[prow] = make_float2(Mv[k][v], Lv[k][v]);
+                    if (r == 0) part_ml[prow] = make_float2(Mv[k][v], brk ? __builtin_nanf("") : Lv[k][v]);
                 }
             return;
         }
@@ -1997,7 +2018,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
             for (int v = 0; v < 4; v++) {
                 const int hs = (hb * NHB + k) * C::HB + 4 * qd + v;
                 if (hs >= R) continue;
-                const float inv = cvs / Lv[k][v];
+                const float inv = brk ? __builtin_nanf("") : cvs / Lv[k][v];
                 const size_t orow = qr.row(ci, cj, hs);
 #pragma unroll
                 for (int nb = 0; nb < C::NB; nb++)
