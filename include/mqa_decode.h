@@ -66,7 +66,14 @@ typedef enum { MQA_F32 = 0, MQA_BF16 = 1, MQA_FP8_E4M3 = 2, MQA_INT8 = 3 } mqa_d
 typedef enum {
     MQA_KERNEL_AUTO = 0, /* bf16: matrix cores; fp32: vector ALUs */
     MQA_KERNEL_VALU = 1, /* vector-ALU kernel (bf16 dot2 / fp32 FMA), any dtype */
-    MQA_KERNEL_MFMA = 2  /* matrix-core kernel, bf16 only */
+    MQA_KERNEL_MFMA = 2, /* matrix-core kernel, bf16 only */
+    /* matrix-core kernel, bf16 only, with results bitwise identical call
+     * after call: on the balanced schedule each wave takes a fixed share of
+     * its work-group's steps (dealt round robin in claim order) instead of
+     * claiming them as it goes, and a segment's states are merged in wave
+     * order; the fixed partitions already repeat bit for bit. Slower where
+     * the waves' memory service is uneven. */
+    MQA_KERNEL_MFMA_DETERMINISTIC = 3
 } mqa_kernel;
 
 /* Bits ORed into *err_flags by the kernels: some seq_lens[i] outside [1, S];
@@ -147,8 +154,12 @@ mqa_status mqa_decode_attn(const void *q, const void *k_cache,
 /*
  * mqa_decode_attn with an explicit choice of partition kernel; same arguments,
  * layouts, workspace and results (to floating-point rounding). MQA_KERNEL_MFMA
- * with dt = MQA_F32 returns MQA_ERR_UNSUPPORTED. mqa_decode_attn is this call
- * with MQA_KERNEL_AUTO.
+ * and MQA_KERNEL_MFMA_DETERMINISTIC with dt = MQA_F32 return
+ * MQA_ERR_UNSUPPORTED. mqa_decode_attn is this call with MQA_KERNEL_AUTO,
+ * whose balanced schedule lets waves claim steps as they go: which wave sums
+ * which steps then varies with timing, and so do the last bits of the sums
+ * (within the bound stated with the tests; the fixed partitions repeat bit
+ * for bit).
  */
 mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache,
                                   const void *v_cache, const int32_t *seq_lens,

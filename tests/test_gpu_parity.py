@@ -171,14 +171,8 @@ def test_scale_argument_is_used():
 # invariants on the device
 # ---------------------------------------------------------------------------
 
-def test_rows_past_length_are_never_read():
-    """NaN in every cache row >= L: output finite and equal to a zero-tail run (to the
-    fp32 rounding of the merge order, which the balanced schedule lets vary between calls;
-    a tail row read as 0 instead of skipped would move the result by far more)."""
-    w = W.Workload("tail", b=6, h=16, g=2, d=128, S=1024, dtype=torch.bfloat16, seed=91)
-    t = W.make_step(w, DEV)
-    t["seq_lens"] = torch.tensor([1, 64, 65, 500, 1000, 1024], dtype=torch.int32, device=DEV)
-    run_step(t)  # append first so row L-1 holds k_new
+def _nan_tail_pair(t: dict):
+    """The step's caches twice: rows >= L zero, and rows >= L NaN."""
     lens = t["seq_lens"].cpu().tolist()
     kz, vz = t["k_cache"].clone(), t["v_cache"].clone()
     kn, vn = t["k_cache"].clone(), t["v_cache"].clone()
@@ -187,30 +181,87 @@ def test_rows_past_length_are_never_read():
         vz[i, :, L:] = 0
         kn[i, :, L:] = float("nan")
         vn[i, :, L:] = float("nan")
+    return (kz, vz), (kn, vn)
+
+
+def test_rows_past_length_are_never_read():
+    """NaN in every cache row >= L: the output is finite and bit for bit the
+    output with zeros there (the rows are never read; one read as 0 instead of
+    skipped would not give NaN, but would move the result). Fixed partitions
+    (this shape), and the balanced schedule in its bitwise-reproducible mode."""
+    w = W.Workload("tail", b=6, h=16, g=2, d=128, S=1024, dtype=torch.bfloat16, seed=91)
+    assert mqa.decode_schedule(w.b, w.h, w.g, w.S, w.d, w.dtype) == "mfma-partitions"
+    t = W.make_step(w, DEV)
+    t["seq_lens"] = torch.tensor([1, 64, 65, 500, 1000, 1024], dtype=torch.int32, device=DEV)
+    run_step(t)  # append first so row L-1 holds k_new
+    (kz, vz), (kn, vn) = _nan_tail_pair(t)
     oz = mqa.decode_attn(t["q"], kz, vz, t["seq_lens"])
     on = mqa.decode_attn(t["q"], kn, vn, t["seq_lens"])
     torch.cuda.synchronize()
     assert torch.isfinite(on).all()
-    assert (oz - on).abs().max().item() <= 1e-5  # fp32 rounding of a different merge order
+    assert torch.equal(oz, on)
+    # the balanced schedule: 256 units of ragged lengths
+    w = W.Workload("tail-bal", b=128, h=16, g=2, d=128, S=1024, dtype=torch.bfloat16, seed=92,
+                   L_lo=1, L_hi=1024)
+    assert mqa.decode_schedule(w.b, w.h, w.g, w.S, w.d, w.dtype) == "mfma-balanced"
+    t = W.make_step(w, DEV)
+    run_step(t)
+    (kz, vz), (kn, vn) = _nan_tail_pair(t)
+    det = mqa.KERNEL_MFMA_DETERMINISTIC
+    oz = mqa.decode_attn(t["q"], kz, vz, t["seq_lens"], kernel=det)
+    on = mqa.decode_attn(t["q"], kn, vn, t["seq_lens"], kernel=det)
+    torch.cuda.synchronize()
+    assert torch.isfinite(on).all()
+    assert torch.equal(oz, on)
+
+
+# Bound on the difference between two calls of the default balanced schedule,
+# whose waves claim steps as they go (so which wave sums which steps, and from
+# which reference max, varies with timing). For an output element
+# o = sum_t a_t v_t / sum_t a_t, each call's result differs from the exact one
+# by at most (n u + 2^-18) sum_t alpha_t |v_t| to first order: u = 2^-24 for
+# each of the n <= L/32 fp32 additions of step results and merges into a
+# running sum, and 2^-18 relative for a weight p split into bf16 hi + lo (lo
+# rounds the exact remainder p - hi, |p - hi| <= 2^-9 p). With L <= 4096,
+# n u <= 2^-17, so two calls differ by at most 2 (2^-17 + 2^-18) < 2^-15 of
+# sum_t alpha_t |v_t|.
+RUN_TWICE_BOUND = 2.0 ** -15
 
 
 def test_deterministic():
-    """Fixed partitions (explicit split_chunk) give bitwise-identical results call
-    after call; the balanced schedule repeats to within the rounding of its merge
-    order (which wave takes which step depends on timing)."""
+    """Fixed partitions (explicit split_chunk) and the balanced schedule in its
+    bitwise-reproducible mode give identical bits call after call; the default
+    balanced schedule repeats within RUN_TWICE_BOUND * sum_t alpha_t |v_t| of
+    each element (alpha from the oracle)."""
     w = W.shrink(W.WORKLOADS["gqa-70b"], b=16)
     t = W.make_step(w, DEV)
     a = mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], split_chunk=512)
     b = mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], split_chunk=512)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
-    w = W.WORKLOADS["gqa-70b"]
+    w = W.shrink(W.WORKLOADS["gqa-70b"], b=32)  # 256 units
     t = W.make_step(w, DEV)
     assert mqa.decode_schedule(w.b, w.h, w.g, w.S, w.d, w.dtype) == "mfma-balanced"
+    det = mqa.KERNEL_MFMA_DETERMINISTIC
+    outs = [mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], kernel=det)
+            for _ in range(3)]
     a = mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"])
     b = mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"])
     torch.cuda.synchronize()
-    assert (a - b).abs().max().item() <= 1e-5  # fp32 rounding of a different merge order
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    scale = float(np.float32(1.0 / math.sqrt(w.d)))
+    ref, alpha, rc = oracle.decode_attn(W.to_oracle(t["q"]), W.to_oracle(t["k_cache"]),
+                                        W.to_oracle(t["v_cache"]), t["seq_lens"].cpu().numpy(),
+                                        scale, want_alpha=True, nthreads=NTHREADS)
+    assert rc == oracle.OK
+    v = torch.from_numpy(oracle.bf16_bits_to_f64(W.to_oracle(t["v_cache"]))).abs()  # [b, g, S, d]
+    al = torch.from_numpy(alpha).view(w.b, w.g, w.h // w.g, w.S)                   # [b, g, G, S]
+    spread = torch.matmul(al, v).reshape(w.b, w.h, w.d).numpy()                     # sum_t a_t |v_t|
+    diff = (a - b).abs().double().cpu().numpy()
+    assert (diff <= RUN_TWICE_BOUND * spread).all(), float((diff / spread).max())
+    # both modes are the same attention
+    compare(outs[0], ref, "deterministic mode")
+    compare(a, ref, "default mode")
 
 
 def test_constant_v_and_zero_k():

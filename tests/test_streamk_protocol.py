@@ -20,7 +20,10 @@ random interleavings (uniform, and with one wave starved), and checks that
     the segment's steps exactly once (from whichever waves computed them);
 and that a protocol with a planted mistake (a record never released, a slot
 never freed) ends with every wait bounded, the stall flag raised and the
-broken work-group's results marked, instead of spinning forever.
+broken work-group's results marked, instead of spinning forever. The same
+checks run the bitwise-reproducible variant (fixed claims, merges in wave
+order), which must also merge every segment identically in every
+interleaving.
 """
 from __future__ import annotations
 
@@ -57,9 +60,11 @@ class WorkGroup:
     """One work-group's range [x0, x1) over units laid end to end (unit u has
     steps [start[u], start[u] + n[u])), one head block of `wph` waves."""
 
-    def __init__(self, lens, x0, x1, wph, ring, cap, mutant=None):
+    def __init__(self, lens, x0, x1, wph, ring, cap, mutant=None, det=False):
         self.lens, self.x0, self.x1, self.wph, self.ring, self.cap = lens, x0, x1, wph, ring, cap
         self.mutant = mutant
+        self.det = det               # fixed round-robin claims, merges in wave order
+        self.nclaims = [0] * wph
         self.start = [0]
         for n in lens:
             self.start.append(self.start[-1] + n)
@@ -71,6 +76,7 @@ class WorkGroup:
         self.broken = False
         self.flags = 0
         self.results = {}  # segment start -> (steps, written while broken)
+        self.orders = {}   # segment start -> the merge as ((wave, its steps), ...) in order
         u_last = self.unit_of(x1 - 1)
         self.xl = max(x0, self.start[u_last])
         self.len_last = x1 - self.xl
@@ -87,9 +93,13 @@ class WorkGroup:
                 hi = mid
         return lo
 
-    def claim(self):
-        c = self.cursor
-        self.cursor += 1
+    def claim(self, w):
+        if self.det:
+            c = w + self.wph * self.nclaims[w]
+            self.nclaims[w] += 1
+        else:
+            c = self.cursor
+            self.cursor += 1
         if c >= self.x1 - self.x0:
             return self.x1
         return self.xl + c if c < self.len_last else self.x0 + (c - self.len_last)
@@ -115,7 +125,7 @@ class WorkGroup:
             if self.mutant != "keep_record":
                 self.rec_tag[e] = sn + self.ring
             yield "step", None
-            self.emit(seg_s, mine)
+            self.emit(seg_s, mine, ((w, frozenset(mine)),))
             return
         yield from self.wait(lambda: self.slot_busy[w] == 0)
         self.slot[w] = set(mine)
@@ -131,13 +141,16 @@ class WorkGroup:
         if (now >> 8) != seg_e - seg_s:
             return  # not the last: the state waits in the slot
         self.slot_busy[w] = 0
-        merged = set(mine)
-        bits = now & 0xFF & ~(1 << w)
+        # (the order of the merge: with det from an empty state, every parked
+        # state in wave order, this wave's own included)
+        merged, order = (set(), []) if self.det else (set(mine), [(w, frozenset(mine))])
+        bits = now & 0xFF & ~(0 if self.det else 1 << w)
         for ww in range(self.wph):
             if bits >> ww & 1:
                 got = self.slot[ww]
                 assert got is not None and not (merged & got), "a step merged twice"
                 merged |= got
+                order.append((ww, frozenset(got)))
                 yield "step", None
                 if self.mutant != "keep_slot":
                     self.slot_busy[ww] = 0
@@ -147,21 +160,22 @@ class WorkGroup:
         if self.mutant != "keep_record":
             self.rec_tag[e] = sn + self.ring
         yield "step", None
-        self.emit(seg_s, merged)
+        self.emit(seg_s, merged, tuple(order))
 
-    def emit(self, seg_s, steps):
+    def emit(self, seg_s, steps, order=None):
         assert seg_s not in self.results, f"segment at {seg_s} written twice"
         self.results[seg_s] = (frozenset(steps), self.broken)
+        self.orders[seg_s] = order
 
     def wave(self, w):
-        t = self.claim()
+        t = self.claim(w)
         yield "step", None
         if t >= self.x1:
             return
         u = self.unit_of(t)
         mine = {t}
         while True:
-            tn = self.claim()
+            tn = self.claim(w)
             yield "step", None
             more = tn < self.x1
             if not more or self.unit_of(tn) != u:
@@ -265,3 +279,28 @@ def test_planted_protocol_mistake_is_bounded_and_flagged(mutant):
             stalled_after = [s for s, (_, b) in wg.results.items() if b]
             assert len(wg.results) < len(wg.segments()) or stalled_after
     assert hit > 0, "the planted mistake never caused a stall"
+
+
+@pytest.mark.parametrize("ring,wph", [(RING, WAVES), (RING, 8), (2, WAVES), (1, 2)])
+def test_fixed_claims_complete_and_merge_in_one_order(ring, wph):
+    """The bitwise-reproducible mode (MQA_KERNEL_MFMA_DETERMINISTIC): the same
+    protocol with each wave's claims dealt round robin never deadlocks either,
+    and every segment is merged from the same wave states in the same order
+    whatever the interleaving (so the fp32 sums repeat bit for bit)."""
+    rng = random.Random(77 + ring * 10 + wph)
+    n = 0
+    while n < 150:
+        lens, x0, x1 = random_case(rng)
+        if x1 <= x0:
+            continue
+        n += 1
+        seen = None
+        for rep in range(4):
+            wg = WorkGroup(lens, x0, x1, wph, ring, cap=10 ** 6, det=True)
+            run(wg, rng, starve=rng.randrange(wph) if rep % 2 else None)
+            assert wg.flags == 0
+            assert {s: st for s, (st, _) in wg.results.items()} == wg.segments()
+            if seen is None:
+                seen = wg.orders
+            else:
+                assert wg.orders == seen, (lens, x0, x1)

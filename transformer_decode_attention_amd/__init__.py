@@ -63,7 +63,7 @@ DEVERR_PAGE = 2
 DEVERR_ROPE = 4
 DEVERR_STALL = 8
 
-KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
+KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA, KERNEL_MFMA_DETERMINISTIC = 0, 1, 2, 3
 
 EXPORTS = (
     "mqa_append_kv", "mqa_decode_workspace_bytes", "mqa_decode_resolve_chunk",
@@ -294,8 +294,9 @@ def decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                 kernel: int = KERNEL_AUTO) -> torch.Tensor:
     """Decode attention: q [b,h,d], caches [b,g,S,d], seq_lens int32 [b] -> out fp32 [b,h,d].
 
-    kernel: KERNEL_AUTO (mqa_decode_attn), or KERNEL_VALU / KERNEL_MFMA
-    (mqa_decode_attn_kernel with that choice).
+    kernel: KERNEL_AUTO (mqa_decode_attn), or KERNEL_VALU / KERNEL_MFMA /
+    KERNEL_MFMA_DETERMINISTIC (mqa_decode_attn_kernel with that choice; the
+    last gives bitwise identical results call after call).
     """
     for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
         _dev(t, n)

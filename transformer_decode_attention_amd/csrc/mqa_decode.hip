@@ -1740,7 +1740,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
                     const float *__restrict__ k_scale, const float *__restrict__ v_scale,
                     float *__restrict__ out, float *__restrict__ part_o,
                     float2 *__restrict__ part_ml, int4 *__restrict__ cut_desc,
-                    int32_t *__restrict__ err) {
+                    int32_t *__restrict__ err, int det) {
     using C = MfmaCfg<D>;
     constexpr bool F8 = KV::kF8;  // fp8 or int8 codes: per-K/V-head scales on scores and outputs
     static_assert(NW == 4 || NW == 8, "waves per work-group (the segment records hold 8 bits)");
@@ -1855,11 +1855,19 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
 #pragma unroll
     for (int k = 0; k < NHB; k++) tau[k] = qr.tok(min((hb * NHB + k) * C::HB + r, R - 1));
 
-    // next step of the range for this head block, in claim order (x1: none left)
+    // next step of the range for this head block, in claim order (x1: none
+    // left): from the shared counter, or with det the wave's own fixed
+    // sequence wb, wb + wph, ... (the same claim order, dealt round robin, so
+    // that every wave always computes the same steps)
+    int nclaims = 0;
     auto claim = [&]() __attribute__((always_inline)) {
         int c = 0;
-        if (lane == 0) c = atomicAdd(&cursor[hb], 1);
-        c = __builtin_amdgcn_readfirstlane(__shfl(c, 0));
+        if (det) {
+            c = wb + wph * nclaims++;
+        } else {
+            if (lane == 0) c = atomicAdd(&cursor[hb], 1);
+            c = __builtin_amdgcn_readfirstlane(__shfl(c, 0));
+        }
         return c >= x1 - x0 ? x1 : c < len_last ? xl + c : x0 + (c - len_last);
     };
     // unit holding flat step tt: sequence i_, its length L_ and steps n_, K/V
@@ -1957,9 +1965,26 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
             if (lane == 0) old = atomicAdd(&rec_val[hb][e], add);
             const uint32_t now_ = __builtin_amdgcn_readfirstlane(__shfl(old, 0)) + add;
             if ((int)(now_ >> 8) != seg_e - seg_s) return;  // not the last: the state waits in the slot
-            // the last share in: merge the others, release their slots and the record
+            // the last share in: merge the others, release their slots and the
+            // record. With det the merge must not depend on which wave came
+            // last: it starts from an empty state and takes every parked
+            // state, its own included, in wave order.
             if (lane == 0) slot_busy[w] = 0;
-            for (uint32_t m = now_ & 0xffu & ~(1u << wb); m; m &= m - 1) {
+            uint32_t parked = now_ & 0xffu & ~(1u << wb);
+            if (det) {
+                parked |= 1u << wb;
+#pragma unroll
+                for (int k = 0; k < NHB; k++) {
+#pragma unroll
+                    for (int v = 0; v < 4; v++) {
+                        Mv[k][v] = -INFINITY;
+                        Lv[k][v] = 0.f;
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < C::NB; nb++) st[k].acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+            for (uint32_t m = parked; m; m &= m - 1) {
                 const int ww = hb * wph + __builtin_ctz(m);
 #pragma unroll
                 for (int k = 0; k < NHB; k++) {
@@ -2443,7 +2468,7 @@ mqa_status run_mfma_rows(const KV &kv, const void *q, const int32_t *seq_lens, i
                          int h, int g, int S, float qs, const float *k_scale,
                          const float *v_scale, float *out, void *workspace, int chunk,
                          int nsplit, bool balanced, int32_t *err_flags, hipStream_t stream,
-                         int W) {
+                         int W, int det = 0) {
     const int Gh = h / g, R = T * Gh;
     const int nhb = (R + 15) / 16;
     const int ngroups = (nhb + NHB - 1) / NHB;
@@ -2467,12 +2492,12 @@ mqa_status run_mfma_rows(const KV &kv, const void *q, const int32_t *seq_lens, i
             hipLaunchKernelGGL((streamk_mfma_kernel<D, NWV, KV, MULTI, NHB, true>), dim3(nwg),
                                dim3(64 * NWV), 0, stream, (const uint16_t *)q, kv, seq_lens, b,
                                qr, g, S, R, ngroups, qs, k_scale, v_scale, out, po, pml, desc,
-                               err_flags);
+                               err_flags, det);
         else
             hipLaunchKernelGGL((streamk_mfma_kernel<D, NWV, KV, MULTI, NHB>), dim3(nwg),
                                dim3(64 * NWV), 0, stream, (const uint16_t *)q, kv, seq_lens, b,
                                qr, g, S, R, ngroups, qs, k_scale, v_scale, out, po, pml, desc,
-                               err_flags);
+                               err_flags, det);
         // pieces per cut unit: ~2 when there are more units than work-groups,
         // ~nwg/units when each unit spans many ranges
         constexpr int HPB = 256 / (D / 4);  // head slots per block with one piece lane
@@ -2515,7 +2540,8 @@ template <int D, class KV>
 mqa_status run_mfma(const KV &kv, const void *q, const int32_t *seq_lens, int b, int T, int h,
                     int g, int S, float qs, float *out, void *workspace, int chunk, int nsplit,
                     bool balanced, int32_t *err_flags, hipStream_t stream,
-                    const float *k_scale = nullptr, const float *v_scale = nullptr, int W = 0) {
+                    const float *k_scale = nullptr, const float *v_scale = nullptr, int W = 0,
+                    int det = 0) {
     const RowBlocks rb = row_blocks(T * (h / g));
     // one-byte codes, balanced schedule, two blocks: one block per wave in
     // eight waves (two head groups reading each step, the second from L2)
@@ -2525,17 +2551,18 @@ mqa_status run_mfma(const KV &kv, const void *q, const int32_t *seq_lens, int b,
         if (two)
             return run_mfma_rows<D, KV, true, 2>(kv, q, seq_lens, b, T, h, g, S, qs, k_scale,
                                                  v_scale, out, workspace, chunk, nsplit, balanced,
-                                                 err_flags, stream, W);
+                                                 err_flags, stream, W, det);
         return run_mfma_rows<D, KV, true, 1>(kv, q, seq_lens, b, T, h, g, S, qs, k_scale, v_scale,
                                              out, workspace, chunk, nsplit, balanced, err_flags,
-                                             stream, W);
+                                             stream, W, det);
     }
     if (two)
         return run_mfma_rows<D, KV, false, 2>(kv, q, seq_lens, b, 1, h, g, S, qs, k_scale, v_scale,
                                               out, workspace, chunk, nsplit, balanced, err_flags,
-                                              stream, 0);
+                                              stream, 0, det);
     return run_mfma_rows<D, KV, false, 1>(kv, q, seq_lens, b, 1, h, g, S, qs, k_scale, v_scale, out,
-                                          workspace, chunk, nsplit, balanced, err_flags, stream, 0);
+                                          workspace, chunk, nsplit, balanced, err_flags, stream, 0,
+                                          det);
 }
 
 // T-token calls: T in [1, S]; beyond one token only the bf16 matrix-core path
@@ -2570,8 +2597,10 @@ uint64_t mqa_kv_bytes(int layers, int g, int64_t S, int d, int dtype_bytes) {
 int mqa_decode_schedule(int b, int h, int g, int S, int d, mqa_dtype dt, int split_chunk,
                         mqa_kernel kernel) {
     if (check_sizes(b, h, g, S, d, dt, split_chunk) != MQA_OK) return -1;
-    if (kernel != MQA_KERNEL_AUTO && kernel != MQA_KERNEL_VALU && kernel != MQA_KERNEL_MFMA) return -1;
-    if (kernel == MQA_KERNEL_MFMA && dt != MQA_BF16) return -1;
+    if (kernel != MQA_KERNEL_AUTO && kernel != MQA_KERNEL_VALU && kernel != MQA_KERNEL_MFMA &&
+        kernel != MQA_KERNEL_MFMA_DETERMINISTIC)
+        return -1;
+    if ((kernel == MQA_KERNEL_MFMA || kernel == MQA_KERNEL_MFMA_DETERMINISTIC) && dt != MQA_BF16) return -1;
     if (use_streamk(b, h, g, S, dt, split_chunk, kernel)) return MQA_SCHEDULE_MFMA_BALANCED;
     return (dt == MQA_BF16 && kernel != MQA_KERNEL_VALU) ? MQA_SCHEDULE_MFMA_PARTITIONS
                                                          : MQA_SCHEDULE_VALU_PARTITIONS;
@@ -2624,9 +2653,11 @@ mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache, const void
     if (!q || !k_cache || !v_cache || !seq_lens || !out) return MQA_ERR_NULL;
     mqa_status st = check_sizes(b, h, g, S, d, dt, split_chunk);
     if (st != MQA_OK) return st;
-    if (kernel != MQA_KERNEL_AUTO && kernel != MQA_KERNEL_VALU && kernel != MQA_KERNEL_MFMA)
+    if (kernel != MQA_KERNEL_AUTO && kernel != MQA_KERNEL_VALU && kernel != MQA_KERNEL_MFMA &&
+        kernel != MQA_KERNEL_MFMA_DETERMINISTIC)
         return MQA_ERR_UNSUPPORTED;
-    if (kernel == MQA_KERNEL_MFMA && dt != MQA_BF16) return MQA_ERR_UNSUPPORTED;
+    if ((kernel == MQA_KERNEL_MFMA || kernel == MQA_KERNEL_MFMA_DETERMINISTIC) && dt != MQA_BF16)
+        return MQA_ERR_UNSUPPORTED;
     const bool use_mfma = dt == MQA_BF16 && kernel != MQA_KERNEL_VALU;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
         return MQA_ERR_ALIGN;
@@ -2646,11 +2677,14 @@ mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache, const void
     if (use_mfma) {
         const bool bal = use_streamk(b, h, g, S, dt, split_chunk, kernel);
         const uint8_t *kb = (const uint8_t *)k_cache, *vb = (const uint8_t *)v_cache;
+        const int det = kernel == MQA_KERNEL_MFMA_DETERMINISTIC;
         if (d == 128)
             return run_mfma<128>(ContigKV<128>{kb, vb, g, S}, q, seq_lens, b, 1, h, g, S, qs, out,
-                                 workspace, chunk, nsplit, bal, err_flags, stream);
+                                 workspace, chunk, nsplit, bal, err_flags, stream, nullptr, nullptr,
+                                 0, det);
         return run_mfma<64>(ContigKV<64>{kb, vb, g, S}, q, seq_lens, b, 1, h, g, S, qs, out,
-                            workspace, chunk, nsplit, bal, err_flags, stream);
+                            workspace, chunk, nsplit, bal, err_flags, stream, nullptr, nullptr, 0,
+                            det);
     } else if (dt == MQA_BF16) {
         if (d == 128) dispatch_rows<uint16_t, 128>(hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream);
         else dispatch_rows<uint16_t, 64>(hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream);
