@@ -54,13 +54,26 @@ typedef enum {
     MQA_ERR_UNSUPPORTED = 3, /* d not 64/128, unknown dtype, bad split_chunk */
     MQA_ERR_ALIGN = 4,       /* a tensor pointer not 16-byte aligned */
     MQA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
-    MQA_ERR_HIP = 6          /* the HIP runtime reported a launch error */
+    MQA_ERR_HIP = 6,         /* the HIP runtime reported a launch error */
+    /* (the two bounds below only pin each enum of this header to the range
+     * of int, so that any int a caller passes is a value of the type: an
+     * invalid one then gets the documented error status, where a value
+     * outside an enum's range would be undefined behaviour in C++) */
+    MQA_STATUS_INT_MIN_ = -2147483647 - 1,
+    MQA_STATUS_INT_MAX_ = 2147483647
 } mqa_status;
 
 /* Element types. MQA_FP8_E4M3 and MQA_INT8 are cache types only
  * (mqa_decode_attn_ex, the _fp8 and _int8 calls); q and new rows are then
  * bf16. */
-typedef enum { MQA_F32 = 0, MQA_BF16 = 1, MQA_FP8_E4M3 = 2, MQA_INT8 = 3 } mqa_dtype;
+typedef enum {
+    MQA_F32 = 0,
+    MQA_BF16 = 1,
+    MQA_FP8_E4M3 = 2,
+    MQA_INT8 = 3,
+    MQA_DTYPE_INT_MIN_ = -2147483647 - 1, /* range of int (see mqa_status) */
+    MQA_DTYPE_INT_MAX_ = 2147483647
+} mqa_dtype;
 
 /* Which partition kernel computes the attention (see mqa_decode_attn_kernel). */
 typedef enum {
@@ -73,7 +86,9 @@ typedef enum {
      * claiming them as it goes, and a segment's states are merged in wave
      * order; the fixed partitions already repeat bit for bit. Slower where
      * the waves' memory service is uneven. */
-    MQA_KERNEL_MFMA_DETERMINISTIC = 3
+    MQA_KERNEL_MFMA_DETERMINISTIC = 3,
+    MQA_KERNEL_INT_MIN_ = -2147483647 - 1, /* range of int (see mqa_status) */
+    MQA_KERNEL_INT_MAX_ = 2147483647
 } mqa_kernel;
 
 /* Bits ORed into *err_flags by the kernels: some seq_lens[i] outside [1, S];

@@ -38,18 +38,20 @@ BAD_SHAPE = 2
 BAD_PAGE = 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+BUILD_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB: load another build of oracle.c instead (the sanitizer test's)
+LIB_PATH = os.environ.get("ORACLE_LIB") or BUILD_PATH
 _SRC = os.path.join(_HERE, "oracle.c")
 
 
 def build() -> str:
     """Compile oracle.c with the host C compiler (gcc) into liboracle.so."""
-    tmp = LIB_PATH + ".tmp"
+    tmp = BUILD_PATH + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror", "-fPIC",
            "-shared", "-pthread", "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, BUILD_PATH)
+    return BUILD_PATH
 
 
 _lib = None
@@ -59,6 +61,8 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
+            if LIB_PATH != BUILD_PATH:
+                raise ImportError(f"ORACLE_LIB={LIB_PATH} does not exist")
             build()
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, dp = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_double)

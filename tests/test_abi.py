@@ -12,6 +12,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 import transformer_decode_attention_amd as mqa
 
@@ -379,3 +380,15 @@ def test_rope_calls_reject_bad_arguments_before_launch():
                                 None) == mqa.ERR_SHAPE
     assert L.mqa_append_kv_rope(FAKE, FAKE, FAKE, FAKE, None, 16, FAKE, 2, 1, 2, 64, 128, None,
                                 None) == mqa.ERR_NULL
+
+
+def test_err_flags_is_checked_before_any_launch():
+    """err_flags must be None or a contiguous int32 device tensor on the
+    call's device: a host tensor (whose pointer the kernels would OR bits
+    into) or another dtype is refused with ValueError by the binding."""
+    like = torch.zeros(4)
+    assert mqa._err(None, like) is None
+    for bad in (torch.zeros(1, dtype=torch.int32), torch.zeros(1, dtype=torch.int64),
+                torch.zeros(0, dtype=torch.int32), [0]):
+        with pytest.raises(ValueError):
+            mqa._err(bad, like)

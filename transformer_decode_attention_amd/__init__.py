@@ -54,7 +54,10 @@ __all__ = [
     "DEVERR_ROPE", "DEVERR_STALL", "FP8_E4M3", "INT8",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa_decode.so")
+# MQA_DECODE_LIB: load another build of the library instead of the in-tree one
+# (for instance the host-only sanitizer build of the CPU tests)
+LIB_PATH = os.environ.get("MQA_DECODE_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmqa_decode.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)
 F32, BF16, FP8_E4M3, INT8 = 0, 1, 2, 3

@@ -24,6 +24,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <type_traits>
+#include <utility>
+
 #include "mqa_decode.h"
 
 namespace {
@@ -2279,34 +2283,47 @@ combine_kernel(const float *__restrict__ part_o, const float2 *__restrict__ part
 // host side
 // ---------------------------------------------------------------------------
 
+// Launch a kernel and return the launch's own status (the runtime's last-error
+// slot may hold an unrelated error left by the caller's earlier calls). The
+// arguments are converted to the kernel's parameter types and passed by address,
+// as hipLaunchKernel copies them at the call.
+template <typename... P, typename... A>
+hipError_t klaunch(void (*k)(P...), dim3 grid, dim3 block, hipStream_t stream, A &&...a) {
+    std::tuple<std::decay_t<P>...> args(std::forward<A>(a)...);
+    return std::apply(
+        [&](auto &...x) {
+            void *ptrs[] = {(void *)&x...};
+            return hipLaunchKernel((const void *)k, grid, block, ptrs, 0, stream);
+        },
+        args);
+}
+#define MQA_LAUNCH(...)                                          \
+    do {                                                          \
+        if (klaunch(__VA_ARGS__) != hipSuccess) return MQA_ERR_HIP; \
+    } while (0)
+
 // The log-sum-exp combine over nsplit partitions per row: eight loads in
 // flight per piece lane when a lane has more than four partitions to merge
 // (one round trip instead of two), four otherwise.
 template <int D>
-void launch_combine(dim3 grid, hipStream_t stream, const float *part_o, const float2 *part_ml,
+mqa_status launch_combine(dim3 grid, hipStream_t stream, const float *part_o, const float2 *part_ml,
                     const int32_t *seq_lens, const QRows<true> &qc, int R, int S, int chunk,
                     int nsplit, float *out, int32_t *err_flags) {
     constexpr int PL = 256 / (D / 4);
     if ((nsplit + PL - 1) / PL > 4)
-        hipLaunchKernelGGL((combine_kernel<D, 8>), grid, dim3(256), 0, stream, part_o, part_ml,
-                           seq_lens, qc, R, S, chunk, nsplit, out, err_flags);
+        MQA_LAUNCH(combine_kernel<D, 8>, grid, dim3(256), stream, part_o, part_ml, seq_lens, qc, R, S, chunk, nsplit, out, err_flags);
     else
-        hipLaunchKernelGGL((combine_kernel<D, 4>), grid, dim3(256), 0, stream, part_o, part_ml,
-                           seq_lens, qc, R, S, chunk, nsplit, out, err_flags);
+        MQA_LAUNCH(combine_kernel<D, 4>, grid, dim3(256), stream, part_o, part_ml, seq_lens, qc, R, S, chunk, nsplit, out, err_flags);
+    return MQA_OK;
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
-// Compute units of the current device (256 on MI355X; also the answer when
-// no device is visible, for the host-only queries).
-int device_cus() {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            cus = v;
-    }
-    return cus;
-}
+// Compute units the schedules are planned for: the 256 of a gfx950 part
+// (MI355X, MI350X). A constant, so that the host-side queries (partition
+// length, workspace size, schedule) are pure functions of their arguments and
+// never touch the HIP runtime or depend on which device is current; on a
+// device with fewer compute units the extra work-groups simply queue.
+constexpr int kPlanCUs = 256;
 
 int heads_per_wg(int G) {
     int hpw = 1;
@@ -2365,7 +2382,7 @@ int resolve_chunk(int b, int h, int g, int S, mqa_dtype dt, int split_chunk, int
     const int G = T * (h / g);
     const long long groups = (long long)b * g *
         (dt == MQA_BF16 ? row_blocks(G).groups : (G + wg_heads(dt, G) - 1) / wg_heads(dt, G));
-    const long long want = (device_cus() + groups - 1) / groups;  // partitions per group
+    const long long want = (kPlanCUs + groups - 1) / groups;  // partitions per group
     long long c = ((long long)S + want - 1) / want;
     c = (c + kTile - 1) / kTile * kTile;
     const long long cap = ((long long)S + kTile - 1) / kTile * kTile;
@@ -2427,7 +2444,7 @@ size_t workspace_need(int b, int h, int g, int S, int d, mqa_dtype dt, int split
 // Work-groups of the balanced schedule: one per compute unit (the kernel
 // uses fewer when the call has fewer than kStreamMinSteps steps for each).
 int streamk_wgs(int b, int g, int S) {
-    const int cus = device_cus();
+    const int cus = kPlanCUs;
     const long long tmax = (long long)b * g * ((S + 31) / 32);
     long long n = (tmax + kStreamMinSteps - 1) / kStreamMinSteps;
     if (n > cus) n = cus;
@@ -2437,26 +2454,25 @@ int streamk_wgs(int b, int g, int S) {
 }
 
 template <typename T, int D, int HPW>
-void launch_rows(const void *q, const void *k, const void *v, const int32_t *seq_lens, int b,
+mqa_status launch_rows(const void *q, const void *k, const void *v, const int32_t *seq_lens, int b,
                  int h, int g, int S, float qk_scale_log2, int chunk, int nsplit, float *part_o,
                  float2 *part_ml, hipStream_t stream) {
     const int G = h / g;
     const int nhc = (G + HPW - 1) / HPW;
     dim3 grid(nsplit, g * nhc, b);
-    hipLaunchKernelGGL((split_rows_kernel<T, D, HPW>), grid, dim3(64 * HPW), 0, stream,
-                       (const T *)q, (const T *)k, (const T *)v, seq_lens, h, g, S, G, nhc, chunk,
-                       nsplit, qk_scale_log2, part_o, part_ml);
+    MQA_LAUNCH(split_rows_kernel<T, D, HPW>, grid, dim3(64 * HPW), stream, (const T *)q, (const T *)k, (const T *)v, seq_lens, h, g, S, G, nhc, chunk, nsplit, qk_scale_log2, part_o, part_ml);
+    return MQA_OK;
 }
 
 template <typename T, int D>
-void dispatch_rows(int hpw, const void *q, const void *k, const void *v, const int32_t *seq_lens,
+mqa_status dispatch_rows(int hpw, const void *q, const void *k, const void *v, const int32_t *seq_lens,
                    int b, int h, int g, int S, float qs, int chunk, int nsplit, float *po,
                    float2 *pml, hipStream_t st) {
     switch (hpw) {
-        case 1: launch_rows<T, D, 1>(q, k, v, seq_lens, b, h, g, S, qs, chunk, nsplit, po, pml, st); break;
-        case 2: launch_rows<T, D, 2>(q, k, v, seq_lens, b, h, g, S, qs, chunk, nsplit, po, pml, st); break;
-        case 4: launch_rows<T, D, 4>(q, k, v, seq_lens, b, h, g, S, qs, chunk, nsplit, po, pml, st); break;
-        default: launch_rows<T, D, 8>(q, k, v, seq_lens, b, h, g, S, qs, chunk, nsplit, po, pml, st); break;
+        case 1: return launch_rows<T, D, 1>(q, k, v, seq_lens, b, h, g, S, qs, chunk, nsplit, po, pml, st);
+        case 2: return launch_rows<T, D, 2>(q, k, v, seq_lens, b, h, g, S, qs, chunk, nsplit, po, pml, st);
+        case 4: return launch_rows<T, D, 4>(q, k, v, seq_lens, b, h, g, S, qs, chunk, nsplit, po, pml, st);
+        default: return launch_rows<T, D, 8>(q, k, v, seq_lens, b, h, g, S, qs, chunk, nsplit, po, pml, st);
     }
 }
 
@@ -2489,25 +2505,17 @@ mqa_status run_mfma_rows(const KV &kv, const void *q, const int32_t *seq_lens, i
         // their reads went to HBM again: 956 MB fetched per call for 643 MB
         // with eight tokens on gqa-70b)
         if (ngroups > 1)
-            hipLaunchKernelGGL((streamk_mfma_kernel<D, NWV, KV, MULTI, NHB, true>), dim3(nwg),
-                               dim3(64 * NWV), 0, stream, (const uint16_t *)q, kv, seq_lens, b,
-                               qr, g, S, R, ngroups, qs, k_scale, v_scale, out, po, pml, desc,
-                               err_flags, det);
+            MQA_LAUNCH(streamk_mfma_kernel<D, NWV, KV, MULTI, NHB, true>, dim3(nwg), dim3(64 * NWV), stream, (const uint16_t *)q, kv, seq_lens, b, qr, g, S, R, ngroups, qs, k_scale, v_scale, out, po, pml, desc, err_flags, det);
         else
-            hipLaunchKernelGGL((streamk_mfma_kernel<D, NWV, KV, MULTI, NHB>), dim3(nwg),
-                               dim3(64 * NWV), 0, stream, (const uint16_t *)q, kv, seq_lens, b,
-                               qr, g, S, R, ngroups, qs, k_scale, v_scale, out, po, pml, desc,
-                               err_flags, det);
+            MQA_LAUNCH(streamk_mfma_kernel<D, NWV, KV, MULTI, NHB>, dim3(nwg), dim3(64 * NWV), stream, (const uint16_t *)q, kv, seq_lens, b, qr, g, S, R, ngroups, qs, k_scale, v_scale, out, po, pml, desc, err_flags, det);
         // pieces per cut unit: ~2 when there are more units than work-groups,
         // ~nwg/units when each unit spans many ranges
         constexpr int HPB = 256 / (D / 4);  // head slots per block with one piece lane
         if ((long long)b * g * 4 < nwg)
-            hipLaunchKernelGGL((streamk_combine_kernel<D, 1>), dim3(nwg, R), dim3(256), 0, stream, po,
-                               pml, desc, qc, R, nhb * 16, out);
+            MQA_LAUNCH(streamk_combine_kernel<D, 1>, dim3(nwg, R), dim3(256), stream, po, pml, desc, qc, R, nhb * 16, out);
         else
-            hipLaunchKernelGGL((streamk_combine_kernel<D, HPB>), dim3(nwg, (R + HPB - 1) / HPB),
-                               dim3(256), 0, stream, po, pml, desc, qc, R, nhb * 16, out);
-        return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+            MQA_LAUNCH(streamk_combine_kernel<D, HPB>, dim3(nwg, (R + HPB - 1) / HPB), dim3(256), stream, po, pml, desc, qc, R, nhb * 16, out);
+        return MQA_OK;
     }
     const size_t rows = (size_t)b * T * h * nsplit;
     float *part_o = (float *)workspace;
@@ -2520,18 +2528,12 @@ mqa_status run_mfma_rows(const KV &kv, const void *q, const int32_t *seq_lens, i
     // pair kernel's per-step barrier costs more than its second wave gains)
     if (nhb > 2) {
         const int ng2 = (nhb + 1) / 2;
-        hipLaunchKernelGGL((split_pair_kernel<D, KV, MULTI>), dim3(nsplit, g * ng2, b), dim3(512), 0,
-                           stream, (const uint16_t *)q, kv, seq_lens, qr, g, S, R, ng2, chunk, nsplit,
-                           qs, k_scale, v_scale, part_o, part_ml, err_flags);
+        MQA_LAUNCH(split_pair_kernel<D, KV, MULTI>, dim3(nsplit, g * ng2, b), dim3(512), stream, (const uint16_t *)q, kv, seq_lens, qr, g, S, R, ng2, chunk, nsplit, qs, k_scale, v_scale, part_o, part_ml, err_flags);
     } else {
-        hipLaunchKernelGGL((split_mfma_kernel<D, KV, MULTI, NHB>), dim3(nsplit, g * ngroups, b),
-                           dim3(256), 0, stream, (const uint16_t *)q, kv, seq_lens, qr, g, S, R,
-                           ngroups, chunk, nsplit, qs, k_scale, v_scale, part_o, part_ml, err_flags);
+        MQA_LAUNCH(split_mfma_kernel<D, KV, MULTI, NHB>, dim3(nsplit, g * ngroups, b), dim3(256), stream, (const uint16_t *)q, kv, seq_lens, qr, g, S, R, ngroups, chunk, nsplit, qs, k_scale, v_scale, part_o, part_ml, err_flags);
     }
-    if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
-    launch_combine<D>(dim3(T * h, b), stream, part_o, part_ml, seq_lens, qc, R, S, chunk, nsplit,
-                      out, err_flags);
-    return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+    return launch_combine<D>(dim3(T * h, b), stream, part_o, part_ml, seq_lens, qc, R, S, chunk,
+                             nsplit, out, err_flags);
 }
 
 // (several tokens or a sliding window: the MULTI kernels, with per-row
@@ -2585,6 +2587,7 @@ const char *mqa_status_string(mqa_status s) {
         case MQA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
         case MQA_ERR_WORKSPACE: return "workspace missing or too small";
         case MQA_ERR_HIP: return "HIP launch error";
+        default: break;
     }
     return "unknown status";
 }
@@ -2632,10 +2635,8 @@ mqa_status mqa_append_kv_multi(void *k_cache, void *v_cache, const void *k_new,
     const int threads = 256;
     const long long blocks = (total + threads - 1) / threads;
     if (blocks > 0x7fffffffll) return MQA_ERR_SHAPE;
-    hipLaunchKernelGGL(append_kv_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                       (uint8_t *)k_cache, (uint8_t *)v_cache, (const uint8_t *)k_new,
-                       (const uint8_t *)v_new, seq_lens, b, T, g, S, row_bytes, err_flags);
-    return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+    MQA_LAUNCH(append_kv_kernel, dim3((unsigned)blocks), dim3(threads), stream, (uint8_t *)k_cache, (uint8_t *)v_cache, (const uint8_t *)k_new, (const uint8_t *)v_new, seq_lens, b, T, g, S, row_bytes, err_flags);
+    return MQA_OK;
 }
 
 mqa_status mqa_append_kv(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
@@ -2685,23 +2686,20 @@ mqa_status mqa_decode_attn_kernel(const void *q, const void *k_cache, const void
         return run_mfma<64>(ContigKV<64>{kb, vb, g, S}, q, seq_lens, b, 1, h, g, S, qs, out,
                             workspace, chunk, nsplit, bal, err_flags, stream, nullptr, nullptr, 0,
                             det);
-    } else if (dt == MQA_BF16) {
-        if (d == 128) dispatch_rows<uint16_t, 128>(hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream);
-        else dispatch_rows<uint16_t, 64>(hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream);
-    } else {
-        // fp32 rows of 128 elements need at least two waves per work-group
-        if (d == 128) dispatch_rows<float, 128>(hpw < 2 ? 2 : hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream);
-        else dispatch_rows<float, 64>(hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream);
     }
-    if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
+    if (dt == MQA_BF16)
+        st = d == 128 ? dispatch_rows<uint16_t, 128>(hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream)
+                      : dispatch_rows<uint16_t, 64>(hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream);
+    else  // fp32 rows of 128 elements need at least two waves per work-group
+        st = d == 128 ? dispatch_rows<float, 128>(hpw < 2 ? 2 : hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream)
+                      : dispatch_rows<float, 64>(hpw, q, k_cache, v_cache, seq_lens, b, h, g, S, qs, chunk, nsplit, part_o, part_ml, stream);
+    if (st != MQA_OK) return st;
     const QRows<true> qc{1, h / g, h, 0};
     if (d == 128)
-        launch_combine<128>(dim3(h, b), stream, part_o, part_ml, seq_lens, qc, h / g, S, chunk,
-                            nsplit, out, err_flags);
-    else
-        launch_combine<64>(dim3(h, b), stream, part_o, part_ml, seq_lens, qc, h / g, S, chunk,
-                           nsplit, out, err_flags);
-    return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+        return launch_combine<128>(dim3(h, b), stream, part_o, part_ml, seq_lens, qc, h / g, S,
+                                   chunk, nsplit, out, err_flags);
+    return launch_combine<64>(dim3(h, b), stream, part_o, part_ml, seq_lens, qc, h / g, S, chunk,
+                              nsplit, out, err_flags);
 }
 
 mqa_status mqa_decode_attn(const void *q, const void *k_cache, const void *v_cache,
@@ -2792,11 +2790,8 @@ mqa_status mqa_append_kv_paged_multi(void *k_pages, void *v_pages, const void *k
     const int row_bytes = d * (dt == MQA_BF16 ? 2 : 4);
     const long long total = 2ll * b * T * g * (row_bytes / 16);
     if ((total + 255) / 256 > 0x7fffffffll) return MQA_ERR_SHAPE;
-    hipLaunchKernelGGL(append_kv_paged_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                       stream, (uint8_t *)k_pages, (uint8_t *)v_pages, (const uint8_t *)k_new,
-                       (const uint8_t *)v_new, block_table, seq_lens, b, T, g, page_size, max_pages,
-                       num_pages, row_bytes, err_flags);
-    return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+    MQA_LAUNCH(append_kv_paged_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), stream, (uint8_t *)k_pages, (uint8_t *)v_pages, (const uint8_t *)k_new, (const uint8_t *)v_new, block_table, seq_lens, b, T, g, page_size, max_pages, num_pages, row_bytes, err_flags);
+    return MQA_OK;
 }
 
 mqa_status mqa_append_kv_paged(void *k_pages, void *v_pages, const void *k_new, const void *v_new,
@@ -2869,11 +2864,8 @@ mqa_status launch_append_codes(void *k, void *v, const void *k_new, const void *
         return MQA_ERR_ALIGN;
     const long long total = 2ll * b * T * g * (d / 8);
     if ((total + 255) / 256 > 0x7fffffffll) return MQA_ERR_SHAPE;
-    hipLaunchKernelGGL(append_kv_codes_kernel<I8>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                       stream, (uint8_t *)k, (uint8_t *)v, (const uint16_t *)k_new,
-                       (const uint16_t *)v_new, k_scale, v_scale, bt, seq_lens, b, T, g, S,
-                       max_pages, num_pages, d, err_flags);
-    return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+    MQA_LAUNCH(append_kv_codes_kernel<I8>, dim3((unsigned)((total + 255) / 256)), dim3(256), stream, (uint8_t *)k, (uint8_t *)v, (const uint16_t *)k_new, (const uint16_t *)v_new, k_scale, v_scale, bt, seq_lens, b, T, g, S, max_pages, num_pages, d, err_flags);
+    return MQA_OK;
 }
 
 // sizes of an fp8-cache call (q, k_new, v_new are bf16; the cache rows are
@@ -3109,9 +3101,8 @@ mqa_status mqa_rope_q(void *q, const float *cos_sin, int n_pos, const int32_t *s
     if (!aligned16(q) || !aligned16(cos_sin)) return MQA_ERR_ALIGN;
     const long long total = (long long)b * T * h * (d / 16);
     if ((total + 255) / 256 > 0x7fffffffll) return MQA_ERR_SHAPE;
-    hipLaunchKernelGGL(rope_q_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                       (uint16_t *)q, cos_sin, n_pos, seq_lens, b, T, h, d, err_flags);
-    return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+    MQA_LAUNCH(rope_q_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), stream, (uint16_t *)q, cos_sin, n_pos, seq_lens, b, T, h, d, err_flags);
+    return MQA_OK;
 }
 
 mqa_status mqa_append_kv_rope(void *k_cache, void *v_cache, const void *k_new,
@@ -3127,10 +3118,8 @@ mqa_status mqa_append_kv_rope(void *k_cache, void *v_cache, const void *k_new,
         return MQA_ERR_ALIGN;
     const long long total = (long long)b * T * g * (d / 16);
     if ((total + 255) / 256 > 0x7fffffffll) return MQA_ERR_SHAPE;
-    hipLaunchKernelGGL(append_kv_rope_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                       stream, (uint16_t *)k_cache, (uint16_t *)v_cache, (const uint16_t *)k_new,
-                       (const uint16_t *)v_new, cos_sin, n_pos, seq_lens, b, T, g, S, d, err_flags);
-    return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+    MQA_LAUNCH(append_kv_rope_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), stream, (uint16_t *)k_cache, (uint16_t *)v_cache, (const uint16_t *)k_new, (const uint16_t *)v_new, cos_sin, n_pos, seq_lens, b, T, g, S, d, err_flags);
+    return MQA_OK;
 }
 
 }  // extern "C"
