@@ -8,13 +8,19 @@ Default workload: gqa-70b (b=64, h=64, g=8, d=128, bf16 cache of capacity
 
 Prints one JSON line:
   value        achieved HBM GB/s of the step (algorithmic bytes / step time)
-  ms_per_step  step time (µs/step = 1000 * ms_per_step, also in "us_per_step")
+  ms_per_step  step time (µs/step = 1000 * ms_per_step, also in "us_per_step"):
+               the --steps timed steps back to back, / steps; "trials" cuts the
+               same steps into --trials consecutive trials (events between them)
+               and gives their median and spread
   roofline     for the dominant kernel launch (mqa_decode_attn), timed with
                HIP events on the stream the kernels run on (a second pass over
                the same steps, each behind a spin kernel so that the events
                time the kernels and not Python's issue of the calls)
   cpu_baseline the CPU oracle, timed on the host's cores on a bounded sample
-               (and on one thread, for scale)
+               (and on one thread, for scale): as many threads as the host grants
+               this process (OMP_NUM_THREADS if set, else every CPU of the
+               affinity mask; --cpu-threads overrides), with the rule, nproc,
+               the affinity count and the CPU model string recorded
   graph        the same steps captured once in a HIP graph and replayed: the
                step time without Python's issue of the calls (context; the
                small configurations are bound by that issue time when eager)
@@ -89,8 +95,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa-70b")
     ap.add_argument("--split-chunk", type=int, default=0)
-    ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto",
-                    help="partition kernel (auto: mqa_decode_attn's own choice)")
+    ap.add_argument("--kernel", choices=["auto", "valu", "mfma", "deterministic"], default="auto",
+                    help="partition kernel (auto: mqa_decode_attn's own choice; deterministic: "
+                         "matrix cores, bitwise-reproducible balanced schedule)")
+    ap.add_argument("--trials", type=int, default=5,
+                    help="the timed steps are cut into this many trials (median and spread reported)")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the CPU-oracle baseline (0: the host's CPU share: "
+                         "OMP_NUM_THREADS if set, else every core the process may run on)")
     ap.add_argument("--replicas", type=int, default=0,
                     help="distinct cache copies rotated across steps (0: enough for >= 2 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
@@ -197,7 +209,8 @@ def main() -> int:
     outs = [torch.empty(oshape, dtype=torch.float32, device=dev) for _ in range(reps)]
     err = torch.zeros(1, dtype=torch.int32, device=dev)
 
-    kernel = {"auto": mqa.KERNEL_AUTO, "valu": mqa.KERNEL_VALU, "mfma": mqa.KERNEL_MFMA}[args.kernel]
+    kernel = {"auto": mqa.KERNEL_AUTO, "valu": mqa.KERNEL_VALU, "mfma": mqa.KERNEL_MFMA,
+              "deterministic": mqa.KERNEL_MFMA_DETERMINISTIC}[args.kernel]
     if T > 1:
         schedule = mqa.decode_multi_schedule(w.b, T, w.h, w.g, cap, w.d, w.dtype, args.split_chunk)
     else:
@@ -285,16 +298,21 @@ def main() -> int:
     torch.cuda.synchronize()
     assert int(err.item()) == 0, "device reported an error during warmup"
 
-    # timed region: the step alone
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # timed region: the step alone, exactly args.steps steps, with events at
+    # the boundaries of `trials` consecutive trials (recorded on the stream,
+    # so the steps run back to back as in one pass)
+    ntr = max(1, min(args.trials, args.steps))
+    bounds = [round(i * args.steps / ntr) for i in range(ntr + 1)]
+    tev = [torch.cuda.Event(enable_timing=True) for _ in range(ntr + 1)]
     torch.cuda.synchronize()
-    t_start.record()
-    for k in range(args.steps):
-        step(k)
-    t_end.record()
+    tev[0].record()
+    for i in range(ntr):
+        for k in range(bounds[i], bounds[i + 1]):
+            step(k)
+        tev[i + 1].record()
     torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    ms_per_step = tev[0].elapsed_time(tev[-1]) / args.steps
+    trial_ms = [tev[i].elapsed_time(tev[i + 1]) / (bounds[i + 1] - bounds[i]) for i in range(ntr)]
 
     # timed region again, with HIP events around every decode launch (same
     # stream). A spin kernel queued ahead of each step keeps the GPU busy while
@@ -350,6 +368,10 @@ def main() -> int:
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_step": round(ms_per_step * 1e3, 3),
+        "trials": {"n": ntr, "steps_each": [bounds[i + 1] - bounds[i] for i in range(ntr)],
+                   "median_us_per_step": round(float(np.median(trial_ms)) * 1e3, 3),
+                   "min_us_per_step": round(min(trial_ms) * 1e3, 3),
+                   "max_us_per_step": round(max(trial_ms) * 1e3, 3)},
         "pct_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
@@ -382,6 +404,10 @@ def main() -> int:
             "traffic": traffic,
             "bytes_per_launch": dec_bytes,
             "us_per_launch": round(dec_ms_avg * 1e3, 3),
+            "us_per_launch_median": round(float(np.median(dec_ms)) * 1e3, 3),
+            "us_per_launch_min": round(min(dec_ms) * 1e3, 3),
+            "us_per_launch_max": round(max(dec_ms) * 1e3, 3),
+            "launches_timed": len(dec_ms),
         },
         "cpu_baseline": None,
         "graph": graph,
@@ -391,7 +417,8 @@ def main() -> int:
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, steps_in[0], lens, per_layer, layers,
-                                              args.cpu_seconds, P, T, F8, WIN, I8)
+                                              args.cpu_seconds, P, T, F8, WIN, I8,
+                                              args.cpu_threads)
 
     print(json.dumps(result), flush=True)
     return 0
@@ -484,14 +511,37 @@ def empty_launch_us(torch, n: int = 200):
     return res
 
 
-def cpu_model() -> str:
+def cpu_info() -> dict:
+    """The host's CPU as /proc/cpuinfo and the OS describe it: model name(s)
+    (the full strings), logical CPUs, sockets, and how many of the CPUs this
+    process may run on."""
+    models, sockets = [], set()
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            key, _, val = line.partition(":")
+            key, val = key.strip(), val.strip()
+            if key == "model name" and val not in models:
+                models.append(val)
+            elif key == "physical id":
+                sockets.add(val)
     except OSError:
         pass
-    return "unknown"
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count() or 1
+    return {"model": "; ".join(models) or "unknown", "nproc": os.cpu_count(),
+            "sockets": len(sockets) or None, "affinity": affinity}
+
+
+def cpu_threads(requested: int) -> tuple[int, str]:
+    """Threads for the CPU baseline and the rule that chose them."""
+    if requested > 0:
+        return requested, "--cpu-threads"
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        return int(omp), "OMP_NUM_THREADS (the host's CPU share for this process)"
+    return cpu_info()["affinity"], "every CPU in the process's affinity mask"
 
 
 def spin_cycles(torch, ms: float) -> int:
@@ -511,14 +561,14 @@ def spin_cycles(torch, ms: float) -> int:
 
 
 def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1, F8=False,
-                 window=0, I8=False):
+                 window=0, I8=False, requested_threads=0):
     """The oracle (plain double loops) on the host cores, one layer's step."""
     import numpy as np
 
     import oracle
     import workloads as W
 
-    nthreads = max(1, min(16, os.cpu_count() or 1))
+    nthreads, rule = cpu_threads(requested_threads)
     threads = [nthreads]  # the thread count run() uses (changed for the one-thread pass)
     scale = float(np.float32(1.0 / math.sqrt(w.d)))
     lens32 = lens.astype(np.int32)
@@ -604,7 +654,9 @@ def cpu_baseline(w, t, lens, per_layer_bytes, layers, budget_s, page_size=0, T=1
                   + (f", mean of {reps} passes" if reps > 1 else ""),
         "est_ms_per_step": round(1e3 * (per_layer_bytes * layers) / (gbs * 1e9), 3),
         "one_thread_gbs": round(one_bytes / dt1 / 1e9, 4),
-        "cpu": cpu_model(),
+        "threads": nthreads,
+        "threads_rule": rule,
+        "cpu": cpu_info(),
     }
 
 

@@ -467,3 +467,22 @@ def test_workspace_reused_across_shapes_and_kernels():
             ref, _ = oracle_ref(t)
             compare(out, ref, f"{w.name} rep {rep}")
             big.fill_(0xFF if rep == 0 else 0x7F)
+
+
+def test_err_flags_checked_before_any_launch():
+    """A device err_flags of another dtype, an empty one or a strided one is
+    refused by the binding before anything is enqueued."""
+    w = W.Workload("errflags", b=2, h=8, g=2, d=64, S=64, dtype=torch.bfloat16, seed=93, L=40)
+    t = W.make_step(w, DEV)
+    for bad in (torch.zeros(1, dtype=torch.int64, device=DEV),
+                torch.zeros(0, dtype=torch.int32, device=DEV),
+                torch.zeros(4, dtype=torch.int32, device=DEV)[::2]):
+        with pytest.raises(ValueError):
+            mqa.append_kv(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], t["seq_lens"],
+                          err_flags=bad)
+        with pytest.raises(ValueError):
+            mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], err_flags=bad)
+    ok = torch.zeros(1, dtype=torch.int32, device=DEV)
+    mqa.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], err_flags=ok)
+    torch.cuda.synchronize()
+    assert int(ok.item()) == 0
