@@ -55,6 +55,8 @@ typedef enum {
     MQA_ERR_ALIGN = 4,       /* a tensor pointer not 16-byte aligned */
     MQA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
     MQA_ERR_HIP = 6,         /* the HIP runtime reported a launch error */
+    MQA_ERR_SCRATCH = 7,     /* mqa_decode_attn_noalloc: the call needs more
+                                scratch than the library's array holds */
     /* (the two bounds below only pin each enum of this header to the range
      * of int, so that any int a caller passes is a value of the type: an
      * invalid one then gets the documented error status, where a value
@@ -165,6 +167,27 @@ mqa_status mqa_decode_attn(const void *q, const void *k_cache,
                            float scale, float *out, void *workspace,
                            size_t workspace_bytes, int split_chunk,
                            int32_t *err_flags, hipStream_t stream);
+
+/*
+ * mqa_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc): the
+ * same arguments, kernels and results without the workspace, whose partials
+ * go to a scratch array of 64 MiB that the library holds on each GPU it runs
+ * on until the process ends. The call allocates nothing and uses the current
+ * device's array (`stream` must belong to the current device); the array's
+ * address is looked up once per device, on the first call there (make that
+ * first call outside graph capture). Calls that need more than 64 MiB of
+ * workspace (mqa_decode_workspace_bytes) return MQA_ERR_SCRATCH before
+ * anything is enqueued. Every call on a GPU shares that GPU's array, which
+ * keeps the last call's contents (nothing in it needs to start at zero):
+ * calls that overlap on one GPU (other streams, other host threads) race.
+ */
+mqa_status mqa_decode_attn_noalloc(const void *q, const void *k_cache,
+                                   const void *v_cache, const int32_t *seq_lens,
+                                   int b, int h, int g, int S, int d,
+                                   mqa_dtype dt, float scale, float *out,
+                                   int split_chunk, int32_t *err_flags,
+                                   hipStream_t stream);
 
 /*
  * mqa_decode_attn with an explicit choice of partition kernel; same arguments,

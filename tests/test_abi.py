@@ -49,7 +49,7 @@ def test_schedule_choice():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert mqa.status_string(s)
     assert mqa.status_string(0) == "ok"
     assert "unknown" in mqa.status_string(99)
@@ -392,3 +392,16 @@ def test_err_flags_is_checked_before_any_launch():
                 torch.zeros(0, dtype=torch.int32), [0]):
         with pytest.raises(ValueError):
             mqa._err(bad, like)
+
+
+def test_noalloc_host_errors_need_no_device():
+    """The no-allocation entry point refuses NULL pointers, bad sizes and a call
+    needing more scratch than it holds before any HIP call (no GPU here)."""
+    L = mqa.lib()
+    fake = ctypes.c_void_p(0x10000)
+    args = lambda q=fake, b=4, S=1024: (q, fake, fake, fake, b, 32, 8, S, 128, mqa.BF16,
+                                        ctypes.c_float(0.1), fake, 0, None, None)
+    assert L.mqa_decode_attn_noalloc(*args(q=None)) == mqa.ERR_NULL
+    assert L.mqa_decode_attn_noalloc(*args(b=0)) == mqa.ERR_SHAPE
+    assert mqa.decode_workspace_bytes(4096, 32, 8, 32768, 128, mqa.BF16) > 64 << 20
+    assert L.mqa_decode_attn_noalloc(*args(b=4096, S=32768)) == mqa.ERR_SCRATCH

@@ -51,7 +51,7 @@ __all__ = [
     "decode_multi_workspace_bytes", "decode_multi_schedule", "append_kv_fp8", "decode_attn_fp8",
     "append_kv_paged_fp8", "decode_attn_paged_fp8", "decode_attn_ex", "decode_ex_workspace_bytes",
     "rope_q", "append_kv_rope", "append_kv_int8", "append_kv_paged_int8",
-    "DEVERR_ROPE", "DEVERR_STALL", "FP8_E4M3", "INT8",
+    "DEVERR_ROPE", "DEVERR_STALL", "FP8_E4M3", "INT8", "decode_attn_noalloc",
 ]
 
 # MQA_DECODE_LIB: load another build of the library instead of the in-tree one
@@ -59,7 +59,7 @@ __all__ = [
 LIB_PATH = os.environ.get("MQA_DECODE_LIB") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libmqa_decode.so")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH = range(8)
 F32, BF16, FP8_E4M3, INT8 = 0, 1, 2, 3
 DEVERR_SEQLEN = 1
 DEVERR_PAGE = 2
@@ -77,7 +77,7 @@ EXPORTS = (
     "mqa_decode_attn_paged_multi", "mqa_append_kv_fp8", "mqa_append_kv_paged_fp8",
     "mqa_decode_attn_fp8", "mqa_decode_attn_paged_fp8", "mqa_decode_ex_workspace_bytes",
     "mqa_decode_attn_ex", "mqa_rope_q", "mqa_append_kv_rope", "mqa_append_kv_int8",
-    "mqa_append_kv_paged_int8",
+    "mqa_append_kv_paged_int8", "mqa_decode_attn_noalloc",
 )
 
 
@@ -121,6 +121,9 @@ def _load() -> ctypes.CDLL:
                                          ctypes.c_float, vp, vp, ctypes.c_size_t, i32, vp, i32,
                                          vp]
     L.mqa_decode_attn_kernel.restype = i32
+    L.mqa_decode_attn_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                          ctypes.c_float, vp, i32, vp, vp]
+    L.mqa_decode_attn_noalloc.restype = i32
     L.mqa_decode_schedule.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
     L.mqa_decode_schedule.restype = i32
     L.mqa_status_string.argtypes = [i32]
@@ -335,6 +338,38 @@ def decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         where = "mqa_decode_attn_kernel"
     if st != OK:
         raise MQAError(st, where)
+    return out
+
+
+def decode_attn_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        seq_lens: torch.Tensor, out: torch.Tensor, scale: float | None = None,
+                        split_chunk: int = 0, err_flags: torch.Tensor | None = None) -> torch.Tensor:
+    """decode_attn without a workspace (mqa_decode_attn_noalloc: the library's
+    own scratch on the current device, nothing allocated); `out` (float32
+    [b, h, d]) is the caller's."""
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens),
+                 ("out", out)):
+        _dev(t, n)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [b, h, d]; k_cache and v_cache [b, g, S, d]")
+    b, h, d = q.shape
+    bb, g, S, dd = k_cache.shape
+    if bb != b or dd != d:
+        raise ValueError("q and the caches disagree on b or d")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q and the caches must share one dtype")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (b,):
+        raise ValueError("seq_lens must be int32 [b]")
+    if out.dtype != torch.float32 or out.shape != (b, h, d):
+        raise ValueError("out must be float32 [b, h, d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().mqa_decode_attn_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), b, h,
+                                       g, S, d, _dtype_code(q.dtype), ctypes.c_float(scale),
+                                       _ptr(out), split_chunk, _err(err_flags, q),
+                                       _stream(q.device))
+    if st != OK:
+        raise MQAError(st, "mqa_decode_attn_noalloc")
     return out
 
 

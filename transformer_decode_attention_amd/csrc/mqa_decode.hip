@@ -24,6 +24,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <tuple>
 #include <type_traits>
 #include <utility>
@@ -2574,6 +2575,36 @@ mqa_status check_tokens(int T, int h, int S, mqa_dtype dt) {
     return MQA_OK;
 }
 
+// ---- the scratch of the no-allocation entry point ----
+
+// Partials of mqa_decode_attn_noalloc, in device memory the library owns: a
+// file-scope array, one copy on each GPU the library runs on (held until the
+// process ends). Its size bounds the calls that entry point takes.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// The device address of the current device's copy. Host code must not pass
+// `scratch` itself to a kernel (on the host it names a stand-in, not device
+// memory): its address is looked up once per device, with that device
+// current, on the first call there, and kept.
+constexpr int kMaxDevices = 64;
+void *g_scratch[kMaxDevices];
+hipError_t g_scratch_rc[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+mqa_status scratch_of_current_device(void **ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MQA_ERR_HIP;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        g_scratch_rc[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch[dev] = p;
+    });
+    if (g_scratch_rc[dev] != hipSuccess || !g_scratch[dev]) return MQA_ERR_HIP;
+    *ptr = g_scratch[dev];
+    return MQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2587,6 +2618,8 @@ const char *mqa_status_string(mqa_status s) {
         case MQA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
         case MQA_ERR_WORKSPACE: return "workspace missing or too small";
         case MQA_ERR_HIP: return "HIP launch error";
+        case MQA_ERR_SCRATCH:
+            return "the call needs more scratch than mqa_decode_attn_noalloc holds (64 MiB)";
         default: break;
     }
     return "unknown status";
@@ -2710,6 +2743,22 @@ mqa_status mqa_decode_attn(const void *q, const void *k_cache, const void *v_cac
     return mqa_decode_attn_kernel(q, k_cache, v_cache, seq_lens, b, h, g, S, d, dt, scale, out,
                                   workspace, workspace_bytes, split_chunk, err_flags,
                                   MQA_KERNEL_AUTO, stream);
+}
+
+mqa_status mqa_decode_attn_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                   const int32_t *seq_lens, int b, int h, int g, int S, int d,
+                                   mqa_dtype dt, float scale, float *out, int split_chunk,
+                                   int32_t *err_flags, hipStream_t stream) {
+    // host-detectable errors first, then the size against the scratch array
+    if (!q || !k_cache || !v_cache || !seq_lens || !out) return MQA_ERR_NULL;
+    const mqa_status st = check_sizes(b, h, g, S, d, dt, split_chunk);
+    if (st != MQA_OK) return st;
+    if (workspace_need(b, h, g, S, d, dt, split_chunk, MQA_KERNEL_AUTO) > kScratchBytes)
+        return MQA_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (scratch_of_current_device(&ws) != MQA_OK) return MQA_ERR_HIP;
+    return mqa_decode_attn_kernel(q, k_cache, v_cache, seq_lens, b, h, g, S, d, dt, scale, out, ws,
+                                  kScratchBytes, split_chunk, err_flags, MQA_KERNEL_AUTO, stream);
 }
 
 // ---- several query tokens per sequence ----
