@@ -1603,9 +1603,11 @@ split_pair_kernel(const uint16_t *__restrict__ q, const KV kv, const int32_t *__
 // Work unit u = (sequence i, K/V head j) with n_i = ceil(L_i / 32) steps;
 // units are numbered i-major and their steps laid end to end (T steps in
 // all; sequences with an invalid length contribute none). Work-group w of
-// nwg (one per compute unit) takes steps [w*T/nwg, (w+1)*T/nwg): equal work
-// whatever the lengths (nwg is cut on the device so that every range holds
-// >= kStreamMinSteps steps). Its waves are split into blocks of 16 query
+// nwg (one per compute unit) takes an equal share of the work whatever the
+// lengths (StepSplit: the steps, plus an allowance of C steps per unit for
+// closing its segment where a kernel's segment closes are dear; nwg is cut
+// on the device so that every range holds >= kStreamMinSteps steps). Its
+// waves are split into blocks of 16 query
 // heads; with nhb blocks, each block's waves walk the whole range, so the
 // blocks read each K/V step at about the same time (the second read comes
 // from L2). A unit entirely inside one range is normalised and written to
@@ -1679,13 +1681,51 @@ __device__ __forceinline__ void unit_prefix(const int32_t *__restrict__ seq_lens
     __syncthreads();
 }
 
-// Work-group owning global step x; the first step of work-group w's range.
-__device__ __forceinline__ int owner_of(int x, int T, int nwg) {
-    return (int)((((long long)x + 1) * nwg - 1) / T);
-}
-__device__ __forceinline__ int range_start(int w, int T, int nwg) {
-    return (int)((long long)T * w / nwg);
-}
+// The ranges of the work-groups. Unit (i, j) weighs its n_i steps plus C:
+// laid end to end, unit (i, j) takes the weights [U, U + C + n_i) with
+// U = pre[i] + C g vpre[i] + j (n_i + C), its allowance first, then its
+// steps (step o of the unit at U + C + o); the total is TW = T + C g (valid
+// sequences). Work-group w takes the weights [TW w / nwg, TW (w + 1) / nwg)
+// and with them every step whose weight falls inside (a boundary inside an
+// allowance falls at the unit's first step). A range of at least
+// kStreamMinSteps > C weights holds at least one step. With C = 0 this is the
+// plain equal split of the steps.
+template <int C>
+struct StepSplit {
+    int T, nwg, g, S, Tq, W, b;
+    const int *pre, *vpre, *lens;  // the prefix sums and lengths in LDS
+    __device__ __forceinline__ long long useq(int i) const {  // weight before sequence i
+        return pre[i] + (long long)C * g * vpre[i];
+    }
+    // the first step of work-group w's range (T for w = nwg)
+    __device__ __forceinline__ int start(int w) const {
+        if constexpr (C == 0) {
+            return (int)((long long)T * w / nwg);
+        } else {
+            const long long TW = useq(b);
+            const long long wb = TW * w / nwg;
+            if (wb >= TW) return T;
+            int lo = 0, hi = b;  // useq(lo) <= wb < useq(hi): sequence lo has steps
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (useq(mid) <= wb)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+            const int n = seq_steps(lens[lo], S, Tq, W);
+            const long long off = wb - useq(lo);
+            const int j = (int)(off / (n + C)), o = (int)(off % (n + C));
+            return pre[lo] + j * n + max(0, o - C);
+        }
+    }
+    // the work-group whose range holds step o of unit (i, j), n steps each
+    __device__ __forceinline__ int owner(int i, int j, int n, int o) const {
+        const long long TW = useq(b);
+        const long long x = useq(i) + (long long)j * (n + C) + C + o;
+        return (int)(((x + 1) * nwg - 1) / TW);
+    }
+};
 
 // Flags between the waves of one work-group, in LDS. A flag is written after
 // the data it guards has left the wave (lgkmcnt drained), and the data is read
@@ -1787,7 +1827,14 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
         if (threadIdx.x == 0) cut_desc[wg] = make_int4(-1, 0, 0, 0);
         return;
     }
-    const int x0 = range_start(wg, T, nwg), x1 = range_start(wg + 1, T, nwg);
+    // a unit's allowance (in steps) for closing its segment, chosen by
+    // measurement: the closes of the kernels with two blocks per wave or a
+    // one-byte cache cost one to three steps' time each, those of the
+    // one-block bf16 kernel under half a step (no allowance)
+    constexpr int kSegC = KV::kF8 ? 4 : NHB == 2 ? (SHARED ? 6 : 3) : 0;
+    const StepSplit<kSegC> split{T, nwg, g, S, qr.T, qr.W, b, pre, vpre, lens};
+    const int x0 = __builtin_amdgcn_readfirstlane(split.start(wg));
+    const int x1 = __builtin_amdgcn_readfirstlane(split.start(wg + 1));
 
     // paged: the page ids of both halves of the range's steps, in step order
     // (entry 2 (x - x0) + half), published by the barrier below
@@ -1842,7 +1889,8 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
     if (threadIdx.x == 0)
         cut_desc[wg] = (u0_last >= x0 && u0_last + n_last > x1)
                            ? make_int4(i_last, (u0_last - p_last) / n_last,
-                                       owner_of(u0_last + n_last - 1, T, nwg), u0_last > x0 ? 1 : 0)
+                                       split.owner(i_last, (u0_last - p_last) / n_last, n_last, n_last - 1),
+                                       u0_last > x0 ? 1 : 0)
                            : make_int4(-1, 0, 0, 0);
 
     const int lane = threadIdx.x & 63;
