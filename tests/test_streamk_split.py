@@ -5,8 +5,9 @@ steps for closing its segment; the units are laid end to end, the allowance
 before the steps, and work-group w takes the weights [TW w / nwg,
 TW (w + 1) / nwg) of the total TW, with every step whose weight falls inside
 (a boundary inside an allowance falls at the unit's first step). The kernel
-(StepSplit in the HIP source) computes the first step of a range by a binary
-search over the per-sequence prefix sums, and the range that holds a given
+(StepSplit in the HIP source) finds the sequence that holds a range's end
+(here by a binary search over the per-sequence prefix sums, there by every
+thread checking its share of the sequences) and the range that holds a given
 step by the inverse formula; this model restates both and checks, over random
 ragged batches with invalid lengths among them, that
   * the ranges cover the steps in order, each exactly once, none empty

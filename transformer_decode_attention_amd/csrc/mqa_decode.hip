@@ -1697,27 +1697,15 @@ struct StepSplit {
     __device__ __forceinline__ long long useq(int i) const {  // weight before sequence i
         return pre[i] + (long long)C * g * vpre[i];
     }
-    // the first step of work-group w's range (T for w = nwg)
-    __device__ __forceinline__ int start(int w) const {
-        if constexpr (C == 0) {
-            return (int)((long long)T * w / nwg);
-        } else {
-            const long long TW = useq(b);
-            const long long wb = TW * w / nwg;
-            if (wb >= TW) return T;
-            int lo = 0, hi = b;  // useq(lo) <= wb < useq(hi): sequence lo has steps
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (useq(mid) <= wb)
-                    lo = mid;
-                else
-                    hi = mid;
-            }
-            const int n = seq_steps(lens[lo], S, Tq, W);
-            const long long off = wb - useq(lo);
-            const int j = (int)(off / (n + C)), o = (int)(off % (n + C));
-            return pre[lo] + j * n + max(0, o - C);
-        }
+    // the weight where work-group w's range begins (the total for w = nwg)
+    __device__ __forceinline__ long long wstart(int w) const { return useq(b) * w / nwg; }
+    // the first step at or after weight wb, for the sequence i that holds it
+    // (useq(i) <= wb < useq(i + 1): a sequence with steps)
+    __device__ __forceinline__ int step_in(int i, long long wb) const {
+        const int n = seq_steps(lens[i], S, Tq, W);
+        const long long off = wb - useq(i);
+        const int j = (int)(off / (n + C)), o = (int)(off % (n + C));
+        return pre[i] + j * n + max(0, o - C);
     }
     // the work-group whose range holds step o of unit (i, j), n steps each
     __device__ __forceinline__ int owner(int i, int j, int n, int o) const {
@@ -1797,6 +1785,7 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
     __shared__ uint32_t rec_val[4][kRing];     // (steps done << 8) | waves (bit per wave of the block)
     __shared__ int cursor[4];                  // steps of the range claimed so far, per head group
     __shared__ int first_seq, last_seq;        // sequences holding the range's first and last steps
+    __shared__ int range_end[2];               // the range's first step and the next range's
     __shared__ int broken;                     // 1 once a wait between waves ran out (lds_flag_wait)
     __shared__ int pre[kStreamMaxSeq + 1];     // steps before sequence i
     __shared__ int vpre[kStreamMaxSeq + 1];    // valid sequences before sequence i
@@ -1833,8 +1822,24 @@ streamk_mfma_kernel(const uint16_t *__restrict__ q, const KV kv,
     // one-block bf16 kernel under half a step (no allowance)
     constexpr int kSegC = KV::kF8 ? 4 : NHB == 2 ? (SHARED ? 6 : 3) : 0;
     const StepSplit<kSegC> split{T, nwg, g, S, qr.T, qr.W, b, pre, vpre, lens};
-    const int x0 = __builtin_amdgcn_readfirstlane(split.start(wg));
-    const int x1 = __builtin_amdgcn_readfirstlane(split.start(wg + 1));
+    int x0, x1;
+    if constexpr (kSegC == 0) {
+        x0 = (int)((long long)T * wg / nwg);
+        x1 = (int)((long long)T * (wg + 1) / nwg);
+    } else {
+        // the sequences that hold the range's two ends, every thread checking
+        // its share of the sequences at once
+        const long long wb0 = split.wstart(wg), wb1 = split.wstart(wg + 1);
+        for (int i = threadIdx.x; i < b; i += 64 * NW) {
+            const long long u0 = split.useq(i), u1 = split.useq(i + 1);
+            if (u0 <= wb0 && wb0 < u1) range_end[0] = split.step_in(i, wb0);
+            if (u0 <= wb1 && wb1 < u1) range_end[1] = split.step_in(i, wb1);
+        }
+        if (threadIdx.x == 0 && wb1 >= split.useq(b)) range_end[1] = T;
+        __syncthreads();
+        x0 = __builtin_amdgcn_readfirstlane(range_end[0]);
+        x1 = __builtin_amdgcn_readfirstlane(range_end[1]);
+    }
 
     // paged: the page ids of both halves of the range's steps, in step order
     // (entry 2 (x - x0) + half), published by the barrier below
