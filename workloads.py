@@ -33,9 +33,12 @@ lengths raised to at least T.
 
 fp8 caches (make_fp8_step): codes drawn bit by bit on the device, not
 converted from values: sign uniform, exponent field 7 + round(N(0, 1.5))
-clipped to [1, 14] (magnitudes around 1, as quantised N(0, 1) data),
-mantissa uniform (stream +11); per-K/V-head scales U[0.25, 1] for K and for
-V (stream +12, CPU); q and the new rows as above (bf16).
+clipped to [0, 15] (magnitudes around 1, as quantised N(0, 1) data, with
+subnormals and the top binade among them), mantissa uniform, the NaN pattern
+(exponent 15, mantissa 7) moved to mantissa 6 (stream +11); per-K/V-head
+scales U[0.25, 1] for K and for V (stream +12, CPU); q and the new rows as
+above (bf16). int8 caches (make_int8_step): codes N(0, 32) rounded and
+clamped to -128 .. 127 (stream +13), scales U[1/48, 1/24] (stream +14).
 
 Paged variants (make_paged_step): the same values scattered into pages of
 page_size rows with page ids drawn as a random permutation (CPU generator,
