@@ -86,7 +86,7 @@ def check_case(w: W.Workload, split_chunk: int = 0, layer: int = 0, q_scale: flo
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", ["tiny-mqa", "mqa-1k", "gqa-70b", "gqa-70b-full", "gqa-70b-tp8",
-                                  "mqa-32k"])
+                                  "gqa-70b-dp8", "mqa-32k"])
 def test_workload_full_size(name):
     print(check_case(W.WORKLOADS[name]), flush=True)
 
