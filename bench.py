@@ -79,11 +79,40 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 SRC = os.path.join(ROOT, "transformer_decode_attention_amd", "csrc", "mqa_decode.hip")
 
 
+def code_text(src: str) -> str:
+    """C++ source without its comments: // and /* */ comments outside string
+    and character literals removed, trailing blanks cut, empty lines dropped.
+    What the compiler turns into code is left as it is, so editing, adding or
+    removing a comment leaves this text unchanged and any other edit does not."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":  # a literal, up to its unescaped closing quote
+            j = i + 1
+            while j < n and src[j] != c and src[j] != "\n":
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (ln.rstrip() for ln in "".join(out).split("\n"))
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_sha() -> str:
-    """Hash of what the library is built from: the kernel source and the
-    compiler flags (a traffic record taken on another build is not reported)."""
+    """Hash of what the library is built from: the kernel source's code (its
+    comments left out, since they build to nothing) and the compiler flags.
+    A traffic record taken on another build is not reported."""
     from transformer_decode_attention_amd import build
-    h = hashlib.sha256(open(SRC, "rb").read())
+    h = hashlib.sha256(code_text(open(SRC, encoding="utf-8").read()).encode())
     h.update(" ".join(build.FLAGS).encode())
     return h.hexdigest()[:16]
 

@@ -1,9 +1,9 @@
 """The rocprofv3 summaries under profiles/ belong to the library as built now.
 
 Every kernel-duration summary, traffic record and counter table names the
-hash of the kernel source and compiler flags it was taken on (bench.py's
-source_sha); the bench reports a traffic record only while that hash is
-unchanged. These checks fail as soon as the kernels change without the
+hash of the kernel source's code (comments left out) and compiler flags it
+was taken on (bench.py's source_sha); the bench reports a traffic record only
+while that hash is unchanged. These checks fail as soon as the kernels change without the
 profiles being taken again, and check that each summary carries the
 command that produced it (a rocprofv3 run of bench.py).
 """
@@ -57,3 +57,38 @@ def test_design_notes_quote_the_current_build():
     text = open(os.path.join(ROOT, "DESIGN.md"), encoding="utf-8").read()
     quoted = set(re.findall(r"build hash `([0-9a-f]{16})`", text))
     assert quoted == {bench.source_sha()}, quoted
+
+
+def test_hash_ignores_comments_and_nothing_else():
+    """The hash leaves out what builds to nothing: comments of either form,
+    comment-only lines, trailing blanks. Any edit of the code, of a literal
+    (also one that holds comment markers) or of the indentation changes it."""
+    base = (
+        '#include "x.h"  // header\n'
+        "/* block\n   comment */\n"
+        "__global__ void k(int *p) {\n"
+        '    asm volatile("s_nop 0 // not a comment" ::: "memory");\n'
+        "    p[0] = 3; /* inline */ p[1] = '/';\n"
+        "}\n"
+    )
+    same = [
+        base.replace("// header", "// another header"),
+        base.replace("/* block\n   comment */", "// one line now"),
+        base.replace("/* inline */", "/* a longer\n inline comment */"),
+        base.replace("{\n", "{  // opens\n\n// a new comment line\n"),
+        base.replace("}\n", "}   \n"),
+    ]
+    differ = [
+        base.replace("p[0] = 3", "p[0] = 4"),
+        base.replace("// not a comment", "// still not one"),
+        base.replace("'/'", "'*'"),
+        base.replace("    p[0]", "  p[0]"),
+        base.replace('"x.h"', '"y.h"'),
+    ]
+    ref = bench.code_text(base)
+    assert "// not a comment" in ref and "'/'" in ref
+    assert "header" not in ref and "block" not in ref and "inline" not in ref
+    for s in same:
+        assert bench.code_text(s) == ref, s
+    for s in differ:
+        assert bench.code_text(s) != ref, s
