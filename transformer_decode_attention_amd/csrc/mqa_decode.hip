@@ -6,18 +6,40 @@
 // G = h/g query heads per K/V head and j = hq / G (§五),
 //   out[i,hq,:] = softmax_t(scale * q[i,hq,:] . K[i,j,t,:]) V[i,j,t,:],  t < L_i.
 //
-// Kernels
-//   append_kv_kernel     one 16-byte chunk per thread, bit copy.
-//   split_rows_kernel    one work-group per (partition of the sequence, K/V head,
-//                        block of up to 8 query heads, sequence). The K and V
-//                        tiles of 64 cache rows are copied global->LDS with
-//                        128-bit DMA loads, read from HBM once, and reused by
-//                        every query head of the group. Scores: one wave per
-//                        query head, one lane per cache row, bf16 dot2 FMAs.
-//                        Online softmax (running max / sum) per head; P.V with
-//                        fp32 FMAs, each lane owning one 16-byte column chunk.
-//                        Writes the partition's (max, sum, unnormalised o).
-//   combine_kernel       log-sum-exp merge of the partitions into out.
+// Kernels, in the order of this file
+//   append_kv_kernel, append_kv_paged_kernel
+//                        the step's new K/V rows into a contiguous or paged
+//                        bf16/fp32 cache: one 16-byte chunk per thread, bit copy.
+//   append_kv_codes_kernel
+//                        the same into a one-byte cache: each value divided by
+//                        its K/V head's scale and rounded to an e4m3 or int8 code.
+//   rope_q_kernel, append_kv_rope_kernel
+//                        rotary position embedding of the query rows in place,
+//                        and of the keys on their way into the cache.
+//   split_rows_kernel    vector-ALU decode (fp32 caches, and bf16 when the caller
+//                        asks for it): one work-group per (partition, K/V head,
+//                        block of query heads, sequence); 64-row K/V tiles go
+//                        global->LDS by DMA and serve every query head of the
+//                        group; one lane per cache row for the scores, one
+//                        16-byte column chunk per lane for P.V.
+//   split_mfma_kernel    matrix-core decode over fixed partitions (bf16 or
+//                        one-byte caches): scores as K.Q^T and P.V with
+//                        v_mfma_f32_16x16x32_bf16, 32 cache rows per step, the
+//                        unit's query rows in blocks of 16, online softmax in
+//                        the accumulator layout; writes per-partition partials.
+//   split_pair_kernel    the same for units of more than 16 query rows: pairs of
+//                        waves share each loaded step through LDS.
+//   streamk_mfma_kernel  the balanced schedule (many ragged units): one
+//                        work-group per compute unit takes an equal share of all
+//                        units' steps, its waves claiming steps from an LDS
+//                        counter; writes out directly, and partials only for
+//                        the units cut between two shares.
+//   streamk_combine_kernel
+//                        merges the pieces of those cut units into out.
+//   combine_kernel       log-sum-exp merge of the fixed partitions into out.
+// Decode runs split_rows_kernel or split_mfma/split_pair_kernel followed by
+// combine_kernel, or streamk_mfma_kernel followed by streamk_combine_kernel;
+// which one is decided on the host from the shapes (use_streamk below).
 //
 // Everything is enqueued on the caller's stream; nothing is allocated here.
 
