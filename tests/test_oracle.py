@@ -14,7 +14,6 @@ that they are caught.
 from __future__ import annotations
 
 import json
-import math
 import os
 import re
 import subprocess
