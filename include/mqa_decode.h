@@ -18,9 +18,11 @@
  *
  * Conventions shared by every entry point
  *  - Tensors are contiguous, row-major, last index fastest, in device memory
- *    owned by the caller. The library allocates nothing, keeps no global
- *    state and never synchronises: work is enqueued on `stream` (a
- *    hipStream_t; NULL is the default stream) and completes in stream order.
+ *    owned by the caller. The library allocates nothing and never
+ *    synchronises: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *    default stream) and completes in stream order. Its only global state is
+ *    mqa_decode_attn_noalloc's scratch array and that array's address per
+ *    device (see there); every other call keeps none.
  *  - Element type `dt` applies to q, k_cache, v_cache, k_new and v_new.
  *    MQA_BF16 is bfloat16 (upper 16 bits of a binary32). Outputs are fp32.
  *  - d (head dimension) is 64 or 128. Every tensor pointer must be 16-byte
