@@ -92,3 +92,46 @@ def test_hash_ignores_comments_and_nothing_else():
         assert bench.code_text(s) == ref, s
     for s in differ:
         assert bench.code_text(s) != ref, s
+
+
+def _summary(tag: str) -> dict:
+    text = open(os.path.join(PROF, f"decode_{tag}_kernel_stats.md"), encoding="utf-8").read()
+    m = re.search(r"kernel time median ([\d.]+) µs \(mean [\d.]+; main kernel ([\d.]+) \+ merge kernel ([\d.]+)\)",
+                  text)
+    b = re.search(r"Algorithmic bytes per call ([\d,]+): [\d.]+ GB/s over the kernel time \(([\d.]+) of 8 TB/s\)",
+                  text)
+    s = re.search(r"schedule ([a-z-]+)", text)
+    assert m and b and s, tag
+    return {"call": float(m.group(1)), "main": float(m.group(2)), "merge": float(m.group(3)),
+            "bytes": int(b.group(1).replace(",", "")), "frac": float(b.group(2)), "schedule": s.group(1)}
+
+
+def test_design_results_table_matches_the_summaries():
+    """Every row of the design notes' results table quotes its profile summary
+    as rounded there: kernel µs (main + merge), algorithmic MB, frac, the
+    schedule and, where a traffic record exists, FETCH / algorithmic bytes;
+    and every kernel-duration summary has its row."""
+    text = open(os.path.join(ROOT, "DESIGN.md"), encoding="utf-8").read()
+    row = re.compile(r"^\| [^|]+ \| ([a-z-]+) \| ([\d,.]+) \| ([\d.]+) \(([\d.]+) \+ ([\d.]+)\) \| ([\d.]+) \| "
+                     r"([\d.]+|–) \| `([\w-]+)` \|$", re.M)
+    rows = row.findall(text)
+    assert len(rows) >= 40
+    seen = set()
+    for sched, mb, call, main, merge, frac, fetch, tag in rows:
+        s = _summary(tag)
+        seen.add(tag)
+        assert sched == s["schedule"], tag
+        assert abs(float(mb.replace(",", "")) - s["bytes"] / 1e6) <= 0.051, (tag, mb)
+        for quoted, key in ((call, "call"), (main, "main"), (merge, "merge")):
+            assert abs(float(quoted) - s[key]) <= 0.051, (tag, key, quoted, s[key])
+        assert abs(float(frac) - s["frac"]) <= 0.00051 + 1e-9, (tag, frac, s["frac"])
+        tf = os.path.join(PROF, f"decode_{tag}_traffic.json")
+        if fetch == "–":
+            assert not os.path.exists(tf), tag
+        else:
+            rec = json.load(open(tf))
+            ratio = rec["fetch_bytes_per_launch"] / rec["algorithmic_bytes_per_launch"]
+            assert abs(float(fetch) - ratio) <= 0.00051, (tag, fetch, ratio)
+    stats = {os.path.basename(f)[len("decode_"):-len("_kernel_stats.md")]
+             for f in glob.glob(os.path.join(PROF, "decode_*_kernel_stats.md"))}
+    assert stats == seen, stats ^ seen
