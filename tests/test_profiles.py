@@ -135,3 +135,22 @@ def test_design_results_table_matches_the_summaries():
     stats = {os.path.basename(f)[len("decode_"):-len("_kernel_stats.md")]
              for f in glob.glob(os.path.join(PROF, "decode_*_kernel_stats.md"))}
     assert stats == seen, stats ^ seen
+
+
+def test_status_table_quotes_results_table_values():
+    """The status table at the top of the design notes repeats figures of the
+    results table: every three-decimal fraction and every µs figure in it is
+    one of the results table's fracs or call times (as rounded there)."""
+    text = open(os.path.join(ROOT, "DESIGN.md"), encoding="utf-8").read()
+    status = text[text.index("**Status at a glance**"):text.index("Rocprofv3 summaries:")]
+    row = re.compile(r"^\| [^|]+ \| [a-z-]+ \| [\d,.]+ \| ([\d.]+) \([\d.]+ \+ [\d.]+\) \| ([\d.]+) \| "
+                     r"(?:[\d.]+|–) \| `[\w-]+` \|$", re.M)
+    calls, fracs = set(), set()
+    for call, frac in row.findall(text):
+        calls.add(call)
+        fracs.add(frac)
+    quoted_fracs = re.findall(r"(?<![\d.])(0\.\d{3})(?![\d])", status)
+    quoted_us = re.findall(r"(\d+\.\d) µs", status)
+    assert quoted_fracs and quoted_us
+    assert set(quoted_fracs) <= fracs, set(quoted_fracs) - fracs
+    assert set(quoted_us) <= calls, set(quoted_us) - calls
