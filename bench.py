@@ -77,6 +77,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 SRC = os.path.join(ROOT, "transformer_decode_attention_amd", "csrc", "mqa_decode.hip")
+HEADER = os.path.join(ROOT, "include", "mqa_decode.h")  # included by SRC: its constants build into the kernels
 
 
 def code_text(src: str) -> str:
@@ -108,11 +109,15 @@ def code_text(src: str) -> str:
 
 
 def source_sha() -> str:
-    """Hash of what the library is built from: the kernel source's code (its
-    comments left out, since they build to nothing) and the compiler flags.
-    A traffic record taken on another build is not reported."""
+    """Hash of what the library is built from: the code of the kernel source
+    and of the C header it includes (comments left out, since they build to
+    nothing) and the compiler flags. A traffic record taken on another build
+    is not reported."""
     from transformer_decode_attention_amd import build
-    h = hashlib.sha256(code_text(open(SRC, encoding="utf-8").read()).encode())
+    h = hashlib.sha256()
+    for path in (SRC, HEADER):
+        h.update(code_text(open(path, encoding="utf-8").read()).encode())
+        h.update(b"\0")
     h.update(" ".join(build.FLAGS).encode())
     return h.hexdigest()[:16]
 

@@ -1,9 +1,9 @@
 """The rocprofv3 summaries under profiles/ belong to the library as built now.
 
 Every kernel-duration summary, traffic record and counter table names the
-hash of the kernel source's code (comments left out) and compiler flags it
-was taken on (bench.py's source_sha); the bench reports a traffic record only
-while that hash is unchanged. These checks fail as soon as the kernels change without the
+hash of the code of the kernel source and its C header (comments left out)
+and of the compiler flags it was taken on (bench.py's source_sha); the bench
+reports a traffic record only while that hash is unchanged. These checks fail as soon as the kernels change without the
 profiles being taken again, and check that each summary carries the
 command that produced it (a rocprofv3 run of bench.py).
 """
