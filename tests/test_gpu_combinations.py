@@ -1,6 +1,7 @@
 """Parity over seeded random combinations of every option.
 
-Forty cases (MQA_COMBO_CASES) drawn from a fixed seed (MQA_COMBO_SEED):
+Forty cases (MQA_COMBO_CASES) drawn from a fixed seed (MQA_COMBO_SEED), with
+MQA_COMBO_LARGE=1 at larger capacities and batches:
 head dimension, K/V heads and group size, query tokens, cache type (bf16,
 fp8 or int8 codes), layout (contiguous or pages of 16 or 32 rows), sliding
 window, automatic or fixed partitions, batch and ragged lengths. Each runs the matching append and the general
@@ -28,7 +29,10 @@ DEV = "cuda:0"
 NTHREADS = min(16, os.cpu_count() or 1)
 
 
-def draw_cases(n=40, seed=2024):
+def draw_cases(n=40, seed=2024, large=False):
+    """With large, capacities up to 5000 and batches up to 256 (halved while
+    the oracle's multiply-adds would pass ~4e9, a few seconds per case, or a
+    cache tensor 2e8 elements)."""
     rng = random.Random(seed)
     cases = []
     for k in range(n):
@@ -38,10 +42,12 @@ def draw_cases(n=40, seed=2024):
         T = rng.choice([1, 1, 2, 3, 5])
         kv = rng.choice(["bf16", "fp8", "int8"])
         P = rng.choice([0, 0, 16, 32])
-        S = rng.randint(max(T, 8), 700)
-        b = rng.choice([1, 3, 17, 48, 96])
+        S = rng.randint(max(T, 8), 5000 if large else 700)
+        b = rng.choice([32, 64, 128, 256] if large else [1, 3, 17, 48, 96])
         window = rng.choice([0, 0, 1, rng.randint(2, 400)])
         chunk = rng.choice([0, 0, 64, 256])
+        while large and b > 1 and (b * S * g * G * d * T > 4e9 or b * S * g * d > 2e8):
+            b //= 2
         cases.append((k, d, g, G, T, kv, P, S, b, window, chunk))
     return cases
 
@@ -89,7 +95,8 @@ def host(x, kv):
 
 
 CASES = draw_cases(int(os.environ.get("MQA_COMBO_CASES", "40")),
-                   int(os.environ.get("MQA_COMBO_SEED", "2024")))
+                   int(os.environ.get("MQA_COMBO_SEED", "2024")),
+                   os.environ.get("MQA_COMBO_LARGE", "0") == "1")
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"case{c[0]}")
