@@ -52,7 +52,8 @@ typedef enum {
     MQA_OK = 0,
     MQA_ERR_NULL = 1,        /* a required pointer is NULL */
     MQA_ERR_SHAPE = 2,       /* a size < 1, h not a multiple of g, b > 65535,
-                                or one K/V head's S rows (S*d*elem) >= 2 GiB */
+                                g*h > 2^30, or one K/V head's S rows
+                                (S*d*elem) >= 2 GiB */
     MQA_ERR_UNSUPPORTED = 3, /* d not 64/128, unknown dtype, bad split_chunk */
     MQA_ERR_ALIGN = 4,       /* a tensor pointer not 16-byte aligned */
     MQA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
